@@ -1,0 +1,149 @@
+"""Python face of the C reference oracle (ref_norm.c).
+
+TEST INFRASTRUCTURE ONLY: the float64 CPU definition of LayerNorm and RMSNorm
+that the GPU kernels are checked against.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import this package.  It imports nothing from the HIP library's package and
+the library imports nothing from here.
+
+Functions take and return numpy arrays (float32 in, float32 out, plus the
+float64 statistics the pins inspect).  The arithmetic itself lives in the C
+file; this module only marshals arguments.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIBS: dict[str, ctypes.CDLL] = {}
+
+_F32P = ctypes.POINTER(ctypes.c_float)
+_F64P = ctypes.POINTER(ctypes.c_double)
+
+
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
+    lib.oracle_layernorm_f64.restype = None
+    lib.oracle_layernorm_f64.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p,
+    ]
+    lib.oracle_rmsnorm_f64.restype = None
+    lib.oracle_rmsnorm_f64.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+    ]
+    lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_plant.restype = ctypes.c_int
+    return lib
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load (building first if absent) the oracle library at ``path``."""
+    path = path or _build.LIB
+    if path not in _LIBS:
+        if not os.path.exists(path):
+            if path != _build.LIB:
+                raise FileNotFoundError(path)
+            _build.build()
+        _LIBS[path] = _bind(ctypes.CDLL(path))
+    return _LIBS[path]
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data
+
+
+def _f32(a, name: str) -> np.ndarray:
+    a = np.asarray(a)
+    if a.dtype != np.float32:
+        raise TypeError(f"{name} must be float32, got {a.dtype}")
+    return np.ascontiguousarray(a)
+
+
+def layernorm(x, gamma, beta, eps: float = 1e-5, lib: ctypes.CDLL | None = None,
+              out: np.ndarray | None = None):
+    """LayerNorm of each row of ``x`` [rows, d].
+
+    Returns ``(y, mean, rstd, mean64, var64)``: y/mean/rstd rounded once to
+    float32, mean64/var64 the float64 statistics before rounding.  ``eps`` is
+    taken as the float32 value the GPU receives and widened exactly.
+    """
+    lib = lib or load()
+    x = _f32(x, "x")
+    if x.ndim != 2:
+        raise ValueError("x must be 2-D [rows, d]")
+    rows, d = x.shape
+    gamma = _f32(gamma, "gamma").reshape(-1)
+    beta = _f32(beta, "beta").reshape(-1)
+    if d < 1 or gamma.size != d or beta.size != d:
+        raise ValueError("need d >= 1 and gamma, beta of length d")
+    y = np.empty_like(x) if out is None else out
+    mean = np.empty(rows, np.float32)
+    rstd = np.empty(rows, np.float32)
+    mean64 = np.empty(rows, np.float64)
+    var64 = np.empty(rows, np.float64)
+    lib.oracle_layernorm_f64(_ptr(x), _ptr(gamma), _ptr(beta), rows, d,
+                             float(np.float32(eps)), _ptr(y), _ptr(mean),
+                             _ptr(rstd), _ptr(mean64), _ptr(var64))
+    return y, mean, rstd, mean64, var64
+
+
+def rmsnorm(x, w, eps: float = 1e-5, lib: ctypes.CDLL | None = None,
+            out: np.ndarray | None = None):
+    """RMSNorm of each row of ``x`` [rows, d].
+
+    Returns ``(y, rstd, ms64)``: y/rstd rounded once to float32, ms64 the
+    float64 mean of squares before rounding.
+    """
+    lib = lib or load()
+    x = _f32(x, "x")
+    if x.ndim != 2:
+        raise ValueError("x must be 2-D [rows, d]")
+    rows, d = x.shape
+    w = _f32(w, "w").reshape(-1)
+    if d < 1 or w.size != d:
+        raise ValueError("need d >= 1 and w of length d")
+    y = np.empty_like(x) if out is None else out
+    rstd = np.empty(rows, np.float32)
+    ms64 = np.empty(rows, np.float64)
+    lib.oracle_rmsnorm_f64(_ptr(x), _ptr(w), rows, d, float(np.float32(eps)),
+                           _ptr(y), _ptr(rstd), _ptr(ms64))
+    return y, rstd, ms64
+
+
+def set_threads(n: int, lib: ctypes.CDLL | None = None) -> None:
+    (lib or load()).oracle_set_threads(int(n))
+
+
+def max_threads(lib: ctypes.CDLL | None = None) -> int:
+    return int((lib or load()).oracle_max_threads())
+
+
+def tolerance_ok(got, ref, atol: float = 1e-5, rtol: float = 1e-4):
+    """Elementwise acceptance used throughout: |got - ref| <= atol + rtol*|ref|.
+
+    The bound is the one stated on "RMSNorm on an RTX 5070" (section
+    "Correctness before timing").  Any NaN/Inf in ``got`` fails.  Returns
+    ``(ok, max_abs_err, max_ratio)`` where max_ratio is the worst
+    err / bound.
+    """
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if got.shape != ref.shape:
+        return False, float("inf"), float("inf")
+    if got.size == 0:
+        return True, 0.0, 0.0
+    if not np.all(np.isfinite(got)) or not np.all(np.isfinite(ref)):
+        return False, float("inf"), float("inf")
+    err = np.abs(got - ref)
+    bound = atol + rtol * np.abs(ref)
+    ratio = err / bound
+    return bool(np.all(err <= bound)), float(err.max()), float(ratio.max())

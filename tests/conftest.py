@@ -1,0 +1,20 @@
+"""Shared pytest set-up: the ``gpu`` marker and import paths.
+
+Tests marked ``gpu`` need a real gfx950 device and call the HIP library
+through its C ABI; everything else runs on the CPU.
+"""
+from __future__ import annotations
+
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+HERE = os.path.dirname(os.path.abspath(__file__))
+if HERE not in sys.path:
+    sys.path.insert(0, HERE)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; calls the HIP library")

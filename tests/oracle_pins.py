@@ -1,0 +1,308 @@
+"""Checks that pin the CPU oracle to facts outside itself.
+
+Each ``check_*`` takes an oracle library handle (``oracle.load(path)``) and
+raises AssertionError when the oracle disagrees with:
+
+* exact rational brute force on tiny inputs (Fraction statistics, 60-digit
+  Decimal root), which is the definition evaluated without rounding;
+* torch's float64 CPU LayerNorm / RMSNorm library routines, an independent
+  implementation of the same definitions;
+* closed forms (zero rows, width 1, alternating +-1, constant rows);
+* invariants (shift and power-of-two scale invariance, column and row
+  permutation equivariance, unit-affine output moments, in-place equality).
+
+The definitions pinned are the statistics equation of "Rewriting the layer
+norm and matmul kernels" (section "A reduction has to meet somewhere") with a
+per-column scale and bias and eps inside the root, and the RMSNorm equation of
+"RMSNorm on an RTX 5070" (section "The operator and the change").
+
+tests/test_oracle_pins.py runs every check on the shipped oracle;
+tests/test_negative_controls.py runs them on builds with a planted mistake
+and requires each mistake to be caught.
+"""
+from __future__ import annotations
+
+import math
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+from row_wise_normalization_layernorm_amd import workloads as wl
+
+EPS32 = np.float32(wl.EPS)
+
+
+# ----------------------------------------------------------------------------
+# small helpers (no normalization arithmetic beyond the exact brute force)
+
+def _ulps(a, b) -> np.ndarray:
+    """Distance in float32 units in the last place between arrays a and b."""
+    a = np.asarray(a, np.float32).astype(np.float64)
+    b = np.asarray(b, np.float32).astype(np.float64)
+    scale = np.spacing(np.maximum(np.abs(a), np.abs(b)).astype(np.float32)).astype(np.float64)
+    scale = np.maximum(scale, np.float64(np.finfo(np.float32).smallest_subnormal))
+    return np.abs(a - b) / scale
+
+
+def _assert_ulps(got, ref, n: float, what: str):
+    u = _ulps(got, ref)
+    assert np.all(np.isfinite(np.asarray(got, np.float64))), f"{what}: non-finite output"
+    assert float(u.max(initial=0.0)) <= n, f"{what}: {float(u.max())} ulp > {n}"
+
+
+def _dec(f: Fraction) -> Decimal:
+    return Decimal(f.numerator) / Decimal(f.denominator)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _ln(lib, x, g, b, eps=EPS32):
+    return oracle.layernorm(x, g, b, float(eps), lib=lib)
+
+
+def _rms(lib, x, w, eps=EPS32):
+    return oracle.rmsnorm(x, w, float(eps), lib=lib)
+
+
+# ----------------------------------------------------------------------------
+# exact brute force
+
+def _exact_ln_row(xrow, g, b, eps):
+    getcontext().prec = 60
+    xs = [Fraction(float(v)) for v in xrow]
+    d = len(xs)
+    mu = sum(xs, Fraction(0)) / d
+    var = sum(((v - mu) ** 2 for v in xs), Fraction(0)) / d
+    rho = 1 / (_dec(var) + _dec(Fraction(float(eps)))).sqrt()
+    ys = [_dec(v - mu) * rho * Decimal(float(gj)) + Decimal(float(bj))
+          for v, gj, bj in zip(xs, g, b)]
+    return mu, var, rho, ys
+
+
+def _exact_rms_row(xrow, w, eps):
+    getcontext().prec = 60
+    xs = [Fraction(float(v)) for v in xrow]
+    ms = sum((v * v for v in xs), Fraction(0)) / len(xs)
+    rho = 1 / (_dec(ms) + _dec(Fraction(float(eps)))).sqrt()
+    ys = [_dec(v) * Decimal(float(wj)) * rho for v, wj in zip(xs, w)]
+    return ms, rho, ys
+
+
+def check_ln_bruteforce(lib):
+    for d in (1, 2, 3, 5, 8):
+        rng = _rng([11, d])
+        rows = 6
+        x = rng.standard_normal((rows, d)).astype(np.float32)
+        x[0] = (x[0].astype(np.float64) * 3 + 0.5).astype(np.float32)
+        g = (1 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+        b = (0.1 * rng.standard_normal(d)).astype(np.float32)
+        y, mean, rstd, mean64, var64 = _ln(lib, x, g, b)
+        for i in range(rows):
+            mu, var, rho, ys = _exact_ln_row(x[i], g, b, EPS32)
+            scale = float(np.abs(x[i]).max()) + 1e-30
+            assert abs(mean64[i] - float(mu)) <= 1e-14 * scale, ("mean64", d, i)
+            assert abs(var64[i] - float(var)) <= 1e-13 * scale * scale, ("var64", d, i)
+            yex = np.array([float(t) for t in ys], np.float32)
+            # float64 evaluation then one rounding: within 1 ulp of the exact
+            # result, plus the float64 cancellation floor near zero outputs
+            err = np.abs(y[i].astype(np.float64) - np.array([float(t) for t in ys]))
+            lim = np.spacing(np.abs(yex)).astype(np.float64) + 1e-14
+            assert np.all(err <= lim), ("y", d, i, float(err.max()))
+            _assert_ulps(mean[i], np.float32(float(mu)), 1, f"mean d={d}")
+            _assert_ulps(rstd[i], np.float32(float(rho)), 1, f"rstd d={d}")
+
+
+def check_rms_bruteforce(lib):
+    for d in (1, 2, 3, 5, 8):
+        rng = _rng([12, d])
+        rows = 6
+        x = rng.standard_normal((rows, d)).astype(np.float32)
+        w = (1 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+        y, rstd, ms64 = _rms(lib, x, w)
+        for i in range(rows):
+            ms, rho, ys = _exact_rms_row(x[i], w, EPS32)
+            assert abs(ms64[i] - float(ms)) <= 1e-14 * float(ms) + 1e-300, ("ms64", d, i)
+            yex = np.array([float(t) for t in ys], np.float32)
+            _assert_ulps(y[i], yex, 1, f"rms y d={d}")
+            _assert_ulps(rstd[i], np.float32(float(rho)), 1, f"rms rstd d={d}")
+
+
+# ----------------------------------------------------------------------------
+# independent library implementation (torch float64 on the CPU)
+
+def check_ln_vs_torch(lib):
+    import torch
+    for rows, d, pat in ((64, 1, "normal"), (37, 7, "offset"), (64, 128, "normal"),
+                         (17, 1000, "offset"), (9, 4096, "tiny"), (33, 33, "alternating")):
+        x = wl.make_x(rows, d, pat, [13, rows, d])
+        g, b = wl.make_affine(d, [13, d])
+        y, mean, rstd, mean64, var64 = _ln(lib, x, g, b)
+        ty, tmean, trstd = torch.native_layer_norm(
+            torch.from_numpy(x).double(), (d,), torch.from_numpy(g).double(),
+            torch.from_numpy(b).double(), float(EPS32))
+        _assert_ulps(y, ty.numpy().astype(np.float32), 1, f"ln vs torch y {rows}x{d}")
+        np.testing.assert_allclose(mean64, tmean.reshape(-1).numpy(), rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(1.0 / np.sqrt(var64 + float(EPS32)), trstd.reshape(-1).numpy(),
+                                   rtol=1e-12)
+        _assert_ulps(rstd, trstd.reshape(-1).numpy().astype(np.float32), 1, "ln vs torch rstd")
+        _assert_ulps(mean, tmean.reshape(-1).numpy().astype(np.float32), 1, "ln vs torch mean")
+
+
+def check_rms_vs_torch(lib):
+    import torch
+    import torch.nn.functional as F
+    for rows, d, pat in ((64, 1, "normal"), (31, 31, "normal"), (64, 128, "tiny"),
+                         (8, 8193, "normal"), (16, 4096, "alternating")):
+        x = wl.make_x(rows, d, pat, [14, rows, d])
+        w = wl.make_weight(d, [14, d])
+        y, rstd, ms64 = _rms(lib, x, w)
+        ty = F.rms_norm(torch.from_numpy(x).double(), (d,), torch.from_numpy(w).double(),
+                        eps=float(EPS32))
+        _assert_ulps(y, ty.numpy().astype(np.float32), 1, f"rms vs torch {rows}x{d}")
+        tms = (torch.from_numpy(x).double() ** 2).mean(dim=1).numpy()
+        np.testing.assert_allclose(ms64, tms, rtol=1e-12, atol=1e-300)
+
+
+# ----------------------------------------------------------------------------
+# closed forms
+
+def check_ln_closed_forms(lib):
+    inv_sqrt_eps = np.float32(1.0 / math.sqrt(float(EPS32)))
+    # zero rows: x - mu = 0 exactly, so y is beta bit for bit
+    d = 257
+    g, b = wl.make_affine(d, [15, d])
+    x = np.zeros((5, d), np.float32)
+    y, mean, rstd, _, _ = _ln(lib, x, g, b)
+    assert np.array_equal(y, np.broadcast_to(b, y.shape)), "zero rows: y != beta"
+    assert np.all(mean == 0), "zero rows: mean != 0"
+    _assert_ulps(rstd, np.full(5, inv_sqrt_eps), 1, "zero rows: rstd != 1/sqrt(eps)")
+    # width 1: the single element is its own mean
+    x = wl.make_x(16, 1, "normal", [15, 1])
+    g1, b1 = wl.make_affine(1, [15, 1])
+    y, mean, rstd, _, _ = _ln(lib, x, g1, b1)
+    assert np.array_equal(y, np.broadcast_to(b1, y.shape)), "width 1: y != beta"
+    assert np.array_equal(mean, x[:, 0]), "width 1: mean != x"
+    _assert_ulps(rstd, np.full(16, inv_sqrt_eps), 1, "width 1: rstd")
+    # constant rows (dyadic value, exact sum): y == beta
+    x = np.full((3, 96), 0.75, np.float32)
+    g96, b96 = wl.make_affine(96, [15, 96])
+    y, mean, _, _, _ = _ln(lib, x, g96, b96)
+    assert np.array_equal(y, np.broadcast_to(b96, y.shape)), "constant rows: y != beta"
+    assert np.all(mean == np.float32(0.75))
+    # alternating +-1 with p plus and m minus per row: mu = (p-m)/d, var = 1 - mu^2
+    for d in (2, 128, 31, 33, 127):
+        x = wl.make_x(4, d, "alternating")
+        g, b = wl.make_affine(d, [15, 2, d])
+        y, mean, rstd, _, var64 = _ln(lib, x, g, b)
+        for i in range(4):
+            p = int(np.sum(x[i] > 0))
+            m = d - p
+            mu = (p - m) / d
+            var = 1.0 - mu * mu
+            rho = 1.0 / math.sqrt(var + float(EPS32))
+            assert abs(var64[i] - var) <= 1e-13, ("alt var", d, i)  # float64 rounding of mu
+            want = ((x[i].astype(np.float64) - mu) * rho * g + b).astype(np.float32)
+            _assert_ulps(y[i], want, 1, f"alternating d={d}")
+            _assert_ulps(rstd[i], np.float32(rho), 1, f"alternating rstd d={d}")
+
+
+def check_rms_closed_forms(lib):
+    d = 129
+    w = wl.make_weight(d, [16, d])
+    y, rstd, _ = _rms(lib, np.zeros((4, d), np.float32), w)
+    assert np.all(y == 0), "zero rows: y != 0"
+    _assert_ulps(rstd, np.full(4, np.float32(1 / math.sqrt(float(EPS32)))), 1, "zero rstd")
+    # width 1: y = x w / sqrt(x^2 + eps)
+    x = wl.make_x(32, 1, "normal", [16, 1])
+    w1 = wl.make_weight(1, [16, 1])
+    y, _, _ = _rms(lib, x, w1)
+    xd = x[:, 0].astype(np.float64)
+    want = (xd * float(w1[0]) / np.sqrt(xd * xd + float(EPS32))).astype(np.float32)
+    _assert_ulps(y[:, 0], want, 1, "rms width 1")
+    # alternating: mean square is exactly 1
+    for d in (31, 128):
+        x = wl.make_x(3, d, "alternating")
+        w = wl.make_weight(d, [16, 2, d])
+        y, rstd, ms64 = _rms(lib, x, w)
+        assert np.all(ms64 == 1.0), "alternating mean square != 1"
+        want = (x.astype(np.float64) * w / math.sqrt(1.0 + float(EPS32))).astype(np.float32)
+        _assert_ulps(y, want, 1, f"rms alternating d={d}")
+
+
+# ----------------------------------------------------------------------------
+# invariants
+
+def _dyadic(rows, d, seed):
+    """Values k/256 with |k| < 2^10: sums of up to 2^20 of them stay exact in float64."""
+    k = _rng(seed).integers(-1023, 1024, size=(rows, d))
+    return (k / 256.0).astype(np.float32)
+
+
+def check_ln_invariants(lib):
+    rows, d = 12, 256  # power-of-two width: mu = s/d is exact, so every step is exact
+    x = _dyadic(rows, d, [17, 1])
+    g, b = wl.make_affine(d, [17, 2])
+    y0, m0, r0, mu0, var0 = _ln(lib, x, g, b)
+    # shift invariance: x + 8 is exact, every float64 step is exact, y is identical
+    y1, m1, r1, _, _ = _ln(lib, (x + np.float32(8.0)).astype(np.float32), g, b)
+    assert np.array_equal(y0, y1), "LN(x + c) != LN(x)"
+    assert np.array_equal(r0, r1), "rstd changed under a shift"
+    assert np.allclose(m1, m0 + 8.0, rtol=0, atol=1e-6), "mean did not shift"
+    # power-of-two scale: LN_eps(2x) == LN_{eps/4}(x) bit for bit
+    y2, _, _, _, _ = _ln(lib, (2 * x).astype(np.float32), g, b, EPS32)
+    y3, _, _, _, _ = _ln(lib, x, g, b, np.float32(EPS32 / 4))
+    assert np.array_equal(y2, y3), "LN_eps(2x) != LN_eps/4(x)"
+    # row permutation: rows are independent
+    perm = _rng([17, 3]).permutation(rows)
+    yp, _, _, _, _ = _ln(lib, x[perm], g, b)
+    assert np.array_equal(yp, y0[perm]), "row permutation"
+    # column permutation: every column keeps its own gamma/beta (sum order changes)
+    xr = wl.make_x(rows, d, "offset", [17, 4])
+    yr, _, _, _, _ = _ln(lib, xr, g, b)
+    cp = _rng([17, 5]).permutation(d)
+    yc, _, _, _, _ = _ln(lib, np.ascontiguousarray(xr[:, cp]), g[cp], b[cp])
+    _assert_ulps(yc, yr[:, cp], 1, "column permutation")
+    # unit affine: output row mean 0, population variance var/(var+eps)
+    ones, zeros = np.ones(d, np.float32), np.zeros(d, np.float32)
+    yu, _, _, _, vu = _ln(lib, xr, ones, zeros)
+    yd = yu.astype(np.float64)
+    assert np.all(np.abs(yd.mean(axis=1)) <= 1e-6), "unit affine: row mean != 0"
+    want = vu / (vu + float(EPS32))
+    np.testing.assert_allclose(yd.var(axis=1), want, rtol=2e-6)
+    # in place: y written over x gives the same values
+    xin = xr.copy()
+    oracle.layernorm(xin, g, b, float(EPS32), lib=lib, out=xin)
+    assert np.array_equal(xin, yr), "in-place LayerNorm differs"
+
+
+def check_rms_invariants(lib):
+    rows, d = 10, 300
+    x = wl.make_x(rows, d, "normal", [18, 1])
+    w = wl.make_weight(d, [18, 2])
+    y0, r0, _ = _rms(lib, x, w)
+    # power-of-two scale: RMS_eps(2x) == RMS_{eps/4}(x) bit for bit
+    y2, _, _ = _rms(lib, (2 * x).astype(np.float32), w, EPS32)
+    y3, _, _ = _rms(lib, x, w, np.float32(EPS32 / 4))
+    assert np.array_equal(y2, y3), "RMS_eps(2x) != RMS_eps/4(x)"
+    # the output is linear in w: w -> 2w doubles y exactly
+    y4, _, _ = _rms(lib, x, (2 * w).astype(np.float32))
+    assert np.array_equal(y4, 2 * y0), "RMS not linear in w"
+    # y / (x w) is the per-row rstd
+    ratio = y0.astype(np.float64) / (x.astype(np.float64) * w)
+    np.testing.assert_allclose(ratio, np.repeat(r0[:, None].astype(np.float64), d, axis=1),
+                               rtol=2e-7)
+    cp = _rng([18, 3]).permutation(d)
+    yc, _, _ = _rms(lib, np.ascontiguousarray(x[:, cp]), w[cp])
+    _assert_ulps(yc, y0[:, cp], 1, "rms column permutation")
+    xin = x.copy()
+    oracle.rmsnorm(xin, w, float(EPS32), lib=lib, out=xin)
+    assert np.array_equal(xin, y0), "in-place RMSNorm differs"
+
+
+LN_CHECKS = (check_ln_bruteforce, check_ln_vs_torch, check_ln_closed_forms, check_ln_invariants)
+RMS_CHECKS = (check_rms_bruteforce, check_rms_vs_torch, check_rms_closed_forms, check_rms_invariants)
+ALL_CHECKS = LN_CHECKS + RMS_CHECKS
