@@ -1,0 +1,351 @@
+#!/usr/bin/env python3
+"""Benchmark: forward LayerNorm FP32 [4096,768] with per-row mean/rstd on one MI355X.
+
+One step is one call of the C ABI (mi_layernorm_fwd: validation, dispatch and
+one kernel launch) over one batch of seeded synthetic input already resident
+in HBM.  The run:
+
+1. draws the inputs (row_wise_normalization_layernorm_amd.workloads) and
+   copies them to the device;
+2. checks the GPU output against the float64 oracle and refuses to time on a
+   mismatch (correctness gates timing);
+3. runs W untimed warm-up steps, then times exactly K steps between HIP events
+   recorded on the stream the kernels run on, with a device synchronization
+   on both sides;
+4. times the oracle on the host cores as a reported CPU baseline;
+5. prints one JSON line.
+
+HBM, not cache: in the default "rotate" mode, step s reads buffer set
+s % n_sets, with enough sets that their total footprint is at least 1 GiB
+(four times the 256 MB Infinity Cache); "warm" reuses one set, as the pages'
+own timers did, and measures cache-resident bandwidth.
+
+Algorithmic bytes per step (LayerNorm): read x and write y (8 B per element),
+read gamma and beta (8 B per column), write mean and rstd (8 B per row).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published peak
+METRIC = "achieved HBM GB/s (% of peak) + kernel µs, LayerNorm FP32 [4096,768]"
+
+# name -> (op, rows, d, pattern, stats)
+BENCH_WORKLOADS = {
+    "ln_4096x768": ("layernorm", 4096, 768, "normal", True),
+    "ln_512x128": ("layernorm", 512, 128, "normal", False),
+    "ln_8192x768": ("layernorm", 8192, 768, "offset", False),
+    "ln_1024x2048": ("layernorm", 1024, 2048, "offset", False),
+    "ln_4096x4096": ("layernorm", 4096, 4096, "offset", False),
+    "ln_32768x8192": ("layernorm", 32768, 8192, "normal", False),
+    "rms_512x128": ("rmsnorm", 512, 128, "normal", False),
+    "rms_4096x768": ("rmsnorm", 4096, 768, "normal", False),
+    "rms_2048x4096": ("rmsnorm", 2048, 4096, "normal", False),
+    "rms_256x8193": ("rmsnorm", 256, 8193, "normal", False),
+    "copy_4096x768": ("copy", 4096, 768, "normal", False),
+    "copy_32768x8192": ("copy", 32768, 8192, "normal", False),
+}
+
+KERNEL_SOURCES = ("row_wise_normalization_layernorm_amd/csrc/norm_kernels.hpp",
+                  "row_wise_normalization_layernorm_amd/csrc/mi_norm.hip")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(op: str, rows: int, d: int, stats: bool) -> int:
+    if op == "layernorm":
+        return 8 * rows * d + 8 * d + (8 * rows if stats else 0)
+    if op == "rmsnorm":
+        return 8 * rows * d + 4 * d + (4 * rows if stats else 0)
+    return 8 * rows * d  # copy: one read, one write per element
+
+
+def describe(op: str, rows: int, d: int, stats: bool) -> str:
+    if op == "copy":
+        return f"streaming copy FP32 {rows*d} elements (calibration, bytes of [{rows},{d}])"
+    name = "LayerNorm" if op == "layernorm" else "RMSNorm"
+    extra = " with per-row mean/rstd" if (stats and op == "layernorm") else (" with rstd" if stats else "")
+    return f"{name} fwd FP32 [{rows},{d}]{extra}"
+
+
+def pmc_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{workload}.txt")
+    if not os.path.exists(path):
+        return None, None
+    text = open(path).read()
+    m = re.search(r"^kernel_source_sha256:\s*(\w+)", text, re.M)
+    t = re.search(r"^traffic_bytes_per_launch:\s*([\d.eE+]+)", text, re.M)
+    if not m or not t or m.group(1) != kernel_source_hash():
+        return None, path
+    return float(t.group(1)), path
+
+
+def load_bench_lib():
+    import row_wise_normalization_layernorm_amd as mn
+    mn.lib()
+    from row_wise_normalization_layernorm_amd import build as B
+    if not os.path.exists(B.BENCH_LIB):
+        raise RuntimeError(f"{B.BENCH_LIB} is not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(B.BENCH_LIB)
+    P = ctypes.c_void_p
+    L.mi_bench_layernorm_loop.argtypes = [P, P, P, P, P, P, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_float, ctypes.c_int, ctypes.c_int, P]
+    L.mi_bench_rmsnorm_loop.argtypes = [P, P, P, P, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_float, ctypes.c_int, ctypes.c_int, P]
+    L.mi_bench_copy_loop.argtypes = [P, P, ctypes.c_int, ctypes.c_int64, ctypes.c_int, P]
+    return L
+
+
+def ptr_array(tensors):
+    arr = (ctypes.c_void_p * len(tensors))(*[t.data_ptr() if t is not None else None for t in tensors])
+    return arr
+
+
+def cpu_baseline(op, x, params, eps, budget_s: float):
+    """The float64 oracle on the host cores over the same workload."""
+    import oracle
+    threads = oracle.max_threads()
+    fn = oracle.layernorm if op == "layernorm" else oracle.rmsnorm
+    fn(x, *params, eps)  # first call loads the library
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn(x, *params, eps)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 200:
+            break
+    return reps, el, threads
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="ln_4096x768", choices=sorted(BENCH_WORKLOADS))
+    ap.add_argument("--mode", default="rotate", choices=["rotate", "warm"])
+    ap.add_argument("--launch", default="native", choices=["native", "graph", "python"])
+    ap.add_argument("--variant", default=None, help="force a kernel variant by name")
+    ap.add_argument("--footprint-gib", type=float, default=1.0)
+    ap.add_argument("--cpu-seconds", type=float, default=2.0, help="wall budget of the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "rows shard across GPUs with no communication, and this build measures one GPU's share.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import row_wise_normalization_layernorm_amd as mn
+    from row_wise_normalization_layernorm_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    op, rows, d, pattern, stats = BENCH_WORKLOADS[args.workload]
+    eps = wl.EPS
+    BL = load_bench_lib()
+    L = mn.lib()
+
+    # -- inputs, resident in HBM before timing
+    seed = wl.case_seed(2, rows, d, pattern)
+    x_h = wl.make_x(rows, d, pattern, seed)
+    if op == "layernorm":
+        params_h = wl.make_affine(d, [2, d, 99])
+    elif op == "rmsnorm":
+        params_h = (wl.make_weight(d, [2, d, 99]),)
+    else:
+        params_h = ()
+    n = rows * d
+    per_set = 8 * n + (8 * rows if stats else 0)
+    nsets = 1 if args.mode == "warm" else max(1, math.ceil(args.footprint_gib * 2**30 / per_set))
+    x0 = torch.from_numpy(x_h).to(dev)
+    xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
+    ys = [torch.empty_like(x0) for _ in range(nsets)]
+    means = [torch.empty(rows, device=dev) for _ in range(nsets)] if (stats and op == "layernorm") else None
+    rstds = [torch.empty(rows, device=dev) for _ in range(nsets)] if stats else None
+    params = [torch.from_numpy(p).to(dev) for p in params_h]
+
+    vid = -1
+    if args.variant:
+        names = [mn.mi_norm_variant_name(i) for i in range(mn.mi_norm_variant_count())]
+        if args.variant not in names:
+            print(f"unknown variant {args.variant}", file=sys.stderr)
+            return 1
+        vid = names.index(args.variant)
+    if op != "copy":
+        sel = vid if vid >= 0 else mn.mi_norm_select_variant(
+            mn.OP_LAYERNORM if op == "layernorm" else mn.OP_RMSNORM, d, x0, ys[0], params[0],
+            params[1] if op == "layernorm" else None)
+        variant_name = mn.mi_norm_variant_name(sel)
+    else:
+        variant_name = "copy_f4"
+
+    stream = torch.cuda.Stream(device=dev)
+    sh = stream.cuda_stream
+    xa, ya = ptr_array(xs), ptr_array(ys)
+    ma = ptr_array(means) if means else None
+    ra = ptr_array(rstds) if rstds else None
+
+    def run_native(k: int):
+        if op == "layernorm":
+            st = BL.mi_bench_layernorm_loop(xa, params[0].data_ptr(), params[1].data_ptr(), ya, ma, ra,
+                                            nsets, rows, d, eps, k, vid, sh)
+        elif op == "rmsnorm":
+            st = BL.mi_bench_rmsnorm_loop(xa, params[0].data_ptr(), ya, ra, nsets, rows, d, eps, k, vid, sh)
+        else:
+            st = BL.mi_bench_copy_loop(xa, ya, nsets, n, k, sh)
+        if st != 0:
+            raise RuntimeError(f"bench loop failed: {mn.mi_norm_status_string(st)}")
+
+    def run_python(k: int, start: int = 0):
+        for s in range(start, start + k):
+            j = s % nsets
+            if op == "layernorm":
+                fwd = mn.mi_layernorm_fwd if vid < 0 else (lambda *a, **kw: mn.mi_layernorm_fwd_variant(vid, *a, **kw))
+                fwd(xs[j], params[0], params[1], ys[j], rows, d, eps,
+                    means[j] if means else None, rstds[j] if rstds else None, stream=sh)
+            elif op == "rmsnorm":
+                fwd = mn.mi_rmsnorm_fwd if vid < 0 else (lambda *a, **kw: mn.mi_rmsnorm_fwd_variant(vid, *a, **kw))
+                fwd(xs[j], params[0], ys[j], rows, d, eps, rstds[j] if rstds else None, stream=sh)
+            else:
+                mn.mi_copy_f32(xs[j], ys[j], n, stream=sh)
+
+    # -- parity gate on set 0 (the first call of the run)
+    with torch.cuda.stream(stream):
+        run_python(1)
+    torch.cuda.synchronize()
+    if op != "copy":
+        import oracle
+        sample = np.arange(rows) if n <= (1 << 26) else np.unique(
+            np.random.default_rng(0).integers(0, rows, 512))
+        xs_h = np.ascontiguousarray(x_h[sample])
+        ref = oracle.layernorm(xs_h, *params_h, eps) if op == "layernorm" else oracle.rmsnorm(xs_h, *params_h, eps)
+        got = ys[0].cpu().numpy()[sample]
+        ok, err, ratio = oracle.tolerance_ok(got, ref[0])
+        if stats:
+            sgot = [means[0], rstds[0]] if op == "layernorm" else [rstds[0]]
+            for g_, r_ in zip(sgot, ref[1:1 + len(sgot)]):
+                ok2, e2, r2 = oracle.tolerance_ok(g_.cpu().numpy()[sample], r_)
+                ok, err, ratio = ok and ok2, max(err, e2), max(ratio, r2)
+        if not ok:
+            print(f"PARITY FAILURE before timing: max abs err {err:.3e}, err/bound {ratio:.3f}", file=sys.stderr)
+            return 3
+        parity = {"rows_checked": int(len(sample)), "max_abs_err": err, "max_err_over_bound": ratio}
+    else:
+        if not torch.equal(ys[0], xs[0]):
+            print("PARITY FAILURE: copy mismatch", file=sys.stderr)
+            return 3
+        parity = {"exact": True}
+
+    # -- warm-up and timed steps
+    graph = None
+    if args.launch == "graph":
+        gw, graph = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gw, stream=stream):
+            run_python(args.warmup)
+        with torch.cuda.graph(graph, stream=stream):
+            run_python(args.steps, start=args.warmup)
+        runner_w, runner_t = gw.replay, graph.replay
+    elif args.launch == "native":
+        runner_w, runner_t = (lambda: run_native(args.warmup)), (lambda: run_native(args.steps))
+    else:
+        def runner_w():
+            with torch.cuda.stream(stream):
+                run_python(args.warmup)
+
+        def runner_t():
+            with torch.cuda.stream(stream):
+                run_python(args.steps, start=args.warmup)
+
+    with torch.cuda.stream(stream):
+        runner_w()
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record(stream)
+    with torch.cuda.stream(stream):
+        runner_t()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    w1 = time.perf_counter()
+    ms = t_start.elapsed_time(t_end)
+    ms_per_step = ms / args.steps
+    bytes_step = algorithmic_bytes(op, rows, d, stats)
+    gbps = bytes_step / (ms_per_step * 1e-3) / 1e9
+
+    traffic, traffic_src = pmc_traffic(args.workload)
+    roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                "traffic": traffic, "kernel": variant_name,
+                "algorithmic_bytes_per_launch": bytes_step,
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-scaled)"}
+
+    cpu = None
+    if not args.no_cpu_baseline and op != "copy":
+        reps, el, threads = cpu_baseline(op, x_h, params_h, eps, args.cpu_seconds)
+        cpu = {"value": round(bytes_step * reps / el / 1e9, 3), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"full {describe(op, rows, d, stats)} workload, {reps} repetitions "
+                         f"({el:.2f} s wall, float64 C oracle, OpenMP over rows)"}
+
+    line = {
+        "metric": METRIC if args.workload == "ln_4096x768" else f"achieved HBM GB/s, {describe(op, rows, d, stats)}",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": describe(op, rows, d, stats), "rows": rows, "d": d, "eps": eps,
+                   "pattern": pattern, "seed": seed, "mode": args.mode, "buffer_sets": nsets,
+                   "footprint_bytes": nsets * per_set, "launch": args.launch, "variant": variant_name,
+                   "parallelism": "single GPU"},
+        "kernel_us": round(ms_per_step * 1e3, 3),
+        "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
+        "rows_per_s": round(rows / (ms_per_step * 1e-3), 1),
+        "wall_ms_per_step": round((w1 - w0) * 1e3 / args.steps, 6),
+        "parity": parity,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernel_source_sha256": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,1 +1,30 @@
-"""MI355X-native forward row-wise normalization (LayerNorm, RMSNorm)."""
+"""MI355X-native forward row-wise normalization (LayerNorm, RMSNorm).
+
+The compute path is libmi_norm.so (hand-written HIP for gfx950, C ABI in
+include/mi_norm.h); this package is its thin Python binding plus the seeded
+synthetic workloads used by tests and benchmarks.
+"""
+from ._binding import (  # noqa: F401
+    MI_NORM_ERR_HIP,
+    MI_NORM_ERR_INVALID,
+    MI_NORM_OK,
+    OP_LAYERNORM,
+    OP_RMSNORM,
+    MiNormError,
+    header_functions,
+    layernorm,
+    lib,
+    mi_copy_f32,
+    mi_layernorm_fwd,
+    mi_layernorm_fwd_variant,
+    mi_norm_select_variant,
+    mi_norm_status_string,
+    mi_norm_variant_count,
+    mi_norm_variant_eligible,
+    mi_norm_variant_get_info,
+    mi_norm_variant_name,
+    mi_norm_version,
+    mi_rmsnorm_fwd,
+    mi_rmsnorm_fwd_variant,
+    rmsnorm,
+)

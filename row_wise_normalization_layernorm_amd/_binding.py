@@ -1,0 +1,245 @@
+"""ctypes binding of libmi_norm.so (include/mi_norm.h).
+
+Argument marshalling only: every arithmetic step runs in the library's HIP
+kernels.  Functions accept torch CUDA tensors (their device pointer is taken)
+or plain integers (raw device addresses).  ``stream`` may be None (torch's
+current stream of the tensors' device, else the null stream), an int handle,
+or a ``torch.cuda.Stream``.
+
+torch is imported before the library is loaded: the library's HIP runtime
+dependency (SONAME libamdhip64.so.7) then resolves to the runtime torch has
+already mapped, so torch's streams and allocations are valid inside it.  If
+the library has not been built, every call raises RuntimeError; there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmi_norm.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "mi_norm.h")
+
+MI_NORM_OK = 0
+MI_NORM_ERR_INVALID = 1
+MI_NORM_ERR_HIP = 2
+OP_LAYERNORM = 0
+OP_RMSNORM = 1
+
+_lib = None
+
+
+class MiNormError(RuntimeError):
+    """A non-OK status from the C ABI; ``.status`` holds the code."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class VariantInfo(ctypes.Structure):
+    _fields_ = [
+        ("op", ctypes.c_int), ("vec", ctypes.c_int), ("peel", ctypes.c_int),
+        ("looped", ctypes.c_int), ("lanes_per_row", ctypes.c_int),
+        ("waves_per_row", ctypes.c_int), ("slots", ctypes.c_int),
+        ("waves_per_block", ctypes.c_int), ("rows_per_block", ctypes.c_int),
+        ("max_d", ctypes.c_int64), ("needs_aligned", ctypes.c_int),
+    ]
+
+    def as_dict(self) -> dict:
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+_VP = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_I = ctypes.c_int
+
+_SIGNATURES = {
+    "mi_norm_status_string": (ctypes.c_char_p, [_I]),
+    "mi_norm_version": (ctypes.c_char_p, []),
+    "mi_layernorm_fwd": (_I, [_VP, _VP, _VP, _VP, _I64, _I64, _F, _VP, _VP, _VP]),
+    "mi_rmsnorm_fwd": (_I, [_VP, _VP, _VP, _I64, _I64, _F, _VP, _VP]),
+    "mi_norm_variant_count": (_I, []),
+    "mi_norm_variant_name": (ctypes.c_char_p, [_I]),
+    "mi_norm_variant_get_info": (_I, [_I, ctypes.POINTER(VariantInfo)]),
+    "mi_norm_select_variant": (_I, [_I, _I64, _VP, _VP, _VP, _VP]),
+    "mi_norm_variant_eligible": (_I, [_I, _I, _I64, _VP, _VP, _VP, _VP]),
+    "mi_layernorm_fwd_variant": (_I, [_I, _VP, _VP, _VP, _VP, _I64, _I64, _F, _VP, _VP, _VP]),
+    "mi_rmsnorm_fwd_variant": (_I, [_I, _VP, _VP, _VP, _I64, _I64, _F, _VP, _VP]),
+    "mi_copy_f32": (_I, [_VP, _VP, _I64, _VP]),
+}
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/mi_norm.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mi_\w+)\s*\(", text)))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loading it on first use)."""
+    global _lib
+    if _lib is None:
+        import torch  # noqa: F401  (see module docstring: runtime order)
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "(python -m row_wise_normalization_layernorm_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != MI_NORM_OK:
+        msg = lib().mi_norm_status_string(status).decode()
+        raise MiNormError(status, f"{what}: {msg}")
+
+
+def _is_tensor(a) -> bool:
+    return type(a).__module__.startswith("torch") and hasattr(a, "data_ptr")
+
+
+def _ptr(a, name: str, need: int | None = None):
+    """Device address of a tensor (validated) or an int; None stays None."""
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    if _is_tensor(a):
+        import torch
+        if a.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor, got {a.device}")
+        if a.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32, got {a.dtype}")
+        if not a.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if need is not None and a.numel() < need:
+            raise ValueError(f"{name} holds {a.numel()} elements, needs {need}")
+        return a.data_ptr()
+    raise TypeError(f"{name}: expected a torch tensor, an int address or None")
+
+
+def _stream(stream, *tensors):
+    if stream is None:
+        for t in tensors:
+            if t is not None and _is_tensor(t) and t.device.type == "cuda":
+                import torch
+                return torch.cuda.current_stream(t.device).cuda_stream
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# --- the C entry points, same names -----------------------------------------
+
+def mi_layernorm_fwd(x, gamma, beta, y, rows: int, d: int, eps: float = 1e-5,
+                     mean=None, rstd=None, stream=None) -> None:
+    n = max(rows, 0) * max(d, 0)
+    st = lib().mi_layernorm_fwd(_ptr(x, "x", n), _ptr(gamma, "gamma", d), _ptr(beta, "beta", d),
+                                _ptr(y, "y", n), rows, d, eps, _ptr(mean, "mean", rows),
+                                _ptr(rstd, "rstd", rows), _stream(stream, x, y))
+    _check(st, "mi_layernorm_fwd")
+
+
+def mi_rmsnorm_fwd(x, w, y, rows: int, d: int, eps: float = 1e-5, rstd=None,
+                   stream=None) -> None:
+    n = max(rows, 0) * max(d, 0)
+    st = lib().mi_rmsnorm_fwd(_ptr(x, "x", n), _ptr(w, "w", d), _ptr(y, "y", n), rows, d, eps,
+                              _ptr(rstd, "rstd", rows), _stream(stream, x, y))
+    _check(st, "mi_rmsnorm_fwd")
+
+
+def mi_layernorm_fwd_variant(vid: int, x, gamma, beta, y, rows: int, d: int, eps: float = 1e-5,
+                             mean=None, rstd=None, stream=None) -> None:
+    n = max(rows, 0) * max(d, 0)
+    st = lib().mi_layernorm_fwd_variant(vid, _ptr(x, "x", n), _ptr(gamma, "gamma", d),
+                                        _ptr(beta, "beta", d), _ptr(y, "y", n), rows, d, eps,
+                                        _ptr(mean, "mean", rows), _ptr(rstd, "rstd", rows),
+                                        _stream(stream, x, y))
+    _check(st, f"mi_layernorm_fwd_variant({vid})")
+
+
+def mi_rmsnorm_fwd_variant(vid: int, x, w, y, rows: int, d: int, eps: float = 1e-5, rstd=None,
+                           stream=None) -> None:
+    n = max(rows, 0) * max(d, 0)
+    st = lib().mi_rmsnorm_fwd_variant(vid, _ptr(x, "x", n), _ptr(w, "w", d), _ptr(y, "y", n),
+                                      rows, d, eps, _ptr(rstd, "rstd", rows), _stream(stream, x, y))
+    _check(st, f"mi_rmsnorm_fwd_variant({vid})")
+
+
+def mi_copy_f32(src, dst, n: int, stream=None) -> None:
+    st = lib().mi_copy_f32(_ptr(src, "src", n), _ptr(dst, "dst", n), n, _stream(stream, src, dst))
+    _check(st, "mi_copy_f32")
+
+
+def mi_norm_status_string(status: int) -> str:
+    return lib().mi_norm_status_string(status).decode()
+
+
+def mi_norm_version() -> str:
+    return lib().mi_norm_version().decode()
+
+
+def mi_norm_variant_count() -> int:
+    return int(lib().mi_norm_variant_count())
+
+
+def mi_norm_variant_name(vid: int) -> str | None:
+    r = lib().mi_norm_variant_name(vid)
+    return None if r is None else r.decode()
+
+
+def mi_norm_variant_get_info(vid: int) -> dict:
+    info = VariantInfo()
+    _check(lib().mi_norm_variant_get_info(vid, ctypes.byref(info)), "mi_norm_variant_get_info")
+    return info.as_dict()
+
+
+def _addr(a):
+    return a if (a is None or isinstance(a, int)) else a.data_ptr()
+
+
+def mi_norm_select_variant(op: int, d: int, x, y, params0, params1=None) -> int:
+    return int(lib().mi_norm_select_variant(op, d, _addr(x), _addr(y), _addr(params0), _addr(params1)))
+
+
+def mi_norm_variant_eligible(vid: int, op: int, d: int, x, y, params0, params1=None) -> bool:
+    return bool(lib().mi_norm_variant_eligible(vid, op, d, _addr(x), _addr(y), _addr(params0),
+                                               _addr(params1)))
+
+
+# --- conveniences over torch tensors (allocation is torch's) -------------------
+
+def layernorm(x, gamma, beta, eps: float = 1e-5, stats: bool = False, out=None, stream=None):
+    """LayerNorm over the last dimension of a contiguous float32 device tensor.
+
+    Returns y, or (y, mean, rstd) with ``stats``.  ``out`` may be x (in place).
+    """
+    import torch
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    y = torch.empty_like(x) if out is None else out
+    mean = torch.empty(x.shape[:-1], device=x.device, dtype=torch.float32) if stats else None
+    rstd = torch.empty(x.shape[:-1], device=x.device, dtype=torch.float32) if stats else None
+    mi_layernorm_fwd(x, gamma, beta, y, rows, d, eps, mean, rstd, stream)
+    return (y, mean, rstd) if stats else y
+
+
+def rmsnorm(x, w, eps: float = 1e-5, stats: bool = False, out=None, stream=None):
+    """RMSNorm over the last dimension; returns y, or (y, rstd) with ``stats``."""
+    import torch
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    y = torch.empty_like(x) if out is None else out
+    rstd = torch.empty(x.shape[:-1], device=x.device, dtype=torch.float32) if stats else None
+    mi_rmsnorm_fwd(x, w, y, rows, d, eps, rstd, stream)
+    return (y, rstd) if stats else y

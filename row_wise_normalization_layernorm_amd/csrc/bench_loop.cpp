@@ -1,0 +1,58 @@
+// bench_loop.cpp — libmi_norm_bench.so: native timing loops for bench.py.
+//
+// Host code only.  Each step is one full call of the public C ABI
+// (validation, dispatch, one kernel launch) on one buffer set; step s uses set
+// s % nsets so that, with enough sets, every step reads x that has left the
+// caches.  Issuing the calls from C keeps the GPU fed: a Python-level call
+// costs more than a kernel of a few microseconds.
+#include <cstdint>
+
+#include "mi_norm.h"
+
+extern "C" {
+
+// LayerNorm: xs/ys/means/rstds are arrays of nsets device pointers
+// (means/rstds may be NULL, or hold NULL entries).  variant < 0 uses the
+// dispatcher.  Returns the first non-OK status, else MI_NORM_OK.
+int mi_bench_layernorm_loop(const float *const *xs, const float *gamma, const float *beta,
+                            float *const *ys, float *const *means, float *const *rstds, int nsets,
+                            int64_t rows, int64_t d, float eps, int steps, int variant,
+                            hipStream_t stream) {
+    for (int s = 0; s < steps; ++s) {
+        const int k = s % nsets;
+        float *m = means ? means[k] : nullptr;
+        float *r = rstds ? rstds[k] : nullptr;
+        const mi_norm_status st =
+            variant < 0 ? mi_layernorm_fwd(xs[k], gamma, beta, ys[k], rows, d, eps, m, r, stream)
+                        : mi_layernorm_fwd_variant(variant, xs[k], gamma, beta, ys[k], rows, d, eps, m,
+                                                   r, stream);
+        if (st != MI_NORM_OK) return st;
+    }
+    return MI_NORM_OK;
+}
+
+int mi_bench_rmsnorm_loop(const float *const *xs, const float *w, float *const *ys,
+                          float *const *rstds, int nsets, int64_t rows, int64_t d, float eps, int steps,
+                          int variant, hipStream_t stream) {
+    for (int s = 0; s < steps; ++s) {
+        const int k = s % nsets;
+        float *r = rstds ? rstds[k] : nullptr;
+        const mi_norm_status st =
+            variant < 0 ? mi_rmsnorm_fwd(xs[k], w, ys[k], rows, d, eps, r, stream)
+                        : mi_rmsnorm_fwd_variant(variant, xs[k], w, ys[k], rows, d, eps, r, stream);
+        if (st != MI_NORM_OK) return st;
+    }
+    return MI_NORM_OK;
+}
+
+int mi_bench_copy_loop(const float *const *srcs, float *const *dsts, int nsets, int64_t n, int steps,
+                       hipStream_t stream) {
+    for (int s = 0; s < steps; ++s) {
+        const int k = s % nsets;
+        const mi_norm_status st = mi_copy_f32(srcs[k], dsts[k], n, stream);
+        if (st != MI_NORM_OK) return st;
+    }
+    return MI_NORM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,514 @@
+// norm_kernels.hpp — gfx950 device code for forward LayerNorm / RMSNorm.
+//
+// The shape follows what "Field note 004: The load in flight, and the shape
+// Triton uses" (section "The layer norm was rewritten in the shape Triton
+// uses") found decisive: one pass over x, the row held in registers from load
+// to store, partial sums meeting once.  On CDNA4 that becomes:
+//
+//  * A row is owned by a 16/32/64-lane group of one wave64, or by W waves of a
+//    workgroup.  Each lane issues all of its 128-bit loads
+//    (global_load_dwordx4) before using any, keeping Q of them in VGPRs.
+//  * Statistics reduce inside the wave with DPP butterflies
+//    (quad_perm, row_half_mirror, row_mirror), then ds_swizzle or
+//    v_readlane across 16-lane rows: no LDS, no barrier.  When W > 1 waves
+//    share a row, each wave reduces its own (mean, centered M2) and the waves
+//    meet once in LDS behind one barrier, merged with the pairwise formula of
+//    Chan, Golub and LeVeque — the counterpart of the single exchange of
+//    "How the kernel time fell, step by step" (section "The layer norm was
+//    short of resident threads"), without its one-pass sum of squares.
+//  * rstd is v_rsq_f32, the one-instruction reciprocal root; gamma/beta are
+//    read once per row group and y leaves the same registers in 128-bit stores.
+//
+// Every lane of a wave executes every cross-lane step (lanes with nothing to
+// hold contribute zeros), so DPP sources are always active lanes and every
+// workgroup reaches every barrier the same number of times.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace minorm {
+
+enum : int { OP_LN = 0, OP_RMS = 1 };
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// Kernel arguments (one struct, passed by value).
+struct NormParams {
+    const float *x;
+    const float *p0;   // gamma (LayerNorm) or w (RMSNorm)
+    const float *p1;   // beta (LayerNorm); unused by RMSNorm
+    float *y;
+    float *mean;       // LayerNorm only; may be null
+    float *rstd;       // may be null
+    int64_t rows;      // rows of this launch
+    int32_t d;
+    float eps;
+    float inv_d;       // 1/d rounded to float32
+};
+
+// ---------------------------------------------------------------------------
+// cross-lane sums
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float readlane(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over aligned groups of G lanes (G = 16, 32 or 64).  Every lane of a
+// group ends with the same bits: each step adds a partner's value, and the
+// two partners add the same pair (IEEE addition commutes).
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(G == 16 || G == 32 || G == 64, "group of 16, 32 or 64 lanes");
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+    v += dpp<0x141>(v);  // row_half_mirror: the other quad of each 8 lanes
+    v += dpp<0x140>(v);  // row_mirror: the other half of each 16-lane row
+    if constexpr (G == 32) {
+        // ds_swizzle bit mode, and_mask 0x1f, xor_mask 0x10: lane ^ 16 within 32
+        v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+    } else if constexpr (G == 64) {
+        // the four 16-lane row sums, read into scalars: a wave-uniform result
+        const float r0 = readlane(v, 0), r1 = readlane(v, 16);
+        const float r2 = readlane(v, 32), r3 = readlane(v, 48);
+        v = (r0 + r1) + (r2 + r3);
+    }
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// memory helpers
+
+template <bool NT>
+__device__ __forceinline__ f4 ld4(const float *p) {
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const f4 *>(p));
+    else return *reinterpret_cast<const f4 *>(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ float ld1(const float *p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <bool NT>
+__device__ __forceinline__ void st4(float *p, f4 v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<f4 *>(p));
+    else *reinterpret_cast<f4 *>(p) = v;
+}
+
+template <bool NT>
+__device__ __forceinline__ void st1(float *p, float v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+__device__ __forceinline__ float hsum(f4 v) { return (v.x + v.y) + (v.z + v.w); }
+__device__ __forceinline__ float hsum(float v) { return v; }
+
+__device__ __forceinline__ float csq(f4 v, float mu) {
+    const f4 c = v - mu;
+    return (c.x * c.x + c.y * c.y) + (c.z * c.z + c.w * c.w);
+}
+__device__ __forceinline__ float csq(float v, float mu) { const float c = v - mu; return c * c; }
+
+__device__ __forceinline__ float sq(f4 v) { return (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w); }
+__device__ __forceinline__ float sq(float v) { return v * v; }
+
+__device__ __forceinline__ float rsq(float v) { return __builtin_amdgcn_rsqf(v); }
+
+// ---------------------------------------------------------------------------
+// Held-row kernel.
+//
+//   OP     OP_LN or OP_RMS
+//   VEC    4: 128-bit accesses (d % 4 == 0, 16-byte-aligned pointers), or
+//          1: 32-bit accesses (any d, any 4-byte alignment)
+//   PEEL   VEC == 4 only: per row, scalar head elements up to the first
+//          16-byte boundary of the row, a 128-bit body, and a scalar tail;
+//          needs x and y congruent mod 16 bytes, any d; gamma/beta are then
+//          read as scalars since their phase follows the row's
+//   LPR    lanes of one wave sharing a row (16, 32, 64); 64 / LPR rows per wave
+//   WPR    waves sharing a row (LPR == 64 when WPR > 1)
+//   Q      accesses held per lane; capacity = VEC * LPR * WPR * Q elements
+//   WAVES  waves per workgroup
+//   NTL/NTS  non-temporal x loads / y stores
+//
+// Lane li of wave rank wr holds access k = li + LPR * (wr + WPR * q),
+// q = 0..Q-1: consecutive lanes touch consecutive 16-byte (or 4-byte) words,
+// so each wave-wide access covers 1 KiB (256 B) of one row contiguously.
+template <int OP, int VEC, bool PEEL, int LPR, int WPR, int Q, int WAVES, bool NTL, bool NTS>
+__global__ __launch_bounds__(WAVES * 64)
+void norm_held(NormParams p)
+{
+    static_assert(VEC == 1 || VEC == 4, "VEC");
+    static_assert(!PEEL || (VEC == 4 && LPR == 64), "PEEL needs 128-bit, full-wave rows");
+    static_assert(LPR == 16 || LPR == 32 || LPR == 64, "LPR");
+    static_assert(WPR == 1 || LPR == 64, "multi-wave rows use full waves");
+    static_assert(WAVES % WPR == 0, "whole rows per workgroup");
+    using VT = typename std::conditional<VEC == 4, f4, float>::type;
+    constexpr int RPW = 64 / LPR;
+    constexpr int RPB = (WPR == 1) ? WAVES * RPW : WAVES / WPR;
+    // Hold gamma/beta (or w) beside x only while x + parameters stay within a
+    // quarter of the per-lane VGPR budget that WAVES-wide workgroups leave
+    // (128 at 16 waves, 256 at 8, 512 below).
+    constexpr int kParams = (OP == OP_LN) ? 2 : 1;
+    constexpr int kBudget = WAVES >= 16 ? 128 : (WAVES >= 8 ? 256 : 512);
+    constexpr bool PRELOAD = VEC * Q * (1 + kParams) <= kBudget / 4;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int wr = (WPR == 1) ? 0 : wave % WPR;
+    const int rib = (WPR == 1) ? wave * RPW + lane / LPR : wave / WPR;
+    const int li = (WPR == 1) ? lane % LPR : lane;
+
+    // (wave mean or sum of squares, wave M2) per row and wave: the one exchange
+    __shared__ float2 xch[RPB][WPR];
+
+    const int d = p.d;
+    const float eps = p.eps;
+    const float inv_d = p.inv_d;
+
+    // one row group per workgroup: the grid covers every row once
+    {
+        // A row past the end (only in the last workgroup) re-reads the last
+        // row and stores nothing, so every load below is in bounds without a
+        // branch: loads are unconditional at clamped addresses, and values a
+        // lane does not own are zeroed by selects.  Only stores are predicated.
+        const int64_t row_raw = (int64_t)blockIdx.x * RPB + rib;
+        const bool rv = row_raw < p.rows;
+        const int64_t row = rv ? row_raw : p.rows - 1;
+        const float *xr = p.x + row * (int64_t)d;
+        float *yr = p.y + row * (int64_t)d;
+
+        // row geometry: h head scalars, nvec body accesses, t tail scalars
+        int h = 0, t = 0, nvec;
+        if constexpr (PEEL) {
+            const int mis = (int)((reinterpret_cast<uintptr_t>(xr) >> 2) & 3);
+            h = (4 - mis) & 3;
+            if (h > d) h = d;
+            nvec = (d - h) >> 2;
+            t = d - h - 4 * nvec;
+        } else {
+            nvec = (VEC == 4) ? (d >> 2) : d;  // >= 1 for these paths
+        }
+        // only a peeled row narrower than 8 elements can have no body
+        const bool body = PEEL ? nvec > 0 : true;
+
+        // 1. issue every load of the row before using any.  Lane li of wave
+        // rank wr holds access k = li + LPR*(wr + WPR*q) of the body; an
+        // access past the body re-reads the body's last one.
+        int kc[Q];
+        bool ok[Q];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int k = li + LPR * (wr + WPR * q);
+            ok[q] = rv && k < nvec;
+            kc[q] = k < nvec ? k : nvec - 1;
+        }
+        VT v[Q];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            VT raw = VT(0.f);
+            if (body) {
+                if constexpr (VEC == 4) raw = ld4<NTL>(xr + h + 4 * kc[q]);
+                else raw = ld1<NTL>(xr + kc[q]);
+            }
+            v[q] = ok[q] ? raw : VT(0.f);
+        }
+        float hx = 0.f, tx = 0.f;
+        bool hok = false, tok = false;
+        int hi = 0, ti = 0;
+        if constexpr (PEEL) {
+            hok = rv && wr == 0 && li < h;
+            tok = rv && wr == 0 && li < t;
+            hi = li < h ? li : 0;
+            ti = h + 4 * nvec + li;
+            ti = ti < d ? ti : d - 1;
+            const float rh = xr[hi], rt = xr[ti];
+            hx = hok ? rh : 0.f;
+            tx = tok ? rt : 0.f;
+        }
+
+        // parameters for the output pass: fetched while x is in flight when
+        // the register budget allows, else slot by slot in the output pass
+        auto load_params = [&](int q, VT &gq, VT &bq) {
+            if constexpr (VEC == 4 && !PEEL) {
+                gq = ld4<false>(p.p0 + 4 * kc[q]);
+                if constexpr (OP == OP_LN) bq = ld4<false>(p.p1 + 4 * kc[q]);
+            } else if constexpr (VEC == 4) {
+                // the body's phase in the row decides the parameters' phase
+                const float *pg = p.p0 + h + 4 * kc[q];
+                gq = f4{pg[0], pg[1], pg[2], pg[3]};
+                if constexpr (OP == OP_LN) {
+                    const float *pb = p.p1 + h + 4 * kc[q];
+                    bq = f4{pb[0], pb[1], pb[2], pb[3]};
+                }
+            } else {
+                gq = p.p0[kc[q]];
+                if constexpr (OP == OP_LN) bq = p.p1[kc[q]];
+            }
+        };
+        VT g[Q], b[Q];
+        if constexpr (PRELOAD) {
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                g[q] = VT(1.f);
+                b[q] = VT(0.f);
+                if (body) load_params(q, g[q], b[q]);
+            }
+        }
+
+        // elements held by wave rank w of this row (all lanes agree)
+        auto wave_count = [&](int w) -> int {
+            int n = 0;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const int s = LPR * (w + WPR * q);
+                const int c = nvec - s;
+                n += c <= 0 ? 0 : (c >= LPR ? LPR : c);
+            }
+            n *= VEC;
+            if (w == 0) n += h + t;
+            return n;
+        };
+
+        float mu, rs;
+        if constexpr (OP == OP_LN) {
+            // 2. mean of what this wave holds
+            float s = 0.f;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) s += hsum(v[q]);
+            s += hx + tx;
+            const float S = group_sum<LPR>(s);
+            float mu_w;
+            if constexpr (WPR == 1) {
+                mu_w = S * inv_d;
+            } else {
+                const int n_w = wave_count(wr);
+                mu_w = n_w > 0 ? S / (float)n_w : 0.f;
+            }
+            // 3. squared deviations around it, from the same registers
+            float m = 0.f;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) m += ok[q] ? csq(v[q], mu_w) : 0.f;
+            m += hok ? csq(hx, mu_w) : 0.f;
+            m += tok ? csq(tx, mu_w) : 0.f;
+            const float M2_w = group_sum<LPR>(m);
+            float M2;
+            if constexpr (WPR == 1) {
+                mu = mu_w;
+                M2 = M2_w;
+            } else {
+                // one exchange: every wave's (mean, M2) meets in LDS behind one barrier
+                if (li == 0) xch[rib][wr] = make_float2(mu_w, M2_w);
+                __syncthreads();
+                // Chan-Golub-LeVeque merge, two passes over the broadcast LDS
+                // entries: mu = sum n_w mu_w / d, M2 = sum M2_w + n_w (mu_w - mu)^2
+                float tot = 0.f;
+#pragma unroll
+                for (int w = 0; w < WPR; ++w) tot += (float)wave_count(w) * xch[rib][w].x;
+                mu = tot * inv_d;
+                M2 = 0.f;
+#pragma unroll
+                for (int w = 0; w < WPR; ++w) {
+                    const float2 e = xch[rib][w];
+                    const float dm = e.x - mu;
+                    M2 += e.y + (float)wave_count(w) * dm * dm;
+                }
+            }
+            rs = rsq(M2 * inv_d + eps);
+        } else {
+            float s2 = 0.f;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) s2 += sq(v[q]);
+            s2 += hx * hx + tx * tx;
+            float S2 = group_sum<LPR>(s2);
+            if constexpr (WPR > 1) {
+                if (li == 0) xch[rib][wr] = make_float2(S2, 0.f);
+                __syncthreads();
+                S2 = 0.f;
+#pragma unroll
+                for (int w = 0; w < WPR; ++w) S2 += xch[rib][w].x;
+            }
+            mu = 0.f;
+            rs = rsq(S2 * inv_d + eps);
+        }
+
+        // 4. normalize, scale, shift; store from the same registers
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            VT gq, bq = VT(0.f);
+            if constexpr (PRELOAD) {
+                gq = g[q];
+                bq = b[q];
+            } else {
+                gq = VT(1.f);
+                if (body) load_params(q, gq, bq);
+            }
+            VT o;
+            if constexpr (OP == OP_LN) o = (v[q] - mu) * rs * gq + bq;
+            else o = v[q] * gq * rs;
+            if (ok[q]) {
+                if constexpr (VEC == 4) st4<NTS>(yr + h + 4 * kc[q], o);
+                else st1<NTS>(yr + kc[q], o);
+            }
+        }
+        if constexpr (PEEL) {
+            const float gh = p.p0[hi], gt = p.p0[ti];
+            const float bh = (OP == OP_LN) ? p.p1[hi] : 0.f;
+            const float bt = (OP == OP_LN) ? p.p1[ti] : 0.f;
+            const float oh = (OP == OP_LN) ? (hx - mu) * rs * gh + bh : hx * gh * rs;
+            const float ot = (OP == OP_LN) ? (tx - mu) * rs * gt + bt : tx * gt * rs;
+            if (hok) yr[hi] = oh;
+            if (tok) yr[ti] = ot;
+        }
+        if (rv && wr == 0 && li == 0) {
+            if (OP == OP_LN && p.mean) p.mean[row] = mu;
+            if (p.rstd) p.rstd[row] = rs;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Streamed-row kernel for rows wider than the held variants cover: one
+// workgroup per row, the row read in chunks; LayerNorm reads x three times
+// (sum, centered sum of squares, output), RMSNorm twice.  VEC as above
+// (no peel).  U accesses per lane per chunk are kept in flight.
+
+template <int WAVES>
+__device__ __forceinline__ float block_sum(float v, float (*red)[WAVES], int &slot, int wave, int lane) {
+    v = group_sum<64>(v);
+    if (lane == 0) red[slot][wave] = v;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) t += red[slot][w];
+    slot ^= 1;
+    return t;
+}
+
+template <int OP, int VEC, int WAVES, int U>
+__global__ __launch_bounds__(WAVES * 64)
+void norm_looped(NormParams p)
+{
+    using VT = typename std::conditional<VEC == 4, f4, float>::type;
+    constexpr int T = WAVES * 64;
+    __shared__ float red[2][WAVES];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int d = p.d;
+    const int nvec = (VEC == 4) ? (d >> 2) : d;
+    int slot = 0;
+
+    auto load = [&](const float *xr, int k) -> VT {
+        if constexpr (VEC == 4) return ld4<false>(xr + 4 * k);
+        else return xr[k];
+    };
+
+    for (int64_t row = blockIdx.x; row < p.rows; row += gridDim.x) {
+        const float *xr = p.x + row * (int64_t)d;
+        float *yr = p.y + row * (int64_t)d;
+        float mu = 0.f, rs;
+
+        // pass 1: sum (LayerNorm) or sum of squares (RMSNorm)
+        float s = 0.f;
+        for (int k0 = 0; k0 < nvec; k0 += T * U) {
+            VT v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k = k0 + tid + T * u;
+                v[u] = k < nvec ? load(xr, k) : VT(0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) s += (OP == OP_LN) ? hsum(v[u]) : sq(v[u]);
+        }
+        const float S = block_sum<WAVES>(s, red, slot, wave, lane);
+
+        if constexpr (OP == OP_LN) {
+            mu = S * p.inv_d;
+            // pass 2: squared deviations around the mean
+            float m = 0.f;
+            for (int k0 = 0; k0 < nvec; k0 += T * U) {
+                VT v[U];
+                bool ok[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int k = k0 + tid + T * u;
+                    ok[u] = k < nvec;
+                    v[u] = ok[u] ? load(xr, k) : VT(0.f);
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) m += ok[u] ? csq(v[u], mu) : 0.f;
+            }
+            const float M2 = block_sum<WAVES>(m, red, slot, wave, lane);
+            rs = rsq(M2 * p.inv_d + p.eps);
+        } else {
+            rs = rsq(S * p.inv_d + p.eps);
+        }
+
+        // final pass: normalize and store
+        for (int k0 = 0; k0 < nvec; k0 += T * U) {
+            VT v[U];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k = k0 + tid + T * u;
+                ok[u] = k < nvec;
+                v[u] = ok[u] ? load(xr, k) : VT(0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (!ok[u]) continue;
+                const int k = k0 + tid + T * u;
+                VT o;
+                if constexpr (OP == OP_LN) o = (v[u] - mu) * rs * load(p.p0, k) + load(p.p1, k);
+                else o = v[u] * load(p.p0, k) * rs;
+                if constexpr (VEC == 4) st4<false>(yr + 4 * k, o);
+                else yr[k] = o;
+            }
+        }
+        if (tid == 0) {
+            if (OP == OP_LN && p.mean) p.mean[row] = mu;
+            if (p.rstd) p.rstd[row] = rs;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Streaming copy (calibration): U 128-bit accesses per lane per step.
+template <int U>
+__global__ __launch_bounds__(256)
+void copy_f4(const float *src, float *dst, int64_t n4)
+{
+    const int64_t stride = (int64_t)gridDim.x * 256 * U;
+    for (int64_t base = (int64_t)blockIdx.x * 256 * U + threadIdx.x; base < n4; base += stride) {
+        f4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + 256 * u;
+            v[u] = i < n4 ? ld4<false>(src + 4 * i) : f4(0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + 256 * u;
+            if (i < n4) st4<false>(dst + 4 * i, v[u]);
+        }
+    }
+}
+
+__global__ __launch_bounds__(256)
+void copy_f1(const float *src, float *dst, int64_t n)
+{
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+}
+
+}  // namespace minorm

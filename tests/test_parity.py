@@ -1,0 +1,256 @@
+"""GPU parity: the HIP library (through its C ABI) against the float64 oracle.
+
+Acceptance is elementwise |gpu - ref| <= 1e-5 + 1e-4 |ref| on y, mean and rstd
+with no NaN/Inf, the bound of "RMSNorm on an RTX 5070" (section "Correctness
+before timing").  Outputs sit between guard regions filled with a sentinel
+that must survive, as on that page.  Every case prints its name first.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import row_wise_normalization_layernorm_amd as mn
+from row_wise_normalization_layernorm_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 1024          # floats of guard on each side of every output
+SENTINEL = -31415.5   # survives only if nothing writes outside its range
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    mn.lib()
+    return torch, torch.device("cuda:0")
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+
+
+class Guarded:
+    """A device float32 buffer of n elements at a chosen float offset, with
+    sentinel-filled guard regions around it."""
+
+    def __init__(self, torch, dev, n: int, offset: int = 0, init: np.ndarray | None = None):
+        self.torch, self.n, self.off = torch, n, GUARD + offset
+        self.buf = torch.full((2 * GUARD + n + 4,), SENTINEL, dtype=torch.float32, device=dev)
+        self.view = self.buf[self.off:self.off + n]
+        if init is not None:
+            self.view.copy_(torch.from_numpy(np.ascontiguousarray(init).reshape(-1)))
+
+    @property
+    def ptr(self) -> int:
+        return self.view.data_ptr()
+
+    def host(self) -> np.ndarray:
+        return self.view.cpu().numpy()
+
+    def guards_intact(self) -> bool:
+        b = self.buf.cpu().numpy()
+        return bool(np.all(b[:self.off] == SENTINEL) and np.all(b[self.off + self.n:] == SENTINEL))
+
+
+def check(got, ref, what: str):
+    ok, err, ratio = oracle.tolerance_ok(got, ref)
+    assert ok, f"{what}: max abs err {err:.3e}, worst err/bound {ratio:.3f}"
+    return err
+
+
+def run_case(torch, dev, op, x, params, eps=wl.EPS, stats=True, variant=None, xo=0, yo=None,
+             po=0, inplace=False):
+    """Run one case through the C ABI with guarded buffers; compare with the oracle."""
+    rows, d = x.shape
+    yo = xo if yo is None else yo
+    X = Guarded(torch, dev, rows * d, xo, x)
+    Y = X if inplace else Guarded(torch, dev, rows * d, yo)
+    P = [Guarded(torch, dev, d, po, p) for p in params]
+    M = Guarded(torch, dev, rows) if (stats and op == "layernorm") else None
+    R = Guarded(torch, dev, rows) if stats else None
+    L = mn.lib()
+    st = torch.cuda.current_stream().cuda_stream
+    if op == "layernorm":
+        if variant is None:
+            s = L.mi_layernorm_fwd(X.ptr, P[0].ptr, P[1].ptr, Y.ptr, rows, d, eps,
+                                   M.ptr if M else None, R.ptr if R else None, st)
+        else:
+            s = L.mi_layernorm_fwd_variant(variant, X.ptr, P[0].ptr, P[1].ptr, Y.ptr, rows, d, eps,
+                                           M.ptr if M else None, R.ptr if R else None, st)
+        ref = oracle.layernorm(x, *params, eps)
+        refs = [(Y, ref[0].reshape(-1), "y"), (M, ref[1], "mean"), (R, ref[2], "rstd")]
+    else:
+        if variant is None:
+            s = L.mi_rmsnorm_fwd(X.ptr, P[0].ptr, Y.ptr, rows, d, eps, R.ptr if R else None, st)
+        else:
+            s = L.mi_rmsnorm_fwd_variant(variant, X.ptr, P[0].ptr, Y.ptr, rows, d, eps,
+                                         R.ptr if R else None, st)
+        ref = oracle.rmsnorm(x, *params, eps)
+        refs = [(Y, ref[0].reshape(-1), "y"), (R, ref[1], "rstd")]
+    assert s == mn.MI_NORM_OK, mn.mi_norm_status_string(s)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for buf, want, what in refs:
+        if buf is None:
+            continue
+        worst = max(worst, check(buf.host(), want, what))
+        assert buf.guards_intact(), f"{what}: write outside the output range"
+    for p in P:
+        assert p.guards_intact()
+    if not inplace:
+        assert np.array_equal(X.host(), x.reshape(-1)), "x was modified"
+    return worst
+
+
+# --- the workload families ----------------------------------------------------
+
+@pytest.mark.parametrize("name", ["ln_small", "ln_4096x768", "ln_sweep", "rms"])
+def test_workload_family(torch_dev, name):
+    torch, dev = torch_dev
+    for case in wl.WORKLOADS[name].cases:
+        say(f"case {case.name}")
+        ins = case.inputs()
+        err = run_case(torch, dev, case.op, ins[0], ins[1:], stats=True)
+        say(f"  max abs err {err:.3e}")
+
+
+def test_ln_32768x8192_full_size(torch_dev):
+    """The bandwidth-saturating shape, every output compared, in the default
+    dispatch the benchmark times."""
+    torch, dev = torch_dev
+    case = wl.WORKLOADS["ln_32768x8192"].cases[0]
+    say(f"case {case.name}")
+    x, g, b = case.inputs()
+    rows, d = x.shape
+    xd = torch.from_numpy(x).to(dev)
+    yd = torch.empty_like(xd)
+    mean = torch.empty(rows, device=dev)
+    rstd = torch.empty(rows, device=dev)
+    mn.mi_layernorm_fwd(xd, torch.from_numpy(g).to(dev), torch.from_numpy(b).to(dev), yd, rows, d,
+                        wl.EPS, mean, rstd)
+    torch.cuda.synchronize()
+    y = yd.cpu().numpy()
+    del yd, xd
+    ry, rm, rr, _, _ = oracle.layernorm(x, g, b, wl.EPS)
+    for r0 in range(0, rows, 4096):
+        check(y[r0:r0 + 4096], ry[r0:r0 + 4096], f"y rows {r0}..")
+    check(mean.cpu().numpy(), rm, "mean")
+    check(rstd.cpu().numpy(), rr, "rstd")
+
+
+# --- every compiled variant, forced ------------------------------------------
+
+def _variant_widths(v):
+    """Widths that fill a variant exactly, leave a ragged last slot, and are small."""
+    if v["looped"]:
+        return [4 * 1237, 40000] if v["vec"] == 4 else [4947, 40001]
+    cap = v["max_d"]
+    if v["peel"]:
+        return sorted(w for w in {cap - 3, cap - 1 - 4 * 64, max(3, cap // 3 - 1), 5} if w >= 1)
+    step = 4 if v["vec"] == 4 else 1
+    widths = {cap, cap - step * max(1, cap // (7 * step)), step}
+    return sorted(w for w in widths if w >= 1)
+
+
+def _variant_layout(v):
+    if v["needs_aligned"]:
+        return dict(xo=0, yo=0, po=0)
+    if v["peel"]:
+        return dict(xo=1, yo=1, po=2)   # x and y share their 16-byte phase
+    return dict(xo=1, yo=2, po=3)       # nothing aligned
+
+
+def test_every_variant(torch_dev):
+    torch, dev = torch_dev
+    n = mn.mi_norm_variant_count()
+    for vid in range(n):
+        v = mn.mi_norm_variant_get_info(vid)
+        name = mn.mi_norm_variant_name(vid)
+        op = "layernorm" if v["op"] == mn.OP_LAYERNORM else "rmsnorm"
+        lay = _variant_layout(v)
+        for d in _variant_widths(v):
+            rows = min(3 * v["rows_per_block"] + 1, max(2, 600000 // d))
+            say(f"variant {vid} {name} rows={rows} d={d} {lay}")
+            x = wl.make_x(rows, d, "offset", [7, vid, d])
+            params = wl.make_affine(d, [7, d]) if op == "layernorm" else (wl.make_weight(d, [7, d]),)
+            run_case(torch, dev, op, x, params, variant=vid, **lay)
+
+
+# --- layouts, aliasing, ordering ---------------------------------------------
+
+@pytest.mark.parametrize("op", ["layernorm", "rmsnorm"])
+@pytest.mark.parametrize("d,xo,yo,po", [(768, 0, 0, 0), (768, 1, 1, 0), (768, 1, 2, 0),
+                                        (768, 0, 0, 1), (8193, 0, 0, 0), (8193, 3, 3, 1),
+                                        (4096, 2, 0, 0), (33, 1, 3, 2), (1, 0, 0, 0)])
+def test_layouts_dispatch(torch_dev, op, d, xo, yo, po):
+    torch, dev = torch_dev
+    rows = 37
+    say(f"layout {op} d={d} xo={xo} yo={yo} po={po}")
+    x = wl.make_x(rows, d, "offset", [8, d, xo, yo])
+    params = wl.make_affine(d, [8, d]) if op == "layernorm" else (wl.make_weight(d, [8, d]),)
+    run_case(torch, dev, op, x, params, xo=xo, yo=yo, po=po)
+
+
+@pytest.mark.parametrize("op", ["layernorm", "rmsnorm"])
+@pytest.mark.parametrize("d,xo", [(768, 0), (2049, 1), (127, 3), (16384, 0)])
+def test_in_place(torch_dev, op, d, xo):
+    torch, dev = torch_dev
+    say(f"in place {op} d={d} xo={xo}")
+    x = wl.make_x(45, d, "normal", [9, d])
+    params = wl.make_affine(d, [9, d]) if op == "layernorm" else (wl.make_weight(d, [9, d]),)
+    run_case(torch, dev, op, x, params, xo=xo, inplace=True)
+
+
+def test_without_stats_and_eps_zero(torch_dev):
+    torch, dev = torch_dev
+    say("no stats, eps = 0")
+    x = wl.make_x(64, 768, "normal", [10])
+    g, b = wl.make_affine(768, [10])
+    run_case(torch, dev, "layernorm", x, (g, b), eps=0.0, stats=False)
+    run_case(torch, dev, "rmsnorm", x, (g,), eps=0.0, stats=False)
+
+
+def test_stream_ordering(torch_dev):
+    """Work enqueued on a side stream runs after the torch op that produced x."""
+    torch, dev = torch_dev
+    say("stream ordering")
+    rows, d = 2048, 1024
+    x = wl.make_x(rows, d, "normal", [11])
+    g, b = wl.make_affine(d, [11])
+    xs = torch.from_numpy(x).to(dev)
+    gd, bd = torch.from_numpy(g).to(dev), torch.from_numpy(b).to(dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        xd = torch.empty_like(xs)
+        xd.copy_(xs * 2.0)      # produced on s, consumed on s
+        yd = torch.empty_like(xd)
+        mn.mi_layernorm_fwd(xd, gd, bd, yd, rows, d, wl.EPS, stream=s)
+    torch.cuda.synchronize()
+    ref = oracle.layernorm((x.astype(np.float64) * 2).astype(np.float32), g, b, wl.EPS)[0]
+    check(yd.cpu().numpy(), ref, "y on a side stream")
+
+
+def test_rows_zero_and_errors_on_device(torch_dev):
+    torch, dev = torch_dev
+    say("rows = 0, bad args with device pointers")
+    x = torch.zeros(4, 8, device=dev)
+    g = torch.ones(8, device=dev)
+    mn.mi_layernorm_fwd(x, g, g, x, 0, 8)
+    with pytest.raises(mn.MiNormError):
+        mn.mi_layernorm_fwd(x, g, g, x, 4, 8, eps=-1.0)
+    assert torch.all(x == 0)
+
+
+def test_copy_calibration_kernel(torch_dev):
+    torch, dev = torch_dev
+    say("copy kernel")
+    for n, off in ((1 << 20, 0), (1000003, 0), (4096, 1)):
+        src = torch.randn(n + 4, device=dev)[off:off + n]
+        dst = torch.zeros(n + 4, device=dev)[off:off + n]
+        mn.mi_copy_f32(src, dst, n)
+        torch.cuda.synchronize()
+        assert torch.equal(src, dst)
