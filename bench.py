@@ -191,6 +191,9 @@ def main(argv=None) -> int:
     means = [torch.empty(rows, device=dev) for _ in range(nsets)] if (stats and op == "layernorm") else None
     rstds = [torch.empty(rows, device=dev) for _ in range(nsets)] if stats else None
     params = [torch.from_numpy(p).to(dev) for p in params_h]
+    # every buffer above was filled on torch's current stream; the kernels run on
+    # their own stream, so make the set-up complete before anything is launched
+    torch.cuda.synchronize()
 
     vid = -1
     if args.variant:
@@ -201,7 +204,7 @@ def main(argv=None) -> int:
         vid = names.index(args.variant)
     if op != "copy":
         sel = vid if vid >= 0 else mn.mi_norm_select_variant(
-            mn.OP_LAYERNORM if op == "layernorm" else mn.OP_RMSNORM, d, x0, ys[0], params[0],
+            mn.OP_LAYERNORM if op == "layernorm" else mn.OP_RMSNORM, rows, d, x0, ys[0], params[0],
             params[1] if op == "layernorm" else None)
         variant_name = mn.mi_norm_variant_name(sel)
     else:

@@ -34,14 +34,15 @@
  *   without waiting.  One kernel launch per call; calls may be captured into a
  *   HIP graph.
  * - Aliasing: y may equal x exactly (in place).  Any other overlap between y
- *   and x is rejected.  mean/rstd must not overlap x, y or the parameters.
+ *   and x, and any overlap of y with gamma, beta or w, is rejected.  mean/rstd
+ *   must not overlap x, y or the parameters.
  * - 16-byte-aligned x, y, gamma, beta (or w) and d % 4 == 0 select the
  *   128-bit vector path; other layouts take a peeled or scalar path with the
  *   same results.
  * - Errors: MI_NORM_ERR_INVALID is returned before any launch for a NULL
  *   required pointer, a pointer not 4-byte aligned, rows < 0, d < 1,
- *   d > 2^31 - 1, a size overflow, eps NaN or negative, or a partial
- *   overlap of y with x.  rows == 0 returns MI_NORM_OK and launches nothing.
+ *   d > 2^31 - 1, a size overflow, eps NaN or negative, a partial overlap of
+ *   y with x, or an overlap of y with a parameter vector.  rows == 0 returns MI_NORM_OK and launches nothing.
  *   MI_NORM_ERR_HIP reports a failed launch (the HIP error is not kept;
  *   faults inside the kernel surface at the caller's next synchronization,
  *   as usual for HIP).  No C++ exception crosses this interface.
@@ -104,7 +105,8 @@ mi_norm_status mi_rmsnorm_fwd(const float *x, const float *w, float *y,
 
 /* ---------------------------------------------------------------------------
  * Kernel variants.  Every call above is served by one compiled kernel variant
- * chosen from (operation, d, pointer alignment).  The calls below expose that
+ * chosen from the operation, the row width d, the pointer alignment and the
+ * row count.  The calls below expose that
  * table so tests can drive every variant and benchmarks can compare them.
  * They follow the same conventions and error rules as the calls above.
  */
@@ -135,9 +137,11 @@ const char *mi_norm_variant_name(int id);
 mi_norm_status mi_norm_variant_get_info(int id, mi_norm_variant_info *out);
 
 /* The variant the dispatcher would choose for these arguments (host logic
- * only, no device access).  params1 is beta for LayerNorm and ignored
- * (may be NULL) for RMSNorm.  Returns -1 when the arguments are invalid. */
-int mi_norm_select_variant(int op, int64_t d, const void *x, const void *y,
+ * only, no device access): the row width and pointer alignment pick the
+ * shape, the row count picks the workgroup size.  params1 is beta for
+ * LayerNorm and ignored (may be NULL) for RMSNorm.  Returns -1 when the
+ * arguments are invalid. */
+int mi_norm_select_variant(int op, int64_t rows, int64_t d, const void *x, const void *y,
                            const void *params0, const void *params1);
 
 /* Whether variant `id` can run these arguments (1) or not (0). */

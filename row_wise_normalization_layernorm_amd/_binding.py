@@ -65,7 +65,7 @@ _SIGNATURES = {
     "mi_norm_variant_count": (_I, []),
     "mi_norm_variant_name": (ctypes.c_char_p, [_I]),
     "mi_norm_variant_get_info": (_I, [_I, ctypes.POINTER(VariantInfo)]),
-    "mi_norm_select_variant": (_I, [_I, _I64, _VP, _VP, _VP, _VP]),
+    "mi_norm_select_variant": (_I, [_I, _I64, _I64, _VP, _VP, _VP, _VP]),
     "mi_norm_variant_eligible": (_I, [_I, _I, _I64, _VP, _VP, _VP, _VP]),
     "mi_layernorm_fwd_variant": (_I, [_I, _VP, _VP, _VP, _VP, _I64, _I64, _F, _VP, _VP, _VP]),
     "mi_rmsnorm_fwd_variant": (_I, [_I, _VP, _VP, _VP, _I64, _I64, _F, _VP, _VP]),
@@ -208,8 +208,9 @@ def _addr(a):
     return a if (a is None or isinstance(a, int)) else a.data_ptr()
 
 
-def mi_norm_select_variant(op: int, d: int, x, y, params0, params1=None) -> int:
-    return int(lib().mi_norm_select_variant(op, d, _addr(x), _addr(y), _addr(params0), _addr(params1)))
+def mi_norm_select_variant(op: int, rows: int, d: int, x, y, params0, params1=None) -> int:
+    return int(lib().mi_norm_select_variant(op, rows, d, _addr(x), _addr(y), _addr(params0),
+                                            _addr(params1)))
 
 
 def mi_norm_variant_eligible(vid: int, op: int, d: int, x, y, params0, params1=None) -> bool:

@@ -31,13 +31,19 @@ struct Variant {
 
 constexpr int64_t kUnbounded = INT64_MAX;
 
+// Every held variant streams x in and y out with non-temporal hints and
+// reads gamma/beta in the output pass (see norm_held's NTL/NTS/PRE).
 #define MI_HELD(OP, OPN, VEC, PEEL, LPR, WPR, Q, WAVES)                                        \
     Variant{OPN "_" #VEC "_p" #PEEL "_l" #LPR "_w" #WPR "_q" #Q "_b" #WAVES,                  \
             mi_norm_variant_info{OP, VEC, PEEL, 0, LPR, WPR, Q, WAVES,                          \
                                  (WPR == 1) ? WAVES * (64 / LPR) : WAVES / WPR,                 \
                                  (int64_t)VEC * LPR * WPR * Q, (VEC == 4 && !PEEL) ? 1 : 0},    \
             reinterpret_cast<const void *>(                                                     \
-                &norm_held<OP, VEC, (PEEL != 0), LPR, WPR, Q, WAVES, false, false>)}
+                &norm_held<OP, VEC, (PEEL != 0), LPR, WPR, Q, WAVES, true, true, 0>)}
+
+// the same shape with 4 and with 16 waves per workgroup
+#define MI_HELD2(OP, OPN, VEC, PEEL, LPR, WPR, Q, WSMALL)                                      \
+    MI_HELD(OP, OPN, VEC, PEEL, LPR, WPR, Q, WSMALL), MI_HELD(OP, OPN, VEC, PEEL, LPR, WPR, Q, 16)
 
 #define MI_LOOP(OP, OPN, VEC, WAVES, U)                                                        \
     Variant{OPN "_" #VEC "_loop_b" #WAVES "_u" #U,                                              \
@@ -47,33 +53,33 @@ constexpr int64_t kUnbounded = INT64_MAX;
 
 #define MI_OP_TABLE(OP, OPN)                                                                   \
     /* 128-bit, aligned, d % 4 == 0 */                                                          \
-    MI_HELD(OP, OPN, 4, 0, 16, 1, 1, 4), MI_HELD(OP, OPN, 4, 0, 32, 1, 1, 4),                   \
-    MI_HELD(OP, OPN, 4, 0, 64, 1, 1, 4), MI_HELD(OP, OPN, 4, 0, 64, 1, 2, 4),                   \
-    MI_HELD(OP, OPN, 4, 0, 64, 1, 3, 4), MI_HELD(OP, OPN, 4, 0, 64, 1, 4, 4),                   \
-    MI_HELD(OP, OPN, 4, 0, 64, 1, 6, 4), MI_HELD(OP, OPN, 4, 0, 64, 1, 8, 4),                   \
-    MI_HELD(OP, OPN, 4, 0, 64, 2, 4, 4), MI_HELD(OP, OPN, 4, 0, 64, 2, 8, 4),                   \
-    MI_HELD(OP, OPN, 4, 0, 64, 4, 2, 4), MI_HELD(OP, OPN, 4, 0, 64, 4, 3, 4),                   \
-    MI_HELD(OP, OPN, 4, 0, 64, 4, 4, 4), MI_HELD(OP, OPN, 4, 0, 64, 4, 6, 4),                   \
-    MI_HELD(OP, OPN, 4, 0, 64, 4, 8, 4),                                                        \
-    MI_HELD(OP, OPN, 4, 0, 64, 8, 2, 8), MI_HELD(OP, OPN, 4, 0, 64, 8, 3, 8),                   \
-    MI_HELD(OP, OPN, 4, 0, 64, 8, 4, 8), MI_HELD(OP, OPN, 4, 0, 64, 8, 6, 8),                   \
-    MI_HELD(OP, OPN, 4, 0, 64, 8, 8, 8),                                                        \
+    MI_HELD2(OP, OPN, 4, 0, 16, 1, 1, 4), MI_HELD2(OP, OPN, 4, 0, 32, 1, 1, 4),                 \
+    MI_HELD2(OP, OPN, 4, 0, 64, 1, 1, 4), MI_HELD2(OP, OPN, 4, 0, 64, 1, 2, 4),                 \
+    MI_HELD2(OP, OPN, 4, 0, 64, 1, 3, 4), MI_HELD2(OP, OPN, 4, 0, 64, 1, 4, 4),                 \
+    MI_HELD2(OP, OPN, 4, 0, 64, 1, 6, 4), MI_HELD2(OP, OPN, 4, 0, 64, 1, 8, 4),                 \
+    MI_HELD2(OP, OPN, 4, 0, 64, 2, 4, 4), MI_HELD2(OP, OPN, 4, 0, 64, 2, 8, 4),                 \
+    MI_HELD2(OP, OPN, 4, 0, 64, 4, 2, 4), MI_HELD2(OP, OPN, 4, 0, 64, 4, 3, 4),                 \
+    MI_HELD2(OP, OPN, 4, 0, 64, 4, 4, 4), MI_HELD2(OP, OPN, 4, 0, 64, 4, 6, 4),                 \
+    MI_HELD2(OP, OPN, 4, 0, 64, 4, 8, 4),                                                       \
+    MI_HELD2(OP, OPN, 4, 0, 64, 8, 2, 8), MI_HELD2(OP, OPN, 4, 0, 64, 8, 3, 8),                 \
+    MI_HELD2(OP, OPN, 4, 0, 64, 8, 4, 8), MI_HELD2(OP, OPN, 4, 0, 64, 8, 6, 8),                 \
+    MI_HELD2(OP, OPN, 4, 0, 64, 8, 8, 8),                                                       \
     MI_HELD(OP, OPN, 4, 0, 64, 16, 3, 16), MI_HELD(OP, OPN, 4, 0, 64, 16, 4, 16),               \
     MI_HELD(OP, OPN, 4, 0, 64, 16, 6, 16), MI_HELD(OP, OPN, 4, 0, 64, 16, 8, 16),               \
     /* 128-bit body with a per-row scalar head and tail: any d, x == y mod 16 B */              \
-    MI_HELD(OP, OPN, 4, 1, 64, 1, 1, 4), MI_HELD(OP, OPN, 4, 1, 64, 1, 2, 4),                   \
-    MI_HELD(OP, OPN, 4, 1, 64, 1, 3, 4), MI_HELD(OP, OPN, 4, 1, 64, 1, 4, 4),                   \
-    MI_HELD(OP, OPN, 4, 1, 64, 1, 6, 4), MI_HELD(OP, OPN, 4, 1, 64, 1, 8, 4),                   \
-    MI_HELD(OP, OPN, 4, 1, 64, 4, 3, 4), MI_HELD(OP, OPN, 4, 1, 64, 4, 4, 4),                   \
-    MI_HELD(OP, OPN, 4, 1, 64, 8, 3, 8), MI_HELD(OP, OPN, 4, 1, 64, 8, 4, 8),                   \
+    MI_HELD2(OP, OPN, 4, 1, 64, 1, 1, 4), MI_HELD2(OP, OPN, 4, 1, 64, 1, 2, 4),                 \
+    MI_HELD2(OP, OPN, 4, 1, 64, 1, 3, 4), MI_HELD2(OP, OPN, 4, 1, 64, 1, 4, 4),                 \
+    MI_HELD2(OP, OPN, 4, 1, 64, 1, 6, 4), MI_HELD2(OP, OPN, 4, 1, 64, 1, 8, 4),                 \
+    MI_HELD2(OP, OPN, 4, 1, 64, 4, 3, 4), MI_HELD2(OP, OPN, 4, 1, 64, 4, 4, 4),                 \
+    MI_HELD2(OP, OPN, 4, 1, 64, 8, 3, 8), MI_HELD2(OP, OPN, 4, 1, 64, 8, 4, 8),                 \
     MI_HELD(OP, OPN, 4, 1, 64, 16, 3, 16), MI_HELD(OP, OPN, 4, 1, 64, 16, 4, 16),               \
     MI_HELD(OP, OPN, 4, 1, 64, 16, 6, 16), MI_HELD(OP, OPN, 4, 1, 64, 16, 8, 16),               \
     /* 32-bit accesses: any d, any 4-byte alignment */                                          \
-    MI_HELD(OP, OPN, 1, 0, 16, 1, 1, 4), MI_HELD(OP, OPN, 1, 0, 32, 1, 1, 4),                   \
-    MI_HELD(OP, OPN, 1, 0, 64, 1, 1, 4), MI_HELD(OP, OPN, 1, 0, 64, 1, 2, 4),                   \
-    MI_HELD(OP, OPN, 1, 0, 64, 1, 4, 4), MI_HELD(OP, OPN, 1, 0, 64, 1, 8, 4),                   \
-    MI_HELD(OP, OPN, 1, 0, 64, 4, 4, 4), MI_HELD(OP, OPN, 1, 0, 64, 4, 8, 4),                   \
-    MI_HELD(OP, OPN, 1, 0, 64, 8, 8, 8),                                                        \
+    MI_HELD2(OP, OPN, 1, 0, 16, 1, 1, 4), MI_HELD2(OP, OPN, 1, 0, 32, 1, 1, 4),                 \
+    MI_HELD2(OP, OPN, 1, 0, 64, 1, 1, 4), MI_HELD2(OP, OPN, 1, 0, 64, 1, 2, 4),                 \
+    MI_HELD2(OP, OPN, 1, 0, 64, 1, 4, 4), MI_HELD2(OP, OPN, 1, 0, 64, 1, 8, 4),                 \
+    MI_HELD2(OP, OPN, 1, 0, 64, 4, 4, 4), MI_HELD2(OP, OPN, 1, 0, 64, 4, 8, 4),                 \
+    MI_HELD2(OP, OPN, 1, 0, 64, 8, 8, 8),                                                       \
     MI_HELD(OP, OPN, 1, 0, 64, 16, 8, 16), MI_HELD(OP, OPN, 1, 0, 64, 16, 16, 16),              \
     /* streamed rows, any width */                                                             \
     MI_LOOP(OP, OPN, 4, 4, 4), MI_LOOP(OP, OPN, 1, 4, 8)
@@ -92,14 +98,28 @@ constexpr int64_t kMaxRowGroups = int64_t(1) << 30;
 inline bool al16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool al4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-int find(int op, int vec, int peel, int looped, int lpr, int wpr, int q) {
+// Fewest workgroups that still cover every CU: of the variants with this
+// shape, the one with the most waves per workgroup whose grid has at least
+// kMinBlocks workgroups; failing that, the one with the most workgroups.
+constexpr int64_t kMinBlocks = 256;
+
+int find(int op, int64_t rows, int vec, int peel, int looped, int lpr, int wpr, int q) {
+    int best = -1, fallback = -1;
+    int64_t fallback_blocks = -1;
     for (int i = 0; i < kNumVariants; ++i) {
         const mi_norm_variant_info &v = kVariants[i].info;
-        if (v.op == op && v.vec == vec && v.peel == peel && v.looped == looped &&
-            (looped || (v.lanes_per_row == lpr && v.waves_per_row == wpr && v.slots == q)))
-            return i;
+        if (v.op != op || v.vec != vec || v.peel != peel || v.looped != looped) continue;
+        if (looped) return i;
+        if (v.lanes_per_row != lpr || v.waves_per_row != wpr || v.slots != q) continue;
+        const int64_t blocks = (rows + v.rows_per_block - 1) / v.rows_per_block;
+        if (blocks >= kMinBlocks && (best < 0 || v.waves_per_block > kVariants[best].info.waves_per_block))
+            best = i;
+        if (blocks > fallback_blocks) {
+            fallback = i;
+            fallback_blocks = blocks;
+        }
     }
-    return -1;
+    return best >= 0 ? best : fallback;
 }
 
 // smallest listed slot count q with cap_per_slot * q >= n, or 0
@@ -174,23 +194,24 @@ bool args_ok(int op, int64_t d, const void *x, const void *y, const void *p0, co
     return true;
 }
 
-int select_variant(int op, int64_t d, const void *x, const void *y, const void *p0, const void *p1) {
-    if (!args_ok(op, d, x, y, p0, p1)) return -1;
+int select_variant(int op, int64_t rows, int64_t d, const void *x, const void *y, const void *p0,
+                   const void *p1) {
+    if (!args_ok(op, d, x, y, p0, p1) || rows < 0) return -1;
     const Layout L = layout_of(op, d, x, y, p0, p1);
     int lpr, wpr, q;
     if (L.a16) {
         ladder4(d / 4, true, lpr, wpr, q);
-        if (wpr) return find(op, 4, 0, 0, lpr, wpr, q);
-        return find(op, 4, 0, 1, 0, 0, 0);
+        if (wpr) return find(op, rows, 4, 0, 0, lpr, wpr, q);
+        return find(op, rows, 4, 0, 1, 0, 0, 0);
     }
     if (L.peel_ok && d >= 256) {
         ladder_peel((d + 3) / 4, wpr, q);
-        if (wpr) return find(op, 4, 1, 0, 64, wpr, q);
-        return find(op, 1, 0, 1, 0, 0, 0);
+        if (wpr) return find(op, rows, 4, 1, 0, 64, wpr, q);
+        return find(op, rows, 1, 0, 1, 0, 0, 0);
     }
     ladder1(d, lpr, wpr, q);
-    if (wpr) return find(op, 1, 0, 0, lpr, wpr, q);
-    return find(op, 1, 0, 1, 0, 0, 0);
+    if (wpr) return find(op, rows, 1, 0, 0, lpr, wpr, q);
+    return find(op, rows, 1, 0, 1, 0, 0, 0);
 }
 
 bool eligible(int id, int op, int64_t d, const void *x, const void *y, const void *p0, const void *p1) {
@@ -213,6 +234,12 @@ bool overlap_ok(const void *x, const void *y, int64_t rows, int64_t d) {
     return a + bytes <= b || b + bytes <= a;
 }
 
+// [a, a + na) and [b, b + nb) (in floats) intersect
+bool ranges_meet(const void *a, int64_t na, const void *b, int64_t nb) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + (uintptr_t)nb * sizeof(float) && pb < pa + (uintptr_t)na * sizeof(float);
+}
+
 mi_norm_status validate(int op, const float *x, const float *p0, const float *p1, const float *y,
                         int64_t rows, int64_t d, float eps, const float *mean, const float *rstd) {
     if (!args_ok(op, d, x, y, p0, p1)) return MI_NORM_ERR_INVALID;
@@ -221,6 +248,9 @@ mi_norm_status validate(int op, const float *x, const float *p0, const float *p1
     if (rows > 0 && rows > (INT64_MAX / (int64_t)sizeof(float)) / d) return MI_NORM_ERR_INVALID;
     if ((mean && !al4(mean)) || (rstd && !al4(rstd))) return MI_NORM_ERR_INVALID;
     if (!overlap_ok(x, y, rows, d)) return MI_NORM_ERR_INVALID;
+    // parameters are read after earlier slots of y are stored
+    if (rows > 0 && (ranges_meet(y, rows * d, p0, d) || (p1 && ranges_meet(y, rows * d, p1, d))))
+        return MI_NORM_ERR_INVALID;
     return MI_NORM_OK;
 }
 
@@ -279,7 +309,7 @@ mi_norm_status run(int op, int forced, const float *x, const float *p0, const fl
     if (st != MI_NORM_OK) return st;
     int id = forced;
     if (id < 0) {
-        id = select_variant(op, d, x, y, p0, p1);
+        id = select_variant(op, rows, d, x, y, p0, p1);
         if (id < 0) return MI_NORM_ERR_INVALID;
     } else if (!eligible(id, op, d, x, y, p0, p1)) {
         return MI_NORM_ERR_INVALID;
@@ -326,9 +356,9 @@ mi_norm_status mi_norm_variant_get_info(int id, mi_norm_variant_info *out) {
     return MI_NORM_OK;
 }
 
-int mi_norm_select_variant(int op, int64_t d, const void *x, const void *y, const void *params0,
-                           const void *params1) {
-    return select_variant(op, d, x, y, params0, params1);
+int mi_norm_select_variant(int op, int64_t rows, int64_t d, const void *x, const void *y,
+                           const void *params0, const void *params1) {
+    return select_variant(op, rows, d, x, y, params0, params1);
 }
 
 int mi_norm_variant_eligible(int id, int op, int64_t d, const void *x, const void *y,
@@ -357,16 +387,20 @@ mi_norm_status mi_copy_f32(const float *src, float *dst, int64_t n, hipStream_t 
     if (!overlap_ok(src, dst, 1, n) || src == dst) return MI_NORM_ERR_INVALID;
     hipError_t e;
     if (n % 4 == 0 && al16(src) && al16(dst)) {
-        constexpr int U = 4;
+        // one 128-bit access per lane for large copies, two below 256 MiB
+        // (the faster shapes on gfx950 at 2 GiB and at 24 MiB)
         const int64_t n4 = n / 4;
+        const bool big = n4 >= (int64_t(1) << 24);
+        const int U = big ? 1 : 2;
         int64_t blocks = (n4 + 256 * U - 1) / (256 * U);
         if (blocks > kMaxGrid) blocks = kMaxGrid;
         int64_t n4a = n4;
         const float *s = src;
         float *dd = dst;
         void *args[] = {&s, &dd, &n4a};
-        e = hipLaunchKernel(reinterpret_cast<const void *>(&copy_f4<U>), dim3((unsigned)blocks), dim3(256),
-                            args, 0, stream);
+        const void *fn = big ? reinterpret_cast<const void *>(&copy_f4<1>)
+                             : reinterpret_cast<const void *>(&copy_f4<2>);
+        e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, stream);
     } else {
         int64_t blocks = (n + 255) / 256;
         if (blocks > kMaxGrid) blocks = kMaxGrid;

@@ -138,11 +138,16 @@ __device__ __forceinline__ float rsq(float v) { return __builtin_amdgcn_rsqf(v);
 //   Q      accesses held per lane; capacity = VEC * LPR * WPR * Q elements
 //   WAVES  waves per workgroup
 //   NTL/NTS  non-temporal x loads / y stores
+//   PRE    where the output pass gets gamma/beta (or w): 0: global loads in
+//          the output pass; 1: global loads issued while x is in flight;
+//          2: staged once per workgroup in LDS at kernel start (128-bit
+//          aligned path only); -1: 1 or 0 by the register budget
 //
 // Lane li of wave rank wr holds access k = li + LPR * (wr + WPR * q),
 // q = 0..Q-1: consecutive lanes touch consecutive 16-byte (or 4-byte) words,
 // so each wave-wide access covers 1 KiB (256 B) of one row contiguously.
-template <int OP, int VEC, bool PEEL, int LPR, int WPR, int Q, int WAVES, bool NTL, bool NTS>
+template <int OP, int VEC, bool PEEL, int LPR, int WPR, int Q, int WAVES, bool NTL, bool NTS,
+          int PRE = -1>
 __global__ __launch_bounds__(WAVES * 64)
 void norm_held(NormParams p)
 {
@@ -159,7 +164,11 @@ void norm_held(NormParams p)
     // (128 at 16 waves, 256 at 8, 512 below).
     constexpr int kParams = (OP == OP_LN) ? 2 : 1;
     constexpr int kBudget = WAVES >= 16 ? 128 : (WAVES >= 8 ? 256 : 512);
-    constexpr bool PRELOAD = VEC * Q * (1 + kParams) <= kBudget / 4;
+    constexpr bool PRELOAD = PRE >= 0 ? PRE == 1 : VEC * Q * (1 + kParams) <= kBudget / 4;
+    constexpr bool PLDS = PRE == 2;
+    static_assert(!PLDS || (VEC == 4 && !PEEL), "LDS parameters need the aligned 128-bit path");
+    constexpr int kCapV = LPR * WPR * Q;  // 16-byte accesses per row the variant covers
+    static_assert(!PLDS || kCapV * kParams * 16 <= 64 * 1024, "LDS parameter stage too large");
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -170,10 +179,21 @@ void norm_held(NormParams p)
 
     // (wave mean or sum of squares, wave M2) per row and wave: the one exchange
     __shared__ float2 xch[RPB][WPR];
+    __shared__ f4 lds_par[PLDS ? kParams : 1][PLDS ? kCapV : 1];
 
     const int d = p.d;
     const float eps = p.eps;
     const float inv_d = p.inv_d;
+
+    if constexpr (PLDS) {
+        // every lane of the workgroup copies part of gamma/beta into LDS; the
+        // barrier before the output pass publishes it
+        const int nv = d >> 2;
+        for (int i = tid; i < nv && i < kCapV; i += WAVES * 64) {
+            lds_par[0][i] = ld4<false>(p.p0 + 4 * i);
+            if constexpr (OP == OP_LN) lds_par[kParams - 1][i] = ld4<false>(p.p1 + 4 * i);
+        }
+    }
 
     // one row group per workgroup: the grid covers every row once
     {
@@ -239,7 +259,10 @@ void norm_held(NormParams p)
         // parameters for the output pass: fetched while x is in flight when
         // the register budget allows, else slot by slot in the output pass
         auto load_params = [&](int q, VT &gq, VT &bq) {
-            if constexpr (VEC == 4 && !PEEL) {
+            if constexpr (PLDS) {
+                gq = lds_par[0][kc[q]];
+                if constexpr (OP == OP_LN) bq = lds_par[kParams - 1][kc[q]];
+            } else if constexpr (VEC == 4 && !PEEL) {
                 gq = ld4<false>(p.p0 + 4 * kc[q]);
                 if constexpr (OP == OP_LN) bq = ld4<false>(p.p1 + 4 * kc[q]);
             } else if constexpr (VEC == 4) {
@@ -341,6 +364,7 @@ void norm_held(NormParams p)
             rs = rsq(S2 * inv_d + eps);
         }
 
+        if constexpr (PLDS && WPR == 1) __syncthreads();  // the LDS parameters are complete
         // 4. normalize, scale, shift; store from the same registers
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
@@ -483,7 +507,8 @@ void norm_looped(NormParams p)
 }
 
 // ---------------------------------------------------------------------------
-// Streaming copy (calibration): U 128-bit accesses per lane per step.
+// Streaming copy (calibration): U 128-bit accesses per lane per step, with
+// the same non-temporal hints as the normalization kernels.
 template <int U>
 __global__ __launch_bounds__(256)
 void copy_f4(const float *src, float *dst, int64_t n4)
@@ -494,12 +519,12 @@ void copy_f4(const float *src, float *dst, int64_t n4)
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t i = base + 256 * u;
-            v[u] = i < n4 ? ld4<false>(src + 4 * i) : f4(0.f);
+            v[u] = i < n4 ? ld4<true>(src + 4 * i) : f4(0.f);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t i = base + 256 * u;
-            if (i < n4) st4<false>(dst + 4 * i, v[u]);
+            if (i < n4) st4<true>(dst + 4 * i, v[u]);
         }
     }
 }

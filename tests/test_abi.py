@@ -71,6 +71,8 @@ def test_status_strings(L):
     (X, G, BETA, Y, 4, 8, 1e-5, 0x1001, None, None),        # mean not 4-byte aligned
     (X, G, BETA, X + 16, 4, 8, 1e-5, None, None, None),     # y partially overlaps x
     (X, G, BETA, Y, 2**62, 8, 1e-5, None, None, None),      # size overflow
+    (X, Y + 64, BETA, Y, 4, 8, 1e-5, None, None, None),     # gamma inside y
+    (X, G, Y, Y, 4, 8, 1e-5, None, None, None),             # beta inside y
 ])
 def test_layernorm_rejects_bad_arguments(L, args):
     assert L.mi_layernorm_fwd(*args) == mn.MI_NORM_ERR_INVALID
@@ -124,6 +126,10 @@ def _infos():
             for i in range(mn.mi_norm_variant_count())]
 
 
+def test_select_rejects_negative_rows(L):
+    assert mn.mi_norm_select_variant(0, -1, 768, X, Y, G, BETA) == -1
+
+
 def test_variant_table_is_consistent(L):
     infos = _infos()
     names = [n for _, n, _ in infos]
@@ -164,7 +170,7 @@ def test_dispatch_picks_an_eligible_covering_variant(L, op, layout):
         x, y = X + 4, Y + 8
     p1 = BETA if op == mn.OP_LAYERNORM else None
     for d in WIDTHS:
-        vid = mn.mi_norm_select_variant(op, d, x, y, G, p1)
+        vid = mn.mi_norm_select_variant(op, 4096, d, x, y, G, p1)
         assert vid >= 0, (op, d, layout)
         v = mn.mi_norm_variant_get_info(vid)
         assert v["op"] == op
@@ -179,15 +185,29 @@ def test_dispatch_picks_an_eligible_covering_variant(L, op, layout):
 
 
 def test_dispatch_examples(L):
-    sel = lambda op, d, x=X, y=Y: mn.mi_norm_variant_name(
-        mn.mi_norm_select_variant(op, d, x, y, G, BETA if op == 0 else None))
-    assert sel(0, 768) == "ln_4_p0_l64_w1_q3_b4"
-    assert sel(0, 128) == "ln_4_p0_l32_w1_q1_b4"
-    assert sel(1, 8193).startswith("rms_4_p1_")
-    assert sel(0, 1) == "ln_1_p0_l16_w1_q1_b4"
+    sel = lambda op, d, rows=4096, x=X, y=Y: mn.mi_norm_variant_name(
+        mn.mi_norm_select_variant(op, rows, d, x, y, G, BETA if op == 0 else None))
+    assert sel(0, 768) == "ln_4_p0_l64_w1_q3_b16"        # 256 workgroups of 16 rows
+    assert sel(0, 768, rows=1000) == "ln_4_p0_l64_w1_q3_b4"  # too few rows for 16-row blocks
+    assert sel(0, 128, rows=512) == "ln_4_p0_l32_w1_q1_b4"
+    assert sel(1, 8193, rows=256).startswith("rms_4_p1_")
+    assert sel(0, 1, rows=64) == "ln_1_p0_l16_w1_q1_b4"
+    assert sel(0, 8192, rows=32768) == "ln_4_p0_l64_w8_q4_b16"
     assert "_loop_" in sel(0, 2**20)
     # gamma misaligned only: no 128-bit parameter reads, so not the aligned path
-    assert mn.mi_norm_variant_get_info(mn.mi_norm_select_variant(0, 768, X, Y, G + 4, BETA))["needs_aligned"] == 0
+    assert mn.mi_norm_variant_get_info(mn.mi_norm_select_variant(0, 4096, 768, X, Y, G + 4, BETA))["needs_aligned"] == 0
+
+
+def test_workgroup_size_follows_row_count(L):
+    for d, wpr in ((768, 1), (2048, 1), (4096, 4), (8192, 8)):
+        for rows in (1, 100, 1000, 5000, 100000):
+            v = mn.mi_norm_variant_get_info(mn.mi_norm_select_variant(0, rows, d, X, Y, G, BETA))
+            blocks = -(-rows // v["rows_per_block"])
+            if v["waves_per_block"] < 16:
+                # a 16-wave shape would have left CUs idle
+                assert -(-rows // (16 // wpr)) < 256, (d, rows)
+            else:
+                assert blocks >= 256, (d, rows)
 
 
 def test_eligibility_rules(L):
