@@ -51,29 +51,26 @@ constexpr int64_t kUnbounded = INT64_MAX;
                                  VEC == 4 ? 1 : 0},                                             \
             reinterpret_cast<const void *>(&norm_looped<OP, VEC, WAVES, U>)}
 
+// every (waves per row, slots) pair of a 128-bit path: slots 1, 2, 3, 4, 6, 8
+// for 1, 2, 4, 8 and 16 waves per row
+#define MI_SLOTS(OP, OPN, PEEL, WPR, WSMALL)                                                   \
+    MI_HELD2(OP, OPN, 4, PEEL, 64, WPR, 1, WSMALL), MI_HELD2(OP, OPN, 4, PEEL, 64, WPR, 2, WSMALL), \
+    MI_HELD2(OP, OPN, 4, PEEL, 64, WPR, 3, WSMALL), MI_HELD2(OP, OPN, 4, PEEL, 64, WPR, 4, WSMALL), \
+    MI_HELD2(OP, OPN, 4, PEEL, 64, WPR, 6, WSMALL), MI_HELD2(OP, OPN, 4, PEEL, 64, WPR, 8, WSMALL)
+#define MI_SLOTS16(OP, OPN, PEEL)                                                              \
+    MI_HELD(OP, OPN, 4, PEEL, 64, 16, 1, 16), MI_HELD(OP, OPN, 4, PEEL, 64, 16, 2, 16),         \
+    MI_HELD(OP, OPN, 4, PEEL, 64, 16, 3, 16), MI_HELD(OP, OPN, 4, PEEL, 64, 16, 4, 16),         \
+    MI_HELD(OP, OPN, 4, PEEL, 64, 16, 6, 16), MI_HELD(OP, OPN, 4, PEEL, 64, 16, 8, 16)
+#define MI_PATH128(OP, OPN, PEEL)                                                              \
+    MI_SLOTS(OP, OPN, PEEL, 1, 4), MI_SLOTS(OP, OPN, PEEL, 2, 4), MI_SLOTS(OP, OPN, PEEL, 4, 4), \
+    MI_SLOTS(OP, OPN, PEEL, 8, 8), MI_SLOTS16(OP, OPN, PEEL)
+
 #define MI_OP_TABLE(OP, OPN)                                                                   \
-    /* 128-bit, aligned, d % 4 == 0 */                                                          \
+    /* 128-bit, aligned, d % 4 == 0; 16 or 32 lanes per row for narrow rows */                  \
     MI_HELD2(OP, OPN, 4, 0, 16, 1, 1, 4), MI_HELD2(OP, OPN, 4, 0, 32, 1, 1, 4),                 \
-    MI_HELD2(OP, OPN, 4, 0, 64, 1, 1, 4), MI_HELD2(OP, OPN, 4, 0, 64, 1, 2, 4),                 \
-    MI_HELD2(OP, OPN, 4, 0, 64, 1, 3, 4), MI_HELD2(OP, OPN, 4, 0, 64, 1, 4, 4),                 \
-    MI_HELD2(OP, OPN, 4, 0, 64, 1, 6, 4), MI_HELD2(OP, OPN, 4, 0, 64, 1, 8, 4),                 \
-    MI_HELD2(OP, OPN, 4, 0, 64, 2, 4, 4), MI_HELD2(OP, OPN, 4, 0, 64, 2, 8, 4),                 \
-    MI_HELD2(OP, OPN, 4, 0, 64, 4, 2, 4), MI_HELD2(OP, OPN, 4, 0, 64, 4, 3, 4),                 \
-    MI_HELD2(OP, OPN, 4, 0, 64, 4, 4, 4), MI_HELD2(OP, OPN, 4, 0, 64, 4, 6, 4),                 \
-    MI_HELD2(OP, OPN, 4, 0, 64, 4, 8, 4),                                                       \
-    MI_HELD2(OP, OPN, 4, 0, 64, 8, 2, 8), MI_HELD2(OP, OPN, 4, 0, 64, 8, 3, 8),                 \
-    MI_HELD2(OP, OPN, 4, 0, 64, 8, 4, 8), MI_HELD2(OP, OPN, 4, 0, 64, 8, 6, 8),                 \
-    MI_HELD2(OP, OPN, 4, 0, 64, 8, 8, 8),                                                       \
-    MI_HELD(OP, OPN, 4, 0, 64, 16, 3, 16), MI_HELD(OP, OPN, 4, 0, 64, 16, 4, 16),               \
-    MI_HELD(OP, OPN, 4, 0, 64, 16, 6, 16), MI_HELD(OP, OPN, 4, 0, 64, 16, 8, 16),               \
+    MI_PATH128(OP, OPN, 0),                                                                     \
     /* 128-bit body with a per-row scalar head and tail: any d, x == y mod 16 B */              \
-    MI_HELD2(OP, OPN, 4, 1, 64, 1, 1, 4), MI_HELD2(OP, OPN, 4, 1, 64, 1, 2, 4),                 \
-    MI_HELD2(OP, OPN, 4, 1, 64, 1, 3, 4), MI_HELD2(OP, OPN, 4, 1, 64, 1, 4, 4),                 \
-    MI_HELD2(OP, OPN, 4, 1, 64, 1, 6, 4), MI_HELD2(OP, OPN, 4, 1, 64, 1, 8, 4),                 \
-    MI_HELD2(OP, OPN, 4, 1, 64, 4, 3, 4), MI_HELD2(OP, OPN, 4, 1, 64, 4, 4, 4),                 \
-    MI_HELD2(OP, OPN, 4, 1, 64, 8, 3, 8), MI_HELD2(OP, OPN, 4, 1, 64, 8, 4, 8),                 \
-    MI_HELD(OP, OPN, 4, 1, 64, 16, 3, 16), MI_HELD(OP, OPN, 4, 1, 64, 16, 4, 16),               \
-    MI_HELD(OP, OPN, 4, 1, 64, 16, 6, 16), MI_HELD(OP, OPN, 4, 1, 64, 16, 8, 16),               \
+    MI_PATH128(OP, OPN, 1),                                                                     \
     /* 32-bit accesses: any d, any 4-byte alignment */                                          \
     MI_HELD2(OP, OPN, 1, 0, 16, 1, 1, 4), MI_HELD2(OP, OPN, 1, 0, 32, 1, 1, 4),                 \
     MI_HELD2(OP, OPN, 1, 0, 64, 1, 1, 4), MI_HELD2(OP, OPN, 1, 0, 64, 1, 2, 4),                 \
@@ -100,8 +97,11 @@ inline bool al4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) ==
 
 // Fewest workgroups that still cover every CU: of the variants with this
 // shape, the one with the most waves per workgroup whose grid has at least
-// kMinBlocks workgroups; failing that, the one with the most workgroups.
-constexpr int64_t kMinBlocks = 256;
+// min_blocks(wpr) workgroups; failing that, the one with the most
+// workgroups.  Rows of one wave need one workgroup per CU (256); rows of
+// several waves share one barrier per workgroup, and 16-wave workgroups only
+// paid off with two of them per CU (512).
+int64_t min_blocks(int wpr) { return wpr > 1 ? 512 : 256; }
 
 int find(int op, int64_t rows, int vec, int peel, int looped, int lpr, int wpr, int q) {
     int best = -1, fallback = -1;
@@ -112,7 +112,7 @@ int find(int op, int64_t rows, int vec, int peel, int looped, int lpr, int wpr, 
         if (looped) return i;
         if (v.lanes_per_row != lpr || v.waves_per_row != wpr || v.slots != q) continue;
         const int64_t blocks = (rows + v.rows_per_block - 1) / v.rows_per_block;
-        if (blocks >= kMinBlocks && (best < 0 || v.waves_per_block > kVariants[best].info.waves_per_block))
+        if (blocks >= min_blocks(wpr) && (best < 0 || v.waves_per_block > kVariants[best].info.waves_per_block))
             best = i;
         if (blocks > fallback_blocks) {
             fallback = i;
@@ -129,34 +129,19 @@ int pick_q(int64_t n, int64_t cap_per_slot, const int *qs, int nq) {
     return 0;
 }
 
-// (lanes per row, waves per row, slots) for a held 128-bit variant covering
-// nvec 16-byte accesses, or wpr = 0 when the row is too wide to hold
-void ladder4(int64_t nvec, bool allow_subwave, int &lpr, int &wpr, int &q) {
-    static const int q1[] = {1, 2, 3, 4, 6, 8};
-    static const int q4[] = {2, 3, 4, 6, 8};
-    static const int q8[] = {2, 3, 4, 6, 8};
-    static const int q16[] = {3, 4, 6, 8};
-    lpr = 64;
-    wpr = 0;
-    q = 0;
-    if (allow_subwave && nvec <= 16) { lpr = 16; wpr = 1; q = 1; return; }
-    if (allow_subwave && nvec <= 32) { lpr = 32; wpr = 1; q = 1; return; }
-    if (nvec <= 512) { wpr = 1; q = pick_q(nvec, 64, q1, 6); return; }
-    if (nvec <= 1024) { wpr = 4; q = pick_q(nvec, 256, q4, 5); return; }
-    if (nvec <= 2048) { wpr = 8; q = pick_q(nvec, 512, q8, 5); return; }
-    if (nvec <= 8192) { wpr = 16; q = pick_q(nvec, 1024, q16, 4); return; }
-}
-
-void ladder_peel(int64_t nvec, int &wpr, int &q) {
-    static const int q1[] = {1, 2, 3, 4, 6, 8};
-    static const int q4[] = {3, 4};
-    static const int q16[] = {3, 4, 6, 8};
-    wpr = 0;
-    q = 0;
-    if (nvec <= 512) { wpr = 1; q = pick_q(nvec, 64, q1, 6); return; }
-    if (nvec <= 1024) { wpr = 4; q = pick_q(nvec, 256, q4, 2); return; }
-    if (nvec <= 2048) { wpr = 8; q = pick_q(nvec, 512, q4, 2); return; }
-    if (nvec <= 8192) { wpr = 16; q = pick_q(nvec, 1024, q16, 4); return; }
+// Waves per row and slots for a 128-bit row of nvec accesses (wpr = 0 when
+// the row is too wide to hold).  About four 16-byte accesses per lane
+// measured best across widths (more per lane cut occupancy, fewer add
+// waves and exchange traffic); with few rows, a row is spread over more waves
+// until the grid holds 4096 waves, as long as every wave keeps one full
+// access per lane.
+void shape128(int64_t nvec, int64_t rows, int &wpr, int &q) {
+    static const int qs[] = {1, 2, 3, 4, 6, 8};
+    wpr = 1;
+    while (wpr < 16 && 64 * wpr * 4 < nvec) wpr *= 2;
+    while (wpr < 16 && rows * wpr < 4096 && nvec >= 64 * 2 * wpr) wpr *= 2;
+    q = pick_q(nvec, 64 * wpr, qs, 6);
+    if (q == 0) wpr = 0;
 }
 
 void ladder1(int64_t n, int &lpr, int &wpr, int &q) {
@@ -200,12 +185,15 @@ int select_variant(int op, int64_t rows, int64_t d, const void *x, const void *y
     const Layout L = layout_of(op, d, x, y, p0, p1);
     int lpr, wpr, q;
     if (L.a16) {
-        ladder4(d / 4, true, lpr, wpr, q);
-        if (wpr) return find(op, rows, 4, 0, 0, lpr, wpr, q);
+        const int64_t nvec = d / 4;
+        if (nvec <= 16) return find(op, rows, 4, 0, 0, 16, 1, 1);
+        if (nvec <= 32) return find(op, rows, 4, 0, 0, 32, 1, 1);
+        shape128(nvec, rows, wpr, q);
+        if (wpr) return find(op, rows, 4, 0, 0, 64, wpr, q);
         return find(op, rows, 4, 0, 1, 0, 0, 0);
     }
     if (L.peel_ok && d >= 256) {
-        ladder_peel((d + 3) / 4, wpr, q);
+        shape128((d + 3) / 4, rows, wpr, q);
         if (wpr) return find(op, rows, 4, 1, 0, 64, wpr, q);
         return find(op, rows, 1, 0, 1, 0, 0, 0);
     }

@@ -138,6 +138,9 @@ __device__ __forceinline__ float rsq(float v) { return __builtin_amdgcn_rsqf(v);
 //   Q      accesses held per lane; capacity = VEC * LPR * WPR * Q elements
 //   WAVES  waves per workgroup
 //   NTL/NTS  non-temporal x loads / y stores
+//   MRG    cross-wave merge: 0 every lane walks all WPR exchanged entries,
+//          1 lane w takes entry w and two 16-lane sums finish the merge;
+//          -1: 1 for 16 waves per row, else 0
 //   PRE    where the output pass gets gamma/beta (or w): 0: global loads in
 //          the output pass; 1: global loads issued while x is in flight;
 //          2: staged once per workgroup in LDS at kernel start (128-bit
@@ -147,7 +150,7 @@ __device__ __forceinline__ float rsq(float v) { return __builtin_amdgcn_rsqf(v);
 // q = 0..Q-1: consecutive lanes touch consecutive 16-byte (or 4-byte) words,
 // so each wave-wide access covers 1 KiB (256 B) of one row contiguously.
 template <int OP, int VEC, bool PEEL, int LPR, int WPR, int Q, int WAVES, bool NTL, bool NTS,
-          int PRE = -1>
+          int PRE = -1, int MRG = -1>
 __global__ __launch_bounds__(WAVES * 64)
 void norm_held(NormParams p)
 {
@@ -156,6 +159,7 @@ void norm_held(NormParams p)
     static_assert(LPR == 16 || LPR == 32 || LPR == 64, "LPR");
     static_assert(WPR == 1 || LPR == 64, "multi-wave rows use full waves");
     static_assert(WAVES % WPR == 0, "whole rows per workgroup");
+    static_assert(WPR <= 16, "the cross-wave merge sums within one 16-lane DPP row");
     using VT = typename std::conditional<VEC == 4, f4, float>::type;
     constexpr int RPW = 64 / LPR;
     constexpr int RPB = (WPR == 1) ? WAVES * RPW : WAVES / WPR;
@@ -166,6 +170,7 @@ void norm_held(NormParams p)
     constexpr int kBudget = WAVES >= 16 ? 128 : (WAVES >= 8 ? 256 : 512);
     constexpr bool PRELOAD = PRE >= 0 ? PRE == 1 : VEC * Q * (1 + kParams) <= kBudget / 4;
     constexpr bool PLDS = PRE == 2;
+    constexpr bool MPAR = MRG >= 0 ? MRG == 1 : WPR >= 16;
     static_assert(!PLDS || (VEC == 4 && !PEEL), "LDS parameters need the aligned 128-bit path");
     constexpr int kCapV = LPR * WPR * Q;  // 16-byte accesses per row the variant covers
     static_assert(!PLDS || kCapV * kParams * 16 <= 64 * 1024, "LDS parameter stage too large");
@@ -329,21 +334,34 @@ void norm_held(NormParams p)
                 mu = mu_w;
                 M2 = M2_w;
             } else {
-                // one exchange: every wave's (mean, M2) meets in LDS behind one barrier
+                // one exchange: every wave's (mean, M2) meets in LDS behind one
+                // barrier, then the Chan-Golub-LeVeque merge
+                //   mu = sum_w n_w mu_w / d,  M2 = sum_w [M2_w + n_w (mu_w - mu)^2].
+                // Every wave reads the same entries and adds them in the same
+                // order, so all waves of the row hold the same mu and M2.
                 if (li == 0) xch[rib][wr] = make_float2(mu_w, M2_w);
                 __syncthreads();
-                // Chan-Golub-LeVeque merge, two passes over the broadcast LDS
-                // entries: mu = sum n_w mu_w / d, M2 = sum M2_w + n_w (mu_w - mu)^2
-                float tot = 0.f;
-#pragma unroll
-                for (int w = 0; w < WPR; ++w) tot += (float)wave_count(w) * xch[rib][w].x;
-                mu = tot * inv_d;
-                M2 = 0.f;
-#pragma unroll
-                for (int w = 0; w < WPR; ++w) {
-                    const float2 e = xch[rib][w];
+                if constexpr (MPAR) {
+                    // lane w < WPR takes wave w's entry; two 16-lane sums
+                    const bool own = lane < WPR;
+                    const float2 e = xch[rib][own ? lane : 0];
+                    const float n_e = own ? (float)wave_count(lane) : 0.f;
+                    mu = readlane(group_sum<16>(own ? n_e * e.x : 0.f), 0) * inv_d;
                     const float dm = e.x - mu;
-                    M2 += e.y + (float)wave_count(w) * dm * dm;
+                    M2 = readlane(group_sum<16>(own ? e.y + n_e * dm * dm : 0.f), 0);
+                } else {
+                    // every lane walks the WPR broadcast entries
+                    float tot = 0.f;
+#pragma unroll
+                    for (int w = 0; w < WPR; ++w) tot += (float)wave_count(w) * xch[rib][w].x;
+                    mu = tot * inv_d;
+                    M2 = 0.f;
+#pragma unroll
+                    for (int w = 0; w < WPR; ++w) {
+                        const float2 e = xch[rib][w];
+                        const float dm = e.x - mu;
+                        M2 += e.y + (float)wave_count(w) * dm * dm;
+                    }
                 }
             }
             rs = rsq(M2 * inv_d + eps);
@@ -356,9 +374,15 @@ void norm_held(NormParams p)
             if constexpr (WPR > 1) {
                 if (li == 0) xch[rib][wr] = make_float2(S2, 0.f);
                 __syncthreads();
-                S2 = 0.f;
+                if constexpr (MPAR) {
+                    const bool own = lane < WPR;
+                    const float e = xch[rib][own ? lane : 0].x;
+                    S2 = readlane(group_sum<16>(own ? e : 0.f), 0);
+                } else {
+                    S2 = 0.f;
 #pragma unroll
-                for (int w = 0; w < WPR; ++w) S2 += xch[rib][w].x;
+                    for (int w = 0; w < WPR; ++w) S2 += xch[rib][w].x;
+                }
             }
             mu = 0.f;
             rs = rsq(S2 * inv_d + eps);

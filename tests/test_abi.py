@@ -187,27 +187,39 @@ def test_dispatch_picks_an_eligible_covering_variant(L, op, layout):
 def test_dispatch_examples(L):
     sel = lambda op, d, rows=4096, x=X, y=Y: mn.mi_norm_variant_name(
         mn.mi_norm_select_variant(op, rows, d, x, y, G, BETA if op == 0 else None))
-    assert sel(0, 768) == "ln_4_p0_l64_w1_q3_b16"        # 256 workgroups of 16 rows
-    assert sel(0, 768, rows=1000) == "ln_4_p0_l64_w1_q3_b4"  # too few rows for 16-row blocks
-    assert sel(0, 128, rows=512) == "ln_4_p0_l32_w1_q1_b4"
-    assert sel(1, 8193, rows=256).startswith("rms_4_p1_")
-    assert sel(0, 1, rows=64) == "ln_1_p0_l16_w1_q1_b4"
+    assert sel(0, 768) == "ln_4_p0_l64_w1_q3_b16"            # 256 workgroups of 16 rows
+    assert sel(0, 768, rows=1000) == "ln_4_p0_l64_w2_q2_b4"  # few rows: two waves per row
+    assert sel(0, 2048, rows=1024) == "ln_4_p0_l64_w4_q2_b4"
+    assert sel(0, 4096, rows=4096) == "ln_4_p0_l64_w4_q4_b16"
     assert sel(0, 8192, rows=32768) == "ln_4_p0_l64_w8_q4_b16"
+    assert sel(0, 128, rows=512) == "ln_4_p0_l32_w1_q1_b4"
+    assert sel(1, 8193, rows=256) == "rms_4_p1_l64_w16_q3_b16"
+    assert sel(0, 1, rows=64) == "ln_1_p0_l16_w1_q1_b4"
     assert "_loop_" in sel(0, 2**20)
     # gamma misaligned only: no 128-bit parameter reads, so not the aligned path
     assert mn.mi_norm_variant_get_info(mn.mi_norm_select_variant(0, 4096, 768, X, Y, G + 4, BETA))["needs_aligned"] == 0
 
 
 def test_workgroup_size_follows_row_count(L):
-    for d, wpr in ((768, 1), (2048, 1), (4096, 4), (8192, 8)):
+    for d in (768, 2048, 4096, 8192, 16384):
         for rows in (1, 100, 1000, 5000, 100000):
             v = mn.mi_norm_variant_get_info(mn.mi_norm_select_variant(0, rows, d, X, Y, G, BETA))
-            blocks = -(-rows // v["rows_per_block"])
+            need = 512 if v["waves_per_row"] > 1 else 256
+            per16 = 16 // v["waves_per_row"]
             if v["waves_per_block"] < 16:
-                # a 16-wave shape would have left CUs idle
-                assert -(-rows // (16 // wpr)) < 256, (d, rows)
+                # a 16-wave workgroup would have left too few workgroups
+                assert -(-rows // per16) < need, (d, rows)
             else:
-                assert blocks >= 256, (d, rows)
+                assert -(-rows // v["rows_per_block"]) >= need or v["waves_per_row"] == 16, (d, rows)
+
+
+def test_rows_spread_over_more_waves_when_few(L):
+    # about four accesses per lane with many rows; more waves per row with few
+    for d, rows, wpr, q in ((768, 4096, 1, 3), (2048, 4096, 2, 4), (2048, 1024, 4, 2),
+                            (4096, 4096, 4, 4), (8192, 32768, 8, 4), (16384, 8192, 16, 4),
+                            (768, 100, 2, 2), (32768, 64, 16, 8)):
+        v = mn.mi_norm_variant_get_info(mn.mi_norm_select_variant(0, rows, d, X, Y, G, BETA))
+        assert (v["waves_per_row"], v["slots"]) == (wpr, q), (d, rows, v)
 
 
 def test_eligibility_rules(L):
