@@ -39,6 +39,18 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
     ]
+    lib.oracle_add_layernorm_f64.restype = None
+    lib.oracle_add_layernorm_f64.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+    ]
+    lib.oracle_add_rmsnorm_f64.restype = None
+    lib.oracle_add_rmsnorm_f64.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+    ]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_plant.restype = ctypes.c_int
@@ -117,6 +129,48 @@ def rmsnorm(x, w, eps: float = 1e-5, lib: ctypes.CDLL | None = None,
     lib.oracle_rmsnorm_f64(_ptr(x), _ptr(w), rows, d, float(np.float32(eps)),
                            _ptr(y), _ptr(rstd), _ptr(ms64))
     return y, rstd, ms64
+
+
+def add_layernorm(x, r, gamma, beta, eps: float = 1e-5, lib: ctypes.CDLL | None = None):
+    """Residual add then LayerNorm: h = x + r (float32), y = LayerNorm(h).
+
+    Returns ``(y, h, mean, rstd)``.
+    """
+    lib = lib or load()
+    x, r = _f32(x, "x"), _f32(r, "r")
+    if x.ndim != 2 or r.shape != x.shape:
+        raise ValueError("x and r must be 2-D [rows, d] of one shape")
+    rows, d = x.shape
+    gamma = _f32(gamma, "gamma").reshape(-1)
+    beta = _f32(beta, "beta").reshape(-1)
+    if d < 1 or gamma.size != d or beta.size != d:
+        raise ValueError("need d >= 1 and gamma, beta of length d")
+    y, h = np.empty_like(x), np.empty_like(x)
+    mean = np.empty(rows, np.float32)
+    rstd = np.empty(rows, np.float32)
+    lib.oracle_add_layernorm_f64(_ptr(x), _ptr(r), _ptr(gamma), _ptr(beta), rows, d,
+                                 float(np.float32(eps)), _ptr(y), _ptr(h), _ptr(mean), _ptr(rstd))
+    return y, h, mean, rstd
+
+
+def add_rmsnorm(x, r, w, eps: float = 1e-5, lib: ctypes.CDLL | None = None):
+    """Residual add then RMSNorm: h = x + r (float32), y = RMSNorm(h).
+
+    Returns ``(y, h, rstd)``.
+    """
+    lib = lib or load()
+    x, r = _f32(x, "x"), _f32(r, "r")
+    if x.ndim != 2 or r.shape != x.shape:
+        raise ValueError("x and r must be 2-D [rows, d] of one shape")
+    rows, d = x.shape
+    w = _f32(w, "w").reshape(-1)
+    if d < 1 or w.size != d:
+        raise ValueError("need d >= 1 and w of length d")
+    y, h = np.empty_like(x), np.empty_like(x)
+    rstd = np.empty(rows, np.float32)
+    lib.oracle_add_rmsnorm_f64(_ptr(x), _ptr(r), _ptr(w), rows, d, float(np.float32(eps)),
+                               _ptr(y), _ptr(h), _ptr(rstd))
+    return y, h, rstd
 
 
 def set_threads(n: int, lib: ctypes.CDLL | None = None) -> None:

@@ -22,6 +22,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <omp.h>
 
 /* ORACLE_PLANT selects one deliberate mistake for the negative-control tests.
@@ -145,5 +146,87 @@ void oracle_rmsnorm_f64(const float *x, const float *w,
             yr[c] = (float)((double)xr[c] * (double)w[c] * rho);
         if (rstd) rstd[r] = (float)rho;
         if (ms64) ms64[r] = ms;
+    }
+}
+
+/*
+ * Residual add fused before the normalization: h = x + r, then LayerNorm
+ * (or RMSNorm) of h.  h is formed as a float32 addition, the precision of
+ * the residual stream a caller stores, and the normalization above is then
+ * applied to that rounded sum exactly as for a plain input.  h may be NULL.
+ * y, h may equal x or r.
+ */
+void oracle_add_layernorm_f64(const float *x, const float *r, const float *gamma,
+                              const float *beta, int64_t rows, int64_t d, float eps,
+                              float *y, float *h, float *mean, float *rstd)
+{
+    #pragma omp parallel
+    {
+        /* the float32 sum of one row, kept before any output is written */
+        float *hs = (float *)malloc((size_t)d * sizeof(float));
+        #pragma omp for schedule(static)
+        for (int64_t i = 0; i < rows; ++i) {
+            const float *xi = x + i * d, *ri = r + i * d;
+            float *yi = y + i * d;
+            for (int64_t j = 0; j < d; ++j)
+                hs[j] = xi[j] + ri[j];
+#if ORACLE_PLANT == 10
+            for (int64_t j = 0; j < d; ++j)
+                hs[j] = xi[j];                   /* planted: residual dropped */
+#endif
+
+            double s = 0.0;
+            for (int64_t j = 0; j < d; ++j)
+                s += (double)hs[j];
+            double mu = s / (double)d;
+            double q = 0.0;
+            for (int64_t j = 0; j < d; ++j) {
+                double c = (double)hs[j] - mu;
+                q += c * c;
+            }
+            double var = q / (double)d;
+            double rho = 1.0 / sqrt(var + (double)eps);
+            for (int64_t j = 0; j < d; ++j)
+                yi[j] = (float)(((double)hs[j] - mu) * rho * (double)gamma[j] + (double)beta[j]);
+            if (h)
+                for (int64_t j = 0; j < d; ++j)
+                    h[i * d + j] = hs[j];
+            if (mean) mean[i] = (float)mu;
+            if (rstd) rstd[i] = (float)rho;
+        }
+        free(hs);
+    }
+}
+
+void oracle_add_rmsnorm_f64(const float *x, const float *r, const float *w,
+                            int64_t rows, int64_t d, float eps,
+                            float *y, float *h, float *rstd)
+{
+    #pragma omp parallel
+    {
+        float *hs = (float *)malloc((size_t)d * sizeof(float));
+        #pragma omp for schedule(static)
+        for (int64_t i = 0; i < rows; ++i) {
+            const float *xi = x + i * d, *ri = r + i * d;
+            float *yi = y + i * d;
+            for (int64_t j = 0; j < d; ++j)
+                hs[j] = xi[j] + ri[j];
+#if ORACLE_PLANT == 11
+            for (int64_t j = 0; j < d; ++j)
+                hs[j] = ri[j];                   /* planted: input dropped */
+#endif
+
+            double s2 = 0.0;
+            for (int64_t j = 0; j < d; ++j)
+                s2 += (double)hs[j] * (double)hs[j];
+            double rho = 1.0 / sqrt(s2 / (double)d + (double)eps);
+            for (int64_t j = 0; j < d; ++j)
+                yi[j] = (float)((double)hs[j] * (double)w[j] * rho);
+            if (h)
+                for (int64_t j = 0; j < d; ++j)
+                    h[i * d + j] = hs[j];
+            if (rstd) rstd[i] = (float)rho;
+        }
+        free(hs);
     }
 }

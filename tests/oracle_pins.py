@@ -303,6 +303,51 @@ def check_rms_invariants(lib):
     assert np.array_equal(xin, y0), "in-place RMSNorm differs"
 
 
+# ----------------------------------------------------------------------------
+# residual add fused before the norm
+
+def check_add_norm(lib):
+    """h is the float32 sum bit for bit; y is the pinned definition applied to h.
+
+    Pinned against: numpy's float32 addition (h), torch float64 LayerNorm /
+    RMSNorm of that sum (y within 1 ulp), a zero residual giving the plain
+    operation bit for bit, and exact brute force on a tiny case."""
+    import torch
+    import torch.nn.functional as F
+    for rows, d in ((33, 1), (17, 127), (40, 768)):
+        x = wl.make_x(rows, d, "offset", [19, rows, d])
+        r = wl.make_x(rows, d, "normal", [20, rows, d])
+        g, b = wl.make_affine(d, [19, d])
+        w = wl.make_weight(d, [19, d])
+        h32 = (x + r).astype(np.float32)               # numpy float32 add, round to nearest even
+        y, h, mean, rstd = oracle.add_layernorm(x, r, g, b, float(EPS32), lib=lib)
+        assert np.array_equal(h, h32), "h != x + r in float32"
+        ty, tm, tr = torch.native_layer_norm(torch.from_numpy(h32).double(), (d,),
+                                             torch.from_numpy(g).double(),
+                                             torch.from_numpy(b).double(), float(EPS32))
+        _assert_ulps(y, ty.numpy().astype(np.float32), 1, f"add+ln vs torch {rows}x{d}")
+        _assert_ulps(rstd, tr.reshape(-1).numpy().astype(np.float32), 1, "add+ln rstd")
+        yr, hr, rr = oracle.add_rmsnorm(x, r, w, float(EPS32), lib=lib)
+        assert np.array_equal(hr, h32)
+        ty = F.rms_norm(torch.from_numpy(h32).double(), (d,), torch.from_numpy(w).double(),
+                        eps=float(EPS32))
+        _assert_ulps(yr, ty.numpy().astype(np.float32), 1, f"add+rms vs torch {rows}x{d}")
+        # a zero residual is the plain operation, bit for bit
+        z = np.zeros_like(x)
+        assert np.array_equal(oracle.add_layernorm(x, z, g, b, float(EPS32), lib=lib)[0],
+                              oracle.layernorm(x, g, b, float(EPS32), lib=lib)[0])
+        assert np.array_equal(oracle.add_rmsnorm(x, z, w, float(EPS32), lib=lib)[0],
+                              oracle.rmsnorm(x, w, float(EPS32), lib=lib)[0])
+    # exact brute force on a tiny case with a non-trivial residual
+    x = np.array([[0.5, -1.25, 2.0, 3.5]], np.float32)
+    r = np.array([[1.0, 0.25, -2.5, 0.125]], np.float32)
+    g = np.array([1.5, 0.5, -1.0, 2.0], np.float32)
+    b = np.array([0.1, 0.2, 0.3, 0.4], np.float32)
+    y, h, _, _ = oracle.add_layernorm(x, r, g, b, float(EPS32), lib=lib)
+    _, _, _, ys = _exact_ln_row((x + r)[0], g, b, EPS32)
+    _assert_ulps(y[0], np.array([float(t) for t in ys], np.float32), 1, "add+ln brute force")
+
+
 LN_CHECKS = (check_ln_bruteforce, check_ln_vs_torch, check_ln_closed_forms, check_ln_invariants)
 RMS_CHECKS = (check_rms_bruteforce, check_rms_vs_torch, check_rms_closed_forms, check_rms_invariants)
-ALL_CHECKS = LN_CHECKS + RMS_CHECKS
+ALL_CHECKS = LN_CHECKS + RMS_CHECKS + (check_add_norm,)

@@ -24,6 +24,8 @@ PLANTS = {
     7: ("rmsnorm eps removed", pins.RMS_CHECKS),
     8: ("rmsnorm wrong denominator", pins.RMS_CHECKS),
     9: ("layernorm eps outside the root", pins.LN_CHECKS),
+    10: ("add+layernorm residual dropped", (pins.check_add_norm,)),
+    11: ("add+rmsnorm input dropped", (pins.check_add_norm,)),
 }
 
 
