@@ -54,6 +54,10 @@ BENCH_WORKLOADS = {
     "rms_4096x768": ("rmsnorm", 4096, 768, "normal", False),
     "rms_2048x4096": ("rmsnorm", 2048, 4096, "normal", False),
     "rms_256x8193": ("rmsnorm", 256, 8193, "normal", False),
+    "addln_4096x768": ("add_layernorm", 4096, 768, "normal", True),
+    "addln_32768x8192": ("add_layernorm", 32768, 8192, "normal", False),
+    "addrms_4096x768": ("add_rmsnorm", 4096, 768, "normal", False),
+    "addrms_2048x4096": ("add_rmsnorm", 2048, 4096, "normal", False),
     "copy_4096x768": ("copy", 4096, 768, "normal", False),
     "copy_32768x8192": ("copy", 32768, 8192, "normal", False),
 }
@@ -71,18 +75,25 @@ def kernel_source_hash() -> str:
 
 
 def algorithmic_bytes(op: str, rows: int, d: int, stats: bool) -> int:
-    if op == "layernorm":
-        return 8 * rows * d + 8 * d + (8 * rows if stats else 0)
-    if op == "rmsnorm":
-        return 8 * rows * d + 4 * d + (4 * rows if stats else 0)
+    """Bytes a step must move: x read, y written (4 B each per element); the
+    fused ops also read r and write h = x + r; gamma/beta (or w) once; the
+    per-row statistics when requested."""
+    per_elem = 16 if op.startswith("add_") else 8
+    if op.endswith("layernorm"):
+        return per_elem * rows * d + 8 * d + (8 * rows if stats else 0)
+    if op.endswith("rmsnorm"):
+        return per_elem * rows * d + 4 * d + (4 * rows if stats else 0)
     return 8 * rows * d  # copy: one read, one write per element
 
 
 def describe(op: str, rows: int, d: int, stats: bool) -> str:
     if op == "copy":
         return f"streaming copy FP32 {rows*d} elements (calibration, bytes of [{rows},{d}])"
-    name = "LayerNorm" if op == "layernorm" else "RMSNorm"
-    extra = " with per-row mean/rstd" if (stats and op == "layernorm") else (" with rstd" if stats else "")
+    name = "LayerNorm" if op.endswith("layernorm") else "RMSNorm"
+    if op.startswith("add_"):
+        name = "residual add (h = x + r written) + " + name
+    ln = op.endswith("layernorm")
+    extra = " with per-row mean/rstd" if (stats and ln) else (" with rstd" if stats else "")
     return f"{name} fwd FP32 [{rows},{d}]{extra}"
 
 
@@ -107,29 +118,43 @@ def load_bench_lib():
     if not os.path.exists(B.BENCH_LIB):
         raise RuntimeError(f"{B.BENCH_LIB} is not built; run __graft_entry__.build()")
     L = ctypes.CDLL(B.BENCH_LIB)
-    P = ctypes.c_void_p
-    L.mi_bench_layernorm_loop.argtypes = [P, P, P, P, P, P, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
-                                          ctypes.c_float, ctypes.c_int, ctypes.c_int, P]
-    L.mi_bench_rmsnorm_loop.argtypes = [P, P, P, P, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
-                                        ctypes.c_float, ctypes.c_int, ctypes.c_int, P]
-    L.mi_bench_copy_loop.argtypes = [P, P, ctypes.c_int, ctypes.c_int64, ctypes.c_int, P]
+    P, I, I64, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    L.mi_bench_layernorm_loop.argtypes = [P, P, P, P, P, P, I, I64, I64, F, I, I, P]
+    L.mi_bench_rmsnorm_loop.argtypes = [P, P, P, P, I, I64, I64, F, I, I, P]
+    L.mi_bench_add_layernorm_loop.argtypes = [P, P, P, P, P, P, P, P, I, I64, I64, F, I, I, P]
+    L.mi_bench_add_rmsnorm_loop.argtypes = [P, P, P, P, P, P, I, I64, I64, F, I, I, P]
+    L.mi_bench_copy_loop.argtypes = [P, P, I, I64, I, P]
     return L
 
 
 def ptr_array(tensors):
-    arr = (ctypes.c_void_p * len(tensors))(*[t.data_ptr() if t is not None else None for t in tensors])
-    return arr
+    return (ctypes.c_void_p * len(tensors))(*[t.data_ptr() if t is not None else None for t in tensors])
 
 
-def cpu_baseline(op, x, params, eps, budget_s: float):
+def oracle_call(op, x, r, params, eps):
+    """(y, [stats...]) from the oracle for one input batch."""
+    import oracle
+    if op == "layernorm":
+        y, mean, rstd, _, _ = oracle.layernorm(x, *params, eps)
+        return y, None, [mean, rstd]
+    if op == "rmsnorm":
+        y, rstd, _ = oracle.rmsnorm(x, *params, eps)
+        return y, None, [rstd]
+    if op == "add_layernorm":
+        y, h, mean, rstd = oracle.add_layernorm(x, r, *params, eps)
+        return y, h, [mean, rstd]
+    y, h, rstd = oracle.add_rmsnorm(x, r, *params, eps)
+    return y, h, [rstd]
+
+
+def cpu_baseline(op, x, r, params, eps, budget_s: float):
     """The float64 oracle on the host cores over the same workload."""
     import oracle
     threads = oracle.max_threads()
-    fn = oracle.layernorm if op == "layernorm" else oracle.rmsnorm
-    fn(x, *params, eps)  # first call loads the library
+    oracle_call(op, x, r, params, eps)  # first call loads the library
     reps, t0 = 0, time.perf_counter()
     while True:
-        fn(x, *params, eps)
+        oracle_call(op, x, r, params, eps)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
@@ -171,31 +196,41 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     op, rows, d, pattern, stats = BENCH_WORKLOADS[args.workload]
     eps = wl.EPS
+    add = op.startswith("add_")
+    ln = op.endswith("layernorm")
     BL = load_bench_lib()
-    L = mn.lib()
+    mn.lib()
 
     # -- inputs, resident in HBM before timing
     seed = wl.case_seed(2, rows, d, pattern)
     x_h = wl.make_x(rows, d, pattern, seed)
-    if op == "layernorm":
-        params_h = wl.make_affine(d, [2, d, 99])
-    elif op == "rmsnorm":
-        params_h = (wl.make_weight(d, [2, d, 99]),)
-    else:
+    r_h = wl.make_x(rows, d, "normal", [6] + seed) if add else None
+    if op == "copy":
         params_h = ()
+    elif ln:
+        params_h = wl.make_affine(d, [2, d, 99])
+    else:
+        params_h = (wl.make_weight(d, [2, d, 99]),)
     n = rows * d
-    per_set = 8 * n + (8 * rows if stats else 0)
+    per_set = (16 if add else 8) * n + (8 * rows if stats else 0)
     nsets = 1 if args.mode == "warm" else max(1, math.ceil(args.footprint_gib * 2**30 / per_set))
     x0 = torch.from_numpy(x_h).to(dev)
     xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
     ys = [torch.empty_like(x0) for _ in range(nsets)]
-    means = [torch.empty(rows, device=dev) for _ in range(nsets)] if (stats and op == "layernorm") else None
-    rstds = [torch.empty(rows, device=dev) for _ in range(nsets)] if stats else None
-    params = [torch.from_numpy(p).to(dev) for p in params_h]
+    rs_, hs = None, None
+    if add:
+        r0 = torch.from_numpy(r_h).to(dev)
+        rs_ = [r0] + [r0.clone() for _ in range(nsets - 1)]
+        hs = [torch.empty_like(x0) for _ in range(nsets)]
+    means = [torch.empty(rows, device=dev) for _ in range(nsets)] if (stats and ln) else None
+    rstds = [torch.empty(rows, device=dev) for _ in range(nsets)] if (stats and op != "copy") else None
+    params = [torch.from_numpy(p_).to(dev) for p_ in params_h]
     # every buffer above was filled on torch's current stream; the kernels run on
     # their own stream, so make the set-up complete before anything is launched
     torch.cuda.synchronize()
 
+    opcode = {"layernorm": mn.OP_LAYERNORM, "rmsnorm": mn.OP_RMSNORM,
+              "add_layernorm": mn.OP_ADD_LAYERNORM, "add_rmsnorm": mn.OP_ADD_RMSNORM}.get(op)
     vid = -1
     if args.variant:
         names = [mn.mi_norm_variant_name(i) for i in range(mn.mi_norm_variant_count())]
@@ -204,9 +239,9 @@ def main(argv=None) -> int:
             return 1
         vid = names.index(args.variant)
     if op != "copy":
-        sel = vid if vid >= 0 else mn.mi_norm_select_variant(
-            mn.OP_LAYERNORM if op == "layernorm" else mn.OP_RMSNORM, rows, d, x0, ys[0], params[0],
-            params[1] if op == "layernorm" else None)
+        sel = vid if vid >= 0 else mn.mi_norm_select(mn.problem(
+            opcode, rows, d, x0, ys[0], params[0], params[1] if ln else None,
+            r=rs_[0] if add else None, h=hs[0] if add else None))
         variant_name = mn.mi_norm_variant_name(sel)
     else:
         variant_name = "copy_f4"
@@ -214,30 +249,57 @@ def main(argv=None) -> int:
     stream = torch.cuda.Stream(device=dev)
     sh = stream.cuda_stream
     xa, ya = ptr_array(xs), ptr_array(ys)
+    ra = ptr_array(rs_) if add else None
+    ha = ptr_array(hs) if add else None
     ma = ptr_array(means) if means else None
-    ra = ptr_array(rstds) if rstds else None
+    sa = ptr_array(rstds) if rstds else None
+    p0 = params[0].data_ptr() if params else None
+    p1 = params[1].data_ptr() if ln else None
 
     def run_native(k: int):
         if op == "layernorm":
-            st = BL.mi_bench_layernorm_loop(xa, params[0].data_ptr(), params[1].data_ptr(), ya, ma, ra,
-                                            nsets, rows, d, eps, k, vid, sh)
+            st = BL.mi_bench_layernorm_loop(xa, p0, p1, ya, ma, sa, nsets, rows, d, eps, k, vid, sh)
         elif op == "rmsnorm":
-            st = BL.mi_bench_rmsnorm_loop(xa, params[0].data_ptr(), ya, ra, nsets, rows, d, eps, k, vid, sh)
+            st = BL.mi_bench_rmsnorm_loop(xa, p0, ya, sa, nsets, rows, d, eps, k, vid, sh)
+        elif op == "add_layernorm":
+            st = BL.mi_bench_add_layernorm_loop(xa, ra, p0, p1, ya, ha, ma, sa, nsets, rows, d, eps, k,
+                                                vid, sh)
+        elif op == "add_rmsnorm":
+            st = BL.mi_bench_add_rmsnorm_loop(xa, ra, p0, ya, ha, sa, nsets, rows, d, eps, k, vid, sh)
         else:
             st = BL.mi_bench_copy_loop(xa, ya, nsets, n, k, sh)
         if st != 0:
             raise RuntimeError(f"bench loop failed: {mn.mi_norm_status_string(st)}")
 
     def run_python(k: int, start: int = 0):
-        for s in range(start, start + k):
-            j = s % nsets
+        for s_ in range(start, start + k):
+            j = s_ % nsets
+            m_ = means[j] if means else None
+            r_ = rstds[j] if rstds else None
             if op == "layernorm":
-                fwd = mn.mi_layernorm_fwd if vid < 0 else (lambda *a, **kw: mn.mi_layernorm_fwd_variant(vid, *a, **kw))
-                fwd(xs[j], params[0], params[1], ys[j], rows, d, eps,
-                    means[j] if means else None, rstds[j] if rstds else None, stream=sh)
+                if vid < 0:
+                    mn.mi_layernorm_fwd(xs[j], *params, ys[j], rows, d, eps, m_, r_, stream=sh)
+                else:
+                    mn.mi_layernorm_fwd_variant(vid, xs[j], *params, ys[j], rows, d, eps, m_, r_, stream=sh)
             elif op == "rmsnorm":
-                fwd = mn.mi_rmsnorm_fwd if vid < 0 else (lambda *a, **kw: mn.mi_rmsnorm_fwd_variant(vid, *a, **kw))
-                fwd(xs[j], params[0], ys[j], rows, d, eps, rstds[j] if rstds else None, stream=sh)
+                if vid < 0:
+                    mn.mi_rmsnorm_fwd(xs[j], params[0], ys[j], rows, d, eps, r_, stream=sh)
+                else:
+                    mn.mi_rmsnorm_fwd_variant(vid, xs[j], params[0], ys[j], rows, d, eps, r_, stream=sh)
+            elif op == "add_layernorm":
+                if vid < 0:
+                    mn.mi_add_layernorm_fwd(xs[j], rs_[j], *params, ys[j], hs[j], rows, d, eps, m_, r_,
+                                            stream=sh)
+                else:
+                    mn.mi_add_layernorm_fwd_variant(vid, xs[j], rs_[j], *params, ys[j], hs[j], rows, d, eps,
+                                                    m_, r_, stream=sh)
+            elif op == "add_rmsnorm":
+                if vid < 0:
+                    mn.mi_add_rmsnorm_fwd(xs[j], rs_[j], params[0], ys[j], hs[j], rows, d, eps, r_,
+                                          stream=sh)
+                else:
+                    mn.mi_add_rmsnorm_fwd_variant(vid, xs[j], rs_[j], params[0], ys[j], hs[j], rows, d, eps,
+                                                  r_, stream=sh)
             else:
                 mn.mi_copy_f32(xs[j], ys[j], n, stream=sh)
 
@@ -250,14 +312,20 @@ def main(argv=None) -> int:
         sample = np.arange(rows) if n <= (1 << 26) else np.unique(
             np.random.default_rng(0).integers(0, rows, 512))
         xs_h = np.ascontiguousarray(x_h[sample])
-        ref = oracle.layernorm(xs_h, *params_h, eps) if op == "layernorm" else oracle.rmsnorm(xs_h, *params_h, eps)
-        got = ys[0].cpu().numpy()[sample]
-        ok, err, ratio = oracle.tolerance_ok(got, ref[0])
+        rs_h = np.ascontiguousarray(r_h[sample]) if add else None
+        ref_y, ref_h, ref_stats = oracle_call(op, xs_h, rs_h, params_h, eps)
+        checks = [(ys[0], ref_y)]
+        if add:
+            checks.append((hs[0], ref_h))
         if stats:
-            sgot = [means[0], rstds[0]] if op == "layernorm" else [rstds[0]]
-            for g_, r_ in zip(sgot, ref[1:1 + len(sgot)]):
-                ok2, e2, r2 = oracle.tolerance_ok(g_.cpu().numpy()[sample], r_)
-                ok, err, ratio = ok and ok2, max(err, e2), max(ratio, r2)
+            got_stats = [means[0], rstds[0]] if ln else [rstds[0]]
+            checks += list(zip(got_stats, ref_stats))
+        ok, err, ratio = True, 0.0, 0.0
+        for got_t, want in checks:
+            o2, e2, r2 = oracle.tolerance_ok(got_t.cpu().numpy()[sample], want)
+            ok, err, ratio = ok and o2, max(err, e2), max(ratio, r2)
+        if add and not np.array_equal(hs[0].cpu().numpy()[sample], ref_h):
+            ok = False
         if not ok:
             print(f"PARITY FAILURE before timing: max abs err {err:.3e}, err/bound {ratio:.3f}", file=sys.stderr)
             return 3
@@ -269,7 +337,6 @@ def main(argv=None) -> int:
         parity = {"exact": True}
 
     # -- warm-up and timed steps
-    graph = None
     if args.launch == "graph":
         gw, graph = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
         with torch.cuda.graph(gw, stream=stream):
@@ -281,12 +348,10 @@ def main(argv=None) -> int:
         runner_w, runner_t = (lambda: run_native(args.warmup)), (lambda: run_native(args.steps))
     else:
         def runner_w():
-            with torch.cuda.stream(stream):
-                run_python(args.warmup)
+            run_python(args.warmup)
 
         def runner_t():
-            with torch.cuda.stream(stream):
-                run_python(args.steps, start=args.warmup)
+            run_python(args.steps, start=args.warmup)
 
     with torch.cuda.stream(stream):
         runner_w()
@@ -306,7 +371,7 @@ def main(argv=None) -> int:
     bytes_step = algorithmic_bytes(op, rows, d, stats)
     gbps = bytes_step / (ms_per_step * 1e-3) / 1e9
 
-    traffic, traffic_src = pmc_traffic(args.workload)
+    traffic, _ = pmc_traffic(args.workload)
     roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(gbps / PEAK_HBM_GBPS, 4),
                 "traffic": traffic, "kernel": variant_name,
@@ -315,7 +380,7 @@ def main(argv=None) -> int:
 
     cpu = None
     if not args.no_cpu_baseline and op != "copy":
-        reps, el, threads = cpu_baseline(op, x_h, params_h, eps, args.cpu_seconds)
+        reps, el, threads = cpu_baseline(op, x_h, r_h, params_h, eps, args.cpu_seconds)
         cpu = {"value": round(bytes_step * reps / el / 1e9, 3), "unit": "GB/s", "cores": threads,
                "kind": "oracle",
                "sample": f"full {describe(op, rows, d, stats)} workload, {reps} repetitions "

@@ -17,6 +17,10 @@
  * threads did not win every shape" (section "The operator and the change"):
  *     y_rc = x_rc * w_c * rsqrt((1/d) sum_j x_rj^2 + eps)
  *
+ * Residual add fused before either norm (the step before the normalization
+ * whose absence the RMSNorm page notes: "no ... fusion with a residual add"):
+ *     h = x + r (a float32 addition, optionally written out), y = Norm(h)
+ *
  * Arithmetic is IEEE float32 with fused multiply-adds and the hardware
  * reciprocal square root; results agree with a float64 evaluation of the same
  * definition within |err| <= 1e-5 + 1e-4 * |ref| (the acceptance bound of the
@@ -33,16 +37,18 @@
  * - Work is enqueued on `stream` (NULL = the null stream) and the call returns
  *   without waiting.  One kernel launch per call; calls may be captured into a
  *   HIP graph.
- * - Aliasing: y may equal x exactly (in place).  Any other overlap between y
- *   and x, and any overlap of y with gamma, beta or w, is rejected.  mean/rstd
- *   must not overlap x, y or the parameters.
+ * - Aliasing: the [rows, d] tensors (x, y, and for the fused calls r, h) are
+ *   each either the same pointer as another or disjoint from it: y may equal
+ *   x (in place), and in the fused calls y and h may each equal x or r, but y
+ *   and h never share memory.  An output overlapping gamma, beta or w is
+ *   rejected.  mean/rstd must not overlap any other argument.
  * - 16-byte-aligned x, y, gamma, beta (or w) and d % 4 == 0 select the
  *   128-bit vector path; other layouts take a peeled or scalar path with the
  *   same results.
  * - Errors: MI_NORM_ERR_INVALID is returned before any launch for a NULL
  *   required pointer, a pointer not 4-byte aligned, rows < 0, d < 1,
- *   d > 2^31 - 1, a size overflow, eps NaN or negative, a partial overlap of
- *   y with x, or an overlap of y with a parameter vector.  rows == 0 returns MI_NORM_OK and launches nothing.
+ *   d > 2^31 - 1, a size overflow, eps NaN or negative, or an aliasing
+ *   pattern the rule above excludes.  rows == 0 returns MI_NORM_OK and launches nothing.
  *   MI_NORM_ERR_HIP reports a failed launch (the HIP error is not kept;
  *   faults inside the kernel surface at the caller's next synchronization,
  *   as usual for HIP).  No C++ exception crosses this interface.
@@ -103,6 +109,28 @@ mi_norm_status mi_rmsnorm_fwd(const float *x, const float *w, float *y,
                               int64_t rows, int64_t d, float eps,
                               float *rstd, hipStream_t stream);
 
+/*
+ * Residual add + LayerNorm forward: h = x + r (float32), y = LayerNorm(h).
+ *   x, r   [rows, d]  inputs                        (required)
+ *   gamma, beta [d]   per-column scale and shift    (required)
+ *   y      [rows, d]  output; may equal x or r      (required)
+ *   h      [rows, d]  x + r; may equal x or r; never y; NULL to skip
+ *   mean, rstd [rows] statistics of h, or NULL to skip
+ * Other arguments as mi_layernorm_fwd.  One kernel reads x and r once and
+ * writes y (and h): 12 (16) bytes per element instead of the 20 of a
+ * separate add and norm.
+ */
+mi_norm_status mi_add_layernorm_fwd(const float *x, const float *r, const float *gamma,
+                                    const float *beta, float *y, float *h,
+                                    int64_t rows, int64_t d, float eps,
+                                    float *mean, float *rstd, hipStream_t stream);
+
+/* Residual add + RMSNorm forward: h = x + r (float32), y = RMSNorm(h); the
+ * arguments follow mi_add_layernorm_fwd and mi_rmsnorm_fwd. */
+mi_norm_status mi_add_rmsnorm_fwd(const float *x, const float *r, const float *w,
+                                  float *y, float *h, int64_t rows, int64_t d, float eps,
+                                  float *rstd, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Kernel variants.  Every call above is served by one compiled kernel variant
  * chosen from the operation, the row width d, the pointer alignment and the
@@ -111,7 +139,25 @@ mi_norm_status mi_rmsnorm_fwd(const float *x, const float *w, float *y,
  * They follow the same conventions and error rules as the calls above.
  */
 
-typedef enum mi_norm_op { MI_NORM_OP_LAYERNORM = 0, MI_NORM_OP_RMSNORM = 1 } mi_norm_op;
+typedef enum mi_norm_op {
+    MI_NORM_OP_LAYERNORM = 0,
+    MI_NORM_OP_RMSNORM = 1,
+    MI_NORM_OP_ADD_LAYERNORM = 2,  /* residual add fused before LayerNorm */
+    MI_NORM_OP_ADD_RMSNORM = 3     /* residual add fused before RMSNorm */
+} mi_norm_op;
+
+/* One call's shape and pointers, for the variant queries below. */
+typedef struct mi_norm_problem {
+    int op;                 /* mi_norm_op */
+    int64_t rows;
+    int64_t d;
+    const void *x;          /* input */
+    const void *r;          /* residual input (MI_NORM_OP_ADD_*), else ignored */
+    const void *y;          /* output */
+    const void *h;          /* x + r output (MI_NORM_OP_ADD_*), NULL if not written */
+    const void *params0;    /* gamma or w */
+    const void *params1;    /* beta (LayerNorm ops), else ignored */
+} mi_norm_problem;
 
 typedef struct mi_norm_variant_info {
     int op;               /* mi_norm_op */
@@ -136,17 +182,14 @@ const char *mi_norm_variant_name(int id);
 /* Fill *out for variant `id`.  Returns MI_NORM_ERR_INVALID when out of range. */
 mi_norm_status mi_norm_variant_get_info(int id, mi_norm_variant_info *out);
 
-/* The variant the dispatcher would choose for these arguments (host logic
- * only, no device access): the row width and pointer alignment pick the
- * shape, the row count picks the workgroup size.  params1 is beta for
- * LayerNorm and ignored (may be NULL) for RMSNorm.  Returns -1 when the
- * arguments are invalid. */
-int mi_norm_select_variant(int op, int64_t rows, int64_t d, const void *x, const void *y,
-                           const void *params0, const void *params1);
+/* The variant the dispatcher would choose for problem *p (host logic only,
+ * no device access): the row width and pointer alignment pick the shape, the
+ * row count picks the waves per row and the workgroup size.  Returns -1 when
+ * the problem is invalid. */
+int mi_norm_select(const mi_norm_problem *p);
 
-/* Whether variant `id` can run these arguments (1) or not (0). */
-int mi_norm_variant_eligible(int id, int op, int64_t d, const void *x, const void *y,
-                             const void *params0, const void *params1);
+/* Whether variant `id` can run problem *p (1) or not (0). */
+int mi_norm_eligible(int id, const mi_norm_problem *p);
 
 /* LayerNorm / RMSNorm forced onto variant `id`.  MI_NORM_ERR_INVALID when the
  * variant does not exist, belongs to the other operation, or cannot run these
@@ -158,6 +201,13 @@ mi_norm_status mi_layernorm_fwd_variant(int id, const float *x, const float *gam
 mi_norm_status mi_rmsnorm_fwd_variant(int id, const float *x, const float *w, float *y,
                                       int64_t rows, int64_t d, float eps, float *rstd,
                                       hipStream_t stream);
+mi_norm_status mi_add_layernorm_fwd_variant(int id, const float *x, const float *r,
+                                            const float *gamma, const float *beta, float *y,
+                                            float *h, int64_t rows, int64_t d, float eps,
+                                            float *mean, float *rstd, hipStream_t stream);
+mi_norm_status mi_add_rmsnorm_fwd_variant(int id, const float *x, const float *r, const float *w,
+                                          float *y, float *h, int64_t rows, int64_t d, float eps,
+                                          float *rstd, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Calibration.  dst[i] = src[i] for i < n: a plain streaming copy with the

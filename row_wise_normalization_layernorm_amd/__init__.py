@@ -8,23 +8,33 @@ from ._binding import (  # noqa: F401
     MI_NORM_ERR_HIP,
     MI_NORM_ERR_INVALID,
     MI_NORM_OK,
+    OP_ADD_LAYERNORM,
+    OP_ADD_RMSNORM,
     OP_LAYERNORM,
     OP_RMSNORM,
     MiNormError,
+    Problem,
+    add_layernorm,
+    add_rmsnorm,
     header_functions,
     layernorm,
     lib,
+    mi_add_layernorm_fwd,
+    mi_add_layernorm_fwd_variant,
+    mi_add_rmsnorm_fwd,
+    mi_add_rmsnorm_fwd_variant,
     mi_copy_f32,
     mi_layernorm_fwd,
     mi_layernorm_fwd_variant,
-    mi_norm_select_variant,
+    mi_norm_eligible,
+    mi_norm_select,
     mi_norm_status_string,
     mi_norm_variant_count,
-    mi_norm_variant_eligible,
     mi_norm_variant_get_info,
     mi_norm_variant_name,
     mi_norm_version,
     mi_rmsnorm_fwd,
     mi_rmsnorm_fwd_variant,
+    problem,
     rmsnorm,
 )

@@ -27,6 +27,8 @@ MI_NORM_ERR_INVALID = 1
 MI_NORM_ERR_HIP = 2
 OP_LAYERNORM = 0
 OP_RMSNORM = 1
+OP_ADD_LAYERNORM = 2
+OP_ADD_RMSNORM = 3
 
 _lib = None
 
@@ -52,6 +54,15 @@ class VariantInfo(ctypes.Structure):
         return {k: getattr(self, k) for k, _ in self._fields_}
 
 
+class Problem(ctypes.Structure):
+    """mi_norm_problem: one call's shape and pointers, for the variant queries."""
+    _fields_ = [
+        ("op", ctypes.c_int), ("rows", ctypes.c_int64), ("d", ctypes.c_int64),
+        ("x", ctypes.c_void_p), ("r", ctypes.c_void_p), ("y", ctypes.c_void_p),
+        ("h", ctypes.c_void_p), ("params0", ctypes.c_void_p), ("params1", ctypes.c_void_p),
+    ]
+
+
 _VP = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _F = ctypes.c_float
@@ -65,8 +76,13 @@ _SIGNATURES = {
     "mi_norm_variant_count": (_I, []),
     "mi_norm_variant_name": (ctypes.c_char_p, [_I]),
     "mi_norm_variant_get_info": (_I, [_I, ctypes.POINTER(VariantInfo)]),
-    "mi_norm_select_variant": (_I, [_I, _I64, _I64, _VP, _VP, _VP, _VP]),
-    "mi_norm_variant_eligible": (_I, [_I, _I, _I64, _VP, _VP, _VP, _VP]),
+    "mi_add_layernorm_fwd": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _F, _VP, _VP, _VP]),
+    "mi_add_rmsnorm_fwd": (_I, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _F, _VP, _VP]),
+    "mi_norm_select": (_I, [ctypes.POINTER(Problem)]),
+    "mi_norm_eligible": (_I, [_I, ctypes.POINTER(Problem)]),
+    "mi_add_layernorm_fwd_variant": (_I, [_I, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _F, _VP, _VP,
+                                          _VP]),
+    "mi_add_rmsnorm_fwd_variant": (_I, [_I, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _F, _VP, _VP]),
     "mi_layernorm_fwd_variant": (_I, [_I, _VP, _VP, _VP, _VP, _I64, _I64, _F, _VP, _VP, _VP]),
     "mi_rmsnorm_fwd_variant": (_I, [_I, _VP, _VP, _VP, _I64, _I64, _F, _VP, _VP]),
     "mi_copy_f32": (_I, [_VP, _VP, _I64, _VP]),
@@ -176,6 +192,45 @@ def mi_rmsnorm_fwd_variant(vid: int, x, w, y, rows: int, d: int, eps: float = 1e
     _check(st, f"mi_rmsnorm_fwd_variant({vid})")
 
 
+def mi_add_layernorm_fwd(x, r, gamma, beta, y, h, rows: int, d: int, eps: float = 1e-5,
+                         mean=None, rstd=None, stream=None) -> None:
+    n = max(rows, 0) * max(d, 0)
+    st = lib().mi_add_layernorm_fwd(_ptr(x, "x", n), _ptr(r, "r", n), _ptr(gamma, "gamma", d),
+                                    _ptr(beta, "beta", d), _ptr(y, "y", n), _ptr(h, "h", n), rows, d,
+                                    eps, _ptr(mean, "mean", rows), _ptr(rstd, "rstd", rows),
+                                    _stream(stream, x, y))
+    _check(st, "mi_add_layernorm_fwd")
+
+
+def mi_add_rmsnorm_fwd(x, r, w, y, h, rows: int, d: int, eps: float = 1e-5, rstd=None,
+                       stream=None) -> None:
+    n = max(rows, 0) * max(d, 0)
+    st = lib().mi_add_rmsnorm_fwd(_ptr(x, "x", n), _ptr(r, "r", n), _ptr(w, "w", d), _ptr(y, "y", n),
+                                  _ptr(h, "h", n), rows, d, eps, _ptr(rstd, "rstd", rows),
+                                  _stream(stream, x, y))
+    _check(st, "mi_add_rmsnorm_fwd")
+
+
+def mi_add_layernorm_fwd_variant(vid: int, x, r, gamma, beta, y, h, rows: int, d: int,
+                                 eps: float = 1e-5, mean=None, rstd=None, stream=None) -> None:
+    n = max(rows, 0) * max(d, 0)
+    st = lib().mi_add_layernorm_fwd_variant(vid, _ptr(x, "x", n), _ptr(r, "r", n),
+                                            _ptr(gamma, "gamma", d), _ptr(beta, "beta", d),
+                                            _ptr(y, "y", n), _ptr(h, "h", n), rows, d, eps,
+                                            _ptr(mean, "mean", rows), _ptr(rstd, "rstd", rows),
+                                            _stream(stream, x, y))
+    _check(st, f"mi_add_layernorm_fwd_variant({vid})")
+
+
+def mi_add_rmsnorm_fwd_variant(vid: int, x, r, w, y, h, rows: int, d: int, eps: float = 1e-5,
+                               rstd=None, stream=None) -> None:
+    n = max(rows, 0) * max(d, 0)
+    st = lib().mi_add_rmsnorm_fwd_variant(vid, _ptr(x, "x", n), _ptr(r, "r", n), _ptr(w, "w", d),
+                                          _ptr(y, "y", n), _ptr(h, "h", n), rows, d, eps,
+                                          _ptr(rstd, "rstd", rows), _stream(stream, x, y))
+    _check(st, f"mi_add_rmsnorm_fwd_variant({vid})")
+
+
 def mi_copy_f32(src, dst, n: int, stream=None) -> None:
     st = lib().mi_copy_f32(_ptr(src, "src", n), _ptr(dst, "dst", n), n, _stream(stream, src, dst))
     _check(st, "mi_copy_f32")
@@ -208,14 +263,17 @@ def _addr(a):
     return a if (a is None or isinstance(a, int)) else a.data_ptr()
 
 
-def mi_norm_select_variant(op: int, rows: int, d: int, x, y, params0, params1=None) -> int:
-    return int(lib().mi_norm_select_variant(op, rows, d, _addr(x), _addr(y), _addr(params0),
-                                            _addr(params1)))
+def problem(op: int, rows: int, d: int, x, y, params0, params1=None, r=None, h=None) -> Problem:
+    """An mi_norm_problem from tensors or integer addresses."""
+    return Problem(op, rows, d, _addr(x), _addr(r), _addr(y), _addr(h), _addr(params0), _addr(params1))
 
 
-def mi_norm_variant_eligible(vid: int, op: int, d: int, x, y, params0, params1=None) -> bool:
-    return bool(lib().mi_norm_variant_eligible(vid, op, d, _addr(x), _addr(y), _addr(params0),
-                                               _addr(params1)))
+def mi_norm_select(p: Problem) -> int:
+    return int(lib().mi_norm_select(ctypes.byref(p)))
+
+
+def mi_norm_eligible(vid: int, p: Problem) -> bool:
+    return bool(lib().mi_norm_eligible(vid, ctypes.byref(p)))
 
 
 # --- conveniences over torch tensors (allocation is torch's) -------------------
@@ -233,6 +291,33 @@ def layernorm(x, gamma, beta, eps: float = 1e-5, stats: bool = False, out=None, 
     rstd = torch.empty(x.shape[:-1], device=x.device, dtype=torch.float32) if stats else None
     mi_layernorm_fwd(x, gamma, beta, y, rows, d, eps, mean, rstd, stream)
     return (y, mean, rstd) if stats else y
+
+
+def add_layernorm(x, r, gamma, beta, eps: float = 1e-5, stats: bool = False, write_sum: bool = True,
+                  stream=None):
+    """h = x + r, y = LayerNorm(h).  Returns (y, h) or (y, h, mean, rstd); h is
+    None without ``write_sum``."""
+    import torch
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    y = torch.empty_like(x)
+    h = torch.empty_like(x) if write_sum else None
+    mean = torch.empty(x.shape[:-1], device=x.device, dtype=torch.float32) if stats else None
+    rstd = torch.empty(x.shape[:-1], device=x.device, dtype=torch.float32) if stats else None
+    mi_add_layernorm_fwd(x, r, gamma, beta, y, h, rows, d, eps, mean, rstd, stream)
+    return (y, h, mean, rstd) if stats else (y, h)
+
+
+def add_rmsnorm(x, r, w, eps: float = 1e-5, stats: bool = False, write_sum: bool = True, stream=None):
+    """h = x + r, y = RMSNorm(h).  Returns (y, h) or (y, h, rstd)."""
+    import torch
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    y = torch.empty_like(x)
+    h = torch.empty_like(x) if write_sum else None
+    rstd = torch.empty(x.shape[:-1], device=x.device, dtype=torch.float32) if stats else None
+    mi_add_rmsnorm_fwd(x, r, w, y, h, rows, d, eps, rstd, stream)
+    return (y, h, rstd) if stats else (y, h)
 
 
 def rmsnorm(x, w, eps: float = 1e-5, stats: bool = False, out=None, stream=None):

@@ -45,6 +45,43 @@ int mi_bench_rmsnorm_loop(const float *const *xs, const float *w, float *const *
     return MI_NORM_OK;
 }
 
+// Residual add + LayerNorm / RMSNorm: rs[k] the residual, hs[k] where x + r is
+// written (hs or its entries may be NULL).
+int mi_bench_add_layernorm_loop(const float *const *xs, const float *const *rs, const float *gamma,
+                                const float *beta, float *const *ys, float *const *hs,
+                                float *const *means, float *const *rstds, int nsets, int64_t rows,
+                                int64_t d, float eps, int steps, int variant, hipStream_t stream) {
+    for (int s = 0; s < steps; ++s) {
+        const int k = s % nsets;
+        float *h = hs ? hs[k] : nullptr;
+        float *m = means ? means[k] : nullptr;
+        float *r = rstds ? rstds[k] : nullptr;
+        const mi_norm_status st =
+            variant < 0 ? mi_add_layernorm_fwd(xs[k], rs[k], gamma, beta, ys[k], h, rows, d, eps, m, r, stream)
+                        : mi_add_layernorm_fwd_variant(variant, xs[k], rs[k], gamma, beta, ys[k], h, rows, d,
+                                                       eps, m, r, stream);
+        if (st != MI_NORM_OK) return st;
+    }
+    return MI_NORM_OK;
+}
+
+int mi_bench_add_rmsnorm_loop(const float *const *xs, const float *const *rs, const float *w,
+                              float *const *ys, float *const *hs, float *const *rstds, int nsets,
+                              int64_t rows, int64_t d, float eps, int steps, int variant,
+                              hipStream_t stream) {
+    for (int s = 0; s < steps; ++s) {
+        const int k = s % nsets;
+        float *h = hs ? hs[k] : nullptr;
+        float *r = rstds ? rstds[k] : nullptr;
+        const mi_norm_status st =
+            variant < 0 ? mi_add_rmsnorm_fwd(xs[k], rs[k], w, ys[k], h, rows, d, eps, r, stream)
+                        : mi_add_rmsnorm_fwd_variant(variant, xs[k], rs[k], w, ys[k], h, rows, d, eps, r,
+                                                     stream);
+        if (st != MI_NORM_OK) return st;
+    }
+    return MI_NORM_OK;
+}
+
 int mi_bench_copy_loop(const float *const *srcs, float *const *dsts, int nsets, int64_t n, int steps,
                        hipStream_t stream) {
     for (int s = 0; s < steps; ++s) {

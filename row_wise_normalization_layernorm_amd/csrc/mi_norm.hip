@@ -31,59 +31,67 @@ struct Variant {
 
 constexpr int64_t kUnbounded = INT64_MAX;
 
-// Every held variant streams x in and y out with non-temporal hints and
-// reads gamma/beta in the output pass (see norm_held's NTL/NTS/PRE).
-#define MI_HELD(OP, OPN, VEC, PEEL, LPR, WPR, Q, WAVES)                                        \
+// ABI op codes: bit 0 picks the normalization, op >= 2 fuses the residual add
+constexpr int kOps = 4;
+constexpr int kop(int op) { return op & 1; }       // OP_LN or OP_RMS
+constexpr bool kres(int op) { return op >= 2; }
+
+// Every held variant streams x (and r) in and y (and h) out with
+// non-temporal hints and reads gamma/beta in the output pass (norm_held's
+// NTL/NTS/PRE); the cross-wave merge follows norm_held's default.
+#define MI_HELD(OPC, OPN, VEC, PEEL, LPR, WPR, Q, WAVES)                                       \
     Variant{OPN "_" #VEC "_p" #PEEL "_l" #LPR "_w" #WPR "_q" #Q "_b" #WAVES,                  \
-            mi_norm_variant_info{OP, VEC, PEEL, 0, LPR, WPR, Q, WAVES,                          \
+            mi_norm_variant_info{OPC, VEC, PEEL, 0, LPR, WPR, Q, WAVES,                         \
                                  (WPR == 1) ? WAVES * (64 / LPR) : WAVES / WPR,                 \
                                  (int64_t)VEC * LPR * WPR * Q, (VEC == 4 && !PEEL) ? 1 : 0},    \
-            reinterpret_cast<const void *>(                                                     \
-                &norm_held<OP, VEC, (PEEL != 0), LPR, WPR, Q, WAVES, true, true, 0>)}
+            reinterpret_cast<const void *>(&norm_held<kop(OPC), VEC, (PEEL != 0), LPR, WPR, Q,  \
+                                                      WAVES, true, true, 0, -1, kres(OPC)>)}
 
 // the same shape with 4 and with 16 waves per workgroup
-#define MI_HELD2(OP, OPN, VEC, PEEL, LPR, WPR, Q, WSMALL)                                      \
-    MI_HELD(OP, OPN, VEC, PEEL, LPR, WPR, Q, WSMALL), MI_HELD(OP, OPN, VEC, PEEL, LPR, WPR, Q, 16)
+#define MI_HELD2(OPC, OPN, VEC, PEEL, LPR, WPR, Q, WSMALL)                                     \
+    MI_HELD(OPC, OPN, VEC, PEEL, LPR, WPR, Q, WSMALL), MI_HELD(OPC, OPN, VEC, PEEL, LPR, WPR, Q, 16)
 
-#define MI_LOOP(OP, OPN, VEC, WAVES, U)                                                        \
+#define MI_LOOP(OPC, OPN, VEC, WAVES, U)                                                       \
     Variant{OPN "_" #VEC "_loop_b" #WAVES "_u" #U,                                              \
-            mi_norm_variant_info{OP, VEC, 0, 1, 64, WAVES, U, WAVES, 1, kUnbounded,             \
+            mi_norm_variant_info{OPC, VEC, 0, 1, 64, WAVES, U, WAVES, 1, kUnbounded,            \
                                  VEC == 4 ? 1 : 0},                                             \
-            reinterpret_cast<const void *>(&norm_looped<OP, VEC, WAVES, U>)}
+            reinterpret_cast<const void *>(&norm_looped<kop(OPC), VEC, WAVES, U, kres(OPC)>)}
 
 // every (waves per row, slots) pair of a 128-bit path: slots 1, 2, 3, 4, 6, 8
 // for 1, 2, 4, 8 and 16 waves per row
-#define MI_SLOTS(OP, OPN, PEEL, WPR, WSMALL)                                                   \
-    MI_HELD2(OP, OPN, 4, PEEL, 64, WPR, 1, WSMALL), MI_HELD2(OP, OPN, 4, PEEL, 64, WPR, 2, WSMALL), \
-    MI_HELD2(OP, OPN, 4, PEEL, 64, WPR, 3, WSMALL), MI_HELD2(OP, OPN, 4, PEEL, 64, WPR, 4, WSMALL), \
-    MI_HELD2(OP, OPN, 4, PEEL, 64, WPR, 6, WSMALL), MI_HELD2(OP, OPN, 4, PEEL, 64, WPR, 8, WSMALL)
-#define MI_SLOTS16(OP, OPN, PEEL)                                                              \
-    MI_HELD(OP, OPN, 4, PEEL, 64, 16, 1, 16), MI_HELD(OP, OPN, 4, PEEL, 64, 16, 2, 16),         \
-    MI_HELD(OP, OPN, 4, PEEL, 64, 16, 3, 16), MI_HELD(OP, OPN, 4, PEEL, 64, 16, 4, 16),         \
-    MI_HELD(OP, OPN, 4, PEEL, 64, 16, 6, 16), MI_HELD(OP, OPN, 4, PEEL, 64, 16, 8, 16)
-#define MI_PATH128(OP, OPN, PEEL)                                                              \
-    MI_SLOTS(OP, OPN, PEEL, 1, 4), MI_SLOTS(OP, OPN, PEEL, 2, 4), MI_SLOTS(OP, OPN, PEEL, 4, 4), \
-    MI_SLOTS(OP, OPN, PEEL, 8, 8), MI_SLOTS16(OP, OPN, PEEL)
+#define MI_SLOTS(OPC, OPN, PEEL, WPR, WSMALL)                                                  \
+    MI_HELD2(OPC, OPN, 4, PEEL, 64, WPR, 1, WSMALL), MI_HELD2(OPC, OPN, 4, PEEL, 64, WPR, 2, WSMALL), \
+    MI_HELD2(OPC, OPN, 4, PEEL, 64, WPR, 3, WSMALL), MI_HELD2(OPC, OPN, 4, PEEL, 64, WPR, 4, WSMALL), \
+    MI_HELD2(OPC, OPN, 4, PEEL, 64, WPR, 6, WSMALL), MI_HELD2(OPC, OPN, 4, PEEL, 64, WPR, 8, WSMALL)
+#define MI_SLOTS16(OPC, OPN, PEEL)                                                             \
+    MI_HELD(OPC, OPN, 4, PEEL, 64, 16, 1, 16), MI_HELD(OPC, OPN, 4, PEEL, 64, 16, 2, 16),        \
+    MI_HELD(OPC, OPN, 4, PEEL, 64, 16, 3, 16), MI_HELD(OPC, OPN, 4, PEEL, 64, 16, 4, 16),        \
+    MI_HELD(OPC, OPN, 4, PEEL, 64, 16, 6, 16), MI_HELD(OPC, OPN, 4, PEEL, 64, 16, 8, 16)
+#define MI_PATH128(OPC, OPN, PEEL)                                                             \
+    MI_SLOTS(OPC, OPN, PEEL, 1, 4), MI_SLOTS(OPC, OPN, PEEL, 2, 4), MI_SLOTS(OPC, OPN, PEEL, 4, 4), \
+    MI_SLOTS(OPC, OPN, PEEL, 8, 8), MI_SLOTS16(OPC, OPN, PEEL)
 
-#define MI_OP_TABLE(OP, OPN)                                                                   \
+#define MI_OP_TABLE(OPC, OPN)                                                                  \
     /* 128-bit, aligned, d % 4 == 0; 16 or 32 lanes per row for narrow rows */                  \
-    MI_HELD2(OP, OPN, 4, 0, 16, 1, 1, 4), MI_HELD2(OP, OPN, 4, 0, 32, 1, 1, 4),                 \
-    MI_PATH128(OP, OPN, 0),                                                                     \
-    /* 128-bit body with a per-row scalar head and tail: any d, x == y mod 16 B */              \
-    MI_PATH128(OP, OPN, 1),                                                                     \
+    MI_HELD2(OPC, OPN, 4, 0, 16, 1, 1, 4), MI_HELD2(OPC, OPN, 4, 0, 32, 1, 1, 4),               \
+    MI_PATH128(OPC, OPN, 0),                                                                    \
+    /* 128-bit body with a per-row scalar head and tail: any d, rows congruent mod 16 B */      \
+    MI_PATH128(OPC, OPN, 1),                                                                    \
     /* 32-bit accesses: any d, any 4-byte alignment */                                          \
-    MI_HELD2(OP, OPN, 1, 0, 16, 1, 1, 4), MI_HELD2(OP, OPN, 1, 0, 32, 1, 1, 4),                 \
-    MI_HELD2(OP, OPN, 1, 0, 64, 1, 1, 4), MI_HELD2(OP, OPN, 1, 0, 64, 1, 2, 4),                 \
-    MI_HELD2(OP, OPN, 1, 0, 64, 1, 4, 4), MI_HELD2(OP, OPN, 1, 0, 64, 1, 8, 4),                 \
-    MI_HELD2(OP, OPN, 1, 0, 64, 4, 4, 4), MI_HELD2(OP, OPN, 1, 0, 64, 4, 8, 4),                 \
-    MI_HELD2(OP, OPN, 1, 0, 64, 8, 8, 8),                                                       \
-    MI_HELD(OP, OPN, 1, 0, 64, 16, 8, 16), MI_HELD(OP, OPN, 1, 0, 64, 16, 16, 16),              \
+    MI_HELD2(OPC, OPN, 1, 0, 16, 1, 1, 4), MI_HELD2(OPC, OPN, 1, 0, 32, 1, 1, 4),               \
+    MI_HELD2(OPC, OPN, 1, 0, 64, 1, 1, 4), MI_HELD2(OPC, OPN, 1, 0, 64, 1, 2, 4),               \
+    MI_HELD2(OPC, OPN, 1, 0, 64, 1, 4, 4), MI_HELD2(OPC, OPN, 1, 0, 64, 1, 8, 4),               \
+    MI_HELD2(OPC, OPN, 1, 0, 64, 4, 4, 4), MI_HELD2(OPC, OPN, 1, 0, 64, 4, 8, 4),               \
+    MI_HELD2(OPC, OPN, 1, 0, 64, 8, 8, 8),                                                      \
+    MI_HELD(OPC, OPN, 1, 0, 64, 16, 8, 16), MI_HELD(OPC, OPN, 1, 0, 64, 16, 16, 16),            \
     /* streamed rows, any width */                                                             \
-    MI_LOOP(OP, OPN, 4, 4, 4), MI_LOOP(OP, OPN, 1, 4, 8)
+    MI_LOOP(OPC, OPN, 4, 4, 4), MI_LOOP(OPC, OPN, 1, 4, 8)
 
 const Variant kVariants[] = {
-    MI_OP_TABLE(OP_LN, "ln"),
-    MI_OP_TABLE(OP_RMS, "rms"),
+    MI_OP_TABLE(MI_NORM_OP_LAYERNORM, "ln"),
+    MI_OP_TABLE(MI_NORM_OP_RMSNORM, "rms"),
+    MI_OP_TABLE(MI_NORM_OP_ADD_LAYERNORM, "addln"),
+    MI_OP_TABLE(MI_NORM_OP_ADD_RMSNORM, "addrms"),
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -94,6 +102,7 @@ constexpr int64_t kMaxRowGroups = int64_t(1) << 30;
 
 inline bool al16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool al4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+inline uintptr_t addr(const void *p) { return reinterpret_cast<uintptr_t>(p); }
 
 // Fewest workgroups that still cover every CU: of the variants with this
 // shape, the one with the most waves per workgroup whose grid has at least
@@ -144,6 +153,7 @@ void shape128(int64_t nvec, int64_t rows, int &wpr, int &q) {
     if (q == 0) wpr = 0;
 }
 
+// (lanes per row, waves per row, slots) of a 32-bit row of n elements
 void ladder1(int64_t n, int &lpr, int &wpr, int &q) {
     static const int q1[] = {1, 2, 4, 8};
     static const int q4[] = {4, 8};
@@ -159,86 +169,114 @@ void ladder1(int64_t n, int &lpr, int &wpr, int &q) {
     if (n <= 16384) { wpr = 16; q = pick_q(n, 1024, q16, 2); return; }
 }
 
-struct Layout {
-    bool a16;      // every pointer 16-byte aligned and d % 4 == 0
-    bool peel_ok;  // x and y share their phase within 16 bytes
+// the [rows, d] row pointers a problem touches: x, r, y, h (absent ones null)
+struct Rows {
+    const void *p[4];
 };
 
-Layout layout_of(int op, int64_t d, const void *x, const void *y, const void *p0, const void *p1) {
-    Layout L;
-    L.a16 = (d % 4 == 0) && al16(x) && al16(y) && al16(p0) && (op == OP_RMS || al16(p1));
-    L.peel_ok = ((reinterpret_cast<uintptr_t>(x) ^ reinterpret_cast<uintptr_t>(y)) & 15u) == 0;
+Rows rows_of(const mi_norm_problem &P) {
+    return Rows{{P.x, kres(P.op) ? P.r : nullptr, P.y, kres(P.op) ? P.h : nullptr}};
+}
+
+struct Layout {
+    bool a16;      // every row pointer and parameter 16-byte aligned, d % 4 == 0
+    bool peel_ok;  // every row pointer has the same phase within 16 bytes
+};
+
+Layout layout_of(const mi_norm_problem &P) {
+    const Rows R = rows_of(P);
+    Layout L{P.d % 4 == 0 && al16(P.params0) && (kop(P.op) == OP_RMS || al16(P.params1)), true};
+    for (const void *q : R.p) {
+        if (!q) continue;
+        L.a16 = L.a16 && al16(q);
+        L.peel_ok = L.peel_ok && ((addr(q) ^ addr(P.x)) & 15u) == 0;
+    }
     return L;
 }
 
-bool args_ok(int op, int64_t d, const void *x, const void *y, const void *p0, const void *p1) {
-    if (op != OP_LN && op != OP_RMS) return false;
-    if (!x || !y || !p0 || (op == OP_LN && !p1)) return false;
-    if (!al4(x) || !al4(y) || !al4(p0) || (op == OP_LN && !al4(p1))) return false;
-    if (d < 1 || d > INT32_MAX) return false;
+// the shape checks every entry point and the variant queries share
+bool shape_ok(const mi_norm_problem &P) {
+    if (P.op < 0 || P.op >= kOps) return false;
+    if (!P.x || !P.y || !P.params0 || (kop(P.op) == OP_LN && !P.params1) || (kres(P.op) && !P.r))
+        return false;
+    const Rows R = rows_of(P);
+    for (const void *q : R.p)
+        if (q && !al4(q)) return false;
+    if (!al4(P.params0) || (kop(P.op) == OP_LN && !al4(P.params1))) return false;
+    if (P.d < 1 || P.d > INT32_MAX || P.rows < 0) return false;
+    if (P.rows > 0 && P.rows > (INT64_MAX / (int64_t)sizeof(float)) / P.d) return false;
     return true;
 }
 
-int select_variant(int op, int64_t rows, int64_t d, const void *x, const void *y, const void *p0,
-                   const void *p1) {
-    if (!args_ok(op, d, x, y, p0, p1) || rows < 0) return -1;
-    const Layout L = layout_of(op, d, x, y, p0, p1);
+int select_variant(const mi_norm_problem &P) {
+    if (!shape_ok(P)) return -1;
+    const Layout L = layout_of(P);
+    const int64_t d = P.d, rows = P.rows;
     int lpr, wpr, q;
     if (L.a16) {
         const int64_t nvec = d / 4;
-        if (nvec <= 16) return find(op, rows, 4, 0, 0, 16, 1, 1);
-        if (nvec <= 32) return find(op, rows, 4, 0, 0, 32, 1, 1);
+        if (nvec <= 16) return find(P.op, rows, 4, 0, 0, 16, 1, 1);
+        if (nvec <= 32) return find(P.op, rows, 4, 0, 0, 32, 1, 1);
         shape128(nvec, rows, wpr, q);
-        if (wpr) return find(op, rows, 4, 0, 0, 64, wpr, q);
-        return find(op, rows, 4, 0, 1, 0, 0, 0);
+        if (wpr) return find(P.op, rows, 4, 0, 0, 64, wpr, q);
+        return find(P.op, rows, 4, 0, 1, 0, 0, 0);
     }
     if (L.peel_ok && d >= 256) {
         shape128((d + 3) / 4, rows, wpr, q);
-        if (wpr) return find(op, rows, 4, 1, 0, 64, wpr, q);
-        return find(op, rows, 1, 0, 1, 0, 0, 0);
+        if (wpr) return find(P.op, rows, 4, 1, 0, 64, wpr, q);
+        return find(P.op, rows, 1, 0, 1, 0, 0, 0);
     }
     ladder1(d, lpr, wpr, q);
-    if (wpr) return find(op, rows, 1, 0, 0, lpr, wpr, q);
-    return find(op, rows, 1, 0, 1, 0, 0, 0);
+    if (wpr) return find(P.op, rows, 1, 0, 0, lpr, wpr, q);
+    return find(P.op, rows, 1, 0, 1, 0, 0, 0);
 }
 
-bool eligible(int id, int op, int64_t d, const void *x, const void *y, const void *p0, const void *p1) {
-    if (id < 0 || id >= kNumVariants) return false;
-    if (!args_ok(op, d, x, y, p0, p1)) return false;
+bool eligible(int id, const mi_norm_problem &P) {
+    if (id < 0 || id >= kNumVariants || !shape_ok(P)) return false;
     const mi_norm_variant_info &v = kVariants[id].info;
-    if (v.op != op) return false;
-    const Layout L = layout_of(op, d, x, y, p0, p1);
+    if (v.op != P.op) return false;
+    const Layout L = layout_of(P);
     if (v.looped) return v.vec == 1 || L.a16;
-    if (v.peel) return L.peel_ok && (d + 3) / 4 <= v.max_d / 4;
-    if (v.vec == 4) return L.a16 && d <= v.max_d;
-    return d <= v.max_d;
-}
-
-// y may equal x; otherwise the two [rows, d] ranges must not intersect
-bool overlap_ok(const void *x, const void *y, int64_t rows, int64_t d) {
-    if (x == y || rows == 0) return true;
-    const uintptr_t bytes = (uintptr_t)rows * (uintptr_t)d * sizeof(float);
-    const uintptr_t a = reinterpret_cast<uintptr_t>(x), b = reinterpret_cast<uintptr_t>(y);
-    return a + bytes <= b || b + bytes <= a;
+    if (v.peel) return L.peel_ok && (P.d + 3) / 4 <= v.max_d / 4;
+    if (v.vec == 4) return L.a16 && P.d <= v.max_d;
+    return P.d <= v.max_d;
 }
 
 // [a, a + na) and [b, b + nb) (in floats) intersect
 bool ranges_meet(const void *a, int64_t na, const void *b, int64_t nb) {
-    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    const uintptr_t pa = addr(a), pb = addr(b);
     return pa < pb + (uintptr_t)nb * sizeof(float) && pb < pa + (uintptr_t)na * sizeof(float);
 }
 
-mi_norm_status validate(int op, const float *x, const float *p0, const float *p1, const float *y,
-                        int64_t rows, int64_t d, float eps, const float *mean, const float *rstd) {
-    if (!args_ok(op, d, x, y, p0, p1)) return MI_NORM_ERR_INVALID;
-    if (rows < 0) return MI_NORM_ERR_INVALID;
+// Aliasing rules: two row tensors are either the same pointer or disjoint,
+// the two outputs y and h never share memory, and no output overlaps a
+// parameter vector (the parameters are read after earlier outputs are stored).
+bool aliasing_ok(const mi_norm_problem &P) {
+    if (P.rows == 0) return true;
+    const int64_t n = P.rows * P.d;
+    const Rows R = rows_of(P);
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j) {
+            if (!R.p[i] || !R.p[j]) continue;
+            if (R.p[i] == R.p[j]) {
+                if (i == 2 && j == 3) return false;  // y == h
+                continue;
+            }
+            if (ranges_meet(R.p[i], n, R.p[j], n)) return false;
+        }
+    for (int o = 2; o < 4; ++o) {
+        if (!R.p[o]) continue;
+        if (ranges_meet(R.p[o], n, P.params0, P.d)) return false;
+        if (kop(P.op) == OP_LN && ranges_meet(R.p[o], n, P.params1, P.d)) return false;
+    }
+    return true;
+}
+
+mi_norm_status validate(const mi_norm_problem &P, float eps, const float *mean, const float *rstd) {
+    if (!shape_ok(P)) return MI_NORM_ERR_INVALID;
     if (!(eps >= 0.f)) return MI_NORM_ERR_INVALID;  // also rejects NaN
-    if (rows > 0 && rows > (INT64_MAX / (int64_t)sizeof(float)) / d) return MI_NORM_ERR_INVALID;
     if ((mean && !al4(mean)) || (rstd && !al4(rstd))) return MI_NORM_ERR_INVALID;
-    if (!overlap_ok(x, y, rows, d)) return MI_NORM_ERR_INVALID;
-    // parameters are read after earlier slots of y are stored
-    if (rows > 0 && (ranges_meet(y, rows * d, p0, d) || (p1 && ranges_meet(y, rows * d, p1, d))))
-        return MI_NORM_ERR_INVALID;
+    if (!aliasing_ok(P)) return MI_NORM_ERR_INVALID;
     return MI_NORM_OK;
 }
 
@@ -262,9 +300,12 @@ mi_norm_status launch(int id, const NormParams &P, hipStream_t stream) {
     for (int64_t r0 = 0; r0 < P.rows; r0 += chunk) {
         NormParams arg = P;
         const int64_t n = (P.rows - r0) < chunk ? (P.rows - r0) : chunk;
+        const int64_t off = r0 * (int64_t)P.d;
         arg.rows = n;
-        arg.x = P.x + r0 * (int64_t)P.d;
-        arg.y = P.y + r0 * (int64_t)P.d;
+        arg.x = P.x + off;
+        arg.y = P.y + off;
+        if (P.r) arg.r = P.r + off;
+        if (P.h) arg.h = P.h + off;
         if (P.mean) arg.mean = P.mean + r0;
         if (P.rstd) arg.rstd = P.rstd + r0;
         void *args[] = {&arg};
@@ -275,35 +316,47 @@ mi_norm_status launch(int id, const NormParams &P, hipStream_t stream) {
     return MI_NORM_OK;
 }
 
-NormParams make_params(const float *x, const float *p0, const float *p1, float *y, int64_t rows,
-                       int64_t d, float eps, float *mean, float *rstd) {
-    NormParams P;
-    P.x = x;
-    P.p0 = p0;
-    P.p1 = p1;
-    P.y = y;
-    P.mean = mean;
-    P.rstd = rstd;
+mi_norm_problem make_problem(int op, int64_t rows, int64_t d, const float *x, const float *r,
+                             const float *y, const float *h, const float *p0, const float *p1) {
+    mi_norm_problem P;
+    P.op = op;
     P.rows = rows;
-    P.d = (int32_t)d;
-    P.eps = eps;
-    P.inv_d = (float)(1.0 / (double)d);
+    P.d = d;
+    P.x = x;
+    P.r = r;
+    P.y = y;
+    P.h = h;
+    P.params0 = p0;
+    P.params1 = p1;
     return P;
 }
 
-mi_norm_status run(int op, int forced, const float *x, const float *p0, const float *p1, float *y,
-                   int64_t rows, int64_t d, float eps, float *mean, float *rstd, hipStream_t stream) {
-    const mi_norm_status st = validate(op, x, p0, p1, y, rows, d, eps, mean, rstd);
+mi_norm_status run(int forced, const mi_norm_problem &Pb, float eps, float *mean, float *rstd,
+                   hipStream_t stream) {
+    const mi_norm_status st = validate(Pb, eps, mean, rstd);
     if (st != MI_NORM_OK) return st;
     int id = forced;
     if (id < 0) {
-        id = select_variant(op, rows, d, x, y, p0, p1);
+        id = select_variant(Pb);
         if (id < 0) return MI_NORM_ERR_INVALID;
-    } else if (!eligible(id, op, d, x, y, p0, p1)) {
+    } else if (!eligible(id, Pb)) {
         return MI_NORM_ERR_INVALID;
     }
-    if (rows == 0) return MI_NORM_OK;
-    return launch(id, make_params(x, p0, p1, y, rows, d, eps, mean, rstd), stream);
+    if (Pb.rows == 0) return MI_NORM_OK;
+    NormParams K;
+    K.x = static_cast<const float *>(Pb.x);
+    K.p0 = static_cast<const float *>(Pb.params0);
+    K.p1 = static_cast<const float *>(Pb.params1);
+    K.y = static_cast<float *>(const_cast<void *>(Pb.y));
+    K.mean = kop(Pb.op) == OP_LN ? mean : nullptr;
+    K.rstd = rstd;
+    K.r = kres(Pb.op) ? static_cast<const float *>(Pb.r) : nullptr;
+    K.h = kres(Pb.op) ? static_cast<float *>(const_cast<void *>(Pb.h)) : nullptr;
+    K.rows = Pb.rows;
+    K.d = (int32_t)Pb.d;
+    K.eps = eps;
+    K.inv_d = (float)(1.0 / (double)Pb.d);
+    return launch(id, K, stream);
 }
 
 }  // namespace
@@ -319,17 +372,33 @@ const char *mi_norm_status_string(mi_norm_status s) {
     return "MI_NORM_UNKNOWN_STATUS";
 }
 
-const char *mi_norm_version(void) { return "mi_norm 0.1.0 gfx950"; }
+const char *mi_norm_version(void) { return "mi_norm 0.2.0 gfx950"; }
 
 mi_norm_status mi_layernorm_fwd(const float *x, const float *gamma, const float *beta, float *y,
                                 int64_t rows, int64_t d, float eps, float *mean, float *rstd,
                                 hipStream_t stream) {
-    return run(OP_LN, -1, x, gamma, beta, y, rows, d, eps, mean, rstd, stream);
+    return run(-1, make_problem(MI_NORM_OP_LAYERNORM, rows, d, x, nullptr, y, nullptr, gamma, beta),
+               eps, mean, rstd, stream);
 }
 
 mi_norm_status mi_rmsnorm_fwd(const float *x, const float *w, float *y, int64_t rows, int64_t d,
                               float eps, float *rstd, hipStream_t stream) {
-    return run(OP_RMS, -1, x, w, nullptr, y, rows, d, eps, nullptr, rstd, stream);
+    return run(-1, make_problem(MI_NORM_OP_RMSNORM, rows, d, x, nullptr, y, nullptr, w, nullptr),
+               eps, nullptr, rstd, stream);
+}
+
+mi_norm_status mi_add_layernorm_fwd(const float *x, const float *r, const float *gamma,
+                                    const float *beta, float *y, float *h, int64_t rows, int64_t d,
+                                    float eps, float *mean, float *rstd, hipStream_t stream) {
+    return run(-1, make_problem(MI_NORM_OP_ADD_LAYERNORM, rows, d, x, r, y, h, gamma, beta), eps,
+               mean, rstd, stream);
+}
+
+mi_norm_status mi_add_rmsnorm_fwd(const float *x, const float *r, const float *w, float *y, float *h,
+                                  int64_t rows, int64_t d, float eps, float *rstd,
+                                  hipStream_t stream) {
+    return run(-1, make_problem(MI_NORM_OP_ADD_RMSNORM, rows, d, x, r, y, h, w, nullptr), eps,
+               nullptr, rstd, stream);
 }
 
 int mi_norm_variant_count(void) { return kNumVariants; }
@@ -344,27 +413,40 @@ mi_norm_status mi_norm_variant_get_info(int id, mi_norm_variant_info *out) {
     return MI_NORM_OK;
 }
 
-int mi_norm_select_variant(int op, int64_t rows, int64_t d, const void *x, const void *y,
-                           const void *params0, const void *params1) {
-    return select_variant(op, rows, d, x, y, params0, params1);
-}
+int mi_norm_select(const mi_norm_problem *p) { return p ? select_variant(*p) : -1; }
 
-int mi_norm_variant_eligible(int id, int op, int64_t d, const void *x, const void *y,
-                             const void *params0, const void *params1) {
-    return eligible(id, op, d, x, y, params0, params1) ? 1 : 0;
-}
+int mi_norm_eligible(int id, const mi_norm_problem *p) { return (p && eligible(id, *p)) ? 1 : 0; }
 
 mi_norm_status mi_layernorm_fwd_variant(int id, const float *x, const float *gamma, const float *beta,
                                         float *y, int64_t rows, int64_t d, float eps, float *mean,
                                         float *rstd, hipStream_t stream) {
     if (id < 0 || id >= kNumVariants) return MI_NORM_ERR_INVALID;
-    return run(OP_LN, id, x, gamma, beta, y, rows, d, eps, mean, rstd, stream);
+    return run(id, make_problem(MI_NORM_OP_LAYERNORM, rows, d, x, nullptr, y, nullptr, gamma, beta),
+               eps, mean, rstd, stream);
 }
 
 mi_norm_status mi_rmsnorm_fwd_variant(int id, const float *x, const float *w, float *y, int64_t rows,
                                       int64_t d, float eps, float *rstd, hipStream_t stream) {
     if (id < 0 || id >= kNumVariants) return MI_NORM_ERR_INVALID;
-    return run(OP_RMS, id, x, w, nullptr, y, rows, d, eps, nullptr, rstd, stream);
+    return run(id, make_problem(MI_NORM_OP_RMSNORM, rows, d, x, nullptr, y, nullptr, w, nullptr), eps,
+               nullptr, rstd, stream);
+}
+
+mi_norm_status mi_add_layernorm_fwd_variant(int id, const float *x, const float *r, const float *gamma,
+                                            const float *beta, float *y, float *h, int64_t rows,
+                                            int64_t d, float eps, float *mean, float *rstd,
+                                            hipStream_t stream) {
+    if (id < 0 || id >= kNumVariants) return MI_NORM_ERR_INVALID;
+    return run(id, make_problem(MI_NORM_OP_ADD_LAYERNORM, rows, d, x, r, y, h, gamma, beta), eps,
+               mean, rstd, stream);
+}
+
+mi_norm_status mi_add_rmsnorm_fwd_variant(int id, const float *x, const float *r, const float *w,
+                                          float *y, float *h, int64_t rows, int64_t d, float eps,
+                                          float *rstd, hipStream_t stream) {
+    if (id < 0 || id >= kNumVariants) return MI_NORM_ERR_INVALID;
+    return run(id, make_problem(MI_NORM_OP_ADD_RMSNORM, rows, d, x, r, y, h, w, nullptr), eps,
+               nullptr, rstd, stream);
 }
 
 mi_norm_status mi_copy_f32(const float *src, float *dst, int64_t n, hipStream_t stream) {
@@ -372,7 +454,7 @@ mi_norm_status mi_copy_f32(const float *src, float *dst, int64_t n, hipStream_t 
     if (n == 0) return MI_NORM_OK;
     if (!src || !dst || !al4(src) || !al4(dst)) return MI_NORM_ERR_INVALID;
     if (n > INT64_MAX / (int64_t)sizeof(float)) return MI_NORM_ERR_INVALID;
-    if (!overlap_ok(src, dst, 1, n) || src == dst) return MI_NORM_ERR_INVALID;
+    if (ranges_meet(src, n, dst, n)) return MI_NORM_ERR_INVALID;
     hipError_t e;
     if (n % 4 == 0 && al16(src) && al16(dst)) {
         // one 128-bit access per lane for large copies, two below 256 MiB

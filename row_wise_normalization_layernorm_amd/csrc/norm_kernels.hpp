@@ -41,6 +41,8 @@ struct NormParams {
     float *y;
     float *mean;       // LayerNorm only; may be null
     float *rstd;       // may be null
+    const float *r;    // residual added to x before the norm (RES kernels)
+    float *h;          // x + r written out (RES kernels); may be null
     int64_t rows;      // rows of this launch
     int32_t d;
     float eps;
@@ -138,6 +140,9 @@ __device__ __forceinline__ float rsq(float v) { return __builtin_amdgcn_rsqf(v);
 //   Q      accesses held per lane; capacity = VEC * LPR * WPR * Q elements
 //   WAVES  waves per workgroup
 //   NTL/NTS  non-temporal x loads / y stores
+//   RES    residual add fused before the norm: each held value is x + r
+//          (a float32 add), written to h when h is given, and the row is
+//          normalized from those sums
 //   MRG    cross-wave merge: 0 every lane walks all WPR exchanged entries,
 //          1 lane w takes entry w and two 16-lane sums finish the merge;
 //          -1: 1 for 16 waves per row, else 0
@@ -150,7 +155,7 @@ __device__ __forceinline__ float rsq(float v) { return __builtin_amdgcn_rsqf(v);
 // q = 0..Q-1: consecutive lanes touch consecutive 16-byte (or 4-byte) words,
 // so each wave-wide access covers 1 KiB (256 B) of one row contiguously.
 template <int OP, int VEC, bool PEEL, int LPR, int WPR, int Q, int WAVES, bool NTL, bool NTS,
-          int PRE = -1, int MRG = -1>
+          int PRE = -1, int MRG = -1, bool RES = false>
 __global__ __launch_bounds__(WAVES * 64)
 void norm_held(NormParams p)
 {
@@ -211,6 +216,8 @@ void norm_held(NormParams p)
         const int64_t row = rv ? row_raw : p.rows - 1;
         const float *xr = p.x + row * (int64_t)d;
         float *yr = p.y + row * (int64_t)d;
+        const float *rr = RES ? p.r + row * (int64_t)d : nullptr;
+        float *hr = (RES && p.h) ? p.h + row * (int64_t)d : nullptr;
 
         // row geometry: h head scalars, nvec body accesses, t tail scalars
         int h = 0, t = 0, nvec;
@@ -245,6 +252,14 @@ void norm_held(NormParams p)
                 if constexpr (VEC == 4) raw = ld4<NTL>(xr + h + 4 * kc[q]);
                 else raw = ld1<NTL>(xr + kc[q]);
             }
+            if constexpr (RES) {
+                VT rres = VT(0.f);
+                if (body) {
+                    if constexpr (VEC == 4) rres = ld4<NTL>(rr + h + 4 * kc[q]);
+                    else rres = ld1<NTL>(rr + kc[q]);
+                }
+                raw = raw + rres;
+            }
             v[q] = ok[q] ? raw : VT(0.f);
         }
         float hx = 0.f, tx = 0.f;
@@ -256,9 +271,27 @@ void norm_held(NormParams p)
             hi = li < h ? li : 0;
             ti = h + 4 * nvec + li;
             ti = ti < d ? ti : d - 1;
-            const float rh = xr[hi], rt = xr[ti];
+            float rh = xr[hi], rt = xr[ti];
+            if constexpr (RES) {
+                rh = rh + rr[hi];
+                rt = rt + rr[ti];
+            }
             hx = hok ? rh : 0.f;
             tx = tok ? rt : 0.f;
+        }
+        if constexpr (RES) {
+            // the sums leave as soon as they exist, overlapping the reductions;
+            // every element is owned by one lane, so h may alias x or r
+            if (hr) {
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    if (!ok[q]) continue;
+                    if constexpr (VEC == 4) st4<NTS>(hr + h + 4 * kc[q], v[q]);
+                    else st1<NTS>(hr + kc[q], v[q]);
+                }
+                if (hok) hr[hi] = hx;
+                if (tok) hr[ti] = tx;
+            }
         }
 
         // parameters for the output pass: fetched while x is in flight when
@@ -442,7 +475,7 @@ __device__ __forceinline__ float block_sum(float v, float (*red)[WAVES], int &sl
     return t;
 }
 
-template <int OP, int VEC, int WAVES, int U>
+template <int OP, int VEC, int WAVES, int U, bool RES = false>
 __global__ __launch_bounds__(WAVES * 64)
 void norm_looped(NormParams p)
 {
@@ -464,7 +497,20 @@ void norm_looped(NormParams p)
     for (int64_t row = blockIdx.x; row < p.rows; row += gridDim.x) {
         const float *xr = p.x + row * (int64_t)d;
         float *yr = p.y + row * (int64_t)d;
+        const float *rr = RES ? p.r + row * (int64_t)d : nullptr;
+        float *hr = (RES && p.h) ? p.h + row * (int64_t)d : nullptr;
         float mu = 0.f, rs;
+        // the value at access k: x, or x + r; once pass 1 has written h (each
+        // thread re-reads only what it stored itself) later passes read it
+        // back, which stays right when h aliases x or r
+        auto value = [&](int k, bool after_pass1) -> VT {
+            if constexpr (RES) {
+                if (after_pass1 && hr) return load(hr, k);
+                return load(xr, k) + load(rr, k);
+            } else {
+                return load(xr, k);
+            }
+        };
 
         // pass 1: sum (LayerNorm) or sum of squares (RMSNorm)
         float s = 0.f;
@@ -473,7 +519,18 @@ void norm_looped(NormParams p)
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int k = k0 + tid + T * u;
-                v[u] = k < nvec ? load(xr, k) : VT(0.f);
+                v[u] = k < nvec ? value(k, false) : VT(0.f);
+            }
+            if constexpr (RES) {
+                if (hr) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int k = k0 + tid + T * u;
+                        if (k >= nvec) continue;
+                        if constexpr (VEC == 4) st4<false>(hr + 4 * k, v[u]);
+                        else hr[k] = v[u];
+                    }
+                }
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) s += (OP == OP_LN) ? hsum(v[u]) : sq(v[u]);
@@ -491,7 +548,7 @@ void norm_looped(NormParams p)
                 for (int u = 0; u < U; ++u) {
                     const int k = k0 + tid + T * u;
                     ok[u] = k < nvec;
-                    v[u] = ok[u] ? load(xr, k) : VT(0.f);
+                    v[u] = ok[u] ? value(k, true) : VT(0.f);
                 }
 #pragma unroll
                 for (int u = 0; u < U; ++u) m += ok[u] ? csq(v[u], mu) : 0.f;
@@ -510,7 +567,7 @@ void norm_looped(NormParams p)
             for (int u = 0; u < U; ++u) {
                 const int k = k0 + tid + T * u;
                 ok[u] = k < nvec;
-                v[u] = ok[u] ? load(xr, k) : VT(0.f);
+                v[u] = ok[u] ? value(k, true) : VT(0.f);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {

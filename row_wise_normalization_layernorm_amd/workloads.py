@@ -72,7 +72,7 @@ def make_weight(d: int, seed=0) -> np.ndarray:
 
 @dataclass(frozen=True)
 class Case:
-    op: str            # "layernorm" or "rmsnorm"
+    op: str            # "layernorm", "rmsnorm", "add_layernorm" or "add_rmsnorm"
     rows: int
     d: int
     pattern: str = "normal"
@@ -85,13 +85,20 @@ class Case:
 
     def inputs(self):
         """(x, params...) for this case: (x, gamma, beta) or (x, w)."""
+        a = self.arrays()
+        return (a["x"],) + a["params"]
+
+    def arrays(self) -> dict:
+        """x, the residual r (fused ops; None otherwise) and the parameters."""
         seed = case_seed(self.tag, self.rows, self.d, self.pattern)
         x = make_x(self.rows, self.d, self.pattern, seed)
+        r = make_x(self.rows, self.d, "normal", [6] + seed) if self.op.startswith("add_") else None
         pseed = [int(self.tag), int(self.d), 99]
-        if self.op == "layernorm":
-            g, b = make_affine(self.d, pseed)
-            return x, g, b
-        return x, make_weight(self.d, pseed)
+        if self.op.endswith("layernorm"):
+            params = make_affine(self.d, pseed)
+        else:
+            params = (make_weight(self.d, pseed),)
+        return {"x": x, "r": r, "params": params}
 
 
 @dataclass(frozen=True)
@@ -117,6 +124,13 @@ WORKLOADS = {
     "rms": Workload("rms", tuple(
         Case("rmsnorm", r, d, p, tag=4)
         for r, d in ((512, 128), (4096, 768), (2048, 4096), (256, 8193)) for p in _BASIC)),
+    # residual add fused before either norm (the sum h = x + r written out)
+    "residual": Workload("residual", tuple(
+        [Case("add_layernorm", 4096, 768, "normal", True, tag=6)]
+        + [Case("add_layernorm", 64, d, p, True, tag=6) for d in (1, 33, 127, 2049, 8193)
+           for p in ("normal", "offset")]
+        + [Case("add_rmsnorm", r, d, p, True, tag=6)
+           for r, d in ((512, 128), (2048, 4096), (256, 8193)) for p in ("normal", "tiny")])),
     # LayerNorm at bandwidth-saturating scale: 1 GiB read + 1 GiB written
     "ln_32768x8192": Workload("ln_32768x8192", (Case("layernorm", 32768, 8192, "normal", tag=5),)),
 }

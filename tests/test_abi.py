@@ -119,15 +119,64 @@ def test_binding_raises_status(L):
     assert e.value.status == mn.MI_NORM_ERR_INVALID
 
 
+# --- fused residual add: validation and aliasing ------------------------------
+
+R_, H_ = 0x7F0400000000, 0x7F0500000000
+
+
+@pytest.mark.parametrize("args", [
+    (X, 0, G, BETA, Y, H_, 4, 8, 1e-5, None, None, None),        # null r
+    (X, R_, G, BETA, Y, Y, 4, 8, 1e-5, None, None, None),        # h == y
+    (X, R_, G, BETA, Y, Y + 16, 4, 8, 1e-5, None, None, None),   # h overlaps y
+    (X, R_, G, BETA, Y, R_ + 4, 4, 8, 1e-5, None, None, None),   # h partially overlaps r
+    (X, X + 8, G, BETA, Y, H_, 4, 8, 1e-5, None, None, None),    # r partially overlaps x
+    (X, R_ + 2, G, BETA, Y, H_, 4, 8, 1e-5, None, None, None),   # r not 4-byte aligned
+    (X, R_, Y + 64, BETA, Y, H_, 4, 8, 1e-5, None, None, None),  # gamma inside y
+    (X, R_, G, BETA, Y, BETA, 4, 8, 1e-5, None, None, None),     # h over beta
+])
+def test_add_layernorm_rejects_bad_arguments(L, args):
+    assert L.mi_add_layernorm_fwd(*args) == mn.MI_NORM_ERR_INVALID
+
+
+@pytest.mark.parametrize("y,h", [(X, None), (R_, None), (X, R_), (R_, X), (Y, X), (Y, R_), (X, H_)])
+def test_add_allowed_aliasing_is_accepted(L, y, h):
+    # rows = 0 validates fully and launches nothing, so this runs without a device
+    assert L.mi_add_layernorm_fwd(X, R_, G, BETA, y, h, 0, 8, 1e-5, None, None, None) == mn.MI_NORM_OK
+    p = mn.problem(mn.OP_ADD_LAYERNORM, 4096, 768, X, y, G, BETA, r=R_, h=h)
+    assert mn.mi_norm_select(p) >= 0
+
+
+def test_add_rmsnorm_validation(L):
+    assert L.mi_add_rmsnorm_fwd(X, R_, G, Y, H_, 0, 8, 1e-5, None, None) == mn.MI_NORM_OK
+    assert L.mi_add_rmsnorm_fwd(X, 0, G, Y, H_, 4, 8, 1e-5, None, None) == mn.MI_NORM_ERR_INVALID
+    assert L.mi_add_rmsnorm_fwd(X, R_, G, Y, Y, 4, 8, 1e-5, None, None) == mn.MI_NORM_ERR_INVALID
+    assert L.mi_add_rmsnorm_fwd(X, R_, Y + 4, Y, H_, 4, 8, 1e-5, None, None) == mn.MI_NORM_ERR_INVALID
+
+
 # --- variant table and dispatch (host logic) ---------------------------------
+
+OPS = (mn.OP_LAYERNORM, mn.OP_RMSNORM, mn.OP_ADD_LAYERNORM, mn.OP_ADD_RMSNORM)
+PREFIX = {mn.OP_LAYERNORM: "ln_", mn.OP_RMSNORM: "rms_", mn.OP_ADD_LAYERNORM: "addln_",
+          mn.OP_ADD_RMSNORM: "addrms_"}
+
 
 def _infos():
     return [(i, mn.mi_norm_variant_name(i), mn.mi_norm_variant_get_info(i))
             for i in range(mn.mi_norm_variant_count())]
 
 
-def test_select_rejects_negative_rows(L):
-    assert mn.mi_norm_select_variant(0, -1, 768, X, Y, G, BETA) == -1
+def _prob(op, rows, d, x=X, y=Y, g=G, b=BETA, r=R_, h=H_):
+    add = op >= mn.OP_ADD_LAYERNORM
+    ln = op in (mn.OP_LAYERNORM, mn.OP_ADD_LAYERNORM)
+    return mn.problem(op, rows, d, x, y, g, b if ln else None, r=r if add else None,
+                      h=h if add else None)
+
+
+def test_select_rejects_invalid_problems(L):
+    assert mn.mi_norm_select(_prob(0, -1, 768)) == -1
+    assert mn.mi_norm_select(_prob(7, 16, 768)) == -1
+    assert mn.mi_norm_select(_prob(mn.OP_ADD_LAYERNORM, 16, 768, r=None)) == -1
+    assert L.mi_norm_select(None) == -1
 
 
 def test_variant_table_is_consistent(L):
@@ -137,7 +186,7 @@ def test_variant_table_is_consistent(L):
     assert mn.mi_norm_variant_name(len(infos)) is None
     assert mn.mi_norm_variant_name(-1) is None
     for i, n, v in infos:
-        assert n.startswith("ln_" if v["op"] == mn.OP_LAYERNORM else "rms_")
+        assert n.startswith(PREFIX[v["op"]]), n
         if v["looped"]:
             assert v["max_d"] == 2**63 - 1 and v["rows_per_block"] == 1
             continue
@@ -149,8 +198,10 @@ def test_variant_table_is_consistent(L):
             assert v["rows_per_block"] * v["waves_per_row"] == v["waves_per_block"]
         assert v["waves_per_block"] * 64 <= 1024
         assert v["needs_aligned"] == (1 if v["vec"] == 4 and not v["peel"] else 0)
-    ops = {v["op"] for _, _, v in infos}
-    assert ops == {mn.OP_LAYERNORM, mn.OP_RMSNORM}
+    assert {v["op"] for _, _, v in infos} == set(OPS)
+    # every operation has the same family of shapes
+    shapes = {op: sorted(n[len(PREFIX[op]):] for _, n, v in infos if v["op"] == op) for op in OPS}
+    assert shapes[0] == shapes[1] == shapes[2] == shapes[3]
 
 
 WIDTHS = sorted({1, 2, 3, 4, 5, 7, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 255, 256,
@@ -159,34 +210,45 @@ WIDTHS = sorted({1, 2, 3, 4, 5, 7, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 1
                  32768, 32769, 65536, 100003, 2**20})
 
 
-@pytest.mark.parametrize("op", [mn.OP_LAYERNORM, mn.OP_RMSNORM])
-@pytest.mark.parametrize("layout", ["aligned", "x_y_same_phase", "x_y_different_phase"])
+@pytest.mark.parametrize("op", OPS)
+@pytest.mark.parametrize("layout", ["aligned", "same_phase", "different_phase"])
 def test_dispatch_picks_an_eligible_covering_variant(L, op, layout):
     if layout == "aligned":
-        x, y = X, Y
-    elif layout == "x_y_same_phase":
-        x, y = X + 4, Y + 4
+        ptrs = dict(x=X, y=Y, r=R_, h=H_)
+    elif layout == "same_phase":
+        ptrs = dict(x=X + 4, y=Y + 4, r=R_ + 4, h=H_ + 4)
     else:
-        x, y = X + 4, Y + 8
-    p1 = BETA if op == mn.OP_LAYERNORM else None
-    for d in WIDTHS:
-        vid = mn.mi_norm_select_variant(op, 4096, d, x, y, G, p1)
-        assert vid >= 0, (op, d, layout)
-        v = mn.mi_norm_variant_get_info(vid)
-        assert v["op"] == op
-        assert mn.mi_norm_variant_eligible(vid, op, d, x, y, G, p1), (d, layout, mn.mi_norm_variant_name(vid))
-        assert v["looped"] or v["max_d"] >= d
-        if layout == "aligned" and d % 4 == 0:
-            assert v["vec"] == 4 and not v["peel"], (d, mn.mi_norm_variant_name(vid))
-        if layout == "x_y_different_phase":
-            assert v["vec"] == 1, (d, mn.mi_norm_variant_name(vid))
-        if layout == "aligned" and d % 4 and 256 <= d <= 32768:
-            assert v["peel"], (d, mn.mi_norm_variant_name(vid))
+        ptrs = dict(x=X + 4, y=Y + 8, r=R_ + 4, h=H_ + 4)
+    for rows in (64, 4096):
+        for d in WIDTHS:
+            p = _prob(op, rows, d, **ptrs)
+            vid = mn.mi_norm_select(p)
+            assert vid >= 0, (op, d, layout)
+            v = mn.mi_norm_variant_get_info(vid)
+            assert v["op"] == op
+            assert mn.mi_norm_eligible(vid, p), (d, layout, mn.mi_norm_variant_name(vid))
+            assert v["looped"] or v["max_d"] >= d
+            if layout == "aligned" and d % 4 == 0:
+                assert v["vec"] == 4 and not v["peel"], (d, mn.mi_norm_variant_name(vid))
+            if layout == "different_phase":
+                assert v["vec"] == 1, (d, mn.mi_norm_variant_name(vid))
+            if layout == "aligned" and d % 4 and 256 <= d <= 32768:
+                assert v["peel"], (d, mn.mi_norm_variant_name(vid))
+
+
+def test_residual_pointers_decide_the_layout(L):
+    # a residual or sum of another 16-byte phase takes the 32-bit path
+    v = mn.mi_norm_variant_get_info(mn.mi_norm_select(_prob(mn.OP_ADD_LAYERNORM, 4096, 768, r=R_ + 4)))
+    assert v["vec"] == 1
+    v = mn.mi_norm_variant_get_info(mn.mi_norm_select(_prob(mn.OP_ADD_LAYERNORM, 4096, 768, h=H_ + 8)))
+    assert v["vec"] == 1
+    # without h, only x, r and y matter
+    v = mn.mi_norm_variant_get_info(mn.mi_norm_select(_prob(mn.OP_ADD_RMSNORM, 4096, 768, h=None)))
+    assert v["vec"] == 4 and not v["peel"]
 
 
 def test_dispatch_examples(L):
-    sel = lambda op, d, rows=4096, x=X, y=Y: mn.mi_norm_variant_name(
-        mn.mi_norm_select_variant(op, rows, d, x, y, G, BETA if op == 0 else None))
+    sel = lambda op, d, rows=4096, **k: mn.mi_norm_variant_name(mn.mi_norm_select(_prob(op, rows, d, **k)))
     assert sel(0, 768) == "ln_4_p0_l64_w1_q3_b16"            # 256 workgroups of 16 rows
     assert sel(0, 768, rows=1000) == "ln_4_p0_l64_w2_q2_b4"  # few rows: two waves per row
     assert sel(0, 2048, rows=1024) == "ln_4_p0_l64_w4_q2_b4"
@@ -195,15 +257,17 @@ def test_dispatch_examples(L):
     assert sel(0, 128, rows=512) == "ln_4_p0_l32_w1_q1_b4"
     assert sel(1, 8193, rows=256) == "rms_4_p1_l64_w16_q3_b16"
     assert sel(0, 1, rows=64) == "ln_1_p0_l16_w1_q1_b4"
+    assert sel(2, 768) == "addln_4_p0_l64_w1_q3_b16"
+    assert sel(3, 8192, rows=32768) == "addrms_4_p0_l64_w8_q4_b16"
     assert "_loop_" in sel(0, 2**20)
     # gamma misaligned only: no 128-bit parameter reads, so not the aligned path
-    assert mn.mi_norm_variant_get_info(mn.mi_norm_select_variant(0, 4096, 768, X, Y, G + 4, BETA))["needs_aligned"] == 0
+    assert mn.mi_norm_variant_get_info(mn.mi_norm_select(_prob(0, 4096, 768, g=G + 4)))["needs_aligned"] == 0
 
 
 def test_workgroup_size_follows_row_count(L):
     for d in (768, 2048, 4096, 8192, 16384):
         for rows in (1, 100, 1000, 5000, 100000):
-            v = mn.mi_norm_variant_get_info(mn.mi_norm_select_variant(0, rows, d, X, Y, G, BETA))
+            v = mn.mi_norm_variant_get_info(mn.mi_norm_select(_prob(0, rows, d)))
             need = 512 if v["waves_per_row"] > 1 else 256
             per16 = 16 // v["waves_per_row"]
             if v["waves_per_block"] < 16:
@@ -218,21 +282,19 @@ def test_rows_spread_over_more_waves_when_few(L):
     for d, rows, wpr, q in ((768, 4096, 1, 3), (2048, 4096, 2, 4), (2048, 1024, 4, 2),
                             (4096, 4096, 4, 4), (8192, 32768, 8, 4), (16384, 8192, 16, 4),
                             (768, 100, 2, 2), (32768, 64, 16, 8)):
-        v = mn.mi_norm_variant_get_info(mn.mi_norm_select_variant(0, rows, d, X, Y, G, BETA))
+        v = mn.mi_norm_variant_get_info(mn.mi_norm_select(_prob(0, rows, d)))
         assert (v["waves_per_row"], v["slots"]) == (wpr, q), (d, rows, v)
 
 
 def test_eligibility_rules(L):
-    infos = _infos()
-    for i, n, v in infos:
+    for i, n, v in _infos():
         op = v["op"]
-        p1 = BETA if op == 0 else None
-        # the other operation never fits
-        assert not mn.mi_norm_variant_eligible(i, 1 - op, 64, X, Y, G, BETA)
+        other = {0: 1, 1: 0, 2: 3, 3: 2}[op]
+        assert not mn.mi_norm_eligible(i, _prob(other, 16, 64))
         if v["needs_aligned"]:
-            assert not mn.mi_norm_variant_eligible(i, op, 64, X + 4, Y, G, p1)
-            assert not mn.mi_norm_variant_eligible(i, op, 6, X, Y, G, p1)
+            assert not mn.mi_norm_eligible(i, _prob(op, 16, 64, x=X + 4))
+            assert not mn.mi_norm_eligible(i, _prob(op, 16, 6))
         if not v["looped"]:
-            assert not mn.mi_norm_variant_eligible(i, op, v["max_d"] + 4, X, Y, G, p1)
-    assert not mn.mi_norm_variant_eligible(-1, 0, 8, X, Y, G, BETA)
+            assert not mn.mi_norm_eligible(i, _prob(op, 16, v["max_d"] + 4))
+    assert not mn.mi_norm_eligible(-1, _prob(0, 16, 8))
     assert L.mi_layernorm_fwd_variant(10**6, X, G, BETA, Y, 4, 8, 1e-5, None, None, None) == mn.MI_NORM_ERR_INVALID

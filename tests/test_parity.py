@@ -62,34 +62,58 @@ def check(got, ref, what: str):
 
 
 def run_case(torch, dev, op, x, params, eps=wl.EPS, stats=True, variant=None, xo=0, yo=None,
-             po=0, inplace=False):
-    """Run one case through the C ABI with guarded buffers; compare with the oracle."""
+             po=0, inplace=False, r=None, h_mode="new", y_mode=None):
+    """Run one case through the C ABI with guarded buffers; compare with the oracle.
+
+    Fused ops take the residual r; h_mode is "new" (a buffer of its own),
+    "none" (not written), "x" or "r" (written over that input); y_mode "x" or
+    "r" writes y over that input (``inplace`` is y_mode "x")."""
     rows, d = x.shape
     yo = xo if yo is None else yo
+    add = op.startswith("add_")
+    ln = op.endswith("layernorm")
+    y_mode = "x" if inplace else y_mode
     X = Guarded(torch, dev, rows * d, xo, x)
-    Y = X if inplace else Guarded(torch, dev, rows * d, yo)
+    Rr = Guarded(torch, dev, rows * d, xo, r) if add else None
+    bufs = {"x": X, "r": Rr}
+    Y = bufs[y_mode] if y_mode else Guarded(torch, dev, rows * d, yo)
+    Hh = None
+    if add and h_mode != "none":
+        Hh = bufs[h_mode] if h_mode in ("x", "r") else Guarded(torch, dev, rows * d, yo)
     P = [Guarded(torch, dev, d, po, p) for p in params]
-    M = Guarded(torch, dev, rows) if (stats and op == "layernorm") else None
+    M = Guarded(torch, dev, rows) if (stats and ln) else None
     R = Guarded(torch, dev, rows) if stats else None
     L = mn.lib()
     st = torch.cuda.current_stream().cuda_stream
+    mp, rp = (M.ptr if M else None), (R.ptr if R else None)
+    hp = Hh.ptr if Hh else None
     if op == "layernorm":
-        if variant is None:
-            s = L.mi_layernorm_fwd(X.ptr, P[0].ptr, P[1].ptr, Y.ptr, rows, d, eps,
-                                   M.ptr if M else None, R.ptr if R else None, st)
-        else:
-            s = L.mi_layernorm_fwd_variant(variant, X.ptr, P[0].ptr, P[1].ptr, Y.ptr, rows, d, eps,
-                                           M.ptr if M else None, R.ptr if R else None, st)
+        s = (L.mi_layernorm_fwd(X.ptr, P[0].ptr, P[1].ptr, Y.ptr, rows, d, eps, mp, rp, st) if variant is None
+             else L.mi_layernorm_fwd_variant(variant, X.ptr, P[0].ptr, P[1].ptr, Y.ptr, rows, d, eps, mp, rp, st))
         ref = oracle.layernorm(x, *params, eps)
         refs = [(Y, ref[0].reshape(-1), "y"), (M, ref[1], "mean"), (R, ref[2], "rstd")]
-    else:
-        if variant is None:
-            s = L.mi_rmsnorm_fwd(X.ptr, P[0].ptr, Y.ptr, rows, d, eps, R.ptr if R else None, st)
-        else:
-            s = L.mi_rmsnorm_fwd_variant(variant, X.ptr, P[0].ptr, Y.ptr, rows, d, eps,
-                                         R.ptr if R else None, st)
+        ref_h = None
+    elif op == "rmsnorm":
+        s = (L.mi_rmsnorm_fwd(X.ptr, P[0].ptr, Y.ptr, rows, d, eps, rp, st) if variant is None
+             else L.mi_rmsnorm_fwd_variant(variant, X.ptr, P[0].ptr, Y.ptr, rows, d, eps, rp, st))
         ref = oracle.rmsnorm(x, *params, eps)
         refs = [(Y, ref[0].reshape(-1), "y"), (R, ref[1], "rstd")]
+        ref_h = None
+    elif op == "add_layernorm":
+        s = (L.mi_add_layernorm_fwd(X.ptr, Rr.ptr, P[0].ptr, P[1].ptr, Y.ptr, hp, rows, d, eps, mp, rp, st)
+             if variant is None else
+             L.mi_add_layernorm_fwd_variant(variant, X.ptr, Rr.ptr, P[0].ptr, P[1].ptr, Y.ptr, hp, rows, d,
+                                            eps, mp, rp, st))
+        ref = oracle.add_layernorm(x, r, *params, eps)
+        refs = [(Y, ref[0].reshape(-1), "y"), (M, ref[2], "mean"), (R, ref[3], "rstd")]
+        ref_h = ref[1].reshape(-1)
+    else:
+        s = (L.mi_add_rmsnorm_fwd(X.ptr, Rr.ptr, P[0].ptr, Y.ptr, hp, rows, d, eps, rp, st)
+             if variant is None else
+             L.mi_add_rmsnorm_fwd_variant(variant, X.ptr, Rr.ptr, P[0].ptr, Y.ptr, hp, rows, d, eps, rp, st))
+        ref = oracle.add_rmsnorm(x, r, *params, eps)
+        refs = [(Y, ref[0].reshape(-1), "y"), (R, ref[2], "rstd")]
+        ref_h = ref[1].reshape(-1)
     assert s == mn.MI_NORM_OK, mn.mi_norm_status_string(s)
     torch.cuda.synchronize()
     worst = 0.0
@@ -98,22 +122,28 @@ def run_case(torch, dev, op, x, params, eps=wl.EPS, stats=True, variant=None, xo
             continue
         worst = max(worst, check(buf.host(), want, what))
         assert buf.guards_intact(), f"{what}: write outside the output range"
+    if Hh is not None:
+        # the same IEEE float32 addition on both sides: bit for bit
+        assert np.array_equal(Hh.host(), ref_h), "h != x + r"
+        assert Hh.guards_intact(), "h: write outside the output range"
     for p in P:
         assert p.guards_intact()
-    if not inplace:
+    if y_mode != "x" and h_mode != "x":
         assert np.array_equal(X.host(), x.reshape(-1)), "x was modified"
+    if add and y_mode != "r" and h_mode != "r":
+        assert np.array_equal(Rr.host(), r.reshape(-1)), "r was modified"
     return worst
 
 
 # --- the workload families ----------------------------------------------------
 
-@pytest.mark.parametrize("name", ["ln_small", "ln_4096x768", "ln_sweep", "rms"])
+@pytest.mark.parametrize("name", ["ln_small", "ln_4096x768", "ln_sweep", "rms", "residual"])
 def test_workload_family(torch_dev, name):
     torch, dev = torch_dev
     for case in wl.WORKLOADS[name].cases:
         say(f"case {case.name}")
-        ins = case.inputs()
-        err = run_case(torch, dev, case.op, ins[0], ins[1:], stats=True)
+        a = case.arrays()
+        err = run_case(torch, dev, case.op, a["x"], a["params"], stats=True, r=a["r"])
         say(f"  max abs err {err:.3e}")
 
 
@@ -163,20 +193,25 @@ def _variant_layout(v):
     return dict(xo=1, yo=2, po=3)       # nothing aligned
 
 
+OPNAME = {mn.OP_LAYERNORM: "layernorm", mn.OP_RMSNORM: "rmsnorm",
+          mn.OP_ADD_LAYERNORM: "add_layernorm", mn.OP_ADD_RMSNORM: "add_rmsnorm"}
+
+
 def test_every_variant(torch_dev):
     torch, dev = torch_dev
     n = mn.mi_norm_variant_count()
     for vid in range(n):
         v = mn.mi_norm_variant_get_info(vid)
         name = mn.mi_norm_variant_name(vid)
-        op = "layernorm" if v["op"] == mn.OP_LAYERNORM else "rmsnorm"
+        op = OPNAME[v["op"]]
         lay = _variant_layout(v)
         for d in _variant_widths(v):
             rows = min(3 * v["rows_per_block"] + 1, max(2, 600000 // d))
             say(f"variant {vid} {name} rows={rows} d={d} {lay}")
             x = wl.make_x(rows, d, "offset", [7, vid, d])
-            params = wl.make_affine(d, [7, d]) if op == "layernorm" else (wl.make_weight(d, [7, d]),)
-            run_case(torch, dev, op, x, params, variant=vid, **lay)
+            r = wl.make_x(rows, d, "normal", [8, vid, d]) if op.startswith("add_") else None
+            params = wl.make_affine(d, [7, d]) if op.endswith("layernorm") else (wl.make_weight(d, [7, d]),)
+            run_case(torch, dev, op, x, params, variant=vid, r=r, **lay)
 
 
 # --- layouts, aliasing, ordering ---------------------------------------------
@@ -202,6 +237,21 @@ def test_in_place(torch_dev, op, d, xo):
     x = wl.make_x(45, d, "normal", [9, d])
     params = wl.make_affine(d, [9, d]) if op == "layernorm" else (wl.make_weight(d, [9, d]),)
     run_case(torch, dev, op, x, params, xo=xo, inplace=True)
+
+
+@pytest.mark.parametrize("op", ["add_layernorm", "add_rmsnorm"])
+@pytest.mark.parametrize("d,xo", [(768, 0), (2049, 1), (127, 3), (40000, 0)])
+@pytest.mark.parametrize("y_mode,h_mode", [(None, "new"), (None, "none"), ("x", "new"), ("r", "new"),
+                                           (None, "x"), (None, "r"), ("x", "r"), ("r", "x")])
+def test_residual_aliasing(torch_dev, op, d, xo, y_mode, h_mode):
+    """y and h written over the inputs in every allowed combination."""
+    torch, dev = torch_dev
+    rows = 37 if d < 10000 else 5
+    say(f"residual aliasing {op} d={d} xo={xo} y={y_mode} h={h_mode}")
+    x = wl.make_x(rows, d, "offset", [12, d])
+    r = wl.make_x(rows, d, "normal", [13, d])
+    params = wl.make_affine(d, [12, d]) if op == "add_layernorm" else (wl.make_weight(d, [12, d]),)
+    run_case(torch, dev, op, x, params, xo=xo, r=r, y_mode=y_mode, h_mode=h_mode)
 
 
 def test_without_stats_and_eps_zero(torch_dev):
