@@ -7,8 +7,9 @@ import this package.  It imports nothing from the HIP library's package and
 the library imports nothing from here.
 
 Functions take and return numpy arrays (float32 in, float32 out, plus the
-float64 statistics the pins inspect).  The arithmetic itself lives in the C
-file; this module only marshals arguments.
+float64 statistics the pins inspect).  16-bit storage (binary16, bfloat16) is
+passed as uint16 bit patterns.  The arithmetic itself lives in the C file;
+this module only marshals arguments and chains those C steps.
 """
 from __future__ import annotations
 
@@ -31,14 +32,25 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-        ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
     ]
     lib.oracle_rmsnorm_f64.restype = None
     lib.oracle_rmsnorm_f64.argtypes = [
         ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
-        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
     ]
+    lib.oracle_widen16.restype = ctypes.c_double
+    lib.oracle_widen16.argtypes = [ctypes.c_uint16, ctypes.c_int]
+    lib.oracle_round16.restype = ctypes.c_uint16
+    lib.oracle_round16.argtypes = [ctypes.c_double, ctypes.c_int]
+    lib.oracle_widen16_n.restype = None
+    lib.oracle_widen16_n.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p]
+    lib.oracle_round16_n.restype = None
+    lib.oracle_round16_n.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p]
+    lib.oracle_add16_n.restype = None
+    lib.oracle_add16_n.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                   ctypes.c_void_p]
     lib.oracle_add_layernorm_f64.restype = None
     lib.oracle_add_layernorm_f64.argtypes = [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -81,12 +93,13 @@ def _f32(a, name: str) -> np.ndarray:
 
 
 def layernorm(x, gamma, beta, eps: float = 1e-5, lib: ctypes.CDLL | None = None,
-              out: np.ndarray | None = None):
+              out: np.ndarray | None = None, y64: np.ndarray | None = None):
     """LayerNorm of each row of ``x`` [rows, d].
 
     Returns ``(y, mean, rstd, mean64, var64)``: y/mean/rstd rounded once to
     float32, mean64/var64 the float64 statistics before rounding.  ``eps`` is
-    taken as the float32 value the GPU receives and widened exactly.
+    taken as the float32 value the GPU receives and widened exactly.  A
+    float64 ``y64`` [rows, d] receives the outputs before rounding.
     """
     lib = lib or load()
     x = _f32(x, "x")
@@ -102,18 +115,19 @@ def layernorm(x, gamma, beta, eps: float = 1e-5, lib: ctypes.CDLL | None = None,
     rstd = np.empty(rows, np.float32)
     mean64 = np.empty(rows, np.float64)
     var64 = np.empty(rows, np.float64)
+    _check64(y64, x.shape)
     lib.oracle_layernorm_f64(_ptr(x), _ptr(gamma), _ptr(beta), rows, d,
                              float(np.float32(eps)), _ptr(y), _ptr(mean),
-                             _ptr(rstd), _ptr(mean64), _ptr(var64))
+                             _ptr(rstd), _ptr(mean64), _ptr(var64), _ptr(y64))
     return y, mean, rstd, mean64, var64
 
 
 def rmsnorm(x, w, eps: float = 1e-5, lib: ctypes.CDLL | None = None,
-            out: np.ndarray | None = None):
+            out: np.ndarray | None = None, y64: np.ndarray | None = None):
     """RMSNorm of each row of ``x`` [rows, d].
 
     Returns ``(y, rstd, ms64)``: y/rstd rounded once to float32, ms64 the
-    float64 mean of squares before rounding.
+    float64 mean of squares before rounding; ``y64`` as for ``layernorm``.
     """
     lib = lib or load()
     x = _f32(x, "x")
@@ -126,8 +140,9 @@ def rmsnorm(x, w, eps: float = 1e-5, lib: ctypes.CDLL | None = None,
     y = np.empty_like(x) if out is None else out
     rstd = np.empty(rows, np.float32)
     ms64 = np.empty(rows, np.float64)
+    _check64(y64, x.shape)
     lib.oracle_rmsnorm_f64(_ptr(x), _ptr(w), rows, d, float(np.float32(eps)),
-                           _ptr(y), _ptr(rstd), _ptr(ms64))
+                           _ptr(y), _ptr(rstd), _ptr(ms64), _ptr(y64))
     return y, rstd, ms64
 
 
@@ -171,6 +186,128 @@ def add_rmsnorm(x, r, w, eps: float = 1e-5, lib: ctypes.CDLL | None = None):
     lib.oracle_add_rmsnorm_f64(_ptr(x), _ptr(r), _ptr(w), rows, d, float(np.float32(eps)),
                                _ptr(y), _ptr(h), _ptr(rstd))
     return y, h, rstd
+
+
+# ----------------------------------------------------------------------------
+# 16-bit storage: exact widening, one rounding of each float64 output
+
+FMT_F16 = 1   # IEEE binary16
+FMT_BF16 = 2  # bfloat16
+_FMT_P_EMIN = {FMT_F16: (11, -14), FMT_BF16: (8, -126)}
+
+
+def _check64(a, shape):
+    if a is not None and (a.dtype != np.float64 or a.shape != tuple(shape) or not a.flags.c_contiguous):
+        raise ValueError("y64 must be a C-contiguous float64 array of x's shape")
+
+
+def _u16(a, name: str) -> np.ndarray:
+    a = np.asarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError(f"{name} must hold uint16 bit patterns, got {a.dtype}")
+    return np.ascontiguousarray(a)
+
+
+def widen16(bits, fmt: int, lib: ctypes.CDLL | None = None) -> np.ndarray:
+    """float32 values of 16-bit patterns (exact)."""
+    lib = lib or load()
+    bits = _u16(bits, "bits")
+    out = np.empty(bits.shape, np.float32)
+    lib.oracle_widen16_n(_ptr(bits), int(fmt), bits.size, _ptr(out))
+    return out
+
+
+def round16(values, fmt: int, lib: ctypes.CDLL | None = None) -> np.ndarray:
+    """16-bit patterns nearest (ties to even) to float64 ``values``."""
+    lib = lib or load()
+    v = np.ascontiguousarray(np.asarray(values, np.float64))
+    out = np.empty(v.shape, np.uint16)
+    lib.oracle_round16_n(_ptr(v), int(fmt), v.size, _ptr(out))
+    return out
+
+
+def add16(x, r, fmt: int, lib: ctypes.CDLL | None = None) -> np.ndarray:
+    """x + r rounded once to the 16-bit format (patterns in, patterns out)."""
+    lib = lib or load()
+    x, r = _u16(x, "x"), _u16(r, "r")
+    if x.shape != r.shape:
+        raise ValueError("x and r must have one shape")
+    h = np.empty(x.shape, np.uint16)
+    lib.oracle_add16_n(_ptr(x), _ptr(r), int(fmt), x.size, _ptr(h))
+    return h
+
+
+def layernorm16(x, fmt: int, gamma, beta, eps: float = 1e-5, lib: ctypes.CDLL | None = None):
+    """LayerNorm over 16-bit storage; float32 parameters and statistics.
+
+    Returns ``(y, y64, mean, rstd)``: y the 16-bit patterns of the float64
+    outputs ``y64`` rounded once, mean/rstd float32."""
+    lib = lib or load()
+    xf = widen16(x, fmt, lib)
+    y64 = np.empty(xf.shape, np.float64)
+    _, mean, rstd, _, _ = layernorm(xf, gamma, beta, eps, lib=lib, y64=y64)
+    return round16(y64, fmt, lib), y64, mean, rstd
+
+
+def rmsnorm16(x, fmt: int, w, eps: float = 1e-5, lib: ctypes.CDLL | None = None):
+    """RMSNorm over 16-bit storage; returns ``(y, y64, rstd)``."""
+    lib = lib or load()
+    xf = widen16(x, fmt, lib)
+    y64 = np.empty(xf.shape, np.float64)
+    _, rstd, _ = rmsnorm(xf, w, eps, lib=lib, y64=y64)
+    return round16(y64, fmt, lib), y64, rstd
+
+
+def add_layernorm16(x, r, fmt: int, gamma, beta, eps: float = 1e-5, lib: ctypes.CDLL | None = None):
+    """Residual add in the storage format, then LayerNorm of that stored sum.
+
+    Returns ``(y, y64, h, mean, rstd)``."""
+    lib = lib or load()
+    h = add16(x, r, fmt, lib)
+    y, y64, mean, rstd = layernorm16(h, fmt, gamma, beta, eps, lib)
+    return y, y64, h, mean, rstd
+
+
+def add_rmsnorm16(x, r, fmt: int, w, eps: float = 1e-5, lib: ctypes.CDLL | None = None):
+    """Residual add in the storage format, then RMSNorm; ``(y, y64, h, rstd)``."""
+    lib = lib or load()
+    h = add16(x, r, fmt, lib)
+    y, y64, rstd = rmsnorm16(h, fmt, w, eps, lib)
+    return y, y64, h, rstd
+
+
+def ulp16(mag, fmt: int) -> np.ndarray:
+    """The spacing of the 16-bit format at magnitude ``mag`` (the subnormal
+    spacing below the normal range)."""
+    p, emin = _FMT_P_EMIN[fmt]
+    m = np.abs(np.asarray(mag, np.float64))
+    _, e = np.frexp(m)                        # m = f * 2^e, 0.5 <= f < 1
+    E = np.maximum(e.astype(np.int64) - 1, emin)
+    return np.ldexp(1.0, (E - (p - 1)).astype(np.int64))
+
+
+def tolerance_ok16(got_bits, ref64, fmt: int, atol: float = 1e-5, rtol: float = 1e-4,
+                   lib: ctypes.CDLL | None = None):
+    """Acceptance for outputs stored in a 16-bit format.
+
+    A kernel that meets the float32 bound tau = atol + rtol*|ref| before its
+    final rounding, then rounds to nearest, lands within tau plus half a
+    16-bit ulp of the exact value; the ulp is taken at the larger of |got| and
+    |ref| + tau, which covers a rounding across a power of two.  Returns
+    ``(ok, max_abs_err, max_ratio)`` like ``tolerance_ok``."""
+    got = widen16(got_bits, fmt, lib).astype(np.float64)
+    ref = np.asarray(ref64, np.float64)
+    if got.shape != ref.shape:
+        return False, float("inf"), float("inf")
+    if got.size == 0:
+        return True, 0.0, 0.0
+    if not np.all(np.isfinite(got)) or not np.all(np.isfinite(ref)):
+        return False, float("inf"), float("inf")
+    tau = atol + rtol * np.abs(ref)
+    bound = tau + 0.5 * ulp16(np.maximum(np.abs(got), np.abs(ref) + tau), fmt)
+    err = np.abs(got - ref)
+    ratio = err / bound
+    return bool(np.all(err <= bound)), float(err.max()), float(ratio.max())
 
 
 def set_threads(n: int, lib: ctypes.CDLL | None = None) -> None:

@@ -48,14 +48,15 @@ int oracle_plant(void) { return ORACLE_PLANT; }
  *     y_ij = (x_ij - mu_i) / sqrt(sigma_i^2 + eps) * gamma_j + beta_j
  * mean[i] = mu_i and rstd[i] = 1/sqrt(sigma_i^2 + eps) are optional outputs
  * (NULL skips them); mean64/var64 optionally expose the float64 statistics
- * before rounding, for the pins.
+ * before rounding, for the pins, and y64 the float64 outputs before their one
+ * rounding (what a narrower storage format is rounded from).
  *
  * x, y: row-major [rows, d] float32; gamma, beta: [d].  y may equal x.
  */
 void oracle_layernorm_f64(const float *x, const float *gamma, const float *beta,
                           int64_t rows, int64_t d, float eps,
                           float *y, float *mean, float *rstd,
-                          double *mean64, double *var64)
+                          double *mean64, double *var64, double *y64)
 {
     #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < rows; ++i) {
@@ -104,7 +105,9 @@ void oracle_layernorm_f64(const float *x, const float *gamma, const float *beta,
 #if ORACLE_PLANT == 5
             g = (double)gamma[i % d];            /* planted: scale indexed by row */
 #endif
-            yi[j] = (float)(((double)xi[j] - mu) * rho * g + b);
+            const double v = ((double)xi[j] - mu) * rho * g + b;
+            yi[j] = (float)v;
+            if (y64) y64[i * d + j] = v;
         }
         if (mean)   mean[i] = (float)mu;
         if (rstd)   rstd[i] = (float)rho;
@@ -118,11 +121,12 @@ void oracle_layernorm_f64(const float *x, const float *gamma, const float *beta,
  * 5070" (section "The operator and the change") defines it:
  *     y_rc = x_rc * w_c * ( (1/D) * sum_j x_rj^2 + eps )^(-1/2)
  * rstd[r] = ((1/D) sum_j x_rj^2 + eps)^(-1/2) is optional (NULL skips it);
- * ms64 optionally exposes the float64 mean square.  y may equal x.
+ * ms64 optionally exposes the float64 mean square and y64 the float64
+ * outputs before rounding.  y may equal x.
  */
 void oracle_rmsnorm_f64(const float *x, const float *w,
                         int64_t rows, int64_t d, float eps,
-                        float *y, float *rstd, double *ms64)
+                        float *y, float *rstd, double *ms64, double *y64)
 {
     #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
@@ -142,8 +146,11 @@ void oracle_rmsnorm_f64(const float *x, const float *w,
         rho = 1.0 / sqrt(ms);                    /* planted: eps removed */
 #endif
 
-        for (int64_t c = 0; c < d; ++c)
-            yr[c] = (float)((double)xr[c] * (double)w[c] * rho);
+        for (int64_t c = 0; c < d; ++c) {
+            const double v = (double)xr[c] * (double)w[c] * rho;
+            yr[c] = (float)v;
+            if (y64) y64[r * d + c] = v;
+        }
         if (rstd) rstd[r] = (float)rho;
         if (ms64) ms64[r] = ms;
     }
@@ -228,5 +235,113 @@ void oracle_add_rmsnorm_f64(const float *x, const float *r, const float *w,
             if (rstd) rstd[i] = (float)rho;
         }
         free(hs);
+    }
+}
+
+/*
+ * 16-bit storage formats: IEEE binary16 (fmt 1) and bfloat16 (fmt 2).
+ *
+ * A format is (p significand bits including the implicit one, emin, emax):
+ * binary16 (11, -14, 15), bfloat16 (8, -126, 127).  A finite value is
+ * (-1)^s * m * 2^(e - p + 1) with integer m < 2^p, and e = emin for the
+ * subnormals.  Widening is exact (every such value is a float32, hence a
+ * float64); narrowing rounds a float64 once, to nearest with ties to even, as
+ * IEEE 754 defines for a conversion to a narrower format: values at or past
+ * the overflow midpoint become infinities.
+ *
+ * The normalization over 16-bit storage is then: widen the inputs exactly,
+ * apply the float64 definition above, round each output once from its float64
+ * value.  The fused residual sum h = x + r is rounded to the storage format
+ * once, from the exact sum, and the norm is applied to that stored h.
+ */
+static void fmt16(int fmt, int *p, int *emin, int *emax)
+{
+    if (fmt == 1) { *p = 11; *emin = -14;  *emax = 15;  }
+    else          { *p = 8;  *emin = -126; *emax = 127; }
+}
+
+double oracle_widen16(uint16_t b, int fmt)
+{
+    int p, emin, emax;
+    fmt16(fmt, &p, &emin, &emax);
+    const int mbits = p - 1;                       /* stored fraction bits */
+    const int ebits = 15 - mbits;
+    const int bias = emax;
+    const int s = b >> 15;
+    const int ef = (b >> mbits) & ((1 << ebits) - 1);
+    const int mf = b & ((1 << mbits) - 1);
+    double v;
+    if (ef == (1 << ebits) - 1)                    /* infinity or NaN */
+        v = mf ? NAN : INFINITY;
+    else if (ef == 0)                              /* zero or subnormal */
+        v = ldexp((double)mf, emin - mbits);
+    else
+        v = ldexp((double)((1 << mbits) | mf), ef - bias - mbits);
+    return s ? -v : v;
+}
+
+uint16_t oracle_round16(double v, int fmt)
+{
+    int p, emin, emax;
+    fmt16(fmt, &p, &emin, &emax);
+    const int mbits = p - 1;
+    const int ebits = 15 - mbits;
+    const uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    const uint16_t inf = (uint16_t)(((1u << ebits) - 1u) << mbits);
+    if (isnan(v)) return (uint16_t)(sign | inf | (1u << (mbits - 1)));
+    double a = fabs(v);
+    if (isinf(a)) return (uint16_t)(sign | inf);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);                                  /* a = f * 2^e, 0.5 <= f < 1 */
+    int E = e - 1;                                 /* floor(log2 a) */
+    if (E < emin) E = emin;                        /* the subnormal quantum */
+    /* a / 2^(E - mbits) is exact (a power-of-two scaling); round that to an
+       integer, ties to even (the default rounding mode of nearbyint) */
+    double m = nearbyint(ldexp(a, mbits - E));
+#if ORACLE_PLANT == 12
+    m = floor(ldexp(a, mbits - E));                /* planted: truncation */
+#endif
+#if ORACLE_PLANT == 13
+    m = round(ldexp(a, mbits - E));                /* planted: ties away from zero */
+#endif
+    if (m >= (double)(1 << p)) {                   /* carried into the next binade */
+        m /= 2.0;
+        E += 1;
+    }
+    if (E > emax) return (uint16_t)(sign | inf);   /* overflow */
+    if (m < (double)(1 << mbits))                  /* subnormal (E == emin) */
+        return (uint16_t)(sign | (uint16_t)m);
+    return (uint16_t)(sign | (uint16_t)((E + emax) << mbits) | ((uint16_t)m & ((1u << mbits) - 1u)));
+}
+
+void oracle_widen16_n(const uint16_t *in, int fmt, int64_t n, float *out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = (float)oracle_widen16(in[i], fmt);
+}
+
+void oracle_round16_n(const double *in, int fmt, int64_t n, uint16_t *out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_round16(in[i], fmt);
+}
+
+/* h = x + r in the storage format.  The float64 sum of two 16-bit values is
+ * exact unless their exponents differ by more than 45 (possible for bfloat16
+ * only); then the smaller addend is below 2^-38 of an ulp of the larger, no
+ * rounding midpoint is near, and rounding the float64 sum gives what rounding
+ * the exact sum gives: the larger addend. */
+void oracle_add16_n(const uint16_t *x, const uint16_t *r, int fmt, int64_t n, uint16_t *h)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        double s = oracle_widen16(x[i], fmt) + oracle_widen16(r[i], fmt);
+#if ORACLE_PLANT == 14
+        s = oracle_widen16(x[i], fmt);             /* planted: residual dropped */
+#endif
+        h[i] = oracle_round16(s, fmt);
     }
 }

@@ -19,6 +19,10 @@ w = 1 + 0.1 N, each formed in float64 and rounded once.
 
 Every draw comes from ``numpy.random.default_rng`` (PCG64) seeded with a short
 integer list, recorded by the callers next to their results.
+
+16-bit inputs (binary16, bfloat16) are the float32 draws cast by numpy
+(binary16) or torch (bfloat16), both round-to-nearest-even library casts,
+and are handled as uint16 bit patterns.
 """
 from __future__ import annotations
 
@@ -54,6 +58,27 @@ def make_x(rows: int, d: int, pattern: str = "normal", seed=0) -> np.ndarray:
     elif pattern == "offset":
         x = (x.astype(np.float64) * 3.0 + 0.5).astype(np.float32)
     return np.ascontiguousarray(x)
+
+
+F16 = 1   # IEEE binary16 storage
+BF16 = 2  # bfloat16 storage
+FORMATS = {"f16": F16, "bf16": BF16}
+
+
+def quantize16(x: np.ndarray, fmt: int) -> np.ndarray:
+    """uint16 patterns of float32 ``x`` cast to a 16-bit format by a library cast."""
+    x = np.ascontiguousarray(x, np.float32)
+    if fmt == F16:
+        return x.astype(np.float16).view(np.uint16)
+    if fmt == BF16:
+        import torch
+        return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    raise ValueError(f"unknown 16-bit format {fmt}")
+
+
+def make_x16(rows: int, d: int, pattern: str, seed, fmt: int) -> np.ndarray:
+    """make_x's draw in a 16-bit storage format (uint16 patterns)."""
+    return quantize16(make_x(rows, d, pattern, seed), fmt)
 
 
 def make_affine(d: int, seed=0) -> tuple[np.ndarray, np.ndarray]:

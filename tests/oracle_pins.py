@@ -351,3 +351,193 @@ def check_add_norm(lib):
 LN_CHECKS = (check_ln_bruteforce, check_ln_vs_torch, check_ln_closed_forms, check_ln_invariants)
 RMS_CHECKS = (check_rms_bruteforce, check_rms_vs_torch, check_rms_closed_forms, check_rms_invariants)
 ALL_CHECKS = LN_CHECKS + RMS_CHECKS + (check_add_norm,)
+
+
+# ----------------------------------------------------------------------------
+# 16-bit storage: exact widening, one round-to-nearest-even narrowing
+
+F16, BF16 = oracle.FMT_F16, oracle.FMT_BF16
+
+
+def _lib_values16(bits: np.ndarray, fmt: int) -> np.ndarray:
+    """float64 values of 16-bit patterns by library casts (numpy binary16,
+    torch bfloat16), independent of the oracle's decoder."""
+    if fmt == F16:
+        return bits.view(np.float16).astype(np.float64)
+    import torch
+    return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _finite_table(fmt: int):
+    """Every finite non-negative value of the format, ascending, with its pattern."""
+    bits = np.arange(0, 0x8000, dtype=np.uint16)
+    vals = _lib_values16(bits, fmt)
+    keep = np.isfinite(vals)
+    order = np.argsort(vals[keep], kind="stable")
+    return vals[keep][order], bits[keep][order]
+
+
+def _nearest16(v: Fraction | float, table, fmt: int) -> int:
+    """The format's pattern nearest to the exact value v, ties to the even
+    pattern, overflow past the last midpoint to infinity, the sign kept (a
+    negative value too small for the format gives -0): the definition,
+    evaluated by search over every finite value."""
+    vals, bits = table
+    f = Fraction(v)
+    neg = f < 0
+    a = -f if neg else f
+    i = int(np.searchsorted(vals, float(a)))
+    cands = {max(0, min(len(vals) - 1, j)) for j in (i - 2, i - 1, i, i + 1)}
+    best = None
+    for j in sorted(cands):
+        dist = abs(Fraction(float(vals[j])) - a)
+        key = (dist, int(bits[j]) & 1)
+        if best is None or key < best[0]:
+            best = (key, j)
+    j = best[1]
+    top = Fraction(float(vals[-1]))
+    ulp_top = top - Fraction(float(vals[-2]))
+    if a >= top + ulp_top / 2:                       # at or past the overflow midpoint
+        out = 0x7C00 if fmt == F16 else 0x7F80
+    else:
+        out = int(bits[j])
+    return out | 0x8000 if neg else out
+
+
+def check_widen16(lib):
+    """Every one of the 65536 patterns of each format decodes to the value the
+    library casts give (NaN patterns to NaN)."""
+    bits = np.arange(65536, dtype=np.uint16)
+    for fmt in (F16, BF16):
+        got = oracle.widen16(bits, fmt, lib=lib).astype(np.float64)
+        want = _lib_values16(bits, fmt)
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(got), nan), f"fmt {fmt}: NaN patterns"
+        assert np.array_equal(got[~nan], want[~nan]), f"fmt {fmt}: decoded values"
+        # signed zeros keep their sign
+        assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def check_round16(lib):
+    """Narrowing is round to nearest, ties to even, from the float64 value.
+
+    Pinned by (a) the nearest-value search over every finite value of the
+    format with exact rational distances, on random magnitudes from the
+    subnormals to past overflow, (b) every midpoint between neighbours and
+    the doubles just beside it, (c) numpy's float64 -> binary16 cast and
+    torch's float32 -> bfloat16 cast on float32 values."""
+    rng = _rng([61])
+    for fmt, (lo, hi) in ((F16, (-27, 17)), (BF16, (-136, 129))):
+        table = _finite_table(fmt)
+        e = rng.uniform(lo, hi, 4000)
+        v = np.ldexp(rng.uniform(0.5, 1.0, e.size), np.floor(e).astype(int)) * rng.choice([-1.0, 1.0], e.size)
+        got = oracle.round16(v, fmt, lib=lib)
+        want = np.array([_nearest16(float(t), table, fmt) for t in v], np.uint16)
+        assert np.array_equal(got, want), f"fmt {fmt}: nearest value"
+        # midpoints between neighbours (exact in float64), and one double ulp each side
+        vals, bits = table
+        idx = rng.integers(0, len(vals) - 1, 3000)
+        mid = (vals[idx] + vals[idx + 1]) / 2
+        even = np.where(bits[idx] % 2 == 0, bits[idx], bits[idx + 1])
+        assert np.array_equal(oracle.round16(mid, fmt, lib=lib), even), f"fmt {fmt}: ties to even"
+        assert np.array_equal(oracle.round16(np.nextafter(mid, -np.inf), fmt, lib=lib), bits[idx])
+        assert np.array_equal(oracle.round16(np.nextafter(mid, np.inf), fmt, lib=lib), bits[idx + 1])
+        assert np.array_equal(oracle.round16(-mid, fmt, lib=lib), even | 0x8000)
+    x = rng.standard_normal(20000) * np.exp2(rng.integers(-30, 18, 20000))
+    with np.errstate(over="ignore"):
+        want16 = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(oracle.round16(x, F16, lib=lib), want16)
+    import torch
+    x32 = (rng.standard_normal(20000) * np.exp2(rng.integers(-140, 120, 20000))).astype(np.float32)
+    want = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.round16(x32.astype(np.float64), BF16, lib=lib), want)
+
+
+def check_add16(lib):
+    """h = x + r rounded once: the nearest-value search on the exact rational
+    sum, including exponent gaps past float64's precision (bfloat16)."""
+    rng = _rng([62])
+    for fmt in (F16, BF16):
+        table = _finite_table(fmt)
+        vals, bits = table
+        n = 3000
+        xi = rng.integers(0, len(vals), n)
+        ri = rng.integers(0, len(vals), n)
+        xb = bits[xi] | np.where(rng.random(n) < 0.5, 0x8000, 0).astype(np.uint16)
+        rb = bits[ri] | np.where(rng.random(n) < 0.5, 0x8000, 0).astype(np.uint16)
+        # and close pairs, where cancellation and ties are likely
+        xb[:500] = bits[rng.integers(len(vals) // 2, len(vals) - 1, 500)]
+        rb[:500] = (xb[:500] + rng.integers(-3, 4, 500).astype(np.uint16)) | 0x8000
+        got = oracle.add16(xb, rb, fmt, lib=lib)
+        xv, rv = _lib_values16(xb, fmt), _lib_values16(rb, fmt)
+        for k in range(n):
+            s = Fraction(float(xv[k])) + Fraction(float(rv[k]))
+            w = _nearest16(s, table, fmt)
+            if s == 0:
+                assert got[k] & 0x7FFF == 0, f"fmt {fmt}: zero sum"
+            else:
+                assert int(got[k]) == w, f"fmt {fmt}: {xv[k]!r} + {rv[k]!r}"
+
+
+def check_norm16(lib):
+    """LayerNorm / RMSNorm over 16-bit storage: the outputs are torch's
+    float64 routines on the exactly widened inputs, rounded once (bit for bit
+    away from rounding midpoints); a zero row gives the rounded bias."""
+    import torch
+    import torch.nn.functional as F
+    for fmt in (F16, BF16):
+        for rows, d, pat in ((16, 768, "offset"), (9, 33, "normal"), (4, 1, "normal")):
+            x16 = wl.make_x16(rows, d, pat, [63, rows, d], fmt)
+            g, b = wl.make_affine(d, [63, d])
+            w = wl.make_weight(d, [63, d])
+            xd = torch.from_numpy(_lib_values16(x16, fmt).reshape(rows, d))
+            y, y64, mean, rstd = oracle.layernorm16(x16, fmt, g, b, float(EPS32), lib=lib)
+            ty, tm, tr = torch.native_layer_norm(xd, (d,), torch.from_numpy(g).double(),
+                                                 torch.from_numpy(b).double(), float(EPS32))
+            assert np.allclose(y64, ty.numpy(), rtol=1e-12, atol=1e-12), "y64 vs torch"
+            table = _finite_table(fmt)
+            wantb = np.array([_nearest16(float(t), table, fmt) for t in ty.numpy().ravel()])
+            agree = np.mean(y.ravel() == wantb)
+            assert agree >= 0.999, f"fmt {fmt}: only {agree:.4f} of outputs round as torch's"
+            _assert_ulps(mean, tm.reshape(-1).numpy().astype(np.float32), 1, "mean16")
+            _assert_ulps(rstd, tr.reshape(-1).numpy().astype(np.float32), 1, "rstd16")
+            yr, yr64, rr = oracle.rmsnorm16(x16, fmt, w, float(EPS32), lib=lib)
+            tyr = F.rms_norm(xd, (d,), torch.from_numpy(w).double(), eps=float(EPS32)).numpy()
+            assert np.allclose(yr64, tyr, rtol=1e-12, atol=1e-12), "rms y64 vs torch"
+        # zero rows: y is beta rounded once to the format (a library cast of float32)
+        d = 40
+        g, b = wl.make_affine(d, [64, d])
+        z = np.zeros((3, d), np.uint16)
+        y, _, mean, _ = oracle.layernorm16(z, fmt, g, b, float(EPS32), lib=lib)
+        assert np.array_equal(y, np.broadcast_to(wl.quantize16(b, fmt), y.shape)), "zero rows give beta"
+        assert not np.any(mean)
+        # fused: h is the stored sum and y the norm of that stored h
+        x16 = wl.make_x16(5, 96, "offset", [65], fmt)
+        r16 = wl.make_x16(5, 96, "normal", [66], fmt)
+        g, b = wl.make_affine(96, [65])
+        y, y64, h, mean, rstd = oracle.add_layernorm16(x16, r16, fmt, g, b, float(EPS32), lib=lib)
+        assert np.array_equal(h, oracle.add16(x16, r16, fmt, lib=lib))
+        y2, y642, _, _ = oracle.layernorm16(h, fmt, g, b, float(EPS32), lib=lib)
+        assert np.array_equal(y, y2) and np.array_equal(y64, y642)
+
+
+def check_tolerance16(lib):
+    """The 16-bit acceptance bound: a float32-accurate value rounded to
+    nearest passes; two ulps off fails; NaN fails."""
+    rng = _rng([67])
+    for fmt in (F16, BF16):
+        ref = rng.standard_normal(5000) * 2.0
+        tau = 1e-5 + 1e-4 * np.abs(ref)
+        near = oracle.round16(ref + 0.99 * tau * rng.choice([-1, 1], ref.size), fmt, lib=lib)
+        assert oracle.tolerance_ok16(near, ref, fmt, lib=lib)[0]
+        step = oracle.round16(ref, fmt, lib=lib).astype(np.int64)
+        off = np.where(step & 0x8000, step - 2, step + 2).astype(np.uint16)   # two ulps toward zero
+        big = np.abs(ref) > 0.01
+        ok, _, _ = oracle.tolerance_ok16(off[big], ref[big], fmt, lib=lib)
+        assert not ok
+        nanb = np.array([0x7E00 if fmt == F16 else 0x7FC0], np.uint16)
+        assert not oracle.tolerance_ok16(nanb, np.array([0.0]), fmt, lib=lib)[0]
+
+
+STORAGE16_CHECKS = (check_widen16, check_round16, check_add16, check_norm16, check_tolerance16)
+ALL_CHECKS = ALL_CHECKS + STORAGE16_CHECKS

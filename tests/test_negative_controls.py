@@ -26,6 +26,9 @@ PLANTS = {
     9: ("layernorm eps outside the root", pins.LN_CHECKS),
     10: ("add+layernorm residual dropped", (pins.check_add_norm,)),
     11: ("add+rmsnorm input dropped", (pins.check_add_norm,)),
+    12: ("16-bit narrowing truncates", (pins.check_round16, pins.check_norm16, pins.check_tolerance16)),
+    13: ("16-bit narrowing ties away from zero", (pins.check_round16, pins.check_add16)),
+    14: ("16-bit residual dropped", (pins.check_add16, pins.check_norm16)),
 }
 
 
