@@ -1,6 +1,7 @@
 /*
  * mi_norm.h — C ABI of libmi_norm.so: forward row-wise normalization of a
- * contiguous float32 [rows, d] matrix on AMD Instinct MI355X (gfx950).
+ * [rows, d] matrix (float32, binary16 or bfloat16 rows, any row stride) on
+ * AMD Instinct MI355X (gfx950).
  *
  * Operations
  * ----------
@@ -17,38 +18,54 @@
  * threads did not win every shape" (section "The operator and the change"):
  *     y_rc = x_rc * w_c * rsqrt((1/d) sum_j x_rj^2 + eps)
  *
- * Residual add fused before either norm (the step before the normalization
- * whose absence the RMSNorm page notes: "no ... fusion with a residual add"):
- *     h = x + r (a float32 addition, optionally written out), y = Norm(h)
+ * Residual add fused before either norm (the RMSNorm page, same section,
+ * lists fusion with a residual add among what its kernels leave out):
+ *     h = x + r (rounded to the row storage type, optionally written out),
+ *     y = Norm(h)
  *
  * Arithmetic is IEEE float32 with fused multiply-adds and the hardware
  * reciprocal square root; results agree with a float64 evaluation of the same
  * definition within |err| <= 1e-5 + 1e-4 * |ref| (the acceptance bound of the
  * RMSNorm page, section "Correctness before timing").
  *
+ * Storage types.  Rows (x, r, y, h) may be float32, IEEE binary16 or
+ * bfloat16 (mi_norm_dtype).  16-bit rows are widened exactly to float32, the
+ * statistics and arithmetic stay float32, parameters (gamma, beta, w) and the
+ * statistics outputs (mean, rstd) are always float32, and each 16-bit output
+ * is rounded once, to nearest with ties to even.  A 16-bit y is therefore
+ * within the float32 bound above plus half a unit in the last place of the
+ * 16-bit format; h is the storage-format rounding of x + r, exactly.
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Pointers are DEVICE pointers (HIP device memory of the current device),
- *   float32, 4-byte aligned.  x and y are row-major [rows, d] with row stride
- *   d; gamma, beta and w are [d]; mean and rstd are [rows].
+ *   aligned to their element size.  The row tensors x, r, y, h are row-major
+ *   [rows, d]: element (i, j) at base + i * ld + j elements, where the named
+ *   float32 calls use ld = d and mi_norm_fwd takes one ld per tensor
+ *   (ld >= d; 0 means d).  gamma, beta and w are float32 [d]; mean and rstd
+ *   are float32 [rows].
  * - Ownership: the caller allocates, owns and frees every buffer.  The library
  *   allocates, frees and synchronizes nothing, keeps no global mutable state
  *   and is reentrant; calls on different streams may run concurrently.
  * - Work is enqueued on `stream` (NULL = the null stream) and the call returns
  *   without waiting.  One kernel launch per call; calls may be captured into a
  *   HIP graph.
- * - Aliasing: the [rows, d] tensors (x, y, and for the fused calls r, h) are
- *   each either the same pointer as another or disjoint from it: y may equal
- *   x (in place), and in the fused calls y and h may each equal x or r, but y
- *   and h never share memory.  An output overlapping gamma, beta or w is
- *   rejected.  mean/rstd must not overlap any other argument.
- * - 16-byte-aligned x, y, gamma, beta (or w) and d % 4 == 0 select the
- *   128-bit vector path; other layouts take a peeled or scalar path with the
- *   same results.
+ * - Aliasing: an output row tensor (y, h) either IS an input row tensor
+ *   (x or r: same pointer, same row stride — in place) or shares no element
+ *   with any other row tensor; y and h never share an element.  Inputs may
+ *   overlap each other freely (e.g. x and r interleaved in one buffer).  No
+ *   output may overlap gamma, beta or w, and mean/rstd may overlap no other
+ *   argument.
+ * - Row tensors aligned to four elements (16 bytes for float32, 8 for the
+ *   16-bit types) with d and every row stride a multiple of four, and 16-byte
+ *   aligned parameters, select the quad-vector path; rows that share their
+ *   phase within four elements take a peeled quad path; any other layout a
+ *   scalar path with the same results.
  * - Errors: MI_NORM_ERR_INVALID is returned before any launch for a NULL
- *   required pointer, a pointer not 4-byte aligned, rows < 0, d < 1,
- *   d > 2^31 - 1, a size overflow, eps NaN or negative, or an aliasing
- *   pattern the rule above excludes.  rows == 0 returns MI_NORM_OK and launches nothing.
+ *   required pointer, a misaligned pointer, an unknown op or dtype, rows < 0,
+ *   d < 1, d > 2^31 - 1, a row stride below d, a size overflow, eps NaN or
+ *   negative, or an aliasing pattern the rule above excludes.  rows == 0
+ *   returns MI_NORM_OK and launches nothing.
  *   MI_NORM_ERR_HIP reports a failed launch (the HIP error is not kept;
  *   faults inside the kernel surface at the caller's next synchronization,
  *   as usual for HIP).  No C++ exception crosses this interface.
@@ -132,11 +149,8 @@ mi_norm_status mi_add_rmsnorm_fwd(const float *x, const float *r, const float *w
                                   float *rstd, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
- * Kernel variants.  Every call above is served by one compiled kernel variant
- * chosen from the operation, the row width d, the pointer alignment and the
- * row count.  The calls below expose that
- * table so tests can drive every variant and benchmarks can compare them.
- * They follow the same conventions and error rules as the calls above.
+ * The general call: any of the four operations over float32, binary16 or
+ * bfloat16 rows with a row stride per tensor, described by one struct.
  */
 
 typedef enum mi_norm_op {
@@ -146,23 +160,54 @@ typedef enum mi_norm_op {
     MI_NORM_OP_ADD_RMSNORM = 3     /* residual add fused before RMSNorm */
 } mi_norm_op;
 
-/* One call's shape and pointers, for the variant queries below. */
+typedef enum mi_norm_dtype {
+    MI_NORM_F32 = 0,   /* IEEE binary32 */
+    MI_NORM_F16 = 1,   /* IEEE binary16 */
+    MI_NORM_BF16 = 2   /* bfloat16: binary32's exponent, 8 significand bits */
+} mi_norm_dtype;
+
+/* One call in full.  Row strides are in elements (0 means d). */
 typedef struct mi_norm_problem {
     int op;                 /* mi_norm_op */
-    int64_t rows;
-    int64_t d;
-    const void *x;          /* input */
-    const void *r;          /* residual input (MI_NORM_OP_ADD_*), else ignored */
-    const void *y;          /* output */
-    const void *h;          /* x + r output (MI_NORM_OP_ADD_*), NULL if not written */
-    const void *params0;    /* gamma or w */
-    const void *params1;    /* beta (LayerNorm ops), else ignored */
+    int dtype;              /* mi_norm_dtype of x, r, y and h */
+    int64_t rows;           /* >= 0 */
+    int64_t d;              /* >= 1 */
+    const void *x;          /* input rows                                      (required) */
+    int64_t ldx;
+    const void *r;          /* residual rows (MI_NORM_OP_ADD_*), else ignored  */
+    int64_t ldr;
+    void *y;                /* output rows                                     (required) */
+    int64_t ldy;
+    void *h;                /* x + r rows (MI_NORM_OP_ADD_*), NULL to skip     */
+    int64_t ldh;
+    const float *params0;   /* gamma (LayerNorm ops) or w, float32 [d]         (required) */
+    const float *params1;   /* beta (LayerNorm ops, required), else ignored    */
+    float eps;              /* >= 0 */
+    float *mean;            /* float32 [rows] or NULL (LayerNorm ops only)     */
+    float *rstd;            /* float32 [rows] or NULL                          */
 } mi_norm_problem;
+
+/* Run problem *p on `stream`: the named calls above are this call with dtype
+ * MI_NORM_F32 and every row stride d.  A NULL p is MI_NORM_ERR_INVALID. */
+mi_norm_status mi_norm_fwd(const mi_norm_problem *p, hipStream_t stream);
+
+/* The argument checks of mi_norm_fwd alone (host logic, nothing launched, no
+ * device access): MI_NORM_OK when mi_norm_fwd would accept *p. */
+mi_norm_status mi_norm_check(const mi_norm_problem *p);
+
+/* ---------------------------------------------------------------------------
+ * Kernel variants.  Every call above is served by one compiled kernel variant
+ * chosen from the operation, the storage type, the row width d, the pointer
+ * alignment and strides, and the row count.  The calls below expose that
+ * table so tests can drive every variant and benchmarks can compare them.
+ * They follow the same conventions and error rules as the calls above.
+ */
 
 typedef struct mi_norm_variant_info {
     int op;               /* mi_norm_op */
-    int vec;              /* elements per lane access: 4 (128-bit) or 1 */
-    int peel;             /* 1: per-row scalar head/tail around an aligned 128-bit body */
+    int dtype;            /* mi_norm_dtype of the rows */
+    int vec;              /* elements per lane access: 4 (one quad) or 1 */
+    int peel;             /* 1: per-row scalar head/tail around an aligned quad body */
     int looped;           /* 1: row streamed in chunks (re-read), any width */
     int lanes_per_row;    /* 16, 32 or 64 lanes of one wave share a row (held variants) */
     int waves_per_row;    /* waves cooperating on one row */
@@ -170,7 +215,8 @@ typedef struct mi_norm_variant_info {
     int waves_per_block;  /* wave64s per workgroup */
     int rows_per_block;   /* rows owned by one workgroup per iteration */
     int64_t max_d;        /* widest row the variant accepts (INT64_MAX if unbounded) */
-    int needs_aligned;    /* 1: x, y, params 16-byte aligned and d % 4 == 0 required */
+    int needs_aligned;    /* 1: quad-aligned rows and strides, 16-byte-aligned
+                             parameters and d % 4 == 0 required */
 } mi_norm_variant_info;
 
 /* Number of compiled variants; ids are 0 .. count-1. */
@@ -183,17 +229,21 @@ const char *mi_norm_variant_name(int id);
 mi_norm_status mi_norm_variant_get_info(int id, mi_norm_variant_info *out);
 
 /* The variant the dispatcher would choose for problem *p (host logic only,
- * no device access): the row width and pointer alignment pick the shape, the
- * row count picks the waves per row and the workgroup size.  Returns -1 when
- * the problem is invalid. */
+ * no device access; eps, mean and rstd are not consulted): the storage type,
+ * row width, alignment and strides pick the shape, the row count picks the
+ * waves per row and the workgroup size.  Returns -1 when the problem's shape
+ * or pointers are invalid. */
 int mi_norm_select(const mi_norm_problem *p);
 
 /* Whether variant `id` can run problem *p (1) or not (0). */
 int mi_norm_eligible(int id, const mi_norm_problem *p);
 
-/* LayerNorm / RMSNorm forced onto variant `id`.  MI_NORM_ERR_INVALID when the
- * variant does not exist, belongs to the other operation, or cannot run these
- * arguments (see mi_norm_variant_eligible). */
+/* mi_norm_fwd forced onto variant `id`.  MI_NORM_ERR_INVALID when the variant
+ * does not exist, belongs to another operation or storage type, or cannot run
+ * these arguments (see mi_norm_eligible). */
+mi_norm_status mi_norm_fwd_variant(int id, const mi_norm_problem *p, hipStream_t stream);
+
+/* The named float32 calls forced onto variant `id`, as mi_norm_fwd_variant. */
 mi_norm_status mi_layernorm_fwd_variant(int id, const float *x, const float *gamma,
                                         const float *beta, float *y, int64_t rows,
                                         int64_t d, float eps, float *mean, float *rstd,

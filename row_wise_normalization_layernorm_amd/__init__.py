@@ -1,4 +1,5 @@
-"""MI355X-native forward row-wise normalization (LayerNorm, RMSNorm).
+"""MI355X-native forward row-wise normalization (LayerNorm, RMSNorm, each with
+an optional fused residual add; float32, binary16 or bfloat16 rows).
 
 The compute path is libmi_norm.so (hand-written HIP for gfx950, C ABI in
 include/mi_norm.h); this package is its thin Python binding plus the seeded
@@ -6,7 +7,10 @@ synthetic workloads used by tests and benchmarks.
 """
 from ._binding import (  # noqa: F401
     MI_NORM_ERR_HIP,
+    MI_NORM_BF16,
     MI_NORM_ERR_INVALID,
+    MI_NORM_F16,
+    MI_NORM_F32,
     MI_NORM_OK,
     OP_ADD_LAYERNORM,
     OP_ADD_RMSNORM,
@@ -26,7 +30,10 @@ from ._binding import (  # noqa: F401
     mi_copy_f32,
     mi_layernorm_fwd,
     mi_layernorm_fwd_variant,
+    mi_norm_check,
     mi_norm_eligible,
+    mi_norm_fwd,
+    mi_norm_fwd_variant,
     mi_norm_select,
     mi_norm_status_string,
     mi_norm_variant_count,

@@ -29,6 +29,9 @@ OP_LAYERNORM = 0
 OP_RMSNORM = 1
 OP_ADD_LAYERNORM = 2
 OP_ADD_RMSNORM = 3
+MI_NORM_F32 = 0
+MI_NORM_F16 = 1
+MI_NORM_BF16 = 2
 
 _lib = None
 
@@ -43,7 +46,7 @@ class MiNormError(RuntimeError):
 
 class VariantInfo(ctypes.Structure):
     _fields_ = [
-        ("op", ctypes.c_int), ("vec", ctypes.c_int), ("peel", ctypes.c_int),
+        ("op", ctypes.c_int), ("dtype", ctypes.c_int), ("vec", ctypes.c_int), ("peel", ctypes.c_int),
         ("looped", ctypes.c_int), ("lanes_per_row", ctypes.c_int),
         ("waves_per_row", ctypes.c_int), ("slots", ctypes.c_int),
         ("waves_per_block", ctypes.c_int), ("rows_per_block", ctypes.c_int),
@@ -55,11 +58,13 @@ class VariantInfo(ctypes.Structure):
 
 
 class Problem(ctypes.Structure):
-    """mi_norm_problem: one call's shape and pointers, for the variant queries."""
+    """mi_norm_problem: one call in full (mi_norm_fwd, the variant queries)."""
     _fields_ = [
-        ("op", ctypes.c_int), ("rows", ctypes.c_int64), ("d", ctypes.c_int64),
-        ("x", ctypes.c_void_p), ("r", ctypes.c_void_p), ("y", ctypes.c_void_p),
-        ("h", ctypes.c_void_p), ("params0", ctypes.c_void_p), ("params1", ctypes.c_void_p),
+        ("op", ctypes.c_int), ("dtype", ctypes.c_int), ("rows", ctypes.c_int64), ("d", ctypes.c_int64),
+        ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64), ("r", ctypes.c_void_p), ("ldr", ctypes.c_int64),
+        ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64), ("h", ctypes.c_void_p), ("ldh", ctypes.c_int64),
+        ("params0", ctypes.c_void_p), ("params1", ctypes.c_void_p), ("eps", ctypes.c_float),
+        ("mean", ctypes.c_void_p), ("rstd", ctypes.c_void_p),
     ]
 
 
@@ -78,6 +83,9 @@ _SIGNATURES = {
     "mi_norm_variant_get_info": (_I, [_I, ctypes.POINTER(VariantInfo)]),
     "mi_add_layernorm_fwd": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _F, _VP, _VP, _VP]),
     "mi_add_rmsnorm_fwd": (_I, [_VP, _VP, _VP, _VP, _VP, _I64, _I64, _F, _VP, _VP]),
+    "mi_norm_fwd": (_I, [ctypes.POINTER(Problem), _VP]),
+    "mi_norm_fwd_variant": (_I, [_I, ctypes.POINTER(Problem), _VP]),
+    "mi_norm_check": (_I, [ctypes.POINTER(Problem)]),
     "mi_norm_select": (_I, [ctypes.POINTER(Problem)]),
     "mi_norm_eligible": (_I, [_I, ctypes.POINTER(Problem)]),
     "mi_add_layernorm_fwd_variant": (_I, [_I, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _F, _VP, _VP,
@@ -263,9 +271,26 @@ def _addr(a):
     return a if (a is None or isinstance(a, int)) else a.data_ptr()
 
 
-def problem(op: int, rows: int, d: int, x, y, params0, params1=None, r=None, h=None) -> Problem:
-    """An mi_norm_problem from tensors or integer addresses."""
-    return Problem(op, rows, d, _addr(x), _addr(r), _addr(y), _addr(h), _addr(params0), _addr(params1))
+def problem(op: int, rows: int, d: int, x, y, params0, params1=None, r=None, h=None, *,
+            dtype: int = MI_NORM_F32, ldx: int = 0, ldr: int = 0, ldy: int = 0, ldh: int = 0,
+            eps: float = 1e-5, mean=None, rstd=None) -> Problem:
+    """An mi_norm_problem from tensors or integer addresses (strides in
+    elements, 0 meaning d)."""
+    return Problem(op, dtype, rows, d, _addr(x), ldx, _addr(r), ldr, _addr(y), ldy, _addr(h), ldh,
+                   _addr(params0), _addr(params1), eps, _addr(mean), _addr(rstd))
+
+
+def mi_norm_fwd(p: Problem, stream=None) -> None:
+    _check(lib().mi_norm_fwd(ctypes.byref(p), _stream(stream)), "mi_norm_fwd")
+
+
+def mi_norm_check(p: Problem) -> int:
+    """Status mi_norm_fwd would return before launching (host logic only)."""
+    return int(lib().mi_norm_check(ctypes.byref(p)))
+
+
+def mi_norm_fwd_variant(vid: int, p: Problem, stream=None) -> None:
+    _check(lib().mi_norm_fwd_variant(vid, ctypes.byref(p), _stream(stream)), f"mi_norm_fwd_variant({vid})")
 
 
 def mi_norm_select(p: Problem) -> int:
@@ -278,18 +303,79 @@ def mi_norm_eligible(vid: int, p: Problem) -> bool:
 
 # --- conveniences over torch tensors (allocation is torch's) -------------------
 
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: MI_NORM_F32, torch.float16: MI_NORM_F16, torch.bfloat16: MI_NORM_BF16}
+    if t.dtype not in codes:
+        raise ValueError(f"rows must be float32, float16 or bfloat16, got {t.dtype}")
+    return codes[t.dtype]
+
+
+def _rows_of(t, name: str) -> tuple[int, int]:
+    """(rows, row stride in elements) of a device tensor [..., d] whose last
+    dimension is contiguous and whose leading dimensions form one strided row
+    index; no copy is made."""
+    if not _is_tensor(t) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() == 0:
+        raise ValueError(f"{name} must have a last dimension")
+    d = t.shape[-1]
+    if d > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    if t.dim() == 1:
+        return 1, d
+    lead = [(s, st) for s, st in zip(t.shape[:-1], t.stride()[:-1]) if s != 1]
+    rows = 1
+    for s, _ in lead:
+        rows *= s
+    if not lead:
+        return rows, d
+    for (s0, st0), (s1, st1) in zip(lead, lead[1:]):
+        if st0 != st1 * s1:
+            raise ValueError(f"{name}: leading dimensions do not form one row stride")
+    return rows, lead[-1][1]
+
+
+def _params(t, name: str, d: int):
+    import torch
+    if t is None:
+        return None
+    if not _is_tensor(t) or t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != d:
+        raise ValueError(f"{name} must be a contiguous float32 device tensor of {d} elements")
+    return t
+
+
+def _norm(op, x, r, p0, p1, eps, stats, out, write_sum, stream):
+    import torch
+    dt = _dtype_code(x)
+    d = x.shape[-1]
+    rows, ldx = _rows_of(x, "x")
+    ldr = 0
+    if r is not None:
+        if r.dtype != x.dtype or r.shape != x.shape:
+            raise ValueError("r must have x's shape and dtype")
+        ldr = _rows_of(r, "r")[1]
+    y = torch.empty(x.shape, device=x.device, dtype=x.dtype) if out is None else out
+    if y.dtype != x.dtype or y.shape != x.shape:
+        raise ValueError("out must have x's shape and dtype")
+    ldy = _rows_of(y, "out")[1]
+    h = torch.empty(x.shape, device=x.device, dtype=x.dtype) if (r is not None and write_sum) else None
+    ln = op in (OP_LAYERNORM, OP_ADD_LAYERNORM)
+    mean = torch.empty(x.shape[:-1], device=x.device, dtype=torch.float32) if (stats and ln) else None
+    rstd = torch.empty(x.shape[:-1], device=x.device, dtype=torch.float32) if stats else None
+    p = problem(op, rows, d, x, y, _params(p0, "gamma" if ln else "w", d), _params(p1, "beta", d), r, h,
+                dtype=dt, ldx=ldx, ldr=ldr, ldy=ldy, ldh=0, eps=eps, mean=mean, rstd=rstd)
+    mi_norm_fwd(p, stream if stream is not None else torch.cuda.current_stream(x.device).cuda_stream)
+    return y, h, mean, rstd
+
+
 def layernorm(x, gamma, beta, eps: float = 1e-5, stats: bool = False, out=None, stream=None):
-    """LayerNorm over the last dimension of a contiguous float32 device tensor.
+    """LayerNorm over the last dimension of a float32, float16 or bfloat16
+    device tensor (rows may be strided; gamma/beta float32).
 
     Returns y, or (y, mean, rstd) with ``stats``.  ``out`` may be x (in place).
     """
-    import torch
-    d = x.shape[-1]
-    rows = x.numel() // d if d else 0
-    y = torch.empty_like(x) if out is None else out
-    mean = torch.empty(x.shape[:-1], device=x.device, dtype=torch.float32) if stats else None
-    rstd = torch.empty(x.shape[:-1], device=x.device, dtype=torch.float32) if stats else None
-    mi_layernorm_fwd(x, gamma, beta, y, rows, d, eps, mean, rstd, stream)
+    y, _, mean, rstd = _norm(OP_LAYERNORM, x, None, gamma, beta, eps, stats, out, False, stream)
     return (y, mean, rstd) if stats else y
 
 
@@ -297,35 +383,17 @@ def add_layernorm(x, r, gamma, beta, eps: float = 1e-5, stats: bool = False, wri
                   stream=None):
     """h = x + r, y = LayerNorm(h).  Returns (y, h) or (y, h, mean, rstd); h is
     None without ``write_sum``."""
-    import torch
-    d = x.shape[-1]
-    rows = x.numel() // d if d else 0
-    y = torch.empty_like(x)
-    h = torch.empty_like(x) if write_sum else None
-    mean = torch.empty(x.shape[:-1], device=x.device, dtype=torch.float32) if stats else None
-    rstd = torch.empty(x.shape[:-1], device=x.device, dtype=torch.float32) if stats else None
-    mi_add_layernorm_fwd(x, r, gamma, beta, y, h, rows, d, eps, mean, rstd, stream)
+    y, h, mean, rstd = _norm(OP_ADD_LAYERNORM, x, r, gamma, beta, eps, stats, None, write_sum, stream)
     return (y, h, mean, rstd) if stats else (y, h)
 
 
 def add_rmsnorm(x, r, w, eps: float = 1e-5, stats: bool = False, write_sum: bool = True, stream=None):
     """h = x + r, y = RMSNorm(h).  Returns (y, h) or (y, h, rstd)."""
-    import torch
-    d = x.shape[-1]
-    rows = x.numel() // d if d else 0
-    y = torch.empty_like(x)
-    h = torch.empty_like(x) if write_sum else None
-    rstd = torch.empty(x.shape[:-1], device=x.device, dtype=torch.float32) if stats else None
-    mi_add_rmsnorm_fwd(x, r, w, y, h, rows, d, eps, rstd, stream)
+    y, h, _, rstd = _norm(OP_ADD_RMSNORM, x, r, w, None, eps, stats, None, write_sum, stream)
     return (y, h, rstd) if stats else (y, h)
 
 
 def rmsnorm(x, w, eps: float = 1e-5, stats: bool = False, out=None, stream=None):
     """RMSNorm over the last dimension; returns y, or (y, rstd) with ``stats``."""
-    import torch
-    d = x.shape[-1]
-    rows = x.numel() // d if d else 0
-    y = torch.empty_like(x) if out is None else out
-    rstd = torch.empty(x.shape[:-1], device=x.device, dtype=torch.float32) if stats else None
-    mi_rmsnorm_fwd(x, w, y, rows, d, eps, rstd, stream)
+    y, _, _, rstd = _norm(OP_RMSNORM, x, None, w, None, eps, stats, out, False, stream)
     return (y, rstd) if stats else y

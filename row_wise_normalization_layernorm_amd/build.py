@@ -2,9 +2,10 @@
 
 Two steps:
 
-1. ``hipcc -c`` compiles csrc/mi_norm.hip (device code for gfx950 plus the
-   host-side launcher and C ABI) into an object.
-2. ``g++ -shared`` links it against the HIP runtime that PyTorch ships.
+1. ``hipcc -c`` compiles, in parallel, csrc/mi_norm.hip (the host-side
+   dispatcher, launcher and C ABI) and one variant table per row storage type
+   (csrc/variants_{f32,f16,bf16}.hip: the gfx950 device code) into objects.
+2. ``g++ -shared`` links them against the HIP runtime that PyTorch ships.
 
 The link step matters: torch's ``libamdhip64.so`` carries no SONAME and is
 loaded under that bare name, while /opt/rocm's copy has SONAME
@@ -30,8 +31,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmi_norm.so")
 BENCH_LIB = os.path.join(PKG, "libmi_norm_bench.so")
-SOURCES = ("mi_norm.hip",)
-HEADERS = ("norm_kernels.hpp",)
+SOURCES = ("mi_norm.hip", "variants_f32.hip", "variants_f16.hip", "variants_bf16.hip")
+HEADERS = ("norm_kernels.hpp", "variant_table.hpp")
 BENCH_SOURCES = ("bench_loop.cpp",)
 ARCH = "gfx950"
 
@@ -61,17 +62,26 @@ def source_paths() -> list[str]:
 
 
 def _run(cmd: list[str], verbose: bool, stderr_to: str | None = None) -> None:
+    _wait(_start(cmd, verbose, stderr_to))
+
+
+def _start(cmd: list[str], verbose: bool, stderr_to: str | None = None):
     if verbose:
         print(" ".join(cmd), flush=True)
-    if stderr_to:
-        with open(stderr_to, "w") as f:
-            r = subprocess.run(cmd, stderr=f)
-        if r.returncode != 0:
+    f = open(stderr_to, "w") if stderr_to else None
+    return cmd, subprocess.Popen(cmd, stderr=f), f, stderr_to
+
+
+def _wait(job) -> None:
+    cmd, proc, f, stderr_to = job
+    rc = proc.wait()
+    if f:
+        f.close()
+    if rc != 0:
+        if stderr_to:
             with open(stderr_to) as f:
                 sys.stderr.write("".join(l for l in f if "remark:" not in l))
-            raise subprocess.CalledProcessError(r.returncode, cmd)
-    else:
-        subprocess.run(cmd, check=True)
+        raise subprocess.CalledProcessError(rc, cmd)
 
 
 def build(verbose: bool = False, resource_report: bool = True) -> str:
@@ -84,16 +94,30 @@ def build(verbose: bool = False, resource_report: bool = True) -> str:
     if not os.path.exists(hipcc):
         hipcc = shutil.which("hipcc") or hipcc
     os.makedirs(BUILD_DIR, exist_ok=True)
-    objs = []
+    objs, jobs, reports = [], [], []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        stem = os.path.splitext(src)[0]
+        obj = os.path.join(BUILD_DIR, stem + ".o")
         cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
-        report = None
+        report = os.path.join(BUILD_DIR, f"remarks_{stem}.txt")
         if resource_report:
             cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
-            report = os.path.join(BUILD_DIR, "resource_usage.txt")
-        _run(cmd, verbose, stderr_to=report)
+            reports.append(report)
+        jobs.append(_start(cmd, verbose, stderr_to=report))
         objs.append(obj)
+    failed = None
+    for job in jobs:
+        try:
+            _wait(job)
+        except subprocess.CalledProcessError as e:
+            failed = failed or e
+    if failed:
+        raise failed
+    if resource_report:
+        with open(os.path.join(BUILD_DIR, "resource_usage.txt"), "w") as out:
+            for r in reports:
+                with open(r) as f:
+                    out.write(f.read())
     tlib = torch_lib_dir()
     rlib = os.path.join(rocm_path(), "lib")
     tmp = LIB + ".tmp"

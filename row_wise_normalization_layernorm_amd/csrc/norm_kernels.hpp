@@ -18,6 +18,12 @@
 //    short of resident threads"), without its one-pass sum of squares.
 //  * rstd is v_rsq_f32, the one-instruction reciprocal root; gamma/beta are
 //    read once per row group and y leaves the same registers in 128-bit stores.
+//  * Rows may be stored as float32, binary16 or bfloat16 (template T): an
+//    access always carries four elements (16 or 8 bytes), widened exactly to
+//    float32 in registers; statistics, parameters and arithmetic stay float32
+//    and each output is rounded once to T (v_cvt_pk_f16_f32 /
+//    v_cvt_pk_bf16_f32, round to nearest even).  Each row tensor has its own
+//    row stride in elements.
 //
 // Every lane of a wave executes every cross-lane step (lanes with nothing to
 // hold contribute zeros), so DPP sources are always active lanes and every
@@ -27,23 +33,28 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace minorm {
 
 enum : int { OP_LN = 0, OP_RMS = 1 };
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u2 __attribute__((ext_vector_type(2)));
 
-// Kernel arguments (one struct, passed by value).
+// Kernel arguments (one struct, passed by value).  Row tensors hold elements
+// of the kernel's storage type T; ld* are their row strides in elements.
 struct NormParams {
-    const float *x;
+    const void *x;
     const float *p0;   // gamma (LayerNorm) or w (RMSNorm)
     const float *p1;   // beta (LayerNorm); unused by RMSNorm
-    float *y;
+    void *y;
     float *mean;       // LayerNorm only; may be null
     float *rstd;       // may be null
-    const float *r;    // residual added to x before the norm (RES kernels)
-    float *h;          // x + r written out (RES kernels); may be null
+    const void *r;     // residual added to x before the norm (RES kernels)
+    void *h;           // x + r written out (RES kernels); may be null
     int64_t rows;      // rows of this launch
+    int64_t ldx, ldr, ldy, ldh;
     int32_t d;
     float eps;
     float inv_d;       // 1/d rounded to float32
@@ -111,6 +122,73 @@ __device__ __forceinline__ void st1(float *p, float v) {
     else *p = v;
 }
 
+// Storage-typed access: four elements (ldq/stq) or one (lde/ste) of T,
+// widened to / rounded from float32.  float32 goes through the helpers above;
+// a 16-bit quad is one 64-bit access.
+template <typename T, bool NT>
+__device__ __forceinline__ f4 ldq(const T *p) {
+    if constexpr (std::is_same_v<T, float>) {
+        return ld4<NT>(p);
+    } else {
+        typedef T t4 __attribute__((ext_vector_type(4)));
+        u2 raw;
+        if constexpr (NT) raw = __builtin_nontemporal_load(reinterpret_cast<const u2 *>(p));
+        else raw = *reinterpret_cast<const u2 *>(p);
+        return __builtin_convertvector(__builtin_bit_cast(t4, raw), f4);
+    }
+}
+
+template <typename T, bool NT>
+__device__ __forceinline__ float lde(const T *p) {
+    if constexpr (std::is_same_v<T, float>) {
+        return ld1<NT>(p);
+    } else {
+        unsigned short raw;
+        if constexpr (NT) raw = __builtin_nontemporal_load(reinterpret_cast<const unsigned short *>(p));
+        else raw = *reinterpret_cast<const unsigned short *>(p);
+        return (float)__builtin_bit_cast(T, raw);
+    }
+}
+
+template <typename T, bool NT>
+__device__ __forceinline__ void stq(T *p, f4 v) {
+    if constexpr (std::is_same_v<T, float>) {
+        st4<NT>(p, v);
+    } else {
+        typedef T t4 __attribute__((ext_vector_type(4)));
+        const u2 raw = __builtin_bit_cast(u2, __builtin_convertvector(v, t4));
+        if constexpr (NT) __builtin_nontemporal_store(raw, reinterpret_cast<u2 *>(p));
+        else *reinterpret_cast<u2 *>(p) = raw;
+    }
+}
+
+template <typename T, bool NT>
+__device__ __forceinline__ void ste(T *p, float v) {
+    if constexpr (std::is_same_v<T, float>) {
+        st1<NT>(p, v);
+    } else {
+        const unsigned short raw = __builtin_bit_cast(unsigned short, (T)v);
+        if constexpr (NT) __builtin_nontemporal_store(raw, reinterpret_cast<unsigned short *>(p));
+        else *reinterpret_cast<unsigned short *>(p) = raw;
+    }
+}
+
+// the value as stored in T (a rounding and an exact widening; identity for float)
+template <typename T>
+__device__ __forceinline__ f4 as_stored(f4 v) {
+    if constexpr (std::is_same_v<T, float>) {
+        return v;
+    } else {
+        typedef T t4 __attribute__((ext_vector_type(4)));
+        return __builtin_convertvector(__builtin_convertvector(v, t4), f4);
+    }
+}
+template <typename T>
+__device__ __forceinline__ float as_stored(float v) {
+    if constexpr (std::is_same_v<T, float>) return v;
+    else return (float)(T)v;
+}
+
 __device__ __forceinline__ float hsum(f4 v) { return (v.x + v.y) + (v.z + v.w); }
 __device__ __forceinline__ float hsum(float v) { return v; }
 
@@ -128,21 +206,23 @@ __device__ __forceinline__ float rsq(float v) { return __builtin_amdgcn_rsqf(v);
 // ---------------------------------------------------------------------------
 // Held-row kernel.
 //
+//   T      storage type of the row tensors: float, _Float16 or __bf16
 //   OP     OP_LN or OP_RMS
-//   VEC    4: 128-bit accesses (d % 4 == 0, 16-byte-aligned pointers), or
-//          1: 32-bit accesses (any d, any 4-byte alignment)
-//   PEEL   VEC == 4 only: per row, scalar head elements up to the first
-//          16-byte boundary of the row, a 128-bit body, and a scalar tail;
-//          needs x and y congruent mod 16 bytes, any d; gamma/beta are then
-//          read as scalars since their phase follows the row's
+//   VEC    4: quad accesses, four elements (128-bit for float, 64-bit for
+//          the 16-bit types; d % 4 == 0, rows aligned to a quad), or
+//          1: single-element accesses (any d, any element alignment)
+//   PEEL   VEC == 4 only: per row, scalar head elements up to the row's
+//          first quad boundary, a quad body, and a scalar tail; needs every
+//          row tensor in the same phase modulo a quad, any d; gamma/beta are
+//          then read as scalars since their phase follows the row's
 //   LPR    lanes of one wave sharing a row (16, 32, 64); 64 / LPR rows per wave
 //   WPR    waves sharing a row (LPR == 64 when WPR > 1)
 //   Q      accesses held per lane; capacity = VEC * LPR * WPR * Q elements
 //   WAVES  waves per workgroup
 //   NTL/NTS  non-temporal x loads / y stores
 //   RES    residual add fused before the norm: each held value is x + r
-//          (a float32 add), written to h when h is given, and the row is
-//          normalized from those sums
+//          (a float32 add, rounded to T), written to h when h is given, and
+//          the row is normalized from those stored sums
 //   MRG    cross-wave merge: 0 every lane walks all WPR exchanged entries,
 //          1 lane w takes entry w and two 16-lane sums finish the merge;
 //          -1: 1 for 16 waves per row, else 0
@@ -152,10 +232,11 @@ __device__ __forceinline__ float rsq(float v) { return __builtin_amdgcn_rsqf(v);
 //          aligned path only); -1: 1 or 0 by the register budget
 //
 // Lane li of wave rank wr holds access k = li + LPR * (wr + WPR * q),
-// q = 0..Q-1: consecutive lanes touch consecutive 16-byte (or 4-byte) words,
-// so each wave-wide access covers 1 KiB (256 B) of one row contiguously.
-template <int OP, int VEC, bool PEEL, int LPR, int WPR, int Q, int WAVES, bool NTL, bool NTS,
-          int PRE = -1, int MRG = -1, bool RES = false>
+// q = 0..Q-1: consecutive lanes touch consecutive quads (or elements), so
+// each wave-wide access covers 64 quads of one row contiguously (1 KiB of
+// float32, 512 B of a 16-bit type).
+template <typename T, int OP, int VEC, bool PEEL, int LPR, int WPR, int Q, int WAVES, bool NTL,
+          bool NTS, int PRE = -1, int MRG = -1, bool RES = false>
 __global__ __launch_bounds__(WAVES * 64)
 void norm_held(NormParams p)
 {
@@ -214,15 +295,15 @@ void norm_held(NormParams p)
         const int64_t row_raw = (int64_t)blockIdx.x * RPB + rib;
         const bool rv = row_raw < p.rows;
         const int64_t row = rv ? row_raw : p.rows - 1;
-        const float *xr = p.x + row * (int64_t)d;
-        float *yr = p.y + row * (int64_t)d;
-        const float *rr = RES ? p.r + row * (int64_t)d : nullptr;
-        float *hr = (RES && p.h) ? p.h + row * (int64_t)d : nullptr;
+        const T *xr = static_cast<const T *>(p.x) + row * p.ldx;
+        T *yr = static_cast<T *>(p.y) + row * p.ldy;
+        const T *rr = RES ? static_cast<const T *>(p.r) + row * p.ldr : nullptr;
+        T *hr = (RES && p.h) ? static_cast<T *>(p.h) + row * p.ldh : nullptr;
 
         // row geometry: h head scalars, nvec body accesses, t tail scalars
         int h = 0, t = 0, nvec;
         if constexpr (PEEL) {
-            const int mis = (int)((reinterpret_cast<uintptr_t>(xr) >> 2) & 3);
+            const int mis = (int)((reinterpret_cast<uintptr_t>(xr) / sizeof(T)) & 3);
             h = (4 - mis) & 3;
             if (h > d) h = d;
             nvec = (d - h) >> 2;
@@ -249,16 +330,16 @@ void norm_held(NormParams p)
         for (int q = 0; q < Q; ++q) {
             VT raw = VT(0.f);
             if (body) {
-                if constexpr (VEC == 4) raw = ld4<NTL>(xr + h + 4 * kc[q]);
-                else raw = ld1<NTL>(xr + kc[q]);
+                if constexpr (VEC == 4) raw = ldq<T, NTL>(xr + h + 4 * kc[q]);
+                else raw = lde<T, NTL>(xr + kc[q]);
             }
             if constexpr (RES) {
                 VT rres = VT(0.f);
                 if (body) {
-                    if constexpr (VEC == 4) rres = ld4<NTL>(rr + h + 4 * kc[q]);
-                    else rres = ld1<NTL>(rr + kc[q]);
+                    if constexpr (VEC == 4) rres = ldq<T, NTL>(rr + h + 4 * kc[q]);
+                    else rres = lde<T, NTL>(rr + kc[q]);
                 }
-                raw = raw + rres;
+                raw = as_stored<T>(raw + rres);
             }
             v[q] = ok[q] ? raw : VT(0.f);
         }
@@ -271,10 +352,10 @@ void norm_held(NormParams p)
             hi = li < h ? li : 0;
             ti = h + 4 * nvec + li;
             ti = ti < d ? ti : d - 1;
-            float rh = xr[hi], rt = xr[ti];
+            float rh = lde<T, false>(xr + hi), rt = lde<T, false>(xr + ti);
             if constexpr (RES) {
-                rh = rh + rr[hi];
-                rt = rt + rr[ti];
+                rh = as_stored<T>(rh + lde<T, false>(rr + hi));
+                rt = as_stored<T>(rt + lde<T, false>(rr + ti));
             }
             hx = hok ? rh : 0.f;
             tx = tok ? rt : 0.f;
@@ -286,11 +367,11 @@ void norm_held(NormParams p)
 #pragma unroll
                 for (int q = 0; q < Q; ++q) {
                     if (!ok[q]) continue;
-                    if constexpr (VEC == 4) st4<NTS>(hr + h + 4 * kc[q], v[q]);
-                    else st1<NTS>(hr + kc[q], v[q]);
+                    if constexpr (VEC == 4) stq<T, NTS>(hr + h + 4 * kc[q], v[q]);
+                    else ste<T, NTS>(hr + kc[q], v[q]);
                 }
-                if (hok) hr[hi] = hx;
-                if (tok) hr[ti] = tx;
+                if (hok) ste<T, false>(hr + hi, hx);
+                if (tok) ste<T, false>(hr + ti, tx);
             }
         }
 
@@ -437,8 +518,8 @@ void norm_held(NormParams p)
             if constexpr (OP == OP_LN) o = (v[q] - mu) * rs * gq + bq;
             else o = v[q] * gq * rs;
             if (ok[q]) {
-                if constexpr (VEC == 4) st4<NTS>(yr + h + 4 * kc[q], o);
-                else st1<NTS>(yr + kc[q], o);
+                if constexpr (VEC == 4) stq<T, NTS>(yr + h + 4 * kc[q], o);
+                else ste<T, NTS>(yr + kc[q], o);
             }
         }
         if constexpr (PEEL) {
@@ -447,8 +528,8 @@ void norm_held(NormParams p)
             const float bt = (OP == OP_LN) ? p.p1[ti] : 0.f;
             const float oh = (OP == OP_LN) ? (hx - mu) * rs * gh + bh : hx * gh * rs;
             const float ot = (OP == OP_LN) ? (tx - mu) * rs * gt + bt : tx * gt * rs;
-            if (hok) yr[hi] = oh;
-            if (tok) yr[ti] = ot;
+            if (hok) ste<T, false>(yr + hi, oh);
+            if (tok) ste<T, false>(yr + ti, ot);
         }
         if (rv && wr == 0 && li == 0) {
             if (OP == OP_LN && p.mean) p.mean[row] = mu;
@@ -475,12 +556,12 @@ __device__ __forceinline__ float block_sum(float v, float (*red)[WAVES], int &sl
     return t;
 }
 
-template <int OP, int VEC, int WAVES, int U, bool RES = false>
+template <typename T, int OP, int VEC, int WAVES, int U, bool RES = false>
 __global__ __launch_bounds__(WAVES * 64)
 void norm_looped(NormParams p)
 {
     using VT = typename std::conditional<VEC == 4, f4, float>::type;
-    constexpr int T = WAVES * 64;
+    constexpr int NT = WAVES * 64;  // threads per workgroup
     __shared__ float red[2][WAVES];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -489,16 +570,20 @@ void norm_looped(NormParams p)
     const int nvec = (VEC == 4) ? (d >> 2) : d;
     int slot = 0;
 
-    auto load = [&](const float *xr, int k) -> VT {
-        if constexpr (VEC == 4) return ld4<false>(xr + 4 * k);
-        else return xr[k];
+    auto load = [&](const T *xr, int k) -> VT {
+        if constexpr (VEC == 4) return ldq<T, false>(xr + 4 * k);
+        else return lde<T, false>(xr + k);
+    };
+    auto param = [&](const float *pr, int k) -> VT {
+        if constexpr (VEC == 4) return ld4<false>(pr + 4 * k);
+        else return pr[k];
     };
 
     for (int64_t row = blockIdx.x; row < p.rows; row += gridDim.x) {
-        const float *xr = p.x + row * (int64_t)d;
-        float *yr = p.y + row * (int64_t)d;
-        const float *rr = RES ? p.r + row * (int64_t)d : nullptr;
-        float *hr = (RES && p.h) ? p.h + row * (int64_t)d : nullptr;
+        const T *xr = static_cast<const T *>(p.x) + row * p.ldx;
+        T *yr = static_cast<T *>(p.y) + row * p.ldy;
+        const T *rr = RES ? static_cast<const T *>(p.r) + row * p.ldr : nullptr;
+        T *hr = (RES && p.h) ? static_cast<T *>(p.h) + row * p.ldh : nullptr;
         float mu = 0.f, rs;
         // the value at access k: x, or x + r; once pass 1 has written h (each
         // thread re-reads only what it stored itself) later passes read it
@@ -506,7 +591,7 @@ void norm_looped(NormParams p)
         auto value = [&](int k, bool after_pass1) -> VT {
             if constexpr (RES) {
                 if (after_pass1 && hr) return load(hr, k);
-                return load(xr, k) + load(rr, k);
+                return as_stored<T>(load(xr, k) + load(rr, k));
             } else {
                 return load(xr, k);
             }
@@ -514,21 +599,21 @@ void norm_looped(NormParams p)
 
         // pass 1: sum (LayerNorm) or sum of squares (RMSNorm)
         float s = 0.f;
-        for (int k0 = 0; k0 < nvec; k0 += T * U) {
+        for (int k0 = 0; k0 < nvec; k0 += NT * U) {
             VT v[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int k = k0 + tid + T * u;
+                const int k = k0 + tid + NT * u;
                 v[u] = k < nvec ? value(k, false) : VT(0.f);
             }
             if constexpr (RES) {
                 if (hr) {
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
-                        const int k = k0 + tid + T * u;
+                        const int k = k0 + tid + NT * u;
                         if (k >= nvec) continue;
-                        if constexpr (VEC == 4) st4<false>(hr + 4 * k, v[u]);
-                        else hr[k] = v[u];
+                        if constexpr (VEC == 4) stq<T, false>(hr + 4 * k, v[u]);
+                        else ste<T, false>(hr + k, v[u]);
                     }
                 }
             }
@@ -541,12 +626,12 @@ void norm_looped(NormParams p)
             mu = S * p.inv_d;
             // pass 2: squared deviations around the mean
             float m = 0.f;
-            for (int k0 = 0; k0 < nvec; k0 += T * U) {
+            for (int k0 = 0; k0 < nvec; k0 += NT * U) {
                 VT v[U];
                 bool ok[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const int k = k0 + tid + T * u;
+                    const int k = k0 + tid + NT * u;
                     ok[u] = k < nvec;
                     v[u] = ok[u] ? value(k, true) : VT(0.f);
                 }
@@ -560,24 +645,24 @@ void norm_looped(NormParams p)
         }
 
         // final pass: normalize and store
-        for (int k0 = 0; k0 < nvec; k0 += T * U) {
+        for (int k0 = 0; k0 < nvec; k0 += NT * U) {
             VT v[U];
             bool ok[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int k = k0 + tid + T * u;
+                const int k = k0 + tid + NT * u;
                 ok[u] = k < nvec;
                 v[u] = ok[u] ? value(k, true) : VT(0.f);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 if (!ok[u]) continue;
-                const int k = k0 + tid + T * u;
+                const int k = k0 + tid + NT * u;
                 VT o;
-                if constexpr (OP == OP_LN) o = (v[u] - mu) * rs * load(p.p0, k) + load(p.p1, k);
-                else o = v[u] * load(p.p0, k) * rs;
-                if constexpr (VEC == 4) st4<false>(yr + 4 * k, o);
-                else yr[k] = o;
+                if constexpr (OP == OP_LN) o = (v[u] - mu) * rs * param(p.p0, k) + param(p.p1, k);
+                else o = v[u] * param(p.p0, k) * rs;
+                if constexpr (VEC == 4) stq<T, false>(yr + 4 * k, o);
+                else ste<T, false>(yr + k, o);
             }
         }
         if (tid == 0) {
@@ -585,36 +670,6 @@ void norm_looped(NormParams p)
             if (p.rstd) p.rstd[row] = rs;
         }
     }
-}
-
-// ---------------------------------------------------------------------------
-// Streaming copy (calibration): U 128-bit accesses per lane per step, with
-// the same non-temporal hints as the normalization kernels.
-template <int U>
-__global__ __launch_bounds__(256)
-void copy_f4(const float *src, float *dst, int64_t n4)
-{
-    const int64_t stride = (int64_t)gridDim.x * 256 * U;
-    for (int64_t base = (int64_t)blockIdx.x * 256 * U + threadIdx.x; base < n4; base += stride) {
-        f4 v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t i = base + 256 * u;
-            v[u] = i < n4 ? ld4<true>(src + 4 * i) : f4(0.f);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t i = base + 256 * u;
-            if (i < n4) st4<true>(dst + 4 * i, v[u]);
-        }
-    }
-}
-
-__global__ __launch_bounds__(256)
-void copy_f1(const float *src, float *dst, int64_t n)
-{
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) dst[i] = src[i];
 }
 
 }  // namespace minorm

@@ -1,0 +1,100 @@
+// variant_table.hpp — the compiled kernel variants of libmi_norm.so.
+//
+// Each storage type's variants are instantiated in a translation unit of
+// their own (variants_f32.hip, variants_f16.hip, variants_bf16.hip), so the
+// three compile in parallel; mi_norm.hip walks the three tables as one.
+#pragma once
+
+#include <climits>
+#include <cstdint>
+
+#include "mi_norm.h"
+#include "norm_kernels.hpp"
+
+namespace minorm {
+
+struct Variant {
+    const char *name;
+    mi_norm_variant_info info;
+    const void *fn;
+};
+
+struct VariantTable {
+    const Variant *v;
+    int n;
+};
+
+extern const VariantTable kTableF32, kTableF16, kTableBF16;
+
+constexpr int64_t kUnbounded = INT64_MAX;
+
+// ABI op codes: bit 0 picks the normalization, op >= 2 fuses the residual add
+constexpr int kOps = 4;
+constexpr int kop(int op) { return op & 1; }       // OP_LN or OP_RMS
+constexpr bool kres(int op) { return op >= 2; }
+
+}  // namespace minorm
+
+// Every held variant streams x (and r) in and y (and h) out with
+// non-temporal hints and reads gamma/beta in the output pass (norm_held's
+// NTL/NTS/PRE); the cross-wave merge follows norm_held's default.
+// T is the storage type, DT its mi_norm_dtype, OPN the name prefix.
+#define MI_HELD(T, DT, OPC, OPN, VEC, PEEL, LPR, WPR, Q, WAVES)                                \
+    Variant{OPN "_" #VEC "_p" #PEEL "_l" #LPR "_w" #WPR "_q" #Q "_b" #WAVES,                  \
+            mi_norm_variant_info{OPC, DT, VEC, PEEL, 0, LPR, WPR, Q, WAVES,                     \
+                                 (WPR == 1) ? WAVES * (64 / LPR) : WAVES / WPR,                 \
+                                 (int64_t)VEC * LPR * WPR * Q, (VEC == 4 && !PEEL) ? 1 : 0},    \
+            reinterpret_cast<const void *>(&norm_held<T, kop(OPC), VEC, (PEEL != 0), LPR, WPR,  \
+                                                      Q, WAVES, true, true, 0, -1, kres(OPC)>)}
+
+// the same shape with 4 (or 8) and with 16 waves per workgroup
+#define MI_HELD2(T, DT, OPC, OPN, VEC, PEEL, LPR, WPR, Q, WSMALL)                              \
+    MI_HELD(T, DT, OPC, OPN, VEC, PEEL, LPR, WPR, Q, WSMALL),                                   \
+    MI_HELD(T, DT, OPC, OPN, VEC, PEEL, LPR, WPR, Q, 16)
+
+#define MI_LOOP(T, DT, OPC, OPN, VEC, WAVES, U)                                                \
+    Variant{OPN "_" #VEC "_loop_b" #WAVES "_u" #U,                                              \
+            mi_norm_variant_info{OPC, DT, VEC, 0, 1, 64, WAVES, U, WAVES, 1, kUnbounded,        \
+                                 VEC == 4 ? 1 : 0},                                             \
+            reinterpret_cast<const void *>(&norm_looped<T, kop(OPC), VEC, WAVES, U, kres(OPC)>)}
+
+// every (waves per row, slots) pair of a quad path: slots 1, 2, 3, 4, 6, 8
+// for 1, 2, 4, 8 and 16 waves per row
+#define MI_SLOTS(T, DT, OPC, OPN, PEEL, WPR, WSMALL)                                           \
+    MI_HELD2(T, DT, OPC, OPN, 4, PEEL, 64, WPR, 1, WSMALL),                                     \
+    MI_HELD2(T, DT, OPC, OPN, 4, PEEL, 64, WPR, 2, WSMALL),                                     \
+    MI_HELD2(T, DT, OPC, OPN, 4, PEEL, 64, WPR, 3, WSMALL),                                     \
+    MI_HELD2(T, DT, OPC, OPN, 4, PEEL, 64, WPR, 4, WSMALL),                                     \
+    MI_HELD2(T, DT, OPC, OPN, 4, PEEL, 64, WPR, 6, WSMALL),                                     \
+    MI_HELD2(T, DT, OPC, OPN, 4, PEEL, 64, WPR, 8, WSMALL)
+#define MI_SLOTS16(T, DT, OPC, OPN, PEEL)                                                      \
+    MI_HELD(T, DT, OPC, OPN, 4, PEEL, 64, 16, 1, 16), MI_HELD(T, DT, OPC, OPN, 4, PEEL, 64, 16, 2, 16), \
+    MI_HELD(T, DT, OPC, OPN, 4, PEEL, 64, 16, 3, 16), MI_HELD(T, DT, OPC, OPN, 4, PEEL, 64, 16, 4, 16), \
+    MI_HELD(T, DT, OPC, OPN, 4, PEEL, 64, 16, 6, 16), MI_HELD(T, DT, OPC, OPN, 4, PEEL, 64, 16, 8, 16)
+#define MI_PATHQ(T, DT, OPC, OPN, PEEL)                                                        \
+    MI_SLOTS(T, DT, OPC, OPN, PEEL, 1, 4), MI_SLOTS(T, DT, OPC, OPN, PEEL, 2, 4),               \
+    MI_SLOTS(T, DT, OPC, OPN, PEEL, 4, 4), MI_SLOTS(T, DT, OPC, OPN, PEEL, 8, 8),               \
+    MI_SLOTS16(T, DT, OPC, OPN, PEEL)
+
+#define MI_OP_TABLE(T, DT, OPC, OPN)                                                           \
+    /* quads, aligned, d % 4 == 0; 16 or 32 lanes per row for narrow rows */                    \
+    MI_HELD2(T, DT, OPC, OPN, 4, 0, 16, 1, 1, 4), MI_HELD2(T, DT, OPC, OPN, 4, 0, 32, 1, 1, 4), \
+    MI_PATHQ(T, DT, OPC, OPN, 0),                                                               \
+    /* quad body with a per-row scalar head and tail: any d, rows in one phase */              \
+    MI_PATHQ(T, DT, OPC, OPN, 1),                                                               \
+    /* single-element accesses: any d, any element alignment */                                \
+    MI_HELD2(T, DT, OPC, OPN, 1, 0, 16, 1, 1, 4), MI_HELD2(T, DT, OPC, OPN, 1, 0, 32, 1, 1, 4), \
+    MI_HELD2(T, DT, OPC, OPN, 1, 0, 64, 1, 1, 4), MI_HELD2(T, DT, OPC, OPN, 1, 0, 64, 1, 2, 4), \
+    MI_HELD2(T, DT, OPC, OPN, 1, 0, 64, 1, 4, 4), MI_HELD2(T, DT, OPC, OPN, 1, 0, 64, 1, 8, 4), \
+    MI_HELD2(T, DT, OPC, OPN, 1, 0, 64, 4, 4, 4), MI_HELD2(T, DT, OPC, OPN, 1, 0, 64, 4, 8, 4), \
+    MI_HELD2(T, DT, OPC, OPN, 1, 0, 64, 8, 8, 8),                                               \
+    MI_HELD(T, DT, OPC, OPN, 1, 0, 64, 16, 8, 16), MI_HELD(T, DT, OPC, OPN, 1, 0, 64, 16, 16, 16), \
+    /* streamed rows, any width */                                                             \
+    MI_LOOP(T, DT, OPC, OPN, 4, 4, 4), MI_LOOP(T, DT, OPC, OPN, 1, 4, 8)
+
+// the four operations of one storage type; SFX is the dtype's name suffix
+#define MI_DTYPE_TABLE(T, DT, SFX)                                                             \
+    MI_OP_TABLE(T, DT, MI_NORM_OP_LAYERNORM, "ln" SFX),                                         \
+    MI_OP_TABLE(T, DT, MI_NORM_OP_RMSNORM, "rms" SFX),                                          \
+    MI_OP_TABLE(T, DT, MI_NORM_OP_ADD_LAYERNORM, "addln" SFX),                                  \
+    MI_OP_TABLE(T, DT, MI_NORM_OP_ADD_RMSNORM, "addrms" SFX)

@@ -1,6 +1,8 @@
 """The C ABI on the CPU: the library loads, exports what the header declares,
 rejects bad arguments before touching a device, and its dispatcher picks an
-eligible variant for every width and layout.  No kernel is launched here."""
+eligible variant for every width, storage type, stride and layout.  No kernel
+is launched here: the addresses below are fake, so the module skips itself
+where a GPU is visible."""
 import ctypes
 import math
 import os
@@ -19,6 +21,9 @@ X, Y, G, BETA = 0x7F0000000000, 0x7F0100000000, 0x7F0200000000, 0x7F0300000000
 
 @pytest.fixture(scope="module")
 def L():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-logic tests pass fake device addresses; run them where no GPU is visible")
     if not os.path.exists(B.LIB_PATH):
         import __graft_entry__
         __graft_entry__.build()
@@ -129,7 +134,8 @@ R_, H_ = 0x7F0400000000, 0x7F0500000000
     (X, R_, G, BETA, Y, Y, 4, 8, 1e-5, None, None, None),        # h == y
     (X, R_, G, BETA, Y, Y + 16, 4, 8, 1e-5, None, None, None),   # h overlaps y
     (X, R_, G, BETA, Y, R_ + 4, 4, 8, 1e-5, None, None, None),   # h partially overlaps r
-    (X, X + 8, G, BETA, Y, H_, 4, 8, 1e-5, None, None, None),    # r partially overlaps x
+    (X, R_, G, BETA, Y, X + 8, 4, 8, 1e-5, None, None, None),    # h partially overlaps x
+    (X, R_, G, BETA, R_ + 4, H_, 4, 8, 1e-5, None, None, None),  # y partially overlaps r
     (X, R_ + 2, G, BETA, Y, H_, 4, 8, 1e-5, None, None, None),   # r not 4-byte aligned
     (X, R_, Y + 64, BETA, Y, H_, 4, 8, 1e-5, None, None, None),  # gamma inside y
     (X, R_, G, BETA, Y, BETA, 4, 8, 1e-5, None, None, None),     # h over beta
@@ -165,11 +171,11 @@ def _infos():
             for i in range(mn.mi_norm_variant_count())]
 
 
-def _prob(op, rows, d, x=X, y=Y, g=G, b=BETA, r=R_, h=H_):
+def _prob(op, rows, d, x=X, y=Y, g=G, b=BETA, r=R_, h=H_, **kw):
     add = op >= mn.OP_ADD_LAYERNORM
     ln = op in (mn.OP_LAYERNORM, mn.OP_ADD_LAYERNORM)
     return mn.problem(op, rows, d, x, y, g, b if ln else None, r=r if add else None,
-                      h=h if add else None)
+                      h=h if add else None, **kw)
 
 
 def test_select_rejects_invalid_problems(L):
@@ -179,6 +185,11 @@ def test_select_rejects_invalid_problems(L):
     assert L.mi_norm_select(None) == -1
 
 
+DTYPES = (mn.MI_NORM_F32, mn.MI_NORM_F16, mn.MI_NORM_BF16)
+DTSFX = {mn.MI_NORM_F32: "", mn.MI_NORM_F16: "f16_", mn.MI_NORM_BF16: "bf16_"}
+ESIZE = {mn.MI_NORM_F32: 4, mn.MI_NORM_F16: 2, mn.MI_NORM_BF16: 2}
+
+
 def test_variant_table_is_consistent(L):
     infos = _infos()
     names = [n for _, n, _ in infos]
@@ -186,7 +197,9 @@ def test_variant_table_is_consistent(L):
     assert mn.mi_norm_variant_name(len(infos)) is None
     assert mn.mi_norm_variant_name(-1) is None
     for i, n, v in infos:
-        assert n.startswith(PREFIX[v["op"]]), n
+        assert n.startswith(PREFIX[v["op"]] + DTSFX[v["dtype"]]), n
+        if v["dtype"] == mn.MI_NORM_F32:
+            assert "f16_" not in n, n
         if v["looped"]:
             assert v["max_d"] == 2**63 - 1 and v["rows_per_block"] == 1
             continue
@@ -199,9 +212,14 @@ def test_variant_table_is_consistent(L):
         assert v["waves_per_block"] * 64 <= 1024
         assert v["needs_aligned"] == (1 if v["vec"] == 4 and not v["peel"] else 0)
     assert {v["op"] for _, _, v in infos} == set(OPS)
-    # every operation has the same family of shapes
-    shapes = {op: sorted(n[len(PREFIX[op]):] for _, n, v in infos if v["op"] == op) for op in OPS}
-    assert shapes[0] == shapes[1] == shapes[2] == shapes[3]
+    assert {v["dtype"] for _, _, v in infos} == set(DTYPES)
+    # every operation and storage type has the same family of shapes
+    shapes = {(op, dt): sorted(n[len(PREFIX[op] + DTSFX[dt]):] for _, n, v in infos
+                               if v["op"] == op and v["dtype"] == dt) for op in OPS for dt in DTYPES}
+    first = shapes[(0, 0)]
+    assert first and all(s == first for s in shapes.values())
+    # float32 ids come first, so they do not move when other types are added
+    assert [v["dtype"] for _, _, v in infos] == sorted(v["dtype"] for _, _, v in infos)
 
 
 WIDTHS = sorted({1, 2, 3, 4, 5, 7, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 255, 256,
@@ -210,22 +228,24 @@ WIDTHS = sorted({1, 2, 3, 4, 5, 7, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 1
                  32768, 32769, 65536, 100003, 2**20})
 
 
+@pytest.mark.parametrize("dt", DTYPES)
 @pytest.mark.parametrize("op", OPS)
 @pytest.mark.parametrize("layout", ["aligned", "same_phase", "different_phase"])
-def test_dispatch_picks_an_eligible_covering_variant(L, op, layout):
+def test_dispatch_picks_an_eligible_covering_variant(L, op, layout, dt):
+    e = ESIZE[dt]
     if layout == "aligned":
         ptrs = dict(x=X, y=Y, r=R_, h=H_)
     elif layout == "same_phase":
-        ptrs = dict(x=X + 4, y=Y + 4, r=R_ + 4, h=H_ + 4)
+        ptrs = dict(x=X + e, y=Y + e, r=R_ + e, h=H_ + e)
     else:
-        ptrs = dict(x=X + 4, y=Y + 8, r=R_ + 4, h=H_ + 4)
+        ptrs = dict(x=X + e, y=Y + 2 * e, r=R_ + e, h=H_ + e)
     for rows in (64, 4096):
         for d in WIDTHS:
-            p = _prob(op, rows, d, **ptrs)
+            p = _prob(op, rows, d, dtype=dt, **ptrs)
             vid = mn.mi_norm_select(p)
             assert vid >= 0, (op, d, layout)
             v = mn.mi_norm_variant_get_info(vid)
-            assert v["op"] == op
+            assert v["op"] == op and v["dtype"] == dt
             assert mn.mi_norm_eligible(vid, p), (d, layout, mn.mi_norm_variant_name(vid))
             assert v["looped"] or v["max_d"] >= d
             if layout == "aligned" and d % 4 == 0:
@@ -288,13 +308,87 @@ def test_rows_spread_over_more_waves_when_few(L):
 
 def test_eligibility_rules(L):
     for i, n, v in _infos():
-        op = v["op"]
+        op, dt = v["op"], v["dtype"]
         other = {0: 1, 1: 0, 2: 3, 3: 2}[op]
-        assert not mn.mi_norm_eligible(i, _prob(other, 16, 64))
+        assert not mn.mi_norm_eligible(i, _prob(other, 16, 64, dtype=dt))
+        assert not mn.mi_norm_eligible(i, _prob(op, 16, 64, dtype=(dt + 1) % 3))
         if v["needs_aligned"]:
-            assert not mn.mi_norm_eligible(i, _prob(op, 16, 64, x=X + 4))
-            assert not mn.mi_norm_eligible(i, _prob(op, 16, 6))
+            assert not mn.mi_norm_eligible(i, _prob(op, 16, 64, x=X + ESIZE[dt], dtype=dt))
+            assert not mn.mi_norm_eligible(i, _prob(op, 16, 6, dtype=dt))
+            assert not mn.mi_norm_eligible(i, _prob(op, 16, 64, ldx=66, dtype=dt))
         if not v["looped"]:
-            assert not mn.mi_norm_eligible(i, _prob(op, 16, v["max_d"] + 4))
+            assert not mn.mi_norm_eligible(i, _prob(op, 16, v["max_d"] + 4, dtype=dt))
     assert not mn.mi_norm_eligible(-1, _prob(0, 16, 8))
     assert L.mi_layernorm_fwd_variant(10**6, X, G, BETA, Y, 4, 8, 1e-5, None, None, None) == mn.MI_NORM_ERR_INVALID
+
+
+# --- storage types, row strides and the general call --------------------------
+
+def _check(op=mn.OP_LAYERNORM, rows=4, d=8, **kw):
+    return mn.mi_norm_check(_prob(op, rows, d, **kw))
+
+
+def test_general_call_validation(L):
+    OK, BAD = mn.MI_NORM_OK, mn.MI_NORM_ERR_INVALID
+    assert _check() == OK
+    assert L.mi_norm_check(None) == BAD and L.mi_norm_fwd(None, None) == BAD
+    assert _check(dtype=3) == BAD and _check(dtype=-1) == BAD
+    assert _check(dtype=mn.MI_NORM_BF16, x=X + 2) == OK          # 2-byte aligned is enough
+    assert _check(dtype=mn.MI_NORM_BF16, x=X + 1) == BAD
+    assert _check(dtype=mn.MI_NORM_F32, x=X + 2) == BAD
+    assert _check(ldx=7) == BAD and _check(ldy=-8) == BAD          # stride below d, negative
+    assert _check(ldx=8, ldy=0) == OK and _check(ldx=1000, ldy=12) == OK
+    assert _check(rows=1, ldx=3) == OK                             # one row: no stride is used
+    assert _check(rows=2**40, d=8, ldx=2**30) == BAD               # extent overflows
+    assert _check(eps=float("nan")) == BAD
+    assert _check(mean=0x7F0600000000 + 2) == BAD                  # misaligned statistics
+    assert _check(op=mn.OP_RMSNORM, b=None, mean=X) == OK          # RMSNorm ignores mean
+    assert _check(mean=X + 4) == BAD                               # mean inside x
+    assert _check(mean=0x7F0600000000, rstd=0x7F0600000000 + 8) == BAD   # mean meets rstd
+    assert _check(rstd=G) == BAD                                   # rstd over gamma
+
+
+def test_strided_aliasing_is_exact_for_equal_strides(L):
+    OK, BAD = mn.MI_NORM_OK, mn.MI_NORM_ERR_INVALID
+    d, ld = 8, 16
+    # y interleaved with x in one [rows, 2d] buffer: no shared element
+    assert _check(d=d, x=X, y=X + 4 * d, ldx=ld, ldy=ld) == OK
+    assert _check(d=d, x=X + 4 * d, y=X, ldx=ld, ldy=ld) == OK
+    # one element off: the rows overlap
+    assert _check(d=d, x=X, y=X + 4 * (d - 1), ldx=ld, ldy=ld) == BAD
+    assert _check(d=d, x=X, y=X + 4 * (d + 1), ldx=ld, ldy=ld) == BAD   # y's row runs into x's next row
+    # in place needs the same stride
+    assert _check(d=d, x=X, y=X, ldx=ld, ldy=ld) == OK
+    assert _check(d=d, x=X, y=X, ldx=ld, ldy=d) == BAD
+    # different strides: any overlap of the extents is refused
+    assert _check(d=d, x=X, y=X + 4 * d, ldx=ld, ldy=ld + 4) == BAD
+    # inputs may share memory: x and r interleaved, or even the same tensor
+    add = mn.OP_ADD_LAYERNORM
+    assert _check(op=add, d=d, x=X, r=X + 4 * d, ldx=ld, ldr=ld, h=None) == OK
+    assert _check(op=add, d=d, x=X, r=X + 4, h=None) == OK
+    assert _check(op=add, d=d, x=X, r=X, h=None) == OK
+    # y and h never share an element, and y may not be h
+    assert _check(op=add, d=d, y=Y, h=Y + 4 * d, ldy=ld, ldh=ld) == OK
+    assert _check(op=add, d=d, y=Y, h=Y, ldy=ld, ldh=ld) == BAD
+
+
+def test_strides_and_types_decide_the_layout(L):
+    info = lambda **kw: mn.mi_norm_variant_get_info(mn.mi_norm_select(_prob(0, 4096, 768, **kw)))
+    name = lambda **kw: mn.mi_norm_variant_name(mn.mi_norm_select(_prob(0, 4096, 768, **kw)))
+    assert name(dtype=mn.MI_NORM_BF16) == "ln_bf16_4_p0_l64_w1_q3_b16"
+    assert name(dtype=mn.MI_NORM_F16) == "ln_f16_4_p0_l64_w1_q3_b16"
+    # a quad of a 16-bit type is 8 bytes: 8-byte alignment is enough for it
+    assert info(dtype=mn.MI_NORM_BF16, x=X + 8, y=Y + 8)["needs_aligned"] == 1
+    assert info(dtype=mn.MI_NORM_F32, x=X + 8, y=Y + 8)["peel"] == 1
+    # strides that keep every row on a quad boundary keep the quad path
+    assert info(ldx=1024, ldy=776)["needs_aligned"] == 1
+    # a stride off the quad grid: rows change phase, together if all strides agree mod 4
+    assert info(ldx=770, ldy=770)["peel"] == 1
+    assert info(ldx=770, ldy=768)["vec"] == 1
+
+
+def test_named_calls_equal_the_general_call(L):
+    p = _prob(mn.OP_ADD_RMSNORM, 4096, 768, dtype=mn.MI_NORM_F32)
+    assert mn.mi_norm_variant_name(mn.mi_norm_select(p)) == "addrms_4_p0_l64_w1_q3_b16"
+    assert L.mi_add_rmsnorm_fwd(X, R_, G, Y, Y, 4, 8, 1e-5, None, None) == mn.MI_NORM_ERR_INVALID
+    assert mn.mi_norm_check(_prob(mn.OP_ADD_RMSNORM, 4, 8, h=Y)) == mn.MI_NORM_ERR_INVALID
