@@ -82,6 +82,27 @@ int mi_bench_add_rmsnorm_loop(const float *const *xs, const float *const *rs, co
     return MI_NORM_OK;
 }
 
+// Any operation, storage type and row strides through mi_norm_fwd: *base
+// holds everything but the per-set row and statistics pointers (rs, hs,
+// means, rstds may be NULL).
+int mi_bench_norm_loop(const mi_norm_problem *base, const void *const *xs, const void *const *rs,
+                       void *const *ys, void *const *hs, float *const *means, float *const *rstds,
+                       int nsets, int steps, int variant, hipStream_t stream) {
+    mi_norm_problem p = *base;
+    for (int s = 0; s < steps; ++s) {
+        const int k = s % nsets;
+        p.x = xs[k];
+        p.r = rs ? rs[k] : nullptr;
+        p.y = ys[k];
+        p.h = hs ? hs[k] : nullptr;
+        p.mean = means ? means[k] : nullptr;
+        p.rstd = rstds ? rstds[k] : nullptr;
+        const mi_norm_status st = variant < 0 ? mi_norm_fwd(&p, stream) : mi_norm_fwd_variant(variant, &p, stream);
+        if (st != MI_NORM_OK) return st;
+    }
+    return MI_NORM_OK;
+}
+
 int mi_bench_copy_loop(const float *const *srcs, float *const *dsts, int nsets, int64_t n, int steps,
                        hipStream_t stream) {
     for (int s = 0; s < steps; ++s) {

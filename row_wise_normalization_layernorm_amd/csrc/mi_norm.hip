@@ -5,9 +5,10 @@
 // "LayerNorm [4096,768] is about 10% behind Triton's kernel": the row kernel
 // covered widths up to a cap, a pair kernel the next range, and wide rows fell
 // back; the fallback cost 41% at 4096 until the cap was raised).  Here every
-// width has a held-row variant up to 32768 elements (quad path), beyond
+// width has a held-row variant up to 32768 float32 elements (65536 of a
+// 16-bit type: the 16-byte vector path), beyond
 // which a streamed-row kernel takes over, and widths that are not a multiple
-// of four keep quad access through a per-row peel instead of a scalar
+// of the vector width keep vector access through a per-row peel instead of a scalar
 // fallback ("Rewriting the layer norm and matmul kernels": the scalar kernel
 // stayed for those widths).
 #include <hip/hip_runtime.h>
@@ -89,6 +90,8 @@ inline bool aligned(const void *p, uintptr_t a) { return (addr(p) & (a - 1)) == 
 inline bool al16(const void *p) { return aligned(p, 16); }
 inline bool al4(const void *p) { return aligned(p, 4); }
 inline int64_t esize(int dtype) { return dtype == MI_NORM_F32 ? 4 : 2; }
+// elements per vector access of the vector paths: 16 bytes of any storage type
+inline int64_t vwidth(int dtype) { return 16 / esize(dtype); }
 
 // Fewest workgroups that still cover every CU: of the variants with this
 // shape, the one with the most waves per workgroup whose grid has at least
@@ -127,17 +130,19 @@ int pick_q(int64_t n, int64_t cap_per_slot, const int *qs, int nq) {
     return 0;
 }
 
-// Waves per row and slots for a row of nvec quad accesses (wpr = 0 when the
+// Waves per row and slots for a row of nvec vector accesses (wpr = 0 when the
 // row is too wide to hold).  About four accesses per lane measured best
 // across widths (more per lane cut occupancy, fewer add waves and exchange
 // traffic); with few rows, a row is spread over more waves until the grid
 // holds 4096 waves, as long as every wave keeps one full access per lane.
-void shape_quads(int64_t nvec, int64_t rows, int &wpr, int &q) {
+// Slots above six are only ever needed at 16 waves per row; the peeled
+// 16-bit path has none there (max_slots 6).
+void shape_vectors(int64_t nvec, int64_t rows, int &wpr, int &q, int max_slots = 8) {
     static const int qs[] = {1, 2, 3, 4, 6, 8};
     wpr = 1;
     while (wpr < 16 && 64 * wpr * 4 < nvec) wpr *= 2;
     while (wpr < 16 && rows * wpr < 4096 && nvec >= 64 * 2 * wpr) wpr *= 2;
-    q = pick_q(nvec, 64 * wpr, qs, 6);
+    q = pick_q(nvec, 64 * wpr, qs, max_slots >= 8 ? 6 : 5);
     if (q == 0) wpr = 0;
 }
 
@@ -177,20 +182,20 @@ Rows rows_of(const mi_norm_problem &P) {
 }
 
 struct Layout {
-    bool aq;       // quad path: rows and strides quad-aligned, params 16 B, d % 4 == 0
-    bool peel_ok;  // every row tensor in x's phase within a quad, on every row
+    bool aq;       // vector path: rows and strides on 16-byte vectors, params 16 B, d % W == 0
+    bool peel_ok;  // every row tensor in x's phase within a vector, on every row
 };
 
 Layout layout_of(const mi_norm_problem &P) {
     const Rows R = rows_of(P);
-    const int64_t es = esize(P.dtype);
-    Layout L{P.d % 4 == 0 && al16(P.params0) && (kop(P.op) == OP_RMS || al16(P.params1)), true};
-    const int64_t phase_x = (int64_t)((addr(P.x) / es) & 3);
+    const int64_t es = esize(P.dtype), W = vwidth(P.dtype);
+    Layout L{P.d % W == 0 && al16(P.params0) && (kop(P.op) == OP_RMS || al16(P.params1)), true};
+    const int64_t phase_x = (int64_t)((addr(P.x) / es) % W);
     for (int i = 0; i < 4; ++i) {
         if (!R.p[i]) continue;
-        L.aq = L.aq && aligned(R.p[i], (uintptr_t)(4 * es)) && R.ld[i] % 4 == 0;
-        L.peel_ok = L.peel_ok && (int64_t)((addr(R.p[i]) / es) & 3) == phase_x &&
-                    (R.ld[i] - R.ld[0]) % 4 == 0;
+        L.aq = L.aq && al16(R.p[i]) && R.ld[i] % W == 0;
+        L.peel_ok = L.peel_ok && (int64_t)((addr(R.p[i]) / es) % W) == phase_x &&
+                    (R.ld[i] - R.ld[0]) % W == 0;
     }
     return L;
 }
@@ -221,18 +226,19 @@ int select_variant(const mi_norm_problem &P) {
     const Layout L = layout_of(P);
     const int64_t d = P.d, rows = P.rows;
     const int op = P.op, dt = P.dtype;
+    const int W = (int)vwidth(dt);
     int lpr, wpr, q;
     if (L.aq) {
-        const int64_t nvec = d / 4;
-        if (nvec <= 16) return find(op, dt, rows, 4, 0, 0, 16, 1, 1);
-        if (nvec <= 32) return find(op, dt, rows, 4, 0, 0, 32, 1, 1);
-        shape_quads(nvec, rows, wpr, q);
-        if (wpr) return find(op, dt, rows, 4, 0, 0, 64, wpr, q);
-        return find(op, dt, rows, 4, 0, 1, 0, 0, 0);
+        const int64_t nvec = d / W;
+        if (nvec <= 16) return find(op, dt, rows, W, 0, 0, 16, 1, 1);
+        if (nvec <= 32) return find(op, dt, rows, W, 0, 0, 32, 1, 1);
+        shape_vectors(nvec, rows, wpr, q);
+        if (wpr) return find(op, dt, rows, W, 0, 0, 64, wpr, q);
+        return find(op, dt, rows, W, 0, 1, 0, 0, 0);
     }
     if (L.peel_ok && d >= 256) {
-        shape_quads((d + 3) / 4, rows, wpr, q);
-        if (wpr) return find(op, dt, rows, 4, 1, 0, 64, wpr, q);
+        shape_vectors((d + W - 1) / W, rows, wpr, q, W == 8 ? 6 : 8);
+        if (wpr) return find(op, dt, rows, W, 1, 0, 64, wpr, q);
         return find(op, dt, rows, 1, 0, 1, 0, 0, 0);
     }
     ladder1(d, lpr, wpr, q);
@@ -247,8 +253,8 @@ bool eligible(int id, const mi_norm_problem &P) {
     if (v.op != P.op || v.dtype != P.dtype) return false;
     const Layout L = layout_of(P);
     if (v.looped) return v.vec == 1 || L.aq;
-    if (v.peel) return L.peel_ok && (P.d + 3) / 4 <= v.max_d / 4;
-    if (v.vec == 4) return L.aq && P.d <= v.max_d;
+    if (v.peel) return L.peel_ok && (P.d + v.vec - 1) / v.vec <= v.max_d / v.vec;
+    if (v.vec > 1) return L.aq && P.d <= v.max_d;
     return P.d <= v.max_d;
 }
 

@@ -40,7 +40,16 @@ namespace minorm {
 enum : int { OP_LN = 0, OP_RMS = 1 };
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+
+// float32 registers holding VEC elements (1, 4 or 8)
+template <int VEC> struct VecOf;
+template <> struct VecOf<1> { using type = float; };
+template <> struct VecOf<4> { using type = f4; };
+template <> struct VecOf<8> { using type = f8; };
+template <int VEC> using vf = typename VecOf<VEC>::type;
 
 // Kernel arguments (one struct, passed by value).  Row tensors hold elements
 // of the kernel's storage type T; ld* are their row strides in elements.
@@ -173,6 +182,62 @@ __device__ __forceinline__ void ste(T *p, float v) {
     }
 }
 
+// An oct: eight 16-bit elements in one 128-bit access.
+template <typename T, bool NT>
+__device__ __forceinline__ f8 ldo(const T *p) {
+    static_assert(sizeof(T) == 2, "octs are 16-bit elements");
+    typedef T t8 __attribute__((ext_vector_type(8)));
+    u4 raw;
+    if constexpr (NT) raw = __builtin_nontemporal_load(reinterpret_cast<const u4 *>(p));
+    else raw = *reinterpret_cast<const u4 *>(p);
+    return __builtin_convertvector(__builtin_bit_cast(t8, raw), f8);
+}
+
+template <typename T, bool NT>
+__device__ __forceinline__ void sto(T *p, f8 v) {
+    static_assert(sizeof(T) == 2, "octs are 16-bit elements");
+    typedef T t8 __attribute__((ext_vector_type(8)));
+    const u4 raw = __builtin_bit_cast(u4, __builtin_convertvector(v, t8));
+    if constexpr (NT) __builtin_nontemporal_store(raw, reinterpret_cast<u4 *>(p));
+    else *reinterpret_cast<u4 *>(p) = raw;
+}
+
+// VEC consecutive elements of T (one access), widened to float32, and back
+template <typename T, int VEC, bool NT>
+__device__ __forceinline__ vf<VEC> ldv(const T *p) {
+    if constexpr (VEC == 1) return lde<T, NT>(p);
+    else if constexpr (VEC == 4) return ldq<T, NT>(p);
+    else return ldo<T, NT>(p);
+}
+
+template <typename T, int VEC, bool NT>
+__device__ __forceinline__ void stv(T *p, vf<VEC> v) {
+    if constexpr (VEC == 1) ste<T, NT>(p, v);
+    else if constexpr (VEC == 4) stq<T, NT>(p, v);
+    else sto<T, NT>(p, v);
+}
+
+// VEC consecutive float32 parameters: 16-byte-aligned vector loads, or
+// (unaligned, the peeled path) element by element
+template <int VEC>
+__device__ __forceinline__ vf<VEC> ldp(const float *p) {
+    if constexpr (VEC == 1) return *p;
+    else if constexpr (VEC == 4) return ld4<false>(p);
+    else return __builtin_shufflevector(ld4<false>(p), ld4<false>(p + 4), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int VEC>
+__device__ __forceinline__ vf<VEC> ldp_scalar(const float *p) {
+    vf<VEC> v;
+    if constexpr (VEC == 1) {
+        v = p[0];
+    } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) v[i] = p[i];
+    }
+    return v;
+}
+
 // the value as stored in T (a rounding and an exact widening; identity for float)
 template <typename T>
 __device__ __forceinline__ f4 as_stored(f4 v) {
@@ -184,12 +249,22 @@ __device__ __forceinline__ f4 as_stored(f4 v) {
     }
 }
 template <typename T>
+__device__ __forceinline__ f8 as_stored(f8 v) {
+    if constexpr (std::is_same_v<T, float>) {
+        return v;
+    } else {
+        typedef T t8 __attribute__((ext_vector_type(8)));
+        return __builtin_convertvector(__builtin_convertvector(v, t8), f8);
+    }
+}
+template <typename T>
 __device__ __forceinline__ float as_stored(float v) {
     if constexpr (std::is_same_v<T, float>) return v;
     else return (float)(T)v;
 }
 
 __device__ __forceinline__ float hsum(f4 v) { return (v.x + v.y) + (v.z + v.w); }
+__device__ __forceinline__ float hsum(f8 v) { return hsum(v.lo) + hsum(v.hi); }
 __device__ __forceinline__ float hsum(float v) { return v; }
 
 __device__ __forceinline__ float csq(f4 v, float mu) {
@@ -197,9 +272,11 @@ __device__ __forceinline__ float csq(f4 v, float mu) {
     return (c.x * c.x + c.y * c.y) + (c.z * c.z + c.w * c.w);
 }
 __device__ __forceinline__ float csq(float v, float mu) { const float c = v - mu; return c * c; }
+__device__ __forceinline__ float csq(f8 v, float mu) { return csq(v.lo, mu) + csq(v.hi, mu); }
 
 __device__ __forceinline__ float sq(f4 v) { return (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w); }
 __device__ __forceinline__ float sq(float v) { return v * v; }
+__device__ __forceinline__ float sq(f8 v) { return sq(v.lo) + sq(v.hi); }
 
 __device__ __forceinline__ float rsq(float v) { return __builtin_amdgcn_rsqf(v); }
 
@@ -208,13 +285,14 @@ __device__ __forceinline__ float rsq(float v) { return __builtin_amdgcn_rsqf(v);
 //
 //   T      storage type of the row tensors: float, _Float16 or __bf16
 //   OP     OP_LN or OP_RMS
-//   VEC    4: quad accesses, four elements (128-bit for float, 64-bit for
-//          the 16-bit types; d % 4 == 0, rows aligned to a quad), or
-//          1: single-element accesses (any d, any element alignment)
-//   PEEL   VEC == 4 only: per row, scalar head elements up to the row's
-//          first quad boundary, a quad body, and a scalar tail; needs every
-//          row tensor in the same phase modulo a quad, any d; gamma/beta are
-//          then read as scalars since their phase follows the row's
+//   VEC    elements per lane access: 4 (a quad: 128-bit for float, 64-bit
+//          for the 16-bit types), 8 (an oct: 128-bit, 16-bit types only) -
+//          d % VEC == 0 and rows aligned to an access - or 1 (any d, any
+//          element alignment)
+//   PEEL   VEC > 1 only: per row, scalar head elements up to the row's first
+//          access boundary, a vector body, and a scalar tail; needs every
+//          row tensor in the same phase modulo an access, any d; gamma/beta
+//          are then read as scalars since their phase follows the row's
 //   LPR    lanes of one wave sharing a row (16, 32, 64); 64 / LPR rows per wave
 //   WPR    waves sharing a row (LPR == 64 when WPR > 1)
 //   Q      accesses held per lane; capacity = VEC * LPR * WPR * Q elements
@@ -240,13 +318,13 @@ template <typename T, int OP, int VEC, bool PEEL, int LPR, int WPR, int Q, int W
 __global__ __launch_bounds__(WAVES * 64)
 void norm_held(NormParams p)
 {
-    static_assert(VEC == 1 || VEC == 4, "VEC");
-    static_assert(!PEEL || (VEC == 4 && LPR == 64), "PEEL needs 128-bit, full-wave rows");
+    static_assert(VEC == 1 || VEC == 4 || (VEC == 8 && sizeof(T) == 2), "VEC");
+    static_assert(!PEEL || (VEC > 1 && LPR == 64), "PEEL needs vector accesses, full-wave rows");
     static_assert(LPR == 16 || LPR == 32 || LPR == 64, "LPR");
     static_assert(WPR == 1 || LPR == 64, "multi-wave rows use full waves");
     static_assert(WAVES % WPR == 0, "whole rows per workgroup");
     static_assert(WPR <= 16, "the cross-wave merge sums within one 16-lane DPP row");
-    using VT = typename std::conditional<VEC == 4, f4, float>::type;
+    using VT = vf<VEC>;
     constexpr int RPW = 64 / LPR;
     constexpr int RPB = (WPR == 1) ? WAVES * RPW : WAVES / WPR;
     // Hold gamma/beta (or w) beside x only while x + parameters stay within a
@@ -303,13 +381,13 @@ void norm_held(NormParams p)
         // row geometry: h head scalars, nvec body accesses, t tail scalars
         int h = 0, t = 0, nvec;
         if constexpr (PEEL) {
-            const int mis = (int)((reinterpret_cast<uintptr_t>(xr) / sizeof(T)) & 3);
-            h = (4 - mis) & 3;
+            const int mis = (int)((reinterpret_cast<uintptr_t>(xr) / sizeof(T)) & (VEC - 1));
+            h = (VEC - mis) & (VEC - 1);
             if (h > d) h = d;
-            nvec = (d - h) >> 2;
-            t = d - h - 4 * nvec;
+            nvec = (int)((unsigned)(d - h) / VEC);
+            t = d - h - VEC * nvec;
         } else {
-            nvec = (VEC == 4) ? (d >> 2) : d;  // >= 1 for these paths
+            nvec = (int)((unsigned)d / VEC);  // >= 1 for these paths
         }
         // only a peeled row narrower than 8 elements can have no body
         const bool body = PEEL ? nvec > 0 : true;
@@ -329,16 +407,10 @@ void norm_held(NormParams p)
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             VT raw = VT(0.f);
-            if (body) {
-                if constexpr (VEC == 4) raw = ldq<T, NTL>(xr + h + 4 * kc[q]);
-                else raw = lde<T, NTL>(xr + kc[q]);
-            }
+            if (body) raw = ldv<T, VEC, NTL>(xr + h + VEC * kc[q]);
             if constexpr (RES) {
                 VT rres = VT(0.f);
-                if (body) {
-                    if constexpr (VEC == 4) rres = ldq<T, NTL>(rr + h + 4 * kc[q]);
-                    else rres = lde<T, NTL>(rr + kc[q]);
-                }
+                if (body) rres = ldv<T, VEC, NTL>(rr + h + VEC * kc[q]);
                 raw = as_stored<T>(raw + rres);
             }
             v[q] = ok[q] ? raw : VT(0.f);
@@ -350,7 +422,7 @@ void norm_held(NormParams p)
             hok = rv && wr == 0 && li < h;
             tok = rv && wr == 0 && li < t;
             hi = li < h ? li : 0;
-            ti = h + 4 * nvec + li;
+            ti = h + VEC * nvec + li;
             ti = ti < d ? ti : d - 1;
             float rh = lde<T, false>(xr + hi), rt = lde<T, false>(xr + ti);
             if constexpr (RES) {
@@ -367,8 +439,7 @@ void norm_held(NormParams p)
 #pragma unroll
                 for (int q = 0; q < Q; ++q) {
                     if (!ok[q]) continue;
-                    if constexpr (VEC == 4) stq<T, NTS>(hr + h + 4 * kc[q], v[q]);
-                    else ste<T, NTS>(hr + kc[q], v[q]);
+                    stv<T, VEC, NTS>(hr + h + VEC * kc[q], v[q]);
                 }
                 if (hok) ste<T, false>(hr + hi, hx);
                 if (tok) ste<T, false>(hr + ti, tx);
@@ -381,20 +452,13 @@ void norm_held(NormParams p)
             if constexpr (PLDS) {
                 gq = lds_par[0][kc[q]];
                 if constexpr (OP == OP_LN) bq = lds_par[kParams - 1][kc[q]];
-            } else if constexpr (VEC == 4 && !PEEL) {
-                gq = ld4<false>(p.p0 + 4 * kc[q]);
-                if constexpr (OP == OP_LN) bq = ld4<false>(p.p1 + 4 * kc[q]);
-            } else if constexpr (VEC == 4) {
-                // the body's phase in the row decides the parameters' phase
-                const float *pg = p.p0 + h + 4 * kc[q];
-                gq = f4{pg[0], pg[1], pg[2], pg[3]};
-                if constexpr (OP == OP_LN) {
-                    const float *pb = p.p1 + h + 4 * kc[q];
-                    bq = f4{pb[0], pb[1], pb[2], pb[3]};
-                }
+            } else if constexpr (!PEEL) {
+                gq = ldp<VEC>(p.p0 + VEC * kc[q]);
+                if constexpr (OP == OP_LN) bq = ldp<VEC>(p.p1 + VEC * kc[q]);
             } else {
-                gq = p.p0[kc[q]];
-                if constexpr (OP == OP_LN) bq = p.p1[kc[q]];
+                // the body's phase in the row decides the parameters' phase
+                gq = ldp_scalar<VEC>(p.p0 + h + VEC * kc[q]);
+                if constexpr (OP == OP_LN) bq = ldp_scalar<VEC>(p.p1 + h + VEC * kc[q]);
             }
         };
         VT g[Q], b[Q];
@@ -517,10 +581,7 @@ void norm_held(NormParams p)
             VT o;
             if constexpr (OP == OP_LN) o = (v[q] - mu) * rs * gq + bq;
             else o = v[q] * gq * rs;
-            if (ok[q]) {
-                if constexpr (VEC == 4) stq<T, NTS>(yr + h + 4 * kc[q], o);
-                else ste<T, NTS>(yr + kc[q], o);
-            }
+            if (ok[q]) stv<T, VEC, NTS>(yr + h + VEC * kc[q], o);
         }
         if constexpr (PEEL) {
             const float gh = p.p0[hi], gt = p.p0[ti];
@@ -560,24 +621,19 @@ template <typename T, int OP, int VEC, int WAVES, int U, bool RES = false>
 __global__ __launch_bounds__(WAVES * 64)
 void norm_looped(NormParams p)
 {
-    using VT = typename std::conditional<VEC == 4, f4, float>::type;
+    static_assert(VEC == 1 || VEC == 4 || (VEC == 8 && sizeof(T) == 2), "VEC");
+    using VT = vf<VEC>;
     constexpr int NT = WAVES * 64;  // threads per workgroup
     __shared__ float red[2][WAVES];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int d = p.d;
-    const int nvec = (VEC == 4) ? (d >> 2) : d;
+    const int nvec = (int)((unsigned)d / VEC);
     int slot = 0;
 
-    auto load = [&](const T *xr, int k) -> VT {
-        if constexpr (VEC == 4) return ldq<T, false>(xr + 4 * k);
-        else return lde<T, false>(xr + k);
-    };
-    auto param = [&](const float *pr, int k) -> VT {
-        if constexpr (VEC == 4) return ld4<false>(pr + 4 * k);
-        else return pr[k];
-    };
+    auto load = [&](const T *xr, int k) -> VT { return ldv<T, VEC, false>(xr + VEC * k); };
+    auto param = [&](const float *pr, int k) -> VT { return ldp<VEC>(pr + VEC * k); };
 
     for (int64_t row = blockIdx.x; row < p.rows; row += gridDim.x) {
         const T *xr = static_cast<const T *>(p.x) + row * p.ldx;
@@ -612,8 +668,7 @@ void norm_looped(NormParams p)
                     for (int u = 0; u < U; ++u) {
                         const int k = k0 + tid + NT * u;
                         if (k >= nvec) continue;
-                        if constexpr (VEC == 4) stq<T, false>(hr + 4 * k, v[u]);
-                        else ste<T, false>(hr + k, v[u]);
+                        stv<T, VEC, false>(hr + VEC * k, v[u]);
                     }
                 }
             }
@@ -661,8 +716,7 @@ void norm_looped(NormParams p)
                 VT o;
                 if constexpr (OP == OP_LN) o = (v[u] - mu) * rs * param(p.p0, k) + param(p.p1, k);
                 else o = v[u] * param(p.p0, k) * rs;
-                if constexpr (VEC == 4) stq<T, false>(yr + 4 * k, o);
-                else ste<T, false>(yr + k, o);
+                stv<T, VEC, false>(yr + VEC * k, o);
             }
         }
         if (tid == 0) {

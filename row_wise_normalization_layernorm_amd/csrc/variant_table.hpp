@@ -43,7 +43,7 @@ constexpr bool kres(int op) { return op >= 2; }
     Variant{OPN "_" #VEC "_p" #PEEL "_l" #LPR "_w" #WPR "_q" #Q "_b" #WAVES,                  \
             mi_norm_variant_info{OPC, DT, VEC, PEEL, 0, LPR, WPR, Q, WAVES,                     \
                                  (WPR == 1) ? WAVES * (64 / LPR) : WAVES / WPR,                 \
-                                 (int64_t)VEC * LPR * WPR * Q, (VEC == 4 && !PEEL) ? 1 : 0},    \
+                                 (int64_t)VEC * LPR * WPR * Q, (VEC > 1 && !PEEL) ? 1 : 0},     \
             reinterpret_cast<const void *>(&norm_held<T, kop(OPC), VEC, (PEEL != 0), LPR, WPR,  \
                                                       Q, WAVES, true, true, 0, -1, kres(OPC)>)}
 
@@ -55,33 +55,48 @@ constexpr bool kres(int op) { return op >= 2; }
 #define MI_LOOP(T, DT, OPC, OPN, VEC, WAVES, U)                                                \
     Variant{OPN "_" #VEC "_loop_b" #WAVES "_u" #U,                                              \
             mi_norm_variant_info{OPC, DT, VEC, 0, 1, 64, WAVES, U, WAVES, 1, kUnbounded,        \
-                                 VEC == 4 ? 1 : 0},                                             \
+                                 VEC > 1 ? 1 : 0},                                              \
             reinterpret_cast<const void *>(&norm_looped<T, kop(OPC), VEC, WAVES, U, kres(OPC)>)}
 
-// every (waves per row, slots) pair of a quad path: slots 1, 2, 3, 4, 6, 8
-// for 1, 2, 4, 8 and 16 waves per row
-#define MI_SLOTS(T, DT, OPC, OPN, PEEL, WPR, WSMALL)                                           \
-    MI_HELD2(T, DT, OPC, OPN, 4, PEEL, 64, WPR, 1, WSMALL),                                     \
-    MI_HELD2(T, DT, OPC, OPN, 4, PEEL, 64, WPR, 2, WSMALL),                                     \
-    MI_HELD2(T, DT, OPC, OPN, 4, PEEL, 64, WPR, 3, WSMALL),                                     \
-    MI_HELD2(T, DT, OPC, OPN, 4, PEEL, 64, WPR, 4, WSMALL),                                     \
-    MI_HELD2(T, DT, OPC, OPN, 4, PEEL, 64, WPR, 6, WSMALL),                                     \
-    MI_HELD2(T, DT, OPC, OPN, 4, PEEL, 64, WPR, 8, WSMALL)
-#define MI_SLOTS16(T, DT, OPC, OPN, PEEL)                                                      \
-    MI_HELD(T, DT, OPC, OPN, 4, PEEL, 64, 16, 1, 16), MI_HELD(T, DT, OPC, OPN, 4, PEEL, 64, 16, 2, 16), \
-    MI_HELD(T, DT, OPC, OPN, 4, PEEL, 64, 16, 3, 16), MI_HELD(T, DT, OPC, OPN, 4, PEEL, 64, 16, 4, 16), \
-    MI_HELD(T, DT, OPC, OPN, 4, PEEL, 64, 16, 6, 16), MI_HELD(T, DT, OPC, OPN, 4, PEEL, 64, 16, 8, 16)
-#define MI_PATHQ(T, DT, OPC, OPN, PEEL)                                                        \
-    MI_SLOTS(T, DT, OPC, OPN, PEEL, 1, 4), MI_SLOTS(T, DT, OPC, OPN, PEEL, 2, 4),               \
-    MI_SLOTS(T, DT, OPC, OPN, PEEL, 4, 4), MI_SLOTS(T, DT, OPC, OPN, PEEL, 8, 8),               \
-    MI_SLOTS16(T, DT, OPC, OPN, PEEL)
+// every (waves per row, slots) pair of a vector path (VW elements per access:
+// 4 for float32, 8 for the 16-bit types, 16 bytes either way except the
+// quads of a 16-bit type): slots 1, 2, 3, 4, 6, 8 for 1, 2, 4, 8 and 16
+// waves per row
+#define MI_SLOTS(T, DT, VW, OPC, OPN, PEEL, WPR, WSMALL)                                           \
+    MI_HELD2(T, DT, OPC, OPN, VW, PEEL, 64, WPR, 1, WSMALL),                                     \
+    MI_HELD2(T, DT, OPC, OPN, VW, PEEL, 64, WPR, 2, WSMALL),                                     \
+    MI_HELD2(T, DT, OPC, OPN, VW, PEEL, 64, WPR, 3, WSMALL),                                     \
+    MI_HELD2(T, DT, OPC, OPN, VW, PEEL, 64, WPR, 4, WSMALL),                                     \
+    MI_HELD2(T, DT, OPC, OPN, VW, PEEL, 64, WPR, 6, WSMALL),                                     \
+    MI_SLOT8_##VW##_##PEEL(T, DT, OPC, OPN, WPR, WSMALL)
+#define MI_SLOTS16(T, DT, VW, OPC, OPN, PEEL)                                                      \
+    MI_HELD(T, DT, OPC, OPN, VW, PEEL, 64, 16, 1, 16), MI_HELD(T, DT, OPC, OPN, VW, PEEL, 64, 16, 2, 16), \
+    MI_HELD(T, DT, OPC, OPN, VW, PEEL, 64, 16, 3, 16), MI_HELD(T, DT, OPC, OPN, VW, PEEL, 64, 16, 4, 16), \
+    MI_HELD(T, DT, OPC, OPN, VW, PEEL, 64, 16, 6, 16) MI_SLOT16_8_##VW##_##PEEL(T, DT, OPC, OPN)
 
-#define MI_OP_TABLE(T, DT, OPC, OPN)                                                           \
-    /* quads, aligned, d % 4 == 0; 16 or 32 lanes per row for narrow rows */                    \
-    MI_HELD2(T, DT, OPC, OPN, 4, 0, 16, 1, 1, 4), MI_HELD2(T, DT, OPC, OPN, 4, 0, 32, 1, 1, 4), \
-    MI_PATHQ(T, DT, OPC, OPN, 0),                                                               \
-    /* quad body with a per-row scalar head and tail: any d, rows in one phase */              \
-    MI_PATHQ(T, DT, OPC, OPN, 1),                                                               \
+// Eight slots: 16-bit octs on the peeled path hold 8 x 8 values plus the
+// peel's scalars, which does not fit the 128 VGPRs of a 16-wave workgroup
+// (the fused variants spilled), so that path stops at six slots in 16-wave
+// workgroups and the dispatcher caps it there.
+#define MI_SLOT8_4_0(T, DT, OPC, OPN, WPR, WS) MI_HELD2(T, DT, OPC, OPN, 4, 0, 64, WPR, 8, WS)
+#define MI_SLOT8_4_1(T, DT, OPC, OPN, WPR, WS) MI_HELD2(T, DT, OPC, OPN, 4, 1, 64, WPR, 8, WS)
+#define MI_SLOT8_8_0(T, DT, OPC, OPN, WPR, WS) MI_HELD2(T, DT, OPC, OPN, 8, 0, 64, WPR, 8, WS)
+#define MI_SLOT8_8_1(T, DT, OPC, OPN, WPR, WS) MI_HELD(T, DT, OPC, OPN, 8, 1, 64, WPR, 8, WS)
+#define MI_SLOT16_8_4_0(T, DT, OPC, OPN) , MI_HELD(T, DT, OPC, OPN, 4, 0, 64, 16, 8, 16)
+#define MI_SLOT16_8_4_1(T, DT, OPC, OPN) , MI_HELD(T, DT, OPC, OPN, 4, 1, 64, 16, 8, 16)
+#define MI_SLOT16_8_8_0(T, DT, OPC, OPN) , MI_HELD(T, DT, OPC, OPN, 8, 0, 64, 16, 8, 16)
+#define MI_SLOT16_8_8_1(T, DT, OPC, OPN)
+#define MI_PATHV(T, DT, VW, OPC, OPN, PEEL)                                                        \
+    MI_SLOTS(T, DT, VW, OPC, OPN, PEEL, 1, 4), MI_SLOTS(T, DT, VW, OPC, OPN, PEEL, 2, 4),               \
+    MI_SLOTS(T, DT, VW, OPC, OPN, PEEL, 4, 4), MI_SLOTS(T, DT, VW, OPC, OPN, PEEL, 8, 8),               \
+    MI_SLOTS16(T, DT, VW, OPC, OPN, PEEL)
+
+#define MI_OP_TABLE(T, DT, VW, OPC, OPN)                                                           \
+    /* vectors, aligned, d % VW == 0; 16 or 32 lanes per row for narrow rows */                 \
+    MI_HELD2(T, DT, OPC, OPN, VW, 0, 16, 1, 1, 4), MI_HELD2(T, DT, OPC, OPN, VW, 0, 32, 1, 1, 4), \
+    MI_PATHV(T, DT, VW, OPC, OPN, 0),                                                               \
+    /* vector body with a per-row scalar head and tail: any d, rows in one phase */            \
+    MI_PATHV(T, DT, VW, OPC, OPN, 1),                                                               \
     /* single-element accesses: any d, any element alignment */                                \
     MI_HELD2(T, DT, OPC, OPN, 1, 0, 16, 1, 1, 4), MI_HELD2(T, DT, OPC, OPN, 1, 0, 32, 1, 1, 4), \
     MI_HELD2(T, DT, OPC, OPN, 1, 0, 64, 1, 1, 4), MI_HELD2(T, DT, OPC, OPN, 1, 0, 64, 1, 2, 4), \
@@ -90,11 +105,12 @@ constexpr bool kres(int op) { return op >= 2; }
     MI_HELD2(T, DT, OPC, OPN, 1, 0, 64, 8, 8, 8),                                               \
     MI_HELD(T, DT, OPC, OPN, 1, 0, 64, 16, 8, 16), MI_HELD(T, DT, OPC, OPN, 1, 0, 64, 16, 16, 16), \
     /* streamed rows, any width */                                                             \
-    MI_LOOP(T, DT, OPC, OPN, 4, 4, 4), MI_LOOP(T, DT, OPC, OPN, 1, 4, 8)
+    MI_LOOP(T, DT, OPC, OPN, VW, 4, 4), MI_LOOP(T, DT, OPC, OPN, 1, 4, 8)
 
-// the four operations of one storage type; SFX is the dtype's name suffix
-#define MI_DTYPE_TABLE(T, DT, SFX)                                                             \
-    MI_OP_TABLE(T, DT, MI_NORM_OP_LAYERNORM, "ln" SFX),                                         \
-    MI_OP_TABLE(T, DT, MI_NORM_OP_RMSNORM, "rms" SFX),                                          \
-    MI_OP_TABLE(T, DT, MI_NORM_OP_ADD_LAYERNORM, "addln" SFX),                                  \
-    MI_OP_TABLE(T, DT, MI_NORM_OP_ADD_RMSNORM, "addrms" SFX)
+// the four operations of one storage type; VW its vector width in
+// elements, SFX its name suffix
+#define MI_DTYPE_TABLE(T, DT, VW, SFX)                                                             \
+    MI_OP_TABLE(T, DT, VW, MI_NORM_OP_LAYERNORM, "ln" SFX),                                         \
+    MI_OP_TABLE(T, DT, VW, MI_NORM_OP_RMSNORM, "rms" SFX),                                          \
+    MI_OP_TABLE(T, DT, VW, MI_NORM_OP_ADD_LAYERNORM, "addln" SFX),                                  \
+    MI_OP_TABLE(T, DT, VW, MI_NORM_OP_ADD_RMSNORM, "addrms" SFX)

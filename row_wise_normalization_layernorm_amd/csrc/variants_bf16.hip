@@ -3,7 +3,7 @@
 
 namespace minorm {
 namespace {
-const Variant kVariants[] = {MI_DTYPE_TABLE(__bf16, MI_NORM_BF16, "_bf16")};
+const Variant kVariants[] = {MI_DTYPE_TABLE(__bf16, MI_NORM_BF16, 8, "_bf16")};
 }  // namespace
 const VariantTable kTableBF16 = {kVariants, (int)(sizeof(kVariants) / sizeof(kVariants[0]))};
 }  // namespace minorm

@@ -210,14 +210,18 @@ def test_variant_table_is_consistent(L):
             assert v["lanes_per_row"] == 64
             assert v["rows_per_block"] * v["waves_per_row"] == v["waves_per_block"]
         assert v["waves_per_block"] * 64 <= 1024
-        assert v["needs_aligned"] == (1 if v["vec"] == 4 and not v["peel"] else 0)
+        assert v["needs_aligned"] == (1 if v["vec"] > 1 and not v["peel"] else 0)
+        # vector accesses are 16 bytes: 4 float32 or 8 16-bit elements
+        assert v["vec"] in (1, 16 // ESIZE[v["dtype"]])
     assert {v["op"] for _, _, v in infos} == set(OPS)
     assert {v["dtype"] for _, _, v in infos} == set(DTYPES)
-    # every operation and storage type has the same family of shapes
+    # within a storage type every operation has the same family of shapes,
+    # and the two 16-bit types have the same family
     shapes = {(op, dt): sorted(n[len(PREFIX[op] + DTSFX[dt]):] for _, n, v in infos
                                if v["op"] == op and v["dtype"] == dt) for op in OPS for dt in DTYPES}
-    first = shapes[(0, 0)]
-    assert first and all(s == first for s in shapes.values())
+    for dt in DTYPES:
+        assert shapes[(0, dt)] and all(shapes[(op, dt)] == shapes[(0, dt)] for op in OPS)
+    assert shapes[(0, mn.MI_NORM_F16)] == shapes[(0, mn.MI_NORM_BF16)]
     # float32 ids come first, so they do not move when other types are added
     assert [v["dtype"] for _, _, v in infos] == sorted(v["dtype"] for _, _, v in infos)
 
@@ -248,11 +252,12 @@ def test_dispatch_picks_an_eligible_covering_variant(L, op, layout, dt):
             assert v["op"] == op and v["dtype"] == dt
             assert mn.mi_norm_eligible(vid, p), (d, layout, mn.mi_norm_variant_name(vid))
             assert v["looped"] or v["max_d"] >= d
-            if layout == "aligned" and d % 4 == 0:
-                assert v["vec"] == 4 and not v["peel"], (d, mn.mi_norm_variant_name(vid))
+            W = 16 // e
+            if layout == "aligned" and d % W == 0:
+                assert v["vec"] == W and not v["peel"], (d, mn.mi_norm_variant_name(vid))
             if layout == "different_phase":
                 assert v["vec"] == 1, (d, mn.mi_norm_variant_name(vid))
-            if layout == "aligned" and d % 4 and 256 <= d <= 32768:
+            if layout == "aligned" and d % W and 256 <= d <= (32768 if W == 4 else 49152):
                 assert v["peel"], (d, mn.mi_norm_variant_name(vid))
 
 
@@ -375,11 +380,18 @@ def test_strided_aliasing_is_exact_for_equal_strides(L):
 def test_strides_and_types_decide_the_layout(L):
     info = lambda **kw: mn.mi_norm_variant_get_info(mn.mi_norm_select(_prob(0, 4096, 768, **kw)))
     name = lambda **kw: mn.mi_norm_variant_name(mn.mi_norm_select(_prob(0, 4096, 768, **kw)))
-    assert name(dtype=mn.MI_NORM_BF16) == "ln_bf16_4_p0_l64_w1_q3_b16"
-    assert name(dtype=mn.MI_NORM_F16) == "ln_f16_4_p0_l64_w1_q3_b16"
-    # a quad of a 16-bit type is 8 bytes: 8-byte alignment is enough for it
-    assert info(dtype=mn.MI_NORM_BF16, x=X + 8, y=Y + 8)["needs_aligned"] == 1
+    # 16-byte accesses: eight 16-bit elements, 96 of them per row of 768
+    assert name(dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w1_q2_b16"
+    assert name(dtype=mn.MI_NORM_F16) == "ln_f16_8_p0_l64_w1_q2_b16"
+    assert info(dtype=mn.MI_NORM_BF16, x=X + 8, y=Y + 8)["peel"] == 1
     assert info(dtype=mn.MI_NORM_F32, x=X + 8, y=Y + 8)["peel"] == 1
+    # a 16-bit row width that is a multiple of 4 but not of 8 is peeled
+    v = mn.mi_norm_variant_get_info(mn.mi_norm_select(_prob(0, 4096, 772, dtype=mn.MI_NORM_BF16)))
+    assert v["peel"] == 1 and v["vec"] == 8
+    # peeled 16-bit rows stop at six slots (49152 elements), then stream
+    v = mn.mi_norm_variant_get_info(mn.mi_norm_select(_prob(2, 64, 49153, x=X + 2, y=Y + 2, r=R_ + 2,
+                                                            h=H_ + 2, dtype=mn.MI_NORM_BF16)))
+    assert v["looped"] == 1 and v["vec"] == 1
     # strides that keep every row on a quad boundary keep the quad path
     assert info(ldx=1024, ldy=776)["needs_aligned"] == 1
     # a stride off the quad grid: rows change phase, together if all strides agree mod 4

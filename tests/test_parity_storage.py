@@ -264,11 +264,11 @@ def test_storage16_full_size(torch_dev, dt):
 
 def _variant_widths(v):
     if v["looped"]:
-        return [4 * 1237, 40000] if v["vec"] == 4 else [4947, 40001]
+        return [v["vec"] * 1237, 40000] if v["vec"] > 1 else [4947, 40001]
     cap = v["max_d"]
     if v["peel"]:
         return sorted(w for w in {cap - 3, cap - 1 - 4 * 64, max(3, cap // 3 - 1), 5} if w >= 1)
-    step = 4 if v["vec"] == 4 else 1
+    step = v["vec"]
     return sorted(w for w in {cap, cap - step * max(1, cap // (7 * step)), step} if w >= 1)
 
 
@@ -277,8 +277,8 @@ def _variant_layout(v, d):
     if v["needs_aligned"]:
         return dict(ld={k: d + 8 for k in "xryh"}, off={k: 0 for k in "xryh"}, po=0)
     if v["peel"]:
-        # one phase within a quad on every row: equal offsets, strides equal mod 4
-        return dict(ld={"x": d + 5, "r": d + 1, "y": d + 9, "h": d + 5}, off={k: 1 for k in "xryh"}, po=2)
+        # one phase within a vector on every row: equal offsets, strides equal mod 8
+        return dict(ld={"x": d + 5, "r": d + 13, "y": d + 21, "h": d + 5}, off={k: 1 for k in "xryh"}, po=2)
     return dict(ld={"x": d + 3, "r": d + 2, "y": d + 1, "h": d + 7}, off={"x": 1, "r": 2, "y": 3, "h": 0}, po=3)
 
 
