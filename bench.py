@@ -92,12 +92,14 @@ BENCH_WORKLOADS = {
 
 ESIZE = {"f32": 4, "f16": 2, "bf16": 2}
 
+# the device code of the forward kernels and the table that instantiates them
+# (launch shapes included); a profile's counters stand for the kernels only
+# while these are unchanged and the dispatcher still picks the profiled variant
 KERNEL_SOURCES = ("row_wise_normalization_layernorm_amd/csrc/norm_kernels.hpp",
                   "row_wise_normalization_layernorm_amd/csrc/variant_table.hpp",
                   "row_wise_normalization_layernorm_amd/csrc/variants_f32.hip",
                   "row_wise_normalization_layernorm_amd/csrc/variants_f16.hip",
-                  "row_wise_normalization_layernorm_amd/csrc/variants_bf16.hip",
-                  "row_wise_normalization_layernorm_amd/csrc/mi_norm.hip")
+                  "row_wise_normalization_layernorm_amd/csrc/variants_bf16.hip")
 
 
 def kernel_source_hash() -> str:
@@ -136,16 +138,18 @@ def describe(op: str, rows: int, d: int, stats: bool, storage: str = "f32", pad:
     return f"{name} fwd {kind} [{rows},{d}]{extra}{strided}"
 
 
-def pmc_traffic(workload: str):
+def pmc_traffic(workload: str, variant: str):
     """HBM bytes per launch from the committed counter summary, or None when
-    there is none or the kernels changed since it was taken."""
+    there is none, the kernels changed since it was taken, or the run uses
+    another variant than the one profiled."""
     path = os.path.join(ROOT, "profiles", f"pmc_{workload}.txt")
     if not os.path.exists(path):
         return None, None
     text = open(path).read()
     m = re.search(r"^kernel_source_sha256:\s*(\w+)", text, re.M)
     t = re.search(r"^traffic_bytes_per_launch:\s*([\d.eE+]+)", text, re.M)
-    if not m or not t or m.group(1) != kernel_source_hash():
+    v = re.search(r"^kernel_variant:\s*(\S+)", text, re.M)
+    if not m or not t or not v or m.group(1) != kernel_source_hash() or v.group(1) != variant:
         return None, path
     return float(t.group(1)), path
 
@@ -340,7 +344,24 @@ def main(argv=None) -> int:
     p0 = params[0].data_ptr() if params else None
     p1 = params[1].data_ptr() if ln else None
 
-    def run_native(k: int):
+    def rot(ts, first):
+        return None if ts is None else ptr_array(ts[first:] + ts[:first])
+
+    def rotated(first: int):
+        """The pointer arrays starting at buffer set `first`."""
+        return (rot(xs, first), rot(ys, first), rot(rs_, first), rot(hs, first), rot(means, first),
+                rot(rstds, first))
+
+    def run_native(k: int, arrays=None):
+        nonlocal xa, ya, ra, ha, ma, sa
+        if arrays is not None:
+            saved = xa, ya, ra, ha, ma, sa
+            xa, ya, ra, ha, ma, sa = arrays
+            try:
+                run_native(k)
+            finally:
+                xa, ya, ra, ha, ma, sa = saved
+            return
         if op == "copy":
             st = BL.mi_bench_copy_loop(xa, ya, nsets, n, k, sh)
         elif general:
@@ -441,10 +462,29 @@ def main(argv=None) -> int:
     w1 = time.perf_counter()
     ms = t_start.elapsed_time(t_end)
     ms_per_step = ms / args.steps
+
+    # single launches on an idle GPU, each between two events: the duration a
+    # kernel tracer reports per dispatch (no overlap with a neighbour's drain).
+    # A short spin kernel holds the stream while the host enqueues the first
+    # event and the launch, so the span holds no host time.
+    iso = []
+    if args.launch == "native":
+        for i in range(20):
+            arrays = rotated((args.steps + i) % nsets)   # a set last touched about n_sets steps ago
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                torch.cuda._sleep(200000)
+                e0.record(stream)
+                run_native(1, arrays)
+                e1.record(stream)
+            torch.cuda.synchronize()
+            iso.append(e0.elapsed_time(e1) * 1e3)
+    iso_us = round(sorted(iso)[len(iso) // 2], 3) if iso else None
     bytes_step = algorithmic_bytes(op, rows, d, stats, storage)
     gbps = bytes_step / (ms_per_step * 1e-3) / 1e9
 
-    traffic, _ = pmc_traffic(args.workload)
+    traffic, _ = pmc_traffic(args.workload, variant_name)
     roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(gbps / PEAK_HBM_GBPS, 4),
                 "traffic": traffic, "kernel": variant_name,
@@ -479,6 +519,7 @@ def main(argv=None) -> int:
                    "footprint_bytes": nsets * per_set, "launch": args.launch, "variant": variant_name,
                    "parallelism": "single GPU"},
         "kernel_us": round(ms_per_step * 1e3, 3),
+        "isolated_launch_us": iso_us,
         "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
         "rows_per_s": round(rows / (ms_per_step * 1e-3), 1),
         "wall_ms_per_step": round((w1 - w0) * 1e3 / args.steps, 6),
