@@ -63,6 +63,11 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
     ]
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.oracle_layernorm_bwd_f64.restype = None
+    lib.oracle_layernorm_bwd_f64.argtypes = [vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_rmsnorm_bwd_f64.restype = None
+    lib.oracle_rmsnorm_bwd_f64.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, vp]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_plant.restype = ctypes.c_int
@@ -308,6 +313,101 @@ def tolerance_ok16(got_bits, ref64, fmt: int, atol: float = 1e-5, rtol: float = 
     err = np.abs(got - ref)
     ratio = err / bound
     return bool(np.all(err <= bound)), float(err.max()), float(ratio.max())
+
+
+# ----------------------------------------------------------------------------
+# backward: gradients with respect to x and the per-column parameters
+
+def _stats64(a, rows: int, name: str) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(a, np.float64).reshape(-1))
+    if a.size != rows:
+        raise ValueError(f"{name} must hold one value per row")
+    return a
+
+
+def layernorm_bwd(dy, x, gamma, mean, rstd, lib: ctypes.CDLL | None = None) -> dict:
+    """LayerNorm backward from the upstream gradient dy and the forward's
+    per-row statistics (float32 or float64; widened exactly).
+
+    Returns a dict: dx (float32) and dx64, dgamma/dbeta (float32) and
+    dgamma64/dbeta64, and abs_dgamma/abs_dbeta (sum over rows of |dy xhat|
+    and |dy|, the magnitudes a float32 column sum's error scales with)."""
+    lib = lib or load()
+    dy, x = _f32(dy, "dy"), _f32(x, "x")
+    if x.ndim != 2 or dy.shape != x.shape:
+        raise ValueError("dy and x must be 2-D [rows, d] of one shape")
+    rows, d = x.shape
+    gamma = _f32(gamma, "gamma").reshape(-1)
+    if d < 1 or gamma.size != d:
+        raise ValueError("need d >= 1 and gamma of length d")
+    m64, r64 = _stats64(mean, rows, "mean"), _stats64(rstd, rows, "rstd")
+    out = dict(dx=np.empty_like(x), dx64=np.empty(x.shape, np.float64),
+               dgamma=np.empty(d, np.float32), dbeta=np.empty(d, np.float32),
+               dgamma64=np.empty(d), dbeta64=np.empty(d), abs_dgamma=np.empty(d), abs_dbeta=np.empty(d))
+    lib.oracle_layernorm_bwd_f64(_ptr(dy), _ptr(x), _ptr(gamma), _ptr(m64), _ptr(r64), rows, d,
+                                 _ptr(out["dx"]), _ptr(out["dx64"]), _ptr(out["dgamma"]), _ptr(out["dbeta"]),
+                                 _ptr(out["dgamma64"]), _ptr(out["dbeta64"]), _ptr(out["abs_dgamma"]),
+                                 _ptr(out["abs_dbeta"]))
+    return out
+
+
+def rmsnorm_bwd(dy, x, w, rstd, lib: ctypes.CDLL | None = None) -> dict:
+    """RMSNorm backward; dict with dx, dx64, dw, dw64, abs_dw."""
+    lib = lib or load()
+    dy, x = _f32(dy, "dy"), _f32(x, "x")
+    if x.ndim != 2 or dy.shape != x.shape:
+        raise ValueError("dy and x must be 2-D [rows, d] of one shape")
+    rows, d = x.shape
+    w = _f32(w, "w").reshape(-1)
+    if d < 1 or w.size != d:
+        raise ValueError("need d >= 1 and w of length d")
+    r64 = _stats64(rstd, rows, "rstd")
+    out = dict(dx=np.empty_like(x), dx64=np.empty(x.shape, np.float64), dw=np.empty(d, np.float32),
+               dw64=np.empty(d), abs_dw=np.empty(d))
+    lib.oracle_rmsnorm_bwd_f64(_ptr(dy), _ptr(x), _ptr(w), _ptr(r64), rows, d, _ptr(out["dx"]),
+                               _ptr(out["dx64"]), _ptr(out["dw"]), _ptr(out["dw64"]), _ptr(out["abs_dw"]))
+    return out
+
+
+def layernorm_bwd16(dy, x, fmt: int, gamma, mean, rstd, lib: ctypes.CDLL | None = None) -> dict:
+    """LayerNorm backward over 16-bit dy and x (patterns); adds dx16, dx
+    rounded once to the format from dx64.  Parameter gradients stay float32."""
+    lib = lib or load()
+    out = layernorm_bwd(widen16(dy, fmt, lib), widen16(x, fmt, lib), gamma, mean, rstd, lib)
+    out["dx16"] = round16(out["dx64"], fmt, lib)
+    return out
+
+
+def rmsnorm_bwd16(dy, x, fmt: int, w, rstd, lib: ctypes.CDLL | None = None) -> dict:
+    lib = lib or load()
+    out = rmsnorm_bwd(widen16(dy, fmt, lib), widen16(x, fmt, lib), w, rstd, lib)
+    out["dx16"] = round16(out["dx64"], fmt, lib)
+    return out
+
+
+U32 = 2.0 ** -24  # unit roundoff of float32
+
+
+def colsum_tolerance_ok(got, ref64, abs_sum, atol: float = 1e-5, rtol: float = 1e-4, k: float = 8.0):
+    """Acceptance for a float32 sum over rows (the parameter gradients).
+
+    The float32 bound of the forward outputs plus k * u * sum|terms|: each
+    term dy * xhat carries a few float32 roundings (relative error <= ~3.1u),
+    the partial sums are each rounded once to float32 (together <= u *
+    sum|terms|), accumulation is float64 and the final rounding is inside
+    rtol; k = 8 leaves margin.  Returns ``(ok, max_abs_err, max_ratio)``."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref64, np.float64)
+    a = np.asarray(abs_sum, np.float64)
+    if got.shape != ref.shape or a.shape != ref.shape:
+        return False, float("inf"), float("inf")
+    if got.size == 0:
+        return True, 0.0, 0.0
+    if not np.all(np.isfinite(got)):
+        return False, float("inf"), float("inf")
+    err = np.abs(got - ref)
+    bound = atol + rtol * np.abs(ref) + k * U32 * a
+    return bool(np.all(err <= bound)), float(err.max()), float((err / bound).max())
 
 
 def set_threads(n: int, lib: ctypes.CDLL | None = None) -> None:

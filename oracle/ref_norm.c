@@ -345,3 +345,119 @@ void oracle_add16_n(const uint16_t *x, const uint16_t *r, int fmt, int64_t n, ui
         h[i] = oracle_round16(s, fmt);
     }
 }
+
+/*
+ * Backward of the two normalizations: the exact derivative of the definitions
+ * above with respect to x and to the per-column parameters, given the
+ * upstream gradient dy and the per-row statistics the forward returned
+ * (taken as inputs, as a training step passes them from forward to backward).
+ *
+ * LayerNorm, per row i, with xhat_ij = (x_ij - mu_i) * rho_i and
+ * g_ij = dy_ij * gamma_j:
+ *     dx_ij    = rho_i * (g_ij - (1/d) sum_k g_ik - xhat_ij * (1/d) sum_k g_ik xhat_ik)
+ *     dgamma_j = sum_i dy_ij * xhat_ij,     dbeta_j = sum_i dy_ij
+ * (differentiating y = xhat * gamma + beta through mu and rho: d mu/d x_k = 1/d
+ * and d rho/d x_k = -rho^3 (x_k - mu) / d.)
+ *
+ * RMSNorm, per row i, with xhat_ij = x_ij * rho_i and g_ij = dy_ij * w_j:
+ *     dx_ij = rho_i * (g_ij - xhat_ij * (1/d) sum_k g_ik xhat_ik),   dw_j = sum_i dy_ij xhat_ij
+ *
+ * The statistics come in as float64 (the forward's float32 values widened,
+ * or exact ones for the pins).  Everything is float64 from the float32
+ * inputs; dx is rounded once to
+ * float32 (dx64 optionally keeps it unrounded), the parameter gradients
+ * likewise (dg64/db64 unrounded).  adg64/adb64 optionally receive
+ * sum_i |dy_ij xhat_ij| and sum_i |dy_ij|, the magnitudes a float32 column
+ * sum's rounding error scales with.  Any optional output may be NULL.
+ */
+void oracle_layernorm_bwd_f64(const float *dy, const float *x, const float *gamma,
+                              const double *mean, const double *rstd, int64_t rows, int64_t d,
+                              float *dx, double *dx64, float *dgamma, float *dbeta,
+                              double *dg64, double *db64, double *adg64, double *adb64)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i) {
+        const float *xi = x + i * d, *dyi = dy + i * d;
+        const double mu = mean[i], rho = rstd[i];
+        double s1 = 0.0, s2 = 0.0;
+        for (int64_t k = 0; k < d; ++k) {
+            const double xh = ((double)xi[k] - mu) * rho;
+            const double g = (double)dyi[k] * (double)gamma[k];
+            s1 += g;
+            s2 += g * xh;
+        }
+        const double m1 = s1 / (double)d, m2 = s2 / (double)d;
+        for (int64_t j = 0; j < d; ++j) {
+            const double xh = ((double)xi[j] - mu) * rho;
+            const double g = (double)dyi[j] * (double)gamma[j];
+            double v = rho * (g - m1 - xh * m2);
+#if ORACLE_PLANT == 15
+            v = rho * (g - xh * m2);                 /* planted: mean of g dropped */
+#endif
+#if ORACLE_PLANT == 16
+            v = rho * (g - m1 + xh * m2);            /* planted: sign of the projection */
+#endif
+            if (dx) dx[i * d + j] = (float)v;
+            if (dx64) dx64[i * d + j] = v;
+        }
+    }
+    /* column sums, rows in ascending order */
+    #pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < d; ++j) {
+        double sg = 0.0, sb = 0.0, ag = 0.0, ab = 0.0;
+        for (int64_t i = 0; i < rows; ++i) {
+            const double dyv = (double)dy[i * d + j];
+            double xh = ((double)x[i * d + j] - mean[i]) * rstd[i];
+#if ORACLE_PLANT == 17
+            xh = (double)x[i * d + j] * rstd[i];           /* planted: mean not removed in dgamma */
+#endif
+            sg += dyv * xh;
+            sb += dyv;
+            ag += fabs(dyv * xh);
+            ab += fabs(dyv);
+        }
+        if (dgamma) dgamma[j] = (float)sg;
+        if (dbeta) dbeta[j] = (float)sb;
+        if (dg64) dg64[j] = sg;
+        if (db64) db64[j] = sb;
+        if (adg64) adg64[j] = ag;
+        if (adb64) adb64[j] = ab;
+    }
+}
+
+void oracle_rmsnorm_bwd_f64(const float *dy, const float *x, const float *w, const double *rstd,
+                            int64_t rows, int64_t d, float *dx, double *dx64, float *dw,
+                            double *dw64, double *adw64)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i) {
+        const float *xi = x + i * d, *dyi = dy + i * d;
+        const double rho = rstd[i];
+        double s2 = 0.0;
+        for (int64_t k = 0; k < d; ++k)
+            s2 += (double)dyi[k] * (double)w[k] * ((double)xi[k] * rho);
+        const double m2 = s2 / (double)d;
+        for (int64_t j = 0; j < d; ++j) {
+            const double xh = (double)xi[j] * rho;
+            const double g = (double)dyi[j] * (double)w[j];
+            double v = rho * (g - xh * m2);
+#if ORACLE_PLANT == 18
+            v = g - xh * m2;                         /* planted: outer rho dropped */
+#endif
+            if (dx) dx[i * d + j] = (float)v;
+            if (dx64) dx64[i * d + j] = v;
+        }
+    }
+    #pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < d; ++j) {
+        double s = 0.0, a = 0.0;
+        for (int64_t i = 0; i < rows; ++i) {
+            const double t = (double)dy[i * d + j] * ((double)x[i * d + j] * rstd[i]);
+            s += t;
+            a += fabs(t);
+        }
+        if (dw) dw[j] = (float)s;
+        if (dw64) dw64[j] = s;
+        if (adw64) adw64[j] = a;
+    }
+}

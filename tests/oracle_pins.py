@@ -541,3 +541,156 @@ def check_tolerance16(lib):
 
 STORAGE16_CHECKS = (check_widen16, check_round16, check_add16, check_norm16, check_tolerance16)
 ALL_CHECKS = ALL_CHECKS + STORAGE16_CHECKS
+
+
+# ----------------------------------------------------------------------------
+# backward: the exact derivative of the pinned forward definitions
+
+def _exact_stats(x, eps):
+    """float64 mean and rstd of each row, from the forward oracle's float64
+    statistics (mean64, var64)."""
+    _, _, _, m64, v64 = oracle.layernorm(x, np.ones(x.shape[1], np.float32),
+                                         np.zeros(x.shape[1], np.float32), float(eps))
+    return m64, 1.0 / np.sqrt(v64 + float(np.float32(eps)))
+
+
+def check_bwd_autograd(lib):
+    """dx, dgamma, dbeta (and RMSNorm dx, dw) equal torch's float64 autograd
+    through F.layer_norm / F.rms_norm when the exact statistics are passed."""
+    import torch
+    import torch.nn.functional as F
+    for rows, d, pat in ((7, 33, "offset"), (5, 1, "normal"), (9, 256, "normal"), (4, 129, "tiny")):
+        x = wl.make_x(rows, d, pat, [70, rows, d])
+        dy = wl.make_x(rows, d, "normal", [71, rows, d])
+        g, b = wl.make_affine(d, [70, d])
+        w = wl.make_weight(d, [70, d])
+        m64, r64 = _exact_stats(x, EPS32)
+        out = oracle.layernorm_bwd(dy, x, g, m64, r64, lib=lib)
+        xt = torch.from_numpy(x).double().requires_grad_(True)
+        gt = torch.from_numpy(g).double().requires_grad_(True)
+        bt = torch.from_numpy(b).double().requires_grad_(True)
+        y = F.layer_norm(xt, (d,), gt, bt, float(EPS32))
+        y.backward(torch.from_numpy(dy).double())
+        for got, want, what in ((out["dx64"], xt.grad, "dx"), (out["dgamma64"], gt.grad, "dgamma"),
+                                (out["dbeta64"], bt.grad, "dbeta")):
+            want = want.numpy()
+            scale = np.abs(want).max() + 1.0       # gradients here are O(1); d = 1 gives dgamma = 0
+            assert np.abs(got - want).max() <= 1e-11 * scale, f"LN {what} {rows}x{d} {pat}"
+        r64 = 1.0 / np.sqrt((x.astype(np.float64) ** 2).mean(axis=1) + float(EPS32))
+        o2 = oracle.rmsnorm_bwd(dy, x, w, r64, lib=lib)
+        xt = torch.from_numpy(x).double().requires_grad_(True)
+        wt = torch.from_numpy(w).double().requires_grad_(True)
+        F.rms_norm(xt, (d,), wt, eps=float(EPS32)).backward(torch.from_numpy(dy).double())
+        for got, want, what in ((o2["dx64"], xt.grad, "dx"), (o2["dw64"], wt.grad, "dw")):
+            want = want.numpy()
+            scale = np.abs(want).max() + 1.0
+            assert np.abs(got - want).max() <= 1e-11 * scale, f"RMS {what} {rows}x{d} {pat}"
+
+
+def check_bwd_finite_differences(lib):
+    """Central differences of the float64 forward outputs (y64 of the pinned
+    forward oracle) match the backward, on dyadic inputs where x +- h and
+    gamma +- h are exact in float32 (no torch involved)."""
+    rng = _rng([72])
+    rows, d, h = 3, 6, 2.0 ** -12
+    x = (rng.integers(-2048, 2048, (rows, d)) * 2.0 ** -10).astype(np.float32)
+    dy = (rng.integers(-64, 64, (rows, d)) * 2.0 ** -5).astype(np.float32)
+    g = (1 + rng.integers(-64, 64, d) * 2.0 ** -8).astype(np.float32)
+    b = (rng.integers(-64, 64, d) * 2.0 ** -8).astype(np.float32)
+
+    def loss_ln(xv, gv, bv):
+        y64 = np.empty(xv.shape)
+        oracle.layernorm(xv, gv, bv, float(EPS32), lib=lib, y64=y64)
+        return float((y64 * dy).sum())
+
+    def loss_rms(xv, wv):
+        y64 = np.empty(xv.shape)
+        oracle.rmsnorm(xv, wv, float(EPS32), lib=lib, y64=y64)
+        return float((y64 * dy).sum())
+
+    m64, r64 = _exact_stats(x, EPS32)
+    out = oracle.layernorm_bwd(dy, x, g, m64, r64, lib=lib)
+    rr = 1.0 / np.sqrt((x.astype(np.float64) ** 2).mean(axis=1) + float(EPS32))
+    o2 = oracle.rmsnorm_bwd(dy, x, g, rr, lib=lib)
+    for i in range(rows):
+        for j in range(d):
+            xp, xm = x.copy(), x.copy()
+            xp[i, j] += np.float32(h)
+            xm[i, j] -= np.float32(h)
+            fd = (loss_ln(xp, g, b) - loss_ln(xm, g, b)) / (2 * h)
+            assert abs(fd - out["dx64"][i, j]) <= 1e-5 * (1 + abs(fd)), ("LN dx", i, j, fd, out["dx64"][i, j])
+            fd = (loss_rms(xp, g) - loss_rms(xm, g)) / (2 * h)
+            assert abs(fd - o2["dx64"][i, j]) <= 1e-5 * (1 + abs(fd)), ("RMS dx", i, j)
+    for j in range(d):
+        gp, gm = g.copy(), g.copy()
+        gp[j] += np.float32(h)
+        gm[j] -= np.float32(h)
+        fd = (loss_ln(x, gp, b) - loss_ln(x, gm, b)) / (2 * h)
+        assert abs(fd - out["dgamma64"][j]) <= 1e-6 * (1 + abs(fd)), ("dgamma", j)
+        fd = (loss_rms(x, gp) - loss_rms(x, gm)) / (2 * h)
+        assert abs(fd - o2["dw64"][j]) <= 1e-6 * (1 + abs(fd)), ("dw", j)
+        bp, bm = b.copy(), b.copy()
+        bp[j] += np.float32(h)
+        bm[j] -= np.float32(h)
+        fd = (loss_ln(x, g, bp) - loss_ln(x, g, bm)) / (2 * h)
+        assert abs(fd - out["dbeta64"][j]) <= 1e-6 * (1 + abs(fd)), ("dbeta", j)
+
+
+def check_bwd_invariants(lib):
+    """Shift invariance of LayerNorm makes every dx row sum to zero; at eps = 0
+    scale invariance makes dx orthogonal to (x - mu) (LayerNorm) and to x
+    (RMSNorm); a power-of-two scale of dy scales every gradient exactly."""
+    for rows, d in ((6, 40), (3, 999)):
+        x = wl.make_x(rows, d, "offset", [73, d])
+        dy = wl.make_x(rows, d, "normal", [74, d])
+        g, _ = wl.make_affine(d, [73, d])
+        m64, r64 = _exact_stats(x, EPS32)
+        out = oracle.layernorm_bwd(dy, x, g, m64, r64, lib=lib)
+        scale = np.abs(out["dx64"]).sum(axis=1)
+        assert np.all(np.abs(out["dx64"].sum(axis=1)) <= 1e-12 * scale), "LN dx rows do not sum to 0"
+        m0, r0 = _exact_stats(x, 0.0)
+        o0 = oracle.layernorm_bwd(dy, x, g, m0, r0, lib=lib)
+        c = x.astype(np.float64) - m0[:, None]
+        dot = (o0["dx64"] * c).sum(axis=1)
+        assert np.all(np.abs(dot) <= 1e-11 * (np.abs(o0["dx64"] * c).sum(axis=1))), "LN eps=0 scale"
+        rr0 = 1.0 / np.sqrt((x.astype(np.float64) ** 2).mean(axis=1))
+        o2 = oracle.rmsnorm_bwd(dy, x, g, rr0, lib=lib)
+        dot = (o2["dx64"] * x).sum(axis=1)
+        assert np.all(np.abs(dot) <= 1e-11 * np.abs(o2["dx64"] * x).sum(axis=1)), "RMS eps=0 scale"
+        o4 = oracle.layernorm_bwd((dy * np.float32(4)).astype(np.float32), x, g, m64, r64, lib=lib)
+        for k in ("dx64", "dgamma64", "dbeta64"):
+            assert np.array_equal(o4[k], 4 * out[k]), f"dy scale {k}"
+
+
+def check_bwd16(lib):
+    """16-bit backward: the float32 backward on the exactly widened inputs with
+    dx rounded once; and the column-sum acceptance bound passes a sum whose
+    terms carry float32 rounding and refuses one missing row."""
+    for fmt in (F16, BF16):
+        rows, d = 12, 96
+        x16 = wl.make_x16(rows, d, "offset", [75], fmt)
+        dy16 = wl.make_x16(rows, d, "normal", [76], fmt)
+        g, _ = wl.make_affine(d, [75])
+        xw = oracle.widen16(x16, fmt, lib=lib)
+        m64, r64 = _exact_stats(xw, EPS32)
+        o16 = oracle.layernorm_bwd16(dy16, x16, fmt, g, m64, r64, lib=lib)
+        o32 = oracle.layernorm_bwd(oracle.widen16(dy16, fmt, lib=lib), xw, g, m64, r64, lib=lib)
+        assert np.array_equal(o16["dx64"], o32["dx64"])
+        assert np.array_equal(o16["dx16"], oracle.round16(o32["dx64"], fmt, lib=lib))
+    # the column-sum bound
+    rows, d = 4096, 64
+    x = wl.make_x(rows, d, "normal", [77])
+    dy = wl.make_x(rows, d, "normal", [78])
+    g, _ = wl.make_affine(d, [77])
+    m64, r64 = _exact_stats(x, EPS32)
+    o = oracle.layernorm_bwd(dy, x, g, m64, r64, lib=lib)
+    xh32 = ((x - m64[:, None].astype(np.float32)) * r64[:, None].astype(np.float32)).astype(np.float32)
+    terms32 = (dy * xh32).astype(np.float32)
+    got = terms32.astype(np.float64).sum(axis=0).astype(np.float32)
+    assert oracle.colsum_tolerance_ok(got, o["dgamma64"], o["abs_dgamma"])[0]
+    missing = terms32[1:].astype(np.float64).sum(axis=0).astype(np.float32)
+    assert not oracle.colsum_tolerance_ok(missing, o["dgamma64"], o["abs_dgamma"])[0]
+
+
+BWD_CHECKS = (check_bwd_autograd, check_bwd_finite_differences, check_bwd_invariants, check_bwd16)
+ALL_CHECKS = ALL_CHECKS + BWD_CHECKS

@@ -29,6 +29,10 @@ PLANTS = {
     12: ("16-bit narrowing truncates", (pins.check_round16, pins.check_norm16, pins.check_tolerance16)),
     13: ("16-bit narrowing ties away from zero", (pins.check_round16, pins.check_add16)),
     14: ("16-bit residual dropped", (pins.check_add16, pins.check_norm16)),
+    15: ("layernorm backward mean of g dropped", pins.BWD_CHECKS),
+    16: ("layernorm backward projection sign", pins.BWD_CHECKS),
+    17: ("layernorm backward dgamma without the mean", pins.BWD_CHECKS),
+    18: ("rmsnorm backward outer rstd dropped", pins.BWD_CHECKS),
 }
 
 
