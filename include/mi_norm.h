@@ -157,7 +157,9 @@ typedef enum mi_norm_op {
     MI_NORM_OP_LAYERNORM = 0,
     MI_NORM_OP_RMSNORM = 1,
     MI_NORM_OP_ADD_LAYERNORM = 2,  /* residual add fused before LayerNorm */
-    MI_NORM_OP_ADD_RMSNORM = 3     /* residual add fused before RMSNorm */
+    MI_NORM_OP_ADD_RMSNORM = 3,    /* residual add fused before RMSNorm */
+    MI_NORM_OP_LAYERNORM_BWD = 4,  /* (variant table only) LayerNorm backward */
+    MI_NORM_OP_RMSNORM_BWD = 5     /* (variant table only) RMSNorm backward */
 } mi_norm_op;
 
 typedef enum mi_norm_dtype {
@@ -194,6 +196,80 @@ mi_norm_status mi_norm_fwd(const mi_norm_problem *p, hipStream_t stream);
 /* The argument checks of mi_norm_fwd alone (host logic, nothing launched, no
  * device access): MI_NORM_OK when mi_norm_fwd would accept *p. */
 mi_norm_status mi_norm_check(const mi_norm_problem *p);
+
+/* ---------------------------------------------------------------------------
+ * Backward.  The gradients of the two normalizations with respect to the rows
+ * and the parameters, from the upstream gradient dy and the per-row
+ * statistics the forward returned.  They are the exact derivative of the
+ * definitions above; no page defines them.  Per row i, with
+ * xhat_ij = (x_ij - mean_i) * rstd_i (RMSNorm: x_ij * rstd_i) and
+ * g_ij = dy_ij * gamma_j (RMSNorm: dy_ij * w_j):
+ *     LayerNorm  dx_ij = rstd_i * (g_ij - mean_k g_ik - xhat_ij * mean_k(g_ik xhat_ik))
+ *     RMSNorm    dx_ij = rstd_i * (g_ij - xhat_ij * mean_k(g_ik xhat_ik))
+ * and over all rows dgamma_j (dw_j) = sum_i dy_ij xhat_ij, dbeta_j = sum_i dy_ij.
+ *
+ * dy, x and dx share a storage type (float32, binary16, bfloat16; each with
+ * its own row stride); gamma/w, mean, rstd, dgamma/dw and dbeta are float32.
+ * dx is within 1e-5 + 1e-4 |ref| + 64 u rstd_i (|g_ij| + mean_k |g_ik| +
+ * |xhat_ij| mean_k |g_ik xhat_ik|) of the float64 derivative (plus half a
+ * 16-bit ulp for 16-bit dx): the subtraction of the row means amplifies
+ * float32 rounding by rstd, which is large for rows of near-zero variance.  The parameter gradients are sums over rows: the
+ * terms are formed in float32 and summed in float64 registers, partial sums
+ * of each workgroup are stored as float32 and added in float64 in a fixed
+ * order, so results are deterministic and within 1e-5 + 1e-4 |ref| +
+ * 12 u sum_i |term_i| (u = 2^-24).
+ *
+ * The parameter gradients need device scratch memory that the caller owns:
+ * mi_norm_bwd_workspace_size says how many bytes (it depends on the shape
+ * only); the pointer must be 256-byte aligned.  Its contents on entry do not
+ * matter and are overwritten; it must not overlap any other argument, and two
+ * calls in flight at once need two workspaces.  With dparams0 and dparams1
+ * both NULL only dx is computed (the workspace may still be needed for rows
+ * wider than the held variants).
+ *
+ * Aliasing: dx may be dy or x in place (same pointer and stride) or share no
+ * element with them; dgamma, dbeta and the workspace overlap nothing.  Each
+ * call launches two or three kernels on `stream`.
+ */
+typedef struct mi_norm_bwd_problem {
+    int op;                 /* MI_NORM_OP_LAYERNORM or MI_NORM_OP_RMSNORM */
+    int dtype;              /* mi_norm_dtype of dy, x and dx */
+    int64_t rows;           /* >= 0 */
+    int64_t d;              /* >= 1 */
+    const void *dy;         /* upstream gradient rows                         (required) */
+    int64_t lddy;
+    const void *x;          /* the forward's input rows                       (required) */
+    int64_t ldx;
+    void *dx;               /* gradient rows out                              (required) */
+    int64_t lddx;
+    const float *params0;   /* gamma or w, float32 [d]                        (required) */
+    const float *mean;      /* float32 [rows] from the forward (LayerNorm)    (required) */
+    const float *rstd;      /* float32 [rows] from the forward                (required) */
+    float *dparams0;        /* dgamma or dw, float32 [d], or NULL to skip     */
+    float *dparams1;        /* dbeta, float32 [d] (LayerNorm), or NULL        */
+    void *workspace;        /* device scratch, 256-byte aligned                */
+    int64_t workspace_bytes;
+} mi_norm_bwd_problem;
+
+/* Bytes of workspace mi_norm_bwd needs for *p (its op, dtype, rows, d and
+ * which parameter gradients are wanted; no pointer is consulted); -1 when
+ * those are invalid. */
+int64_t mi_norm_bwd_workspace_size(const mi_norm_bwd_problem *p);
+
+/* Run the backward described by *p on `stream`. */
+mi_norm_status mi_norm_bwd(const mi_norm_bwd_problem *p, hipStream_t stream);
+
+/* The argument checks of mi_norm_bwd alone (nothing launched). */
+mi_norm_status mi_norm_bwd_check(const mi_norm_bwd_problem *p);
+
+/* The float32 contiguous forms (row stride d). */
+mi_norm_status mi_layernorm_bwd(const float *dy, const float *x, const float *gamma,
+                                const float *mean, const float *rstd, float *dx,
+                                float *dgamma, float *dbeta, int64_t rows, int64_t d,
+                                void *workspace, int64_t workspace_bytes, hipStream_t stream);
+mi_norm_status mi_rmsnorm_bwd(const float *dy, const float *x, const float *w,
+                              const float *rstd, float *dx, float *dw, int64_t rows, int64_t d,
+                              void *workspace, int64_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Kernel variants.  Every call above is served by one compiled kernel variant
@@ -242,6 +318,13 @@ int mi_norm_eligible(int id, const mi_norm_problem *p);
  * does not exist, belongs to another operation or storage type, or cannot run
  * these arguments (see mi_norm_eligible). */
 mi_norm_status mi_norm_fwd_variant(int id, const mi_norm_problem *p, hipStream_t stream);
+
+/* The backward's variant queries: the variant mi_norm_bwd would run (-1 when
+ * *p's shape or pointers are invalid), whether variant `id` (op
+ * MI_NORM_OP_*_BWD) can run *p, and *p forced onto it. */
+int mi_norm_bwd_select(const mi_norm_bwd_problem *p);
+int mi_norm_bwd_eligible(int id, const mi_norm_bwd_problem *p);
+mi_norm_status mi_norm_bwd_variant(int id, const mi_norm_bwd_problem *p, hipStream_t stream);
 
 /* The named float32 calls forced onto variant `id`, as mi_norm_fwd_variant. */
 mi_norm_status mi_layernorm_fwd_variant(int id, const float *x, const float *gamma,

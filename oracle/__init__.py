@@ -65,9 +65,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     ]
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.oracle_layernorm_bwd_f64.restype = None
-    lib.oracle_layernorm_bwd_f64.argtypes = [vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_layernorm_bwd_f64.argtypes = [vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_rmsnorm_bwd_f64.restype = None
-    lib.oracle_rmsnorm_bwd_f64.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, vp]
+    lib.oracle_rmsnorm_bwd_f64.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_plant.restype = ctypes.c_int
@@ -329,9 +329,11 @@ def layernorm_bwd(dy, x, gamma, mean, rstd, lib: ctypes.CDLL | None = None) -> d
     """LayerNorm backward from the upstream gradient dy and the forward's
     per-row statistics (float32 or float64; widened exactly).
 
-    Returns a dict: dx (float32) and dx64, dgamma/dbeta (float32) and
-    dgamma64/dbeta64, and abs_dgamma/abs_dbeta (sum over rows of |dy xhat|
-    and |dy|, the magnitudes a float32 column sum's error scales with)."""
+    Returns a dict: dx (float32) and dx64, dx_scale (per element, the
+    magnitudes a float32 evaluation of dx carries error in proportion to),
+    dgamma/dbeta (float32) and dgamma64/dbeta64, and abs_dgamma/abs_dbeta
+    (sum over rows of |dy xhat| and |dy|, the magnitudes a float32 column
+    sum's error scales with)."""
     lib = lib or load()
     dy, x = _f32(dy, "dy"), _f32(x, "x")
     if x.ndim != 2 or dy.shape != x.shape:
@@ -341,18 +343,19 @@ def layernorm_bwd(dy, x, gamma, mean, rstd, lib: ctypes.CDLL | None = None) -> d
     if d < 1 or gamma.size != d:
         raise ValueError("need d >= 1 and gamma of length d")
     m64, r64 = _stats64(mean, rows, "mean"), _stats64(rstd, rows, "rstd")
-    out = dict(dx=np.empty_like(x), dx64=np.empty(x.shape, np.float64),
+    out = dict(dx=np.empty_like(x), dx64=np.empty(x.shape, np.float64), dx_scale=np.empty(x.shape, np.float64),
                dgamma=np.empty(d, np.float32), dbeta=np.empty(d, np.float32),
                dgamma64=np.empty(d), dbeta64=np.empty(d), abs_dgamma=np.empty(d), abs_dbeta=np.empty(d))
     lib.oracle_layernorm_bwd_f64(_ptr(dy), _ptr(x), _ptr(gamma), _ptr(m64), _ptr(r64), rows, d,
-                                 _ptr(out["dx"]), _ptr(out["dx64"]), _ptr(out["dgamma"]), _ptr(out["dbeta"]),
+                                 _ptr(out["dx"]), _ptr(out["dx64"]), _ptr(out["dx_scale"]),
+                                 _ptr(out["dgamma"]), _ptr(out["dbeta"]),
                                  _ptr(out["dgamma64"]), _ptr(out["dbeta64"]), _ptr(out["abs_dgamma"]),
                                  _ptr(out["abs_dbeta"]))
     return out
 
 
 def rmsnorm_bwd(dy, x, w, rstd, lib: ctypes.CDLL | None = None) -> dict:
-    """RMSNorm backward; dict with dx, dx64, dw, dw64, abs_dw."""
+    """RMSNorm backward; dict with dx, dx64, dx_scale, dw, dw64, abs_dw."""
     lib = lib or load()
     dy, x = _f32(dy, "dy"), _f32(x, "x")
     if x.ndim != 2 or dy.shape != x.shape:
@@ -362,10 +365,11 @@ def rmsnorm_bwd(dy, x, w, rstd, lib: ctypes.CDLL | None = None) -> dict:
     if d < 1 or w.size != d:
         raise ValueError("need d >= 1 and w of length d")
     r64 = _stats64(rstd, rows, "rstd")
-    out = dict(dx=np.empty_like(x), dx64=np.empty(x.shape, np.float64), dw=np.empty(d, np.float32),
-               dw64=np.empty(d), abs_dw=np.empty(d))
+    out = dict(dx=np.empty_like(x), dx64=np.empty(x.shape, np.float64), dx_scale=np.empty(x.shape, np.float64),
+               dw=np.empty(d, np.float32), dw64=np.empty(d), abs_dw=np.empty(d))
     lib.oracle_rmsnorm_bwd_f64(_ptr(dy), _ptr(x), _ptr(w), _ptr(r64), rows, d, _ptr(out["dx"]),
-                               _ptr(out["dx64"]), _ptr(out["dw"]), _ptr(out["dw64"]), _ptr(out["abs_dw"]))
+                               _ptr(out["dx64"]), _ptr(out["dx_scale"]), _ptr(out["dw"]), _ptr(out["dw64"]),
+                               _ptr(out["abs_dw"]))
     return out
 
 
@@ -388,14 +392,17 @@ def rmsnorm_bwd16(dy, x, fmt: int, w, rstd, lib: ctypes.CDLL | None = None) -> d
 U32 = 2.0 ** -24  # unit roundoff of float32
 
 
-def colsum_tolerance_ok(got, ref64, abs_sum, atol: float = 1e-5, rtol: float = 1e-4, k: float = 8.0):
+def colsum_tolerance_ok(got, ref64, abs_sum, atol: float = 1e-5, rtol: float = 1e-4, k: float = 12.0):
     """Acceptance for a float32 sum over rows (the parameter gradients).
 
-    The float32 bound of the forward outputs plus k * u * sum|terms|: each
-    term dy * xhat carries a few float32 roundings (relative error <= ~3.1u),
-    the partial sums are each rounded once to float32 (together <= u *
-    sum|terms|), accumulation is float64 and the final rounding is inside
-    rtol; k = 8 leaves margin.  Returns ``(ok, max_abs_err, max_ratio)``."""
+    The float32 bound of the forward outputs plus k * u * sum|terms|, from
+    the arithmetic the kernels use: each term dy * xhat carries three float32
+    roundings (x - mean, times rstd, times dy: relative error <= ~3u); a lane
+    adds its terms in float64 and rounds the sum once to float32 (<= u); the
+    row slots of a workgroup meet in a float32 tree of at most three levels
+    (<= 3u); the partial rows are added in float64 and rounded once, which
+    rtol covers.  That is <= 7u * sum|terms|; k = 12 leaves margin.
+    Returns ``(ok, max_abs_err, max_ratio)``."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref64, np.float64)
     a = np.asarray(abs_sum, np.float64)
@@ -407,6 +414,39 @@ def colsum_tolerance_ok(got, ref64, abs_sum, atol: float = 1e-5, rtol: float = 1
         return False, float("inf"), float("inf")
     err = np.abs(got - ref)
     bound = atol + rtol * np.abs(ref) + k * U32 * a
+    return bool(np.all(err <= bound)), float(err.max()), float((err / bound).max())
+
+
+def dx_tolerance_ok(got, ref64, scale64, fmt: int | None = None, atol: float = 1e-5, rtol: float = 1e-4,
+                    k: float = 64.0, lib: ctypes.CDLL | None = None):
+    """Acceptance for dx: the float32 bound plus k * u * scale (and, for a
+    16-bit dx given as patterns with ``fmt``, half a 16-bit ulp).
+
+    dx = rstd * (g - mean(g) - xhat * mean(g xhat)) subtracts quantities of
+    the size of |g|, mean|g| and |xhat| mean|g xhat| (``dx_scale`` holds
+    rstd times their sum): a float32 evaluation errs by a few u of each local
+    term and by the summation depth times u of each mean.  The kernels' row
+    sums have depth <= 48 (at most 32 values per lane, six cross-lane steps,
+    up to eight waves, the division); the local terms add a few roundings;
+    k = 64 covers both.  When rstd is large (a row of near-zero variance
+    gives ~1/sqrt(eps)), these errors are far above the float32 bound of the
+    forward outputs while the exact dx may be ~0, which is why the bound
+    scales with rstd.  Returns ``(ok, max_abs_err, max_ratio)``."""
+    ref = np.asarray(ref64, np.float64)
+    if fmt is None:
+        got = np.asarray(got, np.float64)
+    else:
+        got = widen16(got, fmt, lib).astype(np.float64)
+    s = np.asarray(scale64, np.float64)
+    if got.shape != ref.shape or s.shape != ref.shape:
+        return False, float("inf"), float("inf")
+    if got.size == 0:
+        return True, 0.0, 0.0
+    if not np.all(np.isfinite(got)):
+        return False, float("inf"), float("inf")
+    tau = atol + rtol * np.abs(ref) + k * U32 * s
+    bound = tau if fmt is None else tau + 0.5 * ulp16(np.maximum(np.abs(got), np.abs(ref) + tau), fmt)
+    err = np.abs(got - ref)
     return bool(np.all(err <= bound)), float(err.max()), float((err / bound).max())
 
 

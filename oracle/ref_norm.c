@@ -366,27 +366,33 @@ void oracle_add16_n(const uint16_t *x, const uint16_t *r, int fmt, int64_t n, ui
  * or exact ones for the pins).  Everything is float64 from the float32
  * inputs; dx is rounded once to
  * float32 (dx64 optionally keeps it unrounded), the parameter gradients
- * likewise (dg64/db64 unrounded).  adg64/adb64 optionally receive
+ * likewise (dg64/db64 unrounded).  dxs64 optionally receives, per element,
+ * rho_i * (|g_ij| + mean_k |g_ik| + |xhat_ij| * mean_k |g_ik xhat_ik|)
+ * (RMSNorm without the middle term): the magnitudes a float32 evaluation of
+ * dx carries rounding error in proportion to.  adg64/adb64 optionally receive
  * sum_i |dy_ij xhat_ij| and sum_i |dy_ij|, the magnitudes a float32 column
  * sum's rounding error scales with.  Any optional output may be NULL.
  */
 void oracle_layernorm_bwd_f64(const float *dy, const float *x, const float *gamma,
                               const double *mean, const double *rstd, int64_t rows, int64_t d,
-                              float *dx, double *dx64, float *dgamma, float *dbeta,
+                              float *dx, double *dx64, double *dxs64, float *dgamma, float *dbeta,
                               double *dg64, double *db64, double *adg64, double *adb64)
 {
     #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < rows; ++i) {
         const float *xi = x + i * d, *dyi = dy + i * d;
         const double mu = mean[i], rho = rstd[i];
-        double s1 = 0.0, s2 = 0.0;
+        double s1 = 0.0, s2 = 0.0, a1 = 0.0, a2 = 0.0;
         for (int64_t k = 0; k < d; ++k) {
             const double xh = ((double)xi[k] - mu) * rho;
             const double g = (double)dyi[k] * (double)gamma[k];
             s1 += g;
             s2 += g * xh;
+            a1 += fabs(g);
+            a2 += fabs(g * xh);
         }
         const double m1 = s1 / (double)d, m2 = s2 / (double)d;
+        const double am1 = a1 / (double)d, am2 = a2 / (double)d;
         for (int64_t j = 0; j < d; ++j) {
             const double xh = ((double)xi[j] - mu) * rho;
             const double g = (double)dyi[j] * (double)gamma[j];
@@ -399,6 +405,7 @@ void oracle_layernorm_bwd_f64(const float *dy, const float *x, const float *gamm
 #endif
             if (dx) dx[i * d + j] = (float)v;
             if (dx64) dx64[i * d + j] = v;
+            if (dxs64) dxs64[i * d + j] = rho * (fabs(g) + am1 + fabs(xh) * am2);
         }
     }
     /* column sums, rows in ascending order */
@@ -426,17 +433,20 @@ void oracle_layernorm_bwd_f64(const float *dy, const float *x, const float *gamm
 }
 
 void oracle_rmsnorm_bwd_f64(const float *dy, const float *x, const float *w, const double *rstd,
-                            int64_t rows, int64_t d, float *dx, double *dx64, float *dw,
+                            int64_t rows, int64_t d, float *dx, double *dx64, double *dxs64, float *dw,
                             double *dw64, double *adw64)
 {
     #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < rows; ++i) {
         const float *xi = x + i * d, *dyi = dy + i * d;
         const double rho = rstd[i];
-        double s2 = 0.0;
-        for (int64_t k = 0; k < d; ++k)
-            s2 += (double)dyi[k] * (double)w[k] * ((double)xi[k] * rho);
-        const double m2 = s2 / (double)d;
+        double s2 = 0.0, a2 = 0.0;
+        for (int64_t k = 0; k < d; ++k) {
+            const double t = (double)dyi[k] * (double)w[k] * ((double)xi[k] * rho);
+            s2 += t;
+            a2 += fabs(t);
+        }
+        const double m2 = s2 / (double)d, am2 = a2 / (double)d;
         for (int64_t j = 0; j < d; ++j) {
             const double xh = (double)xi[j] * rho;
             const double g = (double)dyi[j] * (double)w[j];
@@ -446,6 +456,7 @@ void oracle_rmsnorm_bwd_f64(const float *dy, const float *x, const float *w, con
 #endif
             if (dx) dx[i * d + j] = (float)v;
             if (dx64) dx64[i * d + j] = v;
+            if (dxs64) dxs64[i * d + j] = rho * (fabs(g) + fabs(xh) * am2);
         }
     }
     #pragma omp parallel for schedule(static)

@@ -29,6 +29,8 @@ OP_LAYERNORM = 0
 OP_RMSNORM = 1
 OP_ADD_LAYERNORM = 2
 OP_ADD_RMSNORM = 3
+OP_LAYERNORM_BWD = 4
+OP_RMSNORM_BWD = 5
 MI_NORM_F32 = 0
 MI_NORM_F16 = 1
 MI_NORM_BF16 = 2
@@ -68,6 +70,17 @@ class Problem(ctypes.Structure):
     ]
 
 
+class BwdProblem(ctypes.Structure):
+    """mi_norm_bwd_problem: one backward call in full."""
+    _fields_ = [
+        ("op", ctypes.c_int), ("dtype", ctypes.c_int), ("rows", ctypes.c_int64), ("d", ctypes.c_int64),
+        ("dy", ctypes.c_void_p), ("lddy", ctypes.c_int64), ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64),
+        ("dx", ctypes.c_void_p), ("lddx", ctypes.c_int64), ("params0", ctypes.c_void_p),
+        ("mean", ctypes.c_void_p), ("rstd", ctypes.c_void_p), ("dparams0", ctypes.c_void_p),
+        ("dparams1", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
+    ]
+
+
 _VP = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _F = ctypes.c_float
@@ -94,6 +107,14 @@ _SIGNATURES = {
     "mi_layernorm_fwd_variant": (_I, [_I, _VP, _VP, _VP, _VP, _I64, _I64, _F, _VP, _VP, _VP]),
     "mi_rmsnorm_fwd_variant": (_I, [_I, _VP, _VP, _VP, _I64, _I64, _F, _VP, _VP]),
     "mi_copy_f32": (_I, [_VP, _VP, _I64, _VP]),
+    "mi_norm_bwd_workspace_size": (_I64, [ctypes.POINTER(BwdProblem)]),
+    "mi_norm_bwd": (_I, [ctypes.POINTER(BwdProblem), _VP]),
+    "mi_norm_bwd_check": (_I, [ctypes.POINTER(BwdProblem)]),
+    "mi_norm_bwd_select": (_I, [ctypes.POINTER(BwdProblem)]),
+    "mi_norm_bwd_eligible": (_I, [_I, ctypes.POINTER(BwdProblem)]),
+    "mi_norm_bwd_variant": (_I, [_I, ctypes.POINTER(BwdProblem), _VP]),
+    "mi_layernorm_bwd": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _VP, _I64, _VP]),
+    "mi_rmsnorm_bwd": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _VP, _I64, _VP]),
 }
 
 
@@ -301,6 +322,59 @@ def mi_norm_eligible(vid: int, p: Problem) -> bool:
     return bool(lib().mi_norm_eligible(vid, ctypes.byref(p)))
 
 
+def bwd_problem(op: int, rows: int, d: int, dy, x, dx, params0, mean=None, rstd=None, dparams0=None,
+                dparams1=None, workspace=None, workspace_bytes: int = 0, *, dtype: int = MI_NORM_F32,
+                lddy: int = 0, ldx: int = 0, lddx: int = 0) -> BwdProblem:
+    """An mi_norm_bwd_problem (op OP_LAYERNORM or OP_RMSNORM) from tensors or
+    integer addresses."""
+    return BwdProblem(op, dtype, rows, d, _addr(dy), lddy, _addr(x), ldx, _addr(dx), lddx, _addr(params0),
+                      _addr(mean), _addr(rstd), _addr(dparams0), _addr(dparams1), _addr(workspace),
+                      workspace_bytes)
+
+
+def mi_norm_bwd_workspace_size(p: BwdProblem) -> int:
+    return int(lib().mi_norm_bwd_workspace_size(ctypes.byref(p)))
+
+
+def mi_norm_bwd(p: BwdProblem, stream=None) -> None:
+    _check(lib().mi_norm_bwd(ctypes.byref(p), _stream(stream)), "mi_norm_bwd")
+
+
+def mi_norm_bwd_check(p: BwdProblem) -> int:
+    return int(lib().mi_norm_bwd_check(ctypes.byref(p)))
+
+
+def mi_norm_bwd_select(p: BwdProblem) -> int:
+    return int(lib().mi_norm_bwd_select(ctypes.byref(p)))
+
+
+def mi_norm_bwd_eligible(vid: int, p: BwdProblem) -> bool:
+    return bool(lib().mi_norm_bwd_eligible(vid, ctypes.byref(p)))
+
+
+def mi_norm_bwd_variant(vid: int, p: BwdProblem, stream=None) -> None:
+    _check(lib().mi_norm_bwd_variant(vid, ctypes.byref(p), _stream(stream)), f"mi_norm_bwd_variant({vid})")
+
+
+def mi_layernorm_bwd(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, rows: int, d: int, workspace,
+                     workspace_bytes: int, stream=None) -> None:
+    n = max(rows, 0) * max(d, 0)
+    st = lib().mi_layernorm_bwd(_ptr(dy, "dy", n), _ptr(x, "x", n), _ptr(gamma, "gamma", d),
+                                _ptr(mean, "mean", rows), _ptr(rstd, "rstd", rows), _ptr(dx, "dx", n),
+                                _ptr(dgamma, "dgamma", d), _ptr(dbeta, "dbeta", d), rows, d,
+                                _addr(workspace), workspace_bytes, _stream(stream, dy, dx))
+    _check(st, "mi_layernorm_bwd")
+
+
+def mi_rmsnorm_bwd(dy, x, w, rstd, dx, dw, rows: int, d: int, workspace, workspace_bytes: int,
+                   stream=None) -> None:
+    n = max(rows, 0) * max(d, 0)
+    st = lib().mi_rmsnorm_bwd(_ptr(dy, "dy", n), _ptr(x, "x", n), _ptr(w, "w", d), _ptr(rstd, "rstd", rows),
+                              _ptr(dx, "dx", n), _ptr(dw, "dw", d), rows, d, _addr(workspace), workspace_bytes,
+                              _stream(stream, dy, dx))
+    _check(st, "mi_rmsnorm_bwd")
+
+
 # --- conveniences over torch tensors (allocation is torch's) -------------------
 
 def _dtype_code(t) -> int:
@@ -391,6 +465,48 @@ def add_rmsnorm(x, r, w, eps: float = 1e-5, stats: bool = False, write_sum: bool
     """h = x + r, y = RMSNorm(h).  Returns (y, h) or (y, h, rstd)."""
     y, h, _, rstd = _norm(OP_ADD_RMSNORM, x, r, w, None, eps, stats, None, write_sum, stream)
     return (y, h, rstd) if stats else (y, h)
+
+
+def _norm_bwd(op, dy, x, p0, mean, rstd, param_grads, out, stream):
+    import torch
+    dt = _dtype_code(x)
+    if dy.dtype != x.dtype or dy.shape != x.shape:
+        raise ValueError("dy must have x's shape and dtype")
+    d = x.shape[-1]
+    rows, ldx = _rows_of(x, "x")
+    lddy = _rows_of(dy, "dy")[1]
+    dx = torch.empty(x.shape, device=x.device, dtype=x.dtype) if out is None else out
+    if dx.dtype != x.dtype or dx.shape != x.shape:
+        raise ValueError("out must have x's shape and dtype")
+    lddx = _rows_of(dx, "out")[1]
+    ln = op == OP_LAYERNORM
+    for t, name in ((mean, "mean"), (rstd, "rstd")):
+        if t is None:
+            continue
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != rows:
+            raise ValueError(f"{name} must be a contiguous float32 tensor of one value per row")
+    dp0 = torch.empty(d, device=x.device, dtype=torch.float32) if param_grads else None
+    dp1 = torch.empty(d, device=x.device, dtype=torch.float32) if (param_grads and ln) else None
+    p = bwd_problem(op, rows, d, dy, x, dx, _params(p0, "gamma" if ln else "w", d), mean, rstd, dp0, dp1,
+                    dtype=dt, lddy=lddy, ldx=ldx, lddx=lddx)
+    nbytes = mi_norm_bwd_workspace_size(p)
+    ws = torch.empty(max(nbytes, 1), device=x.device, dtype=torch.uint8) if nbytes > 0 else None
+    p.workspace, p.workspace_bytes = (ws.data_ptr() if ws is not None else None), max(nbytes, 0)
+    mi_norm_bwd(p, stream if stream is not None else torch.cuda.current_stream(x.device).cuda_stream)
+    return dx, dp0, dp1
+
+
+def layernorm_bwd(dy, x, gamma, mean, rstd, param_grads: bool = True, out=None, stream=None):
+    """LayerNorm backward from the forward's mean/rstd: returns (dx, dgamma,
+    dbeta), the parameter gradients None without ``param_grads``.  ``out``
+    may be dy or x (in place).  The workspace is a torch allocation."""
+    return _norm_bwd(OP_LAYERNORM, dy, x, gamma, mean, rstd, param_grads, out, stream)
+
+
+def rmsnorm_bwd(dy, x, w, rstd, param_grads: bool = True, out=None, stream=None):
+    """RMSNorm backward from the forward's rstd: returns (dx, dw)."""
+    dx, dw, _ = _norm_bwd(OP_RMSNORM, dy, x, w, None, rstd, param_grads, out, stream)
+    return dx, dw
 
 
 def rmsnorm(x, w, eps: float = 1e-5, stats: bool = False, out=None, stream=None):

@@ -2,9 +2,11 @@
 
 Two steps:
 
-1. ``hipcc -c`` compiles, in parallel, csrc/mi_norm.hip (the host-side
-   dispatcher, launcher and C ABI) and one variant table per row storage type
-   (csrc/variants_{f32,f16,bf16}.hip: the gfx950 device code) into objects.
+1. ``hipcc -c`` compiles, in parallel, the host-side dispatchers, launchers
+   and C ABI (csrc/mi_norm.hip forward, csrc/mi_norm_bwd.hip backward) and one
+   variant table per row storage type and direction
+   (csrc/variants_*.hip, csrc/bwd_variants_*.hip: the gfx950 device code)
+   into objects.
 2. ``g++ -shared`` links them against the HIP runtime that PyTorch ships.
 
 The link step matters: torch's ``libamdhip64.so`` carries no SONAME and is
@@ -31,8 +33,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmi_norm.so")
 BENCH_LIB = os.path.join(PKG, "libmi_norm_bench.so")
-SOURCES = ("mi_norm.hip", "variants_f32.hip", "variants_f16.hip", "variants_bf16.hip")
-HEADERS = ("norm_kernels.hpp", "variant_table.hpp")
+SOURCES = ("mi_norm.hip", "variants_f32.hip", "variants_f16.hip", "variants_bf16.hip",
+           "mi_norm_bwd.hip", "bwd_variants_f32.hip", "bwd_variants_f16.hip", "bwd_variants_bf16.hip")
+HEADERS = ("norm_kernels.hpp", "variant_table.hpp", "host_common.hpp", "bwd_kernels.hpp", "bwd_table.hpp")
 BENCH_SOURCES = ("bench_loop.cpp",)
 ARCH = "gfx950"
 

@@ -19,9 +19,11 @@
 
 #include "mi_norm.h"
 #include "norm_kernels.hpp"
+#include "host_common.hpp"
 #include "variant_table.hpp"
 
 using namespace minorm;
+using namespace minorm::host;
 
 namespace minorm {
 
@@ -59,39 +61,10 @@ void copy_f1(const float *src, float *dst, int64_t n)
 
 namespace {
 
-constexpr int kDtypes = 3;
-
-// the three tables as one id space: float32 ids first, then binary16, bfloat16
-const VariantTable &table(int dtype) {
-    return dtype == MI_NORM_F32 ? kTableF32 : (dtype == MI_NORM_F16 ? kTableF16 : kTableBF16);
-}
-int table_base(int dtype) {
-    int base = 0;
-    for (int t = 0; t < dtype; ++t) base += table(t).n;
-    return base;
-}
-int num_variants() { return table_base(kDtypes); }
-const Variant *variant(int id) {
-    if (id < 0) return nullptr;
-    for (int t = 0; t < kDtypes; ++t) {
-        if (id < table(t).n) return &table(t).v[id];
-        id -= table(t).n;
-    }
-    return nullptr;
-}
-
 // grid cap of the grid-stride (streamed-row and copy) kernels
 constexpr int64_t kMaxGrid = 1 << 20;
 // row groups per launch of a held-row kernel
 constexpr int64_t kMaxRowGroups = int64_t(1) << 30;
-
-inline uintptr_t addr(const void *p) { return reinterpret_cast<uintptr_t>(p); }
-inline bool aligned(const void *p, uintptr_t a) { return (addr(p) & (a - 1)) == 0; }
-inline bool al16(const void *p) { return aligned(p, 16); }
-inline bool al4(const void *p) { return aligned(p, 4); }
-inline int64_t esize(int dtype) { return dtype == MI_NORM_F32 ? 4 : 2; }
-// elements per vector access of the vector paths: 16 bytes of any storage type
-inline int64_t vwidth(int dtype) { return 16 / esize(dtype); }
 
 // Fewest workgroups that still cover every CU: of the variants with this
 // shape, the one with the most waves per workgroup whose grid has at least
@@ -123,18 +96,6 @@ int find(int op, int dtype, int64_t rows, int vec, int peel, int looped, int lpr
     return pick >= 0 ? base + pick : -1;
 }
 
-// smallest listed slot count q with cap_per_slot * q >= n, or 0
-int pick_q(int64_t n, int64_t cap_per_slot, const int *qs, int nq) {
-    for (int i = 0; i < nq; ++i)
-        if (cap_per_slot * qs[i] >= n) return qs[i];
-    return 0;
-}
-
-// Waves per row and slots for a row of nvec vector accesses (wpr = 0 when the
-// row is too wide to hold).  About four accesses per lane measured best
-// across widths (more per lane cut occupancy, fewer add waves and exchange
-// traffic); with few rows, a row is spread over more waves until the grid
-// holds 4096 waves, as long as every wave keeps one full access per lane.
 // Slots above six are only ever needed at 16 waves per row; the peeled
 // 16-bit path has none there (max_slots 6).
 void shape_vectors(int64_t nvec, int64_t rows, int &wpr, int &q, int max_slots = 8) {
@@ -256,31 +217,6 @@ bool eligible(int id, const mi_norm_problem &P) {
     if (v.peel) return L.peel_ok && (P.d + v.vec - 1) / v.vec <= v.max_d / v.vec;
     if (v.vec > 1) return L.aq && P.d <= v.max_d;
     return P.d <= v.max_d;
-}
-
-// byte ranges [lo, hi)
-struct Ext {
-    uintptr_t lo, hi;
-};
-inline bool meet(Ext a, Ext b) { return a.lo < b.hi && b.lo < a.hi; }
-inline Ext vec_ext(const void *p, int64_t n, int64_t es) { return Ext{addr(p), addr(p) + (uintptr_t)(n * es)}; }
-inline Ext rows_ext(const void *p, int64_t ld, int64_t rows, int64_t d, int64_t es) {
-    return Ext{addr(p), addr(p) + (uintptr_t)(((rows - 1) * ld + d) * es)};
-}
-
-// Whether two row tensors of one problem share an element.  With equal
-// strides and an element-multiple offset it is exact: b's rows then sit at
-// column offset m = offset mod ld of a's row slots, and the two are disjoint
-// exactly when [m, m + d) stays inside [d, ld).  Otherwise any overlap of
-// their extents counts.
-bool rows_meet(const void *a, int64_t lda, const void *b, int64_t ldb, int64_t rows, int64_t d,
-               int64_t es) {
-    if (!meet(rows_ext(a, lda, rows, d, es), rows_ext(b, ldb, rows, d, es))) return false;
-    if (lda != ldb) return true;
-    const int64_t delta = (int64_t)(addr(b) - addr(a));
-    if (delta % es != 0) return true;
-    const int64_t m = ((delta / es) % lda + lda) % lda;
-    return !(m >= d && m + d <= lda);
 }
 
 // Aliasing rules (see the header): an output row tensor is an input row

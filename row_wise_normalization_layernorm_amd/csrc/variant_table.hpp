@@ -24,7 +24,8 @@ struct VariantTable {
     int n;
 };
 
-extern const VariantTable kTableF32, kTableF16, kTableBF16;
+extern const VariantTable kTableF32, kTableF16, kTableBF16;           // forward
+extern const VariantTable kBwdTableF32, kBwdTableF16, kBwdTableBF16;  // backward
 
 constexpr int64_t kUnbounded = INT64_MAX;
 

@@ -694,3 +694,34 @@ def check_bwd16(lib):
 
 BWD_CHECKS = (check_bwd_autograd, check_bwd_finite_differences, check_bwd_invariants, check_bwd16)
 ALL_CHECKS = ALL_CHECKS + BWD_CHECKS
+
+
+def check_dx_tolerance(lib):
+    """The dx acceptance bound passes a float32 evaluation of the same formula
+    (including rows of zero variance, where rstd ~ 1/sqrt(eps) amplifies its
+    rounding), and refuses dx without the mean of g or with a flipped
+    projection term."""
+    for rows, d, pat in ((64, 1, "normal"), (32, 256, "normal"), (16, 8, "zero"), (16, 77, "offset")):
+        x = wl.make_x(rows, d, pat, [80, d])
+        dy = wl.make_x(rows, d, "normal", [81, d])
+        g, _ = wl.make_affine(d, [80, d])
+        _, mean, rstd, _, _ = oracle.layernorm(x, g, np.zeros(d, np.float32), float(EPS32), lib=lib)
+        ref = oracle.layernorm_bwd(dy, x, g, mean, rstd, lib=lib)
+        # a float32 evaluation: every operation rounded to float32
+        f = np.float32
+        xh = ((x - mean[:, None]).astype(f) * rstd[:, None]).astype(f)
+        gg = (dy * g).astype(f)
+        m1 = (gg.sum(axis=1, dtype=f) * f(1.0 / d)).astype(f)
+        m2 = ((gg * xh).astype(f).sum(axis=1, dtype=f) * f(1.0 / d)).astype(f)
+        dx32 = (rstd[:, None] * ((gg - m1[:, None]).astype(f) - (xh * m2[:, None]).astype(f)).astype(f)).astype(f)
+        ok, _, ratio = oracle.dx_tolerance_ok(dx32, ref["dx64"], ref["dx_scale"])
+        assert ok, f"float32 evaluation refused ({rows}x{d} {pat}, ratio {ratio:.2f})"
+        if d > 1 and pat != "zero":
+            bad = ref["dx64"] + rstd[:, None].astype(np.float64) * (gg.astype(np.float64).mean(axis=1))[:, None]
+            assert not oracle.dx_tolerance_ok(bad, ref["dx64"], ref["dx_scale"])[0], "mean of g dropped"
+            proj = 2 * (rstd[:, None] * xh.astype(np.float64) * m2[:, None])   # the term with its sign flipped
+            assert not oracle.dx_tolerance_ok(ref["dx64"] + proj, ref["dx64"], ref["dx_scale"])[0], "projection sign"
+
+
+BWD_CHECKS = BWD_CHECKS + (check_dx_tolerance,)
+ALL_CHECKS = ALL_CHECKS + (check_dx_tolerance,)

@@ -190,12 +190,34 @@ DTSFX = {mn.MI_NORM_F32: "", mn.MI_NORM_F16: "f16_", mn.MI_NORM_BF16: "bf16_"}
 ESIZE = {mn.MI_NORM_F32: 4, mn.MI_NORM_F16: 2, mn.MI_NORM_BF16: 2}
 
 
+BWD_PREFIX = {mn.OP_LAYERNORM_BWD: "lnbwd_", mn.OP_RMSNORM_BWD: "rmsbwd_"}
+
+
 def test_variant_table_is_consistent(L):
-    infos = _infos()
-    names = [n for _, n, _ in infos]
+    everything = _infos()
+    names = [n for _, n, _ in everything]
     assert len(set(names)) == len(names)
-    assert mn.mi_norm_variant_name(len(infos)) is None
+    assert mn.mi_norm_variant_name(len(everything)) is None
     assert mn.mi_norm_variant_name(-1) is None
+    infos = [t for t in everything if t[2]["op"] in OPS]
+    bwd = [t for t in everything if t[2]["op"] in BWD_PREFIX]
+    assert len(infos) + len(bwd) == len(everything)
+    # forward ids first, then backward
+    assert max(i for i, _, _ in infos) < min(i for i, _, _ in bwd)
+    for i, n, v in bwd:
+        assert n.startswith(BWD_PREFIX[v["op"]] + DTSFX[v["dtype"]]), n
+        assert v["lanes_per_row"] == 64 and not v["peel"]
+        if v["looped"]:
+            assert v["max_d"] == 2**63 - 1 and v["vec"] == 1 and v["needs_aligned"] == 0
+            continue
+        assert v["waves_per_block"] == 8 and v["rows_per_block"] * v["waves_per_row"] == 8
+        assert v["max_d"] == v["vec"] * 64 * v["waves_per_row"] * v["slots"]
+        assert v["needs_aligned"] == (1 if v["vec"] > 1 else 0)
+        assert v["vec"] in (1, 16 // ESIZE[v["dtype"]])
+        # LayerNorm lanes hold at most 24 vector values, RMSNorm 32
+        if v["vec"] > 1:
+            assert v["vec"] * v["slots"] <= (24 if v["op"] == mn.OP_LAYERNORM_BWD else 32), n
+    assert {(v["op"], v["dtype"]) for _, _, v in bwd} == {(o, t) for o in BWD_PREFIX for t in DTYPES}
     for i, n, v in infos:
         assert n.startswith(PREFIX[v["op"]] + DTSFX[v["dtype"]]), n
         if v["dtype"] == mn.MI_NORM_F32:
@@ -314,6 +336,8 @@ def test_rows_spread_over_more_waves_when_few(L):
 def test_eligibility_rules(L):
     for i, n, v in _infos():
         op, dt = v["op"], v["dtype"]
+        if op not in OPS:
+            continue                     # backward variants: test_bwd_dispatch_covers_every_width
         other = {0: 1, 1: 0, 2: 3, 3: 2}[op]
         assert not mn.mi_norm_eligible(i, _prob(other, 16, 64, dtype=dt))
         assert not mn.mi_norm_eligible(i, _prob(op, 16, 64, dtype=(dt + 1) % 3))
@@ -404,3 +428,105 @@ def test_named_calls_equal_the_general_call(L):
     assert mn.mi_norm_variant_name(mn.mi_norm_select(p)) == "addrms_4_p0_l64_w1_q3_b16"
     assert L.mi_add_rmsnorm_fwd(X, R_, G, Y, Y, 4, 8, 1e-5, None, None) == mn.MI_NORM_ERR_INVALID
     assert mn.mi_norm_check(_prob(mn.OP_ADD_RMSNORM, 4, 8, h=Y)) == mn.MI_NORM_ERR_INVALID
+
+
+# --- backward: validation, workspace and dispatch (host logic) ------------------
+
+DY, DX, MEAN, RSTD, DG, DB, WS = (0x7F0700000000, 0x7F0800000000, 0x7F0900000000, 0x7F0A00000000,
+                                  0x7F0B00000000, 0x7F0C00000000, 0x7F0D00000000)
+
+
+def _bprob(op=mn.OP_LAYERNORM, rows=64, d=768, ws=WS, ws_bytes=None, **kw):
+    ln = op == mn.OP_LAYERNORM
+    args = dict(dy=DY, x=X, dx=DX, params0=G, mean=MEAN if ln else None, rstd=RSTD, dparams0=DG,
+                dparams1=DB if ln else None)
+    ptr_keys = set(args)
+    args.update({k: v for k, v in kw.items() if k in ptr_keys})
+    rest = {k: v for k, v in kw.items() if k not in ptr_keys}
+    p = mn.bwd_problem(op, rows, d, args["dy"], args["x"], args["dx"], args["params0"], args["mean"], args["rstd"],
+                       args["dparams0"], args["dparams1"], ws, 0, **rest)
+    p.workspace_bytes = mn.mi_norm_bwd_workspace_size(p) if ws_bytes is None else ws_bytes
+    return p
+
+
+def test_bwd_workspace_size(L):
+    p = _bprob(rows=4096, d=768)
+    n = mn.mi_norm_bwd_workspace_size(p)
+    # 512 partial rows of (dgamma, dbeta), then the per-row statistics; 256-byte sections
+    assert n == 512 * 2 * 768 * 4 + 4096 * 8
+    assert mn.mi_norm_bwd_workspace_size(_bprob(op=mn.OP_RMSNORM, rows=4096, d=768)) == 512 * 768 * 4 + 4096 * 8
+    assert mn.mi_norm_bwd_workspace_size(_bprob(rows=3, d=5)) == 512 * 2 * 8 * 4 + 256
+    # no parameter gradients: only the statistics section
+    assert mn.mi_norm_bwd_workspace_size(_bprob(rows=100, d=64, dparams0=None, dparams1=None)) == 1024
+    assert mn.mi_norm_bwd_workspace_size(_bprob(d=0)) == -1
+    assert mn.mi_norm_bwd_workspace_size(_bprob(dtype=5)) == -1
+    assert L.mi_norm_bwd_workspace_size(None) == -1
+
+
+def test_bwd_validation(L):
+    OK, BAD = mn.MI_NORM_OK, mn.MI_NORM_ERR_INVALID
+    chk = lambda **kw: mn.mi_norm_bwd_check(_bprob(**kw))
+    assert chk() == OK
+    assert chk(op=mn.OP_RMSNORM) == OK
+    assert chk(op=mn.OP_ADD_LAYERNORM) == BAD
+    assert chk(mean=None) == BAD and chk(op=mn.OP_RMSNORM, mean=None) == OK
+    assert chk(rstd=None) == BAD and chk(dy=None) == BAD and chk(dx=None) == BAD
+    assert chk(ws=None) == BAD                       # parameter gradients need the workspace
+    assert chk(ws=None, dparams0=None, dparams1=None) == OK   # dx alone at this width needs none
+    assert chk(ws=WS + 64) == BAD                    # not 256-byte aligned
+    assert chk(ws_bytes=1000) == BAD                 # too small
+    assert chk(dx=DY) == OK and chk(dx=X) == OK      # in place over dy or x
+    assert chk(dx=DY + 4) == BAD                     # partial overlap
+    assert chk(dx=DY, lddx=1024, lddy=768) == BAD    # same pointer, other stride
+    assert chk(dparams0=DB) == BAD                   # dgamma == dbeta
+    assert chk(dparams0=G) == BAD                    # dgamma over gamma
+    assert chk(dparams1=WS + 64) == BAD              # dbeta inside the workspace
+    assert chk(ws=DX) == BAD                         # workspace over dx
+    assert chk(mean=DX) == BAD                       # dx over mean
+    assert chk(lddy=700) == BAD and chk(ldx=1024, lddy=800, lddx=768) == OK
+    assert chk(dtype=mn.MI_NORM_BF16, x=X + 2) == OK and chk(dtype=mn.MI_NORM_F32, x=X + 2) == BAD
+    assert chk(rows=0) == OK
+    assert L.mi_norm_bwd_check(None) == BAD
+    # the named calls validate the same way (nothing launched on refusal)
+    assert L.mi_layernorm_bwd(DY, X, G, MEAN, RSTD, DX, DG, DB, 64, 768, None, 0, None) == BAD
+    assert L.mi_rmsnorm_bwd(DY, X, G, RSTD, DY + 4, DG, 64, 768, WS, 1 << 30, None) == BAD
+
+
+def test_bwd_dispatch(L):
+    name = lambda **kw: mn.mi_norm_variant_name(mn.mi_norm_bwd_select(_bprob(**kw)))
+    assert name(rows=4096, d=768) == "lnbwd_4_w1_q3_b8"
+    assert name(rows=32768, d=8192) == "lnbwd_4_w8_q4_b8"
+    assert name(op=mn.OP_RMSNORM, d=16384) == "rmsbwd_4_w8_q8_b8"
+    assert name(d=16384) == "lnbwd_1_stream_b4_u8"           # past LayerNorm's 24 values per lane
+    assert name(d=12288) == "lnbwd_4_w8_q6_b8"
+    assert name(dtype=mn.MI_NORM_BF16, d=8192) == "lnbwd_bf16_8_w8_q2_b8"
+    assert name(dtype=mn.MI_NORM_BF16, d=768) == "lnbwd_bf16_8_w1_q2_b8"
+    assert name(dtype=mn.MI_NORM_BF16, op=mn.OP_RMSNORM, d=2048) == "rmsbwd_bf16_8_w1_q4_b8"
+    assert name(dtype=mn.MI_NORM_BF16, d=2048) == "lnbwd_bf16_8_w2_q2_b8"
+    assert name(d=767) == "lnbwd_1_w2_q8_b8"                  # scalar: 767 elements over 2 waves
+    assert name(x=X + 4) == "lnbwd_1_w2_q8_b8"
+    assert name(d=9000, x=X + 4) == "lnbwd_1_stream_b4_u8"
+    assert name(d=1) == "lnbwd_1_w1_q1_b8"
+
+
+@pytest.mark.parametrize("op", [mn.OP_LAYERNORM, mn.OP_RMSNORM])
+@pytest.mark.parametrize("dt", DTYPES)
+def test_bwd_dispatch_covers_every_width(L, op, dt):
+    for layout in ("aligned", "misaligned"):
+        for d in WIDTHS:
+            x = X if layout == "aligned" else X + ESIZE[dt]
+            p = _bprob(op=op, rows=4096, d=d, dtype=dt, x=x)
+            vid = mn.mi_norm_bwd_select(p)
+            assert vid >= 0, (op, dt, d, layout)
+            v = mn.mi_norm_variant_get_info(vid)
+            assert v["dtype"] == dt and v["op"] == (4 if op == mn.OP_LAYERNORM else 5)
+            assert mn.mi_norm_bwd_eligible(vid, p)
+            assert v["looped"] or v["max_d"] >= d
+            if layout == "aligned" and d % (16 // ESIZE[dt]) == 0 and d <= 12288:
+                assert v["vec"] > 1, (d, mn.mi_norm_variant_name(vid))
+            if layout == "misaligned":
+                assert v["vec"] == 1
+    # forward variants are not backward ones, and the reverse
+    p = _bprob()
+    assert not mn.mi_norm_bwd_eligible(mn.mi_norm_select(_prob(0, 64, 768)), p)
+    assert mn.mi_norm_eligible(mn.mi_norm_bwd_select(p), _prob(0, 64, 768)) is False

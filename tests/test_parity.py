@@ -204,8 +204,8 @@ def test_every_variant(torch_dev):
     n = mn.mi_norm_variant_count()
     for vid in range(n):
         v = mn.mi_norm_variant_get_info(vid)
-        if v["dtype"] != mn.MI_NORM_F32:
-            continue
+        if v["dtype"] != mn.MI_NORM_F32 or v["op"] not in OPNAME:
+            continue                     # 16-bit and backward variants: their own tests
         name = mn.mi_norm_variant_name(vid)
         op = OPNAME[v["op"]]
         lay = _variant_layout(v)
