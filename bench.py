@@ -80,6 +80,13 @@ BENCH_WORKLOADS = {
     "rms_bf16_8192x8192": W("rmsnorm", "bf16", 8192, 8192),
     "addrms_bf16_4096x768": W("add_rmsnorm", "bf16", 4096, 768),
     "addln_bf16_32768x8192": W("add_layernorm", "bf16", 32768, 8192),
+    # backward (dx and the parameter gradients) from the forward's statistics
+    "lnbwd_4096x768": W("layernorm_bwd", "f32", 4096, 768),
+    "lnbwd_32768x8192": W("layernorm_bwd", "f32", 32768, 8192),
+    "rmsbwd_4096x768": W("rmsnorm_bwd", "f32", 4096, 768),
+    "rmsbwd_8192x8192": W("rmsnorm_bwd", "f32", 8192, 8192),
+    "lnbwd_bf16_4096x768": W("layernorm_bwd", "bf16", 4096, 768),
+    "lnbwd_bf16_32768x8192": W("layernorm_bwd", "bf16", 32768, 8192),
     # strided rows: each row of x and y sits in a wider row of its buffer
     "ln_4096x768_ld1024": W("layernorm", "f32", 4096, 768, "normal", True, 256),
     "ln_bf16_32768x8192_ld8448": W("layernorm", "bf16", 32768, 8192, "normal", False, 256),
@@ -113,9 +120,14 @@ def kernel_source_hash() -> str:
 def algorithmic_bytes(op: str, rows: int, d: int, stats: bool, storage: str = "f32") -> int:
     """Bytes a step must move: x read and y written (one element each); the
     fused ops also read r and write h = x + r; gamma/beta (or w, float32)
-    once; the per-row float32 statistics when requested.  Row padding is not
-    touched and does not count."""
+    once; the per-row float32 statistics when requested.  The backward reads
+    dy and x, writes dx, reads gamma (w) and the statistics and writes the
+    parameter gradients; its workspace traffic is overhead, not counted.  Row
+    padding is not touched and does not count."""
     e = ESIZE[storage]
+    if op.endswith("_bwd"):
+        ln = op.startswith("layernorm")
+        return 3 * e * rows * d + (12 if ln else 8) * d + (8 if ln else 4) * rows
     per_elem = (4 if op.startswith("add_") else 2) * e
     if op.endswith("layernorm"):
         return per_elem * rows * d + 8 * d + (8 * rows if stats else 0)
@@ -127,6 +139,12 @@ def algorithmic_bytes(op: str, rows: int, d: int, stats: bool, storage: str = "f
 def describe(op: str, rows: int, d: int, stats: bool, storage: str = "f32", pad: int = 0) -> str:
     if op == "copy":
         return f"streaming copy FP32 {rows*d} elements (calibration, bytes of [{rows},{d}])"
+    kind = {"f32": "FP32", "f16": "FP16 storage, FP32 statistics",
+            "bf16": "BF16 storage, FP32 statistics"}[storage]
+    if op.endswith("_bwd"):
+        grads = "dx, dgamma, dbeta" if op.startswith("layernorm") else "dx, dw"
+        name = "LayerNorm" if op.startswith("layernorm") else "RMSNorm"
+        return f"{name} backward ({grads}) {kind} [{rows},{d}]"
     name = "LayerNorm" if op.endswith("layernorm") else "RMSNorm"
     if op.startswith("add_"):
         name = "residual add (h = x + r written) + " + name
@@ -168,6 +186,7 @@ def load_bench_lib():
     L.mi_bench_add_rmsnorm_loop.argtypes = [P, P, P, P, P, P, I, I64, I64, F, I, I, P]
     L.mi_bench_copy_loop.argtypes = [P, P, I, I64, I, P]
     L.mi_bench_norm_loop.argtypes = [P, P, P, P, P, P, P, I, I, I, P]
+    L.mi_bench_bwd_loop.argtypes = [P, P, P, P, P, P, P, P, I, I, I, P]
     return L
 
 
@@ -221,6 +240,254 @@ def cpu_baseline(op, x, r, params, eps, budget_s: float, storage: str = "f32"):
     return reps, el, threads
 
 
+def measure_and_print(args, torch, stream, run_native, run_python, rotated, nsets, per_set, variant_name,
+                      bytes_step, parity, cpu_fn, workload, config, rows) -> int:
+    """Warm-up, the timed steps between stream events, the single launches,
+    and the one JSON line.  ``run_native(k[, arrays])`` / ``run_python(k,
+    start)`` run k steps; ``rotated(first)`` gives the pointer arrays from
+    buffer set ``first``; ``cpu_fn(budget)`` times the oracle."""
+    # -- warm-up and timed steps
+    if args.launch == "graph":
+        gw, graph = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gw, stream=stream):
+            run_python(args.warmup)
+        with torch.cuda.graph(graph, stream=stream):
+            run_python(args.steps, start=args.warmup)
+        runner_w, runner_t = gw.replay, graph.replay
+    elif args.launch == "native":
+        runner_w, runner_t = (lambda: run_native(args.warmup)), (lambda: run_native(args.steps))
+    else:
+        def runner_w():
+            run_python(args.warmup)
+
+        def runner_t():
+            run_python(args.steps, start=args.warmup)
+
+    with torch.cuda.stream(stream):
+        runner_w()
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record(stream)
+    with torch.cuda.stream(stream):
+        runner_t()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    w1 = time.perf_counter()
+    ms = t_start.elapsed_time(t_end)
+    ms_per_step = ms / args.steps
+
+    # single launches on an idle GPU, each between two events: the duration a
+    # kernel tracer reports per dispatch (no overlap with a neighbour's drain).
+    # A short spin kernel holds the stream while the host enqueues the first
+    # event and the launch, so the span holds no host time.
+    iso = []
+    if args.launch == "native":
+        for i in range(20):
+            arrays = rotated((args.steps + i) % nsets)   # a set last touched about n_sets steps ago
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                torch.cuda._sleep(200000)
+                e0.record(stream)
+                run_native(1, arrays)
+                e1.record(stream)
+            torch.cuda.synchronize()
+            iso.append(e0.elapsed_time(e1) * 1e3)
+    iso_us = round(sorted(iso)[len(iso) // 2], 3) if iso else None
+    gbps = bytes_step / (ms_per_step * 1e-3) / 1e9
+
+    traffic, _ = pmc_traffic(args.workload, variant_name)
+    roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                "traffic": traffic, "kernel": variant_name,
+                "algorithmic_bytes_per_launch": bytes_step,
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-scaled)"}
+
+    cpu = None
+    if cpu_fn is not None:
+        reps, el, threads = cpu_fn(args.cpu_seconds)
+        cpu = {"value": round(bytes_step * reps / el / 1e9, 3), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"full {workload} workload, {reps} repetitions "
+                         f"({el:.2f} s wall, float64 C oracle, OpenMP over rows)"}
+
+    line = {
+        "metric": (METRIC if args.workload == "ln_4096x768" else f"achieved HBM GB/s, {workload}"),
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": workload, **config, "mode": args.mode, "buffer_sets": nsets,
+                   "footprint_bytes": nsets * per_set, "launch": args.launch, "variant": variant_name,
+                   "parallelism": "single GPU"},
+        "kernel_us": round(ms_per_step * 1e3, 3),
+        "isolated_launch_us": iso_us,
+        "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
+        "rows_per_s": round(rows / (ms_per_step * 1e-3), 1),
+        "wall_ms_per_step": round((w1 - w0) * 1e3 / args.steps, 6),
+        "parity": parity,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernel_source_sha256": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def bench_bwd(args, torch, np, mn, wl, dev, wk) -> int:
+    """Backward workloads: one mi_norm_bwd call per step (the row kernel and
+    the column reduction of the parameter gradients), on inputs resident in
+    HBM, parity-gated against the float64 oracle."""
+    import oracle
+    op_b, storage, rows, d, pattern, _, pad = wk
+    ln = op_b.startswith("layernorm")
+    es, ld = ESIZE[storage], d + pad
+    dtcode = {"f32": mn.MI_NORM_F32, "f16": mn.MI_NORM_F16, "bf16": mn.MI_NORM_BF16}[storage]
+    tdtype = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[storage]
+    eps = wl.EPS
+    BL = load_bench_lib()
+
+    seed = wl.case_seed(7, rows, d, pattern)
+    x_h = wl.make_x(rows, d, pattern, seed)
+    dy_h = wl.make_x(rows, d, "normal", [8] + seed)
+    p0_h = wl.make_affine(d, [7, d, 99])[0] if ln else wl.make_weight(d, [7, d, 99])
+    fmt = None
+    if storage != "f32":
+        fmt = wl.F16 if storage == "f16" else wl.BF16
+        x_h, dy_h = wl.quantize16(x_h, fmt), wl.quantize16(dy_h, fmt)
+        xw = oracle.widen16(x_h, fmt)
+    else:
+        xw = x_h
+    if ln:
+        _, mean_h, rstd_h, _, _ = oracle.layernorm(xw, p0_h, np.zeros(d, np.float32), eps)
+    else:
+        _, rstd_h, _ = oracle.rmsnorm(xw, p0_h, eps)
+        mean_h = None
+
+    per_set = 3 * es * rows * ld + 8 * rows
+    nsets = 1 if args.mode == "warm" else max(1, math.ceil(args.footprint_gib * 2**30 / per_set))
+
+    def device_rows(host):
+        t = torch.from_numpy(host.view(np.int16) if es == 2 else host).to(dev)
+        t = t.view(tdtype) if es == 2 else t
+        if pad == 0:
+            return t
+        buf = torch.zeros(rows, ld, dtype=tdtype, device=dev)
+        buf[:, :d].copy_(t)
+        return buf[:, :d]
+
+    def empty_rows():
+        return torch.empty(rows, ld, dtype=tdtype, device=dev)[:, :d]
+
+    xs = [device_rows(x_h) for _ in range(nsets)]
+    dys = [device_rows(dy_h) for _ in range(nsets)]
+    dxs = [empty_rows() for _ in range(nsets)]
+    means = [torch.from_numpy(mean_h).to(dev) for _ in range(nsets)] if ln else None
+    rstds = [torch.from_numpy(rstd_h).to(dev) for _ in range(nsets)]
+    dgs = [torch.empty(d, device=dev) for _ in range(nsets)]
+    dbs = [torch.empty(d, device=dev) for _ in range(nsets)] if ln else None
+    p0 = torch.from_numpy(p0_h).to(dev)
+    opcode = mn.OP_LAYERNORM if ln else mn.OP_RMSNORM
+
+    def problem_for(j, ws=None, ws_bytes=0):
+        return mn.bwd_problem(opcode, rows, d, dys[j], xs[j], dxs[j], p0, means[j] if ln else None, rstds[j],
+                              dgs[j], dbs[j] if ln else None, ws, ws_bytes, dtype=dtcode, lddy=ld, ldx=ld, lddx=ld)
+
+    nbytes = mn.mi_norm_bwd_workspace_size(problem_for(0))
+    workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    probs = [problem_for(j, workspace, nbytes) for j in range(nsets)]
+    torch.cuda.synchronize()
+
+    vid = -1
+    if args.variant:
+        names = [mn.mi_norm_variant_name(i) for i in range(mn.mi_norm_variant_count())]
+        if args.variant not in names:
+            print(f"unknown variant {args.variant}", file=sys.stderr)
+            return 1
+        vid = names.index(args.variant)
+    variant_name = mn.mi_norm_variant_name(vid if vid >= 0 else mn.mi_norm_bwd_select(probs[0]))
+
+    stream = torch.cuda.Stream(device=dev)
+    sh = stream.cuda_stream
+
+    def rot(ts, first):
+        return None if ts is None else ptr_array(ts[first:] + ts[:first])
+
+    def rotated(first: int):
+        return tuple(rot(t, first) for t in (dys, xs, dxs, means, rstds, dgs, dbs))
+
+    base_arrays = rotated(0)
+
+    def run_native(k: int, arrays=None):
+        a = arrays if arrays is not None else base_arrays
+        st = BL.mi_bench_bwd_loop(ctypes.byref(probs[0]), *a, nsets, k, vid, sh)
+        if st != 0:
+            raise RuntimeError(f"bench loop failed: {mn.mi_norm_status_string(st)}")
+
+    def run_python(k: int, start: int = 0):
+        for s_ in range(start, start + k):
+            if vid < 0:
+                mn.mi_norm_bwd(probs[s_ % nsets], sh)
+            else:
+                mn.mi_norm_bwd_variant(vid, probs[s_ % nsets], sh)
+
+    # -- parity gate on set 0
+    with torch.cuda.stream(stream):
+        run_python(1)
+    torch.cuda.synchronize()
+    ref = (oracle.layernorm_bwd16(dy_h, x_h, fmt, p0_h, mean_h, rstd_h) if (ln and fmt) else
+           oracle.rmsnorm_bwd16(dy_h, x_h, fmt, p0_h, rstd_h) if fmt else
+           oracle.layernorm_bwd(dy_h, x_h, p0_h, mean_h, rstd_h) if ln else
+           oracle.rmsnorm_bwd(dy_h, x_h, p0_h, rstd_h))
+    sample = np.arange(rows) if rows * d <= (1 << 26) else np.unique(np.random.default_rng(0).integers(0, rows, 512))
+    got = dxs[0].cpu()
+    got = got.view(torch.int16).numpy().view(np.uint16) if es == 2 else got.numpy()
+    ok, err, ratio = oracle.dx_tolerance_ok(np.ascontiguousarray(got[sample]), ref["dx64"][sample],
+                                            ref["dx_scale"][sample], fmt)
+    grads = [(dgs[0], "dgamma" if ln else "dw")] + ([(dbs[0], "dbeta")] if ln else [])
+    for t, key in grads:
+        o2, e2, r2 = oracle.colsum_tolerance_ok(t.cpu().numpy(), ref[key + "64"], ref["abs_" + key])
+        ok, err, ratio = ok and o2, max(err, e2), max(ratio, r2)
+    if not ok:
+        print(f"PARITY FAILURE before timing: max abs err {err:.3e}, err/bound {ratio:.3f}", file=sys.stderr)
+        return 3
+    parity = {"rows_checked": int(len(sample)), "max_abs_err": err, "max_err_over_bound": ratio}
+
+    def cpu_fn(budget):
+        def call():
+            if fmt:
+                return (oracle.layernorm_bwd16(dy_h, x_h, fmt, p0_h, mean_h, rstd_h) if ln
+                        else oracle.rmsnorm_bwd16(dy_h, x_h, fmt, p0_h, rstd_h))
+            return (oracle.layernorm_bwd(dy_h, x_h, p0_h, mean_h, rstd_h) if ln
+                    else oracle.rmsnorm_bwd(dy_h, x_h, p0_h, rstd_h))
+        threads = oracle.max_threads()
+        call()
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            call()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return reps, el, threads
+
+    return measure_and_print(args, torch, stream, run_native, run_python, rotated, nsets, per_set, variant_name,
+                             algorithmic_bytes(op_b, rows, d, False, storage), parity,
+                             None if args.no_cpu_baseline else cpu_fn,
+                             describe(op_b, rows, d, False, storage, pad),
+                             {"rows": rows, "d": d, "row_stride": ld, "storage": storage, "eps": eps,
+                              "pattern": pattern, "seed": seed, "workspace_bytes": nbytes}, rows)
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,6 +521,8 @@ def main(argv=None) -> int:
         return 1
     dev = torch.device("cuda:0")
     wk = BENCH_WORKLOADS[args.workload]
+    if wk.op.endswith("_bwd"):
+        return bench_bwd(args, torch, np, mn, wl, dev, wk)
     op, storage, rows, d, pattern, stats, pad = wk
     eps = wl.EPS
     add = op.startswith("add_")
@@ -430,106 +699,15 @@ def main(argv=None) -> int:
             return 3
         parity = {"exact": True}
 
-    # -- warm-up and timed steps
-    if args.launch == "graph":
-        gw, graph = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gw, stream=stream):
-            run_python(args.warmup)
-        with torch.cuda.graph(graph, stream=stream):
-            run_python(args.steps, start=args.warmup)
-        runner_w, runner_t = gw.replay, graph.replay
-    elif args.launch == "native":
-        runner_w, runner_t = (lambda: run_native(args.warmup)), (lambda: run_native(args.steps))
-    else:
-        def runner_w():
-            run_python(args.warmup)
-
-        def runner_t():
-            run_python(args.steps, start=args.warmup)
-
-    with torch.cuda.stream(stream):
-        runner_w()
-    torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    t_start.record(stream)
-    with torch.cuda.stream(stream):
-        runner_t()
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    w1 = time.perf_counter()
-    ms = t_start.elapsed_time(t_end)
-    ms_per_step = ms / args.steps
-
-    # single launches on an idle GPU, each between two events: the duration a
-    # kernel tracer reports per dispatch (no overlap with a neighbour's drain).
-    # A short spin kernel holds the stream while the host enqueues the first
-    # event and the launch, so the span holds no host time.
-    iso = []
-    if args.launch == "native":
-        for i in range(20):
-            arrays = rotated((args.steps + i) % nsets)   # a set last touched about n_sets steps ago
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            with torch.cuda.stream(stream):
-                torch.cuda._sleep(200000)
-                e0.record(stream)
-                run_native(1, arrays)
-                e1.record(stream)
-            torch.cuda.synchronize()
-            iso.append(e0.elapsed_time(e1) * 1e3)
-    iso_us = round(sorted(iso)[len(iso) // 2], 3) if iso else None
-    bytes_step = algorithmic_bytes(op, rows, d, stats, storage)
-    gbps = bytes_step / (ms_per_step * 1e-3) / 1e9
-
-    traffic, _ = pmc_traffic(args.workload, variant_name)
-    roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(gbps / PEAK_HBM_GBPS, 4),
-                "traffic": traffic, "kernel": variant_name,
-                "algorithmic_bytes_per_launch": bytes_step,
-                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-scaled)"}
-
-    cpu = None
+    cpu_fn = None
     if not args.no_cpu_baseline and op != "copy":
-        reps, el, threads = cpu_baseline(op, x_h, r_h, params_h, eps, args.cpu_seconds, storage)
-        cpu = {"value": round(bytes_step * reps / el / 1e9, 3), "unit": "GB/s", "cores": threads,
-               "kind": "oracle",
-               "sample": f"full {describe(op, rows, d, stats, storage)} workload, {reps} repetitions "
-                         f"({el:.2f} s wall, float64 C oracle, OpenMP over rows)"}
-
-    line = {
-        "metric": (METRIC if args.workload == "ln_4096x768"
-                   else f"achieved HBM GB/s, {describe(op, rows, d, stats, storage, pad)}"),
-        "value": round(gbps, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": describe(op, rows, d, stats, storage, pad), "rows": rows, "d": d,
-                   "row_stride": ld, "storage": storage, "eps": eps,
-                   "pattern": pattern, "seed": seed, "mode": args.mode, "buffer_sets": nsets,
-                   "footprint_bytes": nsets * per_set, "launch": args.launch, "variant": variant_name,
-                   "parallelism": "single GPU"},
-        "kernel_us": round(ms_per_step * 1e3, 3),
-        "isolated_launch_us": iso_us,
-        "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
-        "rows_per_s": round(rows / (ms_per_step * 1e-3), 1),
-        "wall_ms_per_step": round((w1 - w0) * 1e3 / args.steps, 6),
-        "parity": parity,
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "kernel_source_sha256": kernel_source_hash(),
-    }
-    print(json.dumps(line), flush=True)
-    return 0
+        def cpu_fn(budget):
+            return cpu_baseline(op, x_h, r_h, params_h, eps, budget, storage)
+    return measure_and_print(args, torch, stream, run_native, run_python, rotated, nsets, per_set, variant_name,
+                             algorithmic_bytes(op, rows, d, stats, storage), parity, cpu_fn,
+                             describe(op, rows, d, stats, storage, pad),
+                             {"rows": rows, "d": d, "row_stride": ld, "storage": storage, "eps": eps,
+                              "pattern": pattern, "seed": seed}, rows)
 
 
 if __name__ == "__main__":

@@ -103,6 +103,28 @@ int mi_bench_norm_loop(const mi_norm_problem *base, const void *const *xs, const
     return MI_NORM_OK;
 }
 
+// Backward: *base holds everything but the per-set pointers (dgs, dbs may
+// be NULL or hold NULL entries); the workspace in *base serves every step.
+int mi_bench_bwd_loop(const mi_norm_bwd_problem *base, const void *const *dys, const void *const *xs,
+                      void *const *dxs, const float *const *means, const float *const *rstds,
+                      float *const *dgs, float *const *dbs, int nsets, int steps, int variant,
+                      hipStream_t stream) {
+    mi_norm_bwd_problem p = *base;
+    for (int s = 0; s < steps; ++s) {
+        const int k = s % nsets;
+        p.dy = dys[k];
+        p.x = xs[k];
+        p.dx = dxs[k];
+        p.mean = means ? means[k] : nullptr;
+        p.rstd = rstds[k];
+        p.dparams0 = dgs ? dgs[k] : nullptr;
+        p.dparams1 = dbs ? dbs[k] : nullptr;
+        const mi_norm_status st = variant < 0 ? mi_norm_bwd(&p, stream) : mi_norm_bwd_variant(variant, &p, stream);
+        if (st != MI_NORM_OK) return st;
+    }
+    return MI_NORM_OK;
+}
+
 int mi_bench_copy_loop(const float *const *srcs, float *const *dsts, int nsets, int64_t n, int steps,
                        hipStream_t stream) {
     for (int s = 0; s < steps; ++s) {

@@ -231,30 +231,40 @@ void norm_bwd_held(BwdParams p)
 }
 
 // ---------------------------------------------------------------------------
-// Sum of the partial rows: out_g[j] = sum_b part[b][g][j] in float64, blocks
-// in a fixed order.  A workgroup covers 64 columns: 16 column quads by 16
-// slices of the partial rows, the slices then added in order.
+// Sum of the partial rows: out_g[j] = sum_b part[b][g][j] in float64, in a
+// fixed order.  A workgroup covers 16 columns: 4 column quads by 64 slices of
+// the partial rows (slice s takes rows s, s + 64, ...; with at most 512
+// partial rows a lane issues at most 8 loads, all before any add), then the
+// slices are added in order.  Memory-latency bound: many small workgroups.
 template <int NG>
 __global__ __launch_bounds__(256)
 void norm_bwd_reduce(const float *part, int64_t nblk, int32_t d, int32_t dpad, float *out0, float *out1)
 {
-    const int cq = threadIdx.x & 15;
-    const int sl = threadIdx.x >> 4;
+    constexpr int SL = 64, CQ = 4, U = 8;
+    const int cq = threadIdx.x % CQ;
+    const int sl = threadIdx.x / CQ;
     const int g = blockIdx.y;
-    const int col = (blockIdx.x * 16 + cq) * 4;
-    __shared__ d4 red[16][16];
+    const int col = (blockIdx.x * CQ + cq) * 4;
+    __shared__ d4 red[SL][CQ];
     d4 acc = d4(0.0);
     if (col < dpad) {
         const float *base = part + (int64_t)g * dpad + col;
-        for (int64_t b = sl; b < nblk; b += 16)
-            acc += __builtin_convertvector(ld4<false>(base + b * NG * dpad), d4);
+        for (int64_t b0 = sl; b0 < nblk; b0 += (int64_t)SL * U) {
+            f4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t b = b0 + (int64_t)SL * u;
+                v[u] = b < nblk ? ld4<false>(base + b * NG * dpad) : f4(0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) acc += __builtin_convertvector(v[u], d4);
+        }
     }
     red[sl][cq] = acc;
     __syncthreads();
     if (sl == 0 && col < d) {
         d4 t = red[0][cq];
-#pragma unroll
-        for (int s = 1; s < 16; ++s) t += red[s][cq];
+        for (int s = 1; s < SL; ++s) t += red[s][cq];
         float *out = g == 0 ? out0 : out1;
         if (out) {
 #pragma unroll

@@ -5,5 +5,5 @@ namespace minorm {
 namespace {
 const Variant kVariants[] = {MI_BWD_DTYPE_TABLE(__bf16, MI_NORM_BF16, 8, "_bf16")};
 }  // namespace
-const VariantTable kBwdTableBF16 = {kVariants, (int)(sizeof(kVariants) / sizeof(kVariants[0]))};
+extern const VariantTable kBwdTableBF16 = {kVariants, (int)(sizeof(kVariants) / sizeof(kVariants[0]))};
 }  // namespace minorm

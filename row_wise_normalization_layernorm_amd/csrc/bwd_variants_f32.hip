@@ -5,5 +5,5 @@ namespace minorm {
 namespace {
 const Variant kVariants[] = {MI_BWD_DTYPE_TABLE(float, MI_NORM_F32, 4, "")};
 }  // namespace
-const VariantTable kBwdTableF32 = {kVariants, (int)(sizeof(kVariants) / sizeof(kVariants[0]))};
+extern const VariantTable kBwdTableF32 = {kVariants, (int)(sizeof(kVariants) / sizeof(kVariants[0]))};
 }  // namespace minorm

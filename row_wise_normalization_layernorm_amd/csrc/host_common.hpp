@@ -9,6 +9,11 @@
 #include "variant_table.hpp"
 
 namespace minorm {
+
+// defined in variants_*.hip and bwd_variants_*.hip
+extern const VariantTable kTableF32, kTableF16, kTableBF16;           // forward
+extern const VariantTable kBwdTableF32, kBwdTableF16, kBwdTableBF16;  // backward
+
 namespace host {
 
 // The tables in id order: forward float32, binary16, bfloat16, then the

@@ -220,7 +220,7 @@ mi_norm_status launch_reduce(const mi_norm_bwd_problem &P, const float *part, in
     float *o0 = P.dparams0;
     float *o1 = is_ln(P) ? P.dparams1 : nullptr;
     void *args[] = {&part, &nblk, &d, &dpad, &o0, &o1};
-    const dim3 grid((unsigned)((dpad + 63) / 64), (unsigned)ngrads(P));
+    const dim3 grid((unsigned)((dpad + 15) / 16), (unsigned)ngrads(P));  // 16 columns per workgroup
     const void *fn = is_ln(P) ? reinterpret_cast<const void *>(&norm_bwd_reduce<2>)
                               : reinterpret_cast<const void *>(&norm_bwd_reduce<1>);
     return hipLaunchKernel(fn, grid, dim3(256), args, 0, stream) == hipSuccess ? MI_NORM_OK : MI_NORM_ERR_HIP;

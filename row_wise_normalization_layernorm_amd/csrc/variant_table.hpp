@@ -24,8 +24,6 @@ struct VariantTable {
     int n;
 };
 
-extern const VariantTable kTableF32, kTableF16, kTableBF16;           // forward
-extern const VariantTable kBwdTableF32, kBwdTableF16, kBwdTableBF16;  // backward
 
 constexpr int64_t kUnbounded = INT64_MAX;
 

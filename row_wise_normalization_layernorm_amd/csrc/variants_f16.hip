@@ -5,5 +5,5 @@ namespace minorm {
 namespace {
 const Variant kVariants[] = {MI_DTYPE_TABLE(_Float16, MI_NORM_F16, 8, "_f16")};
 }  // namespace
-const VariantTable kTableF16 = {kVariants, (int)(sizeof(kVariants) / sizeof(kVariants[0]))};
+extern const VariantTable kTableF16 = {kVariants, (int)(sizeof(kVariants) / sizeof(kVariants[0]))};
 }  // namespace minorm
