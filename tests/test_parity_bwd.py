@@ -307,3 +307,45 @@ def test_binding_bwd_16bit_strided_view(torch_dev):
     assert oracle.dx_tolerance_ok(bits(dx), ref["dx64"], ref["dx_scale"], oracle.FMT_BF16)[0]
     assert oracle.colsum_tolerance_ok(dg.cpu().numpy(), ref["dgamma64"], ref["abs_dgamma"])[0]
     assert oracle.colsum_tolerance_ok(db.cpu().numpy(), ref["dbeta64"], ref["abs_dbeta"])[0]
+
+
+def test_graph_capture_replays(torch_dev):
+    """Forward and backward calls captured in a HIP graph (no allocation or
+    memset inside) give the eager results on every replay, with the program's
+    own eager work and synchronizations between replays."""
+    torch, dev = torch_dev
+    rows, d = 2048, 1024
+    say("graph capture fwd + bwd")
+    x = wl.make_x(rows, d, "offset", [42])
+    dy = wl.make_x(rows, d, "normal", [43])
+    g, b = wl.make_affine(d, [42, d])
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    X, DY, G, B = t(x), t(dy), t(g), t(b)
+    Y, M, S = torch.empty_like(X), torch.empty(rows, device=dev), torch.empty(rows, device=dev)
+    DX, DG, DB = torch.empty_like(X), torch.empty(d, device=dev), torch.empty(d, device=dev)
+    p = mn.bwd_problem(mn.OP_LAYERNORM, rows, d, DY, X, DX, G, M, S, DG, DB)
+    nbytes = mn.mi_norm_bwd_workspace_size(p)
+    WS = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    p.workspace, p.workspace_bytes = WS.data_ptr(), nbytes
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def step(stream):
+        mn.mi_layernorm_fwd(X, G, B, Y, rows, d, wl.EPS, M, S, stream=stream)
+        mn.mi_norm_bwd(p, stream)
+
+    with torch.cuda.stream(s):
+        step(s.cuda_stream)
+    torch.cuda.synchronize()
+    eager = [a.clone() for a in (Y, M, S, DX, DG, DB)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        step(s.cuda_stream)
+    for k in range(4):
+        for a in (Y, M, S, DX, DG, DB):
+            a.fill_(float("nan"))           # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, e in zip((Y, M, S, DX, DG, DB), eager):
+            assert torch.equal(a, e), f"replay {k} differs from the eager call"
