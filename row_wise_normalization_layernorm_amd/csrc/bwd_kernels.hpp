@@ -235,7 +235,8 @@ void norm_bwd_held(BwdParams p)
 // fixed order.  A workgroup covers 16 columns: 4 column quads by 64 slices of
 // the partial rows (slice s takes rows s, s + 64, ...; with at most 512
 // partial rows a lane issues at most 8 loads, all before any add), then the
-// slices are added in order.  Memory-latency bound: many small workgroups.
+// slices meet in a fixed binary tree in LDS.  Memory-latency bound: many
+// small workgroups.
 template <int NG>
 __global__ __launch_bounds__(256)
 void norm_bwd_reduce(const float *part, int64_t nblk, int32_t d, int32_t dpad, float *out0, float *out1)
@@ -262,9 +263,13 @@ void norm_bwd_reduce(const float *part, int64_t nblk, int32_t d, int32_t dpad, f
     }
     red[sl][cq] = acc;
     __syncthreads();
+#pragma unroll
+    for (int half = SL / 2; half >= 1; half /= 2) {
+        if (sl < half) red[sl][cq] += red[sl + half][cq];
+        __syncthreads();
+    }
     if (sl == 0 && col < d) {
-        d4 t = red[0][cq];
-        for (int s = 1; s < SL; ++s) t += red[s][cq];
+        const d4 t = red[0][cq];
         float *out = g == 0 ? out0 : out1;
         if (out) {
 #pragma unroll
