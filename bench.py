@@ -99,22 +99,29 @@ BENCH_WORKLOADS = {
 
 ESIZE = {"f32": 4, "f16": 2, "bf16": 2}
 
-# the device code of the forward kernels and the table that instantiates them
-# (launch shapes included); a profile's counters stand for the kernels only
-# while these are unchanged and the dispatcher still picks the profiled variant
-KERNEL_SOURCES = ("row_wise_normalization_layernorm_amd/csrc/norm_kernels.hpp",
-                  "row_wise_normalization_layernorm_amd/csrc/variant_table.hpp",
-                  "row_wise_normalization_layernorm_amd/csrc/variants_f32.hip",
-                  "row_wise_normalization_layernorm_amd/csrc/variants_f16.hip",
-                  "row_wise_normalization_layernorm_amd/csrc/variants_bf16.hip")
+# the device code of the kernels and the tables that instantiate them (launch
+# shapes included), per direction; a profile's counters stand for the kernels
+# only while these are unchanged and the dispatcher still picks the profiled
+# variant
+_CSRC = "row_wise_normalization_layernorm_amd/csrc/"
+KERNEL_SOURCES = {
+    "fwd": tuple(_CSRC + f for f in ("norm_kernels.hpp", "variant_table.hpp", "variants_f32.hip",
+                                     "variants_f16.hip", "variants_bf16.hip")),
+    "bwd": tuple(_CSRC + f for f in ("norm_kernels.hpp", "bwd_kernels.hpp", "bwd_table.hpp",
+                                     "bwd_variants_f32.hip", "bwd_variants_f16.hip", "bwd_variants_bf16.hip")),
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(direction: str = "fwd") -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[direction]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def direction_of(workload: str) -> str:
+    return "bwd" if BENCH_WORKLOADS[workload].op.endswith("_bwd") else "fwd"
 
 
 def algorithmic_bytes(op: str, rows: int, d: int, stats: bool, storage: str = "f32") -> int:
@@ -167,7 +174,7 @@ def pmc_traffic(workload: str, variant: str):
     m = re.search(r"^kernel_source_sha256:\s*(\w+)", text, re.M)
     t = re.search(r"^traffic_bytes_per_launch:\s*([\d.eE+]+)", text, re.M)
     v = re.search(r"^kernel_variant:\s*(\S+)", text, re.M)
-    if not m or not t or not v or m.group(1) != kernel_source_hash() or v.group(1) != variant:
+    if not m or not t or not v or m.group(1) != kernel_source_hash(direction_of(workload)) or v.group(1) != variant:
         return None, path
     return float(t.group(1)), path
 
@@ -338,7 +345,7 @@ def measure_and_print(args, torch, stream, run_native, run_python, rotated, nset
         "parity": parity,
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "kernel_source_sha256": kernel_source_hash(),
+        "kernel_source_sha256": kernel_source_hash(direction_of(args.workload)),
     }
     print(json.dumps(line), flush=True)
     return 0
