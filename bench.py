@@ -112,11 +112,30 @@ KERNEL_SOURCES = {
 }
 
 
+_CODE_TOKENS = re.compile(r'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|//[^\n]*|/\*.*?\*/|\s+|[^"\'/\s]+|/',
+                          re.S)
+
+
+def code_text(src: str) -> str:
+    """The source with its comments dropped and each run of white space made
+    one blank: what the compiler sees, so that rewording a comment leaves the
+    pairing of the committed counter summaries intact."""
+    out = []
+    for tok in _CODE_TOKENS.findall(src):
+        if tok.startswith("//") or tok.startswith("/*") or tok.isspace():
+            if out and out[-1] != " ":
+                out.append(" ")
+        else:
+            out.append(tok)
+    return "".join(out).strip()
+
+
 def kernel_source_hash(direction: str = "fwd") -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[direction]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

@@ -56,11 +56,11 @@
  *   overlap each other freely (e.g. x and r interleaved in one buffer).  No
  *   output may overlap gamma, beta or w, and mean/rstd may overlap no other
  *   argument.
- * - Row tensors aligned to four elements (16 bytes for float32, 8 for the
- *   16-bit types) with d and every row stride a multiple of four, and 16-byte
- *   aligned parameters, select the quad-vector path; rows that share their
- *   phase within four elements take a peeled quad path; any other layout a
- *   scalar path with the same results.
+ * - Row tensors 16-byte aligned, with d and every row stride a multiple of
+ *   the elements in 16 bytes (4 float32, 8 of a 16-bit type), and 16-byte
+ *   aligned parameters select the vector path (16-byte accesses); rows that
+ *   share their phase within 16 bytes take a peeled vector path; any other
+ *   layout a scalar path with the same results.
  * - Errors: MI_NORM_ERR_INVALID is returned before any launch for a NULL
  *   required pointer, a misaligned pointer, an unknown op or dtype, rows < 0,
  *   d < 1, d > 2^31 - 1, a row stride below d, a size overflow, eps NaN or
@@ -282,8 +282,9 @@ mi_norm_status mi_rmsnorm_bwd(const float *dy, const float *x, const float *w,
 typedef struct mi_norm_variant_info {
     int op;               /* mi_norm_op */
     int dtype;            /* mi_norm_dtype of the rows */
-    int vec;              /* elements per lane access: 4 (one quad) or 1 */
-    int peel;             /* 1: per-row scalar head/tail around an aligned quad body */
+    int vec;              /* elements per lane access: 16 bytes' worth (4 float32,
+                             8 of a 16-bit type) or 1 */
+    int peel;             /* 1: per-row scalar head/tail around an aligned vector body */
     int looped;           /* 1: row streamed in chunks (re-read), any width */
     int lanes_per_row;    /* 16, 32 or 64 lanes of one wave share a row (held variants) */
     int waves_per_row;    /* waves cooperating on one row */
@@ -291,8 +292,8 @@ typedef struct mi_norm_variant_info {
     int waves_per_block;  /* wave64s per workgroup */
     int rows_per_block;   /* rows owned by one workgroup per iteration */
     int64_t max_d;        /* widest row the variant accepts (INT64_MAX if unbounded) */
-    int needs_aligned;    /* 1: quad-aligned rows and strides, 16-byte-aligned
-                             parameters and d % 4 == 0 required */
+    int needs_aligned;    /* 1: 16-byte-aligned rows and parameters, strides and d
+                             multiples of vec, required */
 } mi_norm_variant_info;
 
 /* Number of compiled variants; ids are 0 .. count-1. */

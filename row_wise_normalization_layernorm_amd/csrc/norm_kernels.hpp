@@ -310,9 +310,9 @@ __device__ __forceinline__ float rsq(float v) { return __builtin_amdgcn_rsqf(v);
 //          aligned path only); -1: 1 or 0 by the register budget
 //
 // Lane li of wave rank wr holds access k = li + LPR * (wr + WPR * q),
-// q = 0..Q-1: consecutive lanes touch consecutive quads (or elements), so
-// each wave-wide access covers 64 quads of one row contiguously (1 KiB of
-// float32, 512 B of a 16-bit type).
+// q = 0..Q-1: consecutive lanes touch consecutive vectors (or elements), so
+// each wave-wide access covers 64 vectors of one row contiguously (1 KiB on
+// the vector paths).
 template <typename T, int OP, int VEC, bool PEEL, int LPR, int WPR, int Q, int WAVES, bool NTL,
           bool NTS, int PRE = -1, int MRG = -1, bool RES = false>
 __global__ __launch_bounds__(WAVES * 64)

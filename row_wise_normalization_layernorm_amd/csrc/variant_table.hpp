@@ -58,9 +58,8 @@ constexpr bool kres(int op) { return op >= 2; }
             reinterpret_cast<const void *>(&norm_looped<T, kop(OPC), VEC, WAVES, U, kres(OPC)>)}
 
 // every (waves per row, slots) pair of a vector path (VW elements per access:
-// 4 for float32, 8 for the 16-bit types, 16 bytes either way except the
-// quads of a 16-bit type): slots 1, 2, 3, 4, 6, 8 for 1, 2, 4, 8 and 16
-// waves per row
+// 4 for float32, 8 for the 16-bit types, 16 bytes either way): slots 1, 2,
+// 3, 4, 6, 8 for 1, 2, 4, 8 and 16 waves per row
 #define MI_SLOTS(T, DT, VW, OPC, OPN, PEEL, WPR, WSMALL)                                           \
     MI_HELD2(T, DT, OPC, OPN, VW, PEEL, 64, WPR, 1, WSMALL),                                     \
     MI_HELD2(T, DT, OPC, OPN, VW, PEEL, 64, WPR, 2, WSMALL),                                     \

@@ -64,6 +64,16 @@ def test_profile_pairing(tmp_path, monkeypatch):
     assert bench.kernel_source_hash("bwd") != h
 
 
+def test_code_text_drops_comments_only():
+    src = ('// head\nint a = 1; /* two\nlines */ const char *s = "x // y /* z */";\n'
+           "char c = '/'; int b = a / 2;  // tail\n")
+    assert bench.code_text(src) == ("int a = 1; const char *s = \"x // y /* z */\"; "
+                                    "char c = '/'; int b = a / 2;")
+    # a change of code is seen, a change of comment or spacing is not
+    assert bench.code_text("x = a + b; // sum") == bench.code_text("x = a +  b;\n// the sum")
+    assert bench.code_text("x = a + b;") != bench.code_text("x = a - b;")
+
+
 def test_committed_profiles_name_their_command_and_kernel():
     prof = os.path.join(ROOT, "profiles")
     for name in os.listdir(prof):
