@@ -63,6 +63,9 @@ BENCH_WORKLOADS = {
     "ln_1024x2048": W("layernorm", "f32", 1024, 2048, "offset"),
     "ln_4096x4096": W("layernorm", "f32", 4096, 4096, "offset"),
     "ln_32768x8192": W("layernorm", "f32", 32768, 8192),
+    # one GPU's share when the rows of [4096,768] and [32768,8192] are split over eight
+    "ln_512x768": W("layernorm", "f32", 512, 768, "normal", True),
+    "ln_4096x8192": W("layernorm", "f32", 4096, 8192),
     "rms_512x128": W("rmsnorm", "f32", 512, 128),
     "rms_4096x768": W("rmsnorm", "f32", 4096, 768),
     "rms_2048x4096": W("rmsnorm", "f32", 2048, 4096),
@@ -251,19 +254,67 @@ def oracle_call(op, x, r, params, eps, storage: str = "f32"):
     return y, h, [rstd]
 
 
-def cpu_baseline(op, x, r, params, eps, budget_s: float, storage: str = "f32"):
-    """The float64 oracle on the host cores over the same workload."""
+def time_oracle(call, budget_s: float, threads: int | None = None):
+    """Repeat ``call`` (one oracle pass over the workload) until ``budget_s``
+    of wall time has passed, on ``threads`` OpenMP threads (None: all the
+    host gives); returns (repetitions, seconds, threads used)."""
     import oracle
-    threads = oracle.max_threads()
-    oracle_call(op, x, r, params, eps, storage)  # first call loads the library
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle_call(op, x, r, params, eps, storage)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return reps, el, threads
+    most = oracle.max_threads()
+    n = most if threads is None else min(threads, most)
+    oracle.set_threads(n)
+    try:
+        call()  # the first call loads the library and touches the pages
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            call()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                return reps, el, n
+    finally:
+        oracle.set_threads(most)
+
+
+def cpu_baseline(op, x, r, params, eps, budget_s: float, storage: str = "f32", threads: int | None = None):
+    """The float64 oracle on the host cores over the same workload."""
+    return time_oracle(lambda: oracle_call(op, x, r, params, eps, storage), budget_s, threads)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def copy_reference(torch, BL, stream, bytes_step: int, steps: int, warmup: int, mode: str,
+                   footprint_gib: float):
+    """The calibration copy moving a step's bytes (half read, half written),
+    timed like the step on rotated buffers: (µs per copy, buffer sets)."""
+    n = max(4, (bytes_step // 8) // 4 * 4)
+    nsets = 1 if mode == "warm" else max(1, math.ceil(footprint_gib * 2**30 / (8 * n)))
+    dev = torch.device("cuda:0")
+    srcs = [torch.zeros(n, device=dev) for _ in range(nsets)]
+    dsts = [torch.empty(n, device=dev) for _ in range(nsets)]
+    torch.cuda.synchronize()
+    sa, da = ptr_array(srcs), ptr_array(dsts)
+    sh = stream.cuda_stream
+    if BL.mi_bench_copy_loop(sa, da, nsets, n, warmup, sh) != 0:
+        raise RuntimeError("copy loop failed")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    if BL.mi_bench_copy_loop(sa, da, nsets, n, steps, sh) != 0:
+        raise RuntimeError("copy loop failed")
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    del srcs, dsts
+    return us, nsets
 
 
 def measure_and_print(args, torch, stream, run_native, run_python, rotated, nsets, per_set, variant_name,
@@ -332,13 +383,27 @@ def measure_and_print(args, torch, stream, run_native, run_python, rotated, nset
                 "algorithmic_bytes_per_launch": bytes_step,
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-scaled)"}
 
+    copy = None
+    if not args.no_copy and args.launch == "native" and not args.workload.startswith("copy_"):
+        copy_us, copy_sets = copy_reference(torch, load_bench_lib(), stream, bytes_step, args.steps,
+                                            args.warmup, args.mode, args.footprint_gib)
+        copy = {"us": round(copy_us, 3), "bytes": 8 * max(4, (bytes_step // 8) // 4 * 4),
+                "buffer_sets": copy_sets,
+                "pct_of_copy": round(100 * copy_us / (ms_per_step * 1e3), 2),
+                "what": "copy_f4 moving the step's bytes (half read, half written), timed the same way"}
+
     cpu = None
     if cpu_fn is not None:
-        reps, el, threads = cpu_fn(args.cpu_seconds)
+        reps, el, threads = cpu_fn(args.cpu_seconds, None)
+        reps1, el1, _ = cpu_fn(args.cpu_seconds / 2, 1)
         cpu = {"value": round(bytes_step * reps / el / 1e9, 3), "unit": "GB/s", "cores": threads,
                "kind": "oracle",
                "sample": f"full {workload} workload, {reps} repetitions "
-                         f"({el:.2f} s wall, float64 C oracle, OpenMP over rows)"}
+                         f"({el:.2f} s wall, float64 C oracle, OpenMP over rows)",
+               "value_1core": round(bytes_step * reps1 / el1 / 1e9, 3),
+               "sample_1core": f"{reps1} repetitions ({el1:.2f} s wall) on one thread",
+               "ms_per_pass": round(el * 1e3 / reps, 3),
+               "cpu_model": cpu_model()}
 
     line = {
         "metric": (METRIC if args.workload == "ln_4096x768" else f"achieved HBM GB/s, {workload}"),
@@ -363,6 +428,7 @@ def measure_and_print(args, torch, stream, run_native, run_python, rotated, nset
         "wall_ms_per_step": round((w1 - w0) * 1e3 / args.steps, 6),
         "parity": parity,
         "roofline": roofline,
+        "copy_reference": copy,
         "cpu_baseline": cpu,
         "kernel_source_sha256": kernel_source_hash(direction_of(args.workload)),
     }
@@ -489,22 +555,14 @@ def bench_bwd(args, torch, np, mn, wl, dev, wk) -> int:
         return 3
     parity = {"rows_checked": int(len(sample)), "max_abs_err": err, "max_err_over_bound": ratio}
 
-    def cpu_fn(budget):
+    def cpu_fn(budget, threads):
         def call():
             if fmt:
                 return (oracle.layernorm_bwd16(dy_h, x_h, fmt, p0_h, mean_h, rstd_h) if ln
                         else oracle.rmsnorm_bwd16(dy_h, x_h, fmt, p0_h, rstd_h))
             return (oracle.layernorm_bwd(dy_h, x_h, p0_h, mean_h, rstd_h) if ln
                     else oracle.rmsnorm_bwd(dy_h, x_h, p0_h, rstd_h))
-        threads = oracle.max_threads()
-        call()
-        reps, t0 = 0, time.perf_counter()
-        while True:
-            call()
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= budget:
-                return reps, el, threads
+        return time_oracle(call, budget, threads)
 
     return measure_and_print(args, torch, stream, run_native, run_python, rotated, nsets, per_set, variant_name,
                              algorithmic_bytes(op_b, rows, d, False, storage), parity,
@@ -527,6 +585,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=2.0,
                     help="wall-clock budget of the CPU baseline (all host threads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy", action="store_true",
+                    help="skip the calibration copy of the step's bytes")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -727,8 +787,8 @@ def main(argv=None) -> int:
 
     cpu_fn = None
     if not args.no_cpu_baseline and op != "copy":
-        def cpu_fn(budget):
-            return cpu_baseline(op, x_h, r_h, params_h, eps, budget, storage)
+        def cpu_fn(budget, threads):
+            return cpu_baseline(op, x_h, r_h, params_h, eps, budget, storage, threads)
     return measure_and_print(args, torch, stream, run_native, run_python, rotated, nsets, per_set, variant_name,
                              algorithmic_bytes(op, rows, d, stats, storage), parity, cpu_fn,
                              describe(op, rows, d, stats, storage, pad),
