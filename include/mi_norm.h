@@ -294,6 +294,9 @@ typedef struct mi_norm_variant_info {
     int64_t max_d;        /* widest row the variant accepts (INT64_MAX if unbounded) */
     int needs_aligned;    /* 1: 16-byte-aligned rows and parameters, strides and d
                              multiples of vec, required */
+    int rows_per_lane;    /* rows whose elements a lane holds at once: 1, or 2 for
+                             the multi-row variants, whose wave groups hold two rows
+                             and fetch the parameters once for both */
 } mi_norm_variant_info;
 
 /* Number of compiled variants; ids are 0 .. count-1. */

@@ -52,7 +52,7 @@ class VariantInfo(ctypes.Structure):
         ("looped", ctypes.c_int), ("lanes_per_row", ctypes.c_int),
         ("waves_per_row", ctypes.c_int), ("slots", ctypes.c_int),
         ("waves_per_block", ctypes.c_int), ("rows_per_block", ctypes.c_int),
-        ("max_d", ctypes.c_int64), ("needs_aligned", ctypes.c_int),
+        ("max_d", ctypes.c_int64), ("needs_aligned", ctypes.c_int), ("rows_per_lane", ctypes.c_int),
     ]
 
     def as_dict(self) -> dict:

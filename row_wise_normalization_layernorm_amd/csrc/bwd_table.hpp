@@ -14,14 +14,14 @@
 #define MI_BWD_HELD(T, DT, OPC, OPN, VEC, WPR, Q)                                               \
     Variant{OPN "_" #VEC "_w" #WPR "_q" #Q "_b8",                                                \
             mi_norm_variant_info{OPC, DT, VEC, 0, 0, 64, WPR, Q, 8, 8 / WPR,                     \
-                                 (int64_t)VEC * 64 * WPR * Q, VEC > 1 ? 1 : 0},                  \
+                                 (int64_t)VEC * 64 * WPR * Q, VEC > 1 ? 1 : 0, 1},               \
             reinterpret_cast<const void *>(                                                     \
                 &norm_bwd_held<T, (OPC == MI_NORM_OP_LAYERNORM_BWD ? OP_LN : OP_RMS), VEC, WPR, Q, 8>)}
 
 // streamed rows: the column-chunk kernel (4 waves, 8 elements per lane)
 #define MI_BWD_STREAM(T, DT, OPC, OPN)                                                         \
     Variant{OPN "_1_stream_b4_u8",                                                              \
-            mi_norm_variant_info{OPC, DT, 1, 0, 1, 64, 4, 8, 4, 1, kUnbounded, 0},             \
+            mi_norm_variant_info{OPC, DT, 1, 0, 1, 64, 4, 8, 4, 1, kUnbounded, 0, 1},          \
             reinterpret_cast<const void *>(                                                     \
                 &norm_bwd_chunks<T, (OPC == MI_NORM_OP_LAYERNORM_BWD ? OP_LN : OP_RMS), 4, 8>)}
 

@@ -600,6 +600,220 @@ void norm_held(NormParams p)
 }
 
 // ---------------------------------------------------------------------------
+// Multi-row held kernel: the 16-byte vector path of norm_held (LPR = 64, no
+// peel) with RV rows held at once by every group of WPR waves.  A lane holds
+// the same Q accesses, hence the same columns, of each of its RV rows, so one
+// fetch of gamma/beta (or w) serves RV rows.  In norm_held every row fetches
+// its own parameters; at float32 that is twice the row's own bytes through
+// the CU's vector memory path (four times for a 16-bit row), which costs more
+// than the row's HBM traffic once a launch runs many rows.
+//
+// The parameters are fetched for every slot in one batch once the
+// statistics are known: fetched slot by slot between the predicated stores,
+// each fetch's latency would be paid in turn.  keep() ties the batch ahead of
+// the stores.
+//
+// Arithmetic and its order are norm_held's (the same sums, the same
+// per-wave merge, the same output expression), so for equal (WPR, Q) the
+// two kernels produce the same bits.  Rows of the group are grp*RV .. +RV-1
+// within the workgroup's RPB rows; a row past the end re-reads the last row
+// and stores nothing.
+
+template <typename V>
+__device__ __forceinline__ void keep(V &v) { asm volatile("" : "+v"(v)); }
+
+template <typename T, int OP, int VEC, int WPR, int Q, int RV, int WAVES, bool RES>
+__global__ __launch_bounds__(WAVES * 64)
+void norm_multi(NormParams p)
+{
+    static_assert(VEC == 4 || (VEC == 8 && sizeof(T) == 2), "16-byte accesses");
+    static_assert(WAVES % WPR == 0 && WPR <= 8, "whole row groups per workgroup, walk merge");
+    static_assert(RV >= 2, "several rows per wave group");
+    using VT = vf<VEC>;
+    constexpr int GPB = WAVES / WPR;  // wave groups per workgroup
+    constexpr int RPB = GPB * RV;     // rows per workgroup
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int wr = (WPR == 1) ? 0 : wave % WPR;
+    const int grp = (WPR == 1) ? wave : wave / WPR;
+    __shared__ float2 xch[WPR > 1 ? RPB : 1][WPR];
+
+    const int d = p.d;
+    const int nvec = (int)((unsigned)d / VEC);  // >= 1: d % VEC == 0, d >= VEC
+    const float eps = p.eps;
+    const float inv_d = p.inv_d;
+
+    int kc[Q];
+    bool okc[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int k = lane + 64 * (wr + WPR * q);
+        okc[q] = k < nvec;
+        kc[q] = okc[q] ? k : nvec - 1;
+    }
+    int64_t row[RV];
+    bool rv[RV];
+#pragma unroll
+    for (int j = 0; j < RV; ++j) {
+        const int64_t r = (int64_t)blockIdx.x * RPB + grp * RV + j;
+        rv[j] = r < p.rows;
+        row[j] = rv[j] ? r : p.rows - 1;
+    }
+
+    // 1. every load of the group's RV rows before any use
+    VT v[RV][Q];
+#pragma unroll
+    for (int j = 0; j < RV; ++j) {
+        const T *xr = static_cast<const T *>(p.x) + row[j] * p.ldx;
+        const T *rr = RES ? static_cast<const T *>(p.r) + row[j] * p.ldr : nullptr;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            VT raw = ldv<T, VEC, true>(xr + VEC * kc[q]);
+            if constexpr (RES) raw = as_stored<T>(raw + ldv<T, VEC, true>(rr + VEC * kc[q]));
+            v[j][q] = okc[q] ? raw : VT(0.f);
+        }
+    }
+    if constexpr (RES) {
+        if (p.h) {
+#pragma unroll
+            for (int j = 0; j < RV; ++j) {
+                T *hr = static_cast<T *>(p.h) + row[j] * p.ldh;
+#pragma unroll
+                for (int q = 0; q < Q; ++q)
+                    if (okc[q] && rv[j]) stv<T, VEC, true>(hr + VEC * kc[q], v[j][q]);
+            }
+        }
+    }
+
+    // elements held by wave rank w of a row (all lanes agree)
+    auto wave_count = [&](int w) -> int {
+        int n = 0;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int c = nvec - 64 * (w + WPR * q);
+            n += c <= 0 ? 0 : (c >= 64 ? 64 : c);
+        }
+        return n * VEC;
+    };
+
+    // 2.-3. the statistics of each row, one exchange for all RV rows
+    float mu[RV], rs[RV];
+    if constexpr (OP == OP_LN) {
+        float muw[RV], m[RV];
+#pragma unroll
+        for (int j = 0; j < RV; ++j) {
+            float s = 0.f;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) s += hsum(v[j][q]);
+            const float S = group_sum<64>(s);
+            if constexpr (WPR == 1) {
+                muw[j] = S * inv_d;
+            } else {
+                const int n_w = wave_count(wr);
+                muw[j] = n_w > 0 ? S / (float)n_w : 0.f;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < RV; ++j) {
+            float t = 0.f;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) t += okc[q] ? csq(v[j][q], muw[j]) : 0.f;
+            m[j] = group_sum<64>(t);
+        }
+        if constexpr (WPR == 1) {
+#pragma unroll
+            for (int j = 0; j < RV; ++j) {
+                mu[j] = muw[j];
+                rs[j] = rsq(m[j] * inv_d + eps);
+            }
+        } else {
+            if (lane == 0) {
+#pragma unroll
+                for (int j = 0; j < RV; ++j) xch[grp * RV + j][wr] = make_float2(muw[j], m[j]);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < RV; ++j) {
+                float tot = 0.f;
+#pragma unroll
+                for (int w = 0; w < WPR; ++w) tot += (float)wave_count(w) * xch[grp * RV + j][w].x;
+                mu[j] = tot * inv_d;
+                float M2 = 0.f;
+#pragma unroll
+                for (int w = 0; w < WPR; ++w) {
+                    const float2 e = xch[grp * RV + j][w];
+                    const float dm = e.x - mu[j];
+                    M2 += e.y + (float)wave_count(w) * dm * dm;
+                }
+                rs[j] = rsq(M2 * inv_d + eps);
+            }
+        }
+    } else {
+        float S2[RV];
+#pragma unroll
+        for (int j = 0; j < RV; ++j) {
+            float s2 = 0.f;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) s2 += sq(v[j][q]);
+            S2[j] = group_sum<64>(s2);
+        }
+        if constexpr (WPR > 1) {
+            if (lane == 0) {
+#pragma unroll
+                for (int j = 0; j < RV; ++j) xch[grp * RV + j][wr] = make_float2(S2[j], 0.f);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < RV; ++j) {
+                float t = 0.f;
+#pragma unroll
+                for (int w = 0; w < WPR; ++w) t += xch[grp * RV + j][w].x;
+                S2[j] = t;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < RV; ++j) {
+            mu[j] = 0.f;
+            rs[j] = rsq(S2[j] * inv_d + eps);
+        }
+    }
+
+    // 4. the parameters of every slot in one batch, then normalize, scale,
+    // shift and store each row from the same registers
+    VT g[Q], b[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        g[q] = ldp<VEC>(p.p0 + VEC * kc[q]);
+        b[q] = (OP == OP_LN) ? ldp<VEC>(p.p1 + VEC * kc[q]) : VT(0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        keep(g[q]);
+        if constexpr (OP == OP_LN) keep(b[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+#pragma unroll
+        for (int j = 0; j < RV; ++j) {
+            T *yr = static_cast<T *>(p.y) + row[j] * p.ldy;
+            VT o;
+            if constexpr (OP == OP_LN) o = (v[j][q] - mu[j]) * rs[j] * g[q] + b[q];
+            else o = v[j][q] * g[q] * rs[j];
+            if (okc[q] && rv[j]) stv<T, VEC, true>(yr + VEC * kc[q], o);
+        }
+    }
+    if (wr == 0 && lane == 0) {
+#pragma unroll
+        for (int j = 0; j < RV; ++j) {
+            if (!rv[j]) continue;
+            if (OP == OP_LN && p.mean) p.mean[row[j]] = mu[j];
+            if (p.rstd) p.rstd[row[j]] = rs[j];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Streamed-row kernel for rows wider than the held variants cover: one
 // workgroup per row, the row read in chunks; LayerNorm reads x three times
 // (sum, centered sum of squares, output), RMSNorm twice.  VEC as above

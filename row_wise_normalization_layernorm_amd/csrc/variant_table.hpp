@@ -42,7 +42,7 @@ constexpr bool kres(int op) { return op >= 2; }
     Variant{OPN "_" #VEC "_p" #PEEL "_l" #LPR "_w" #WPR "_q" #Q "_b" #WAVES,                  \
             mi_norm_variant_info{OPC, DT, VEC, PEEL, 0, LPR, WPR, Q, WAVES,                     \
                                  (WPR == 1) ? WAVES * (64 / LPR) : WAVES / WPR,                 \
-                                 (int64_t)VEC * LPR * WPR * Q, (VEC > 1 && !PEEL) ? 1 : 0},     \
+                                 (int64_t)VEC * LPR * WPR * Q, (VEC > 1 && !PEEL) ? 1 : 0, 1},  \
             reinterpret_cast<const void *>(&norm_held<T, kop(OPC), VEC, (PEEL != 0), LPR, WPR,  \
                                                       Q, WAVES, true, true, 0, -1, kres(OPC)>)}
 
@@ -54,8 +54,29 @@ constexpr bool kres(int op) { return op >= 2; }
 #define MI_LOOP(T, DT, OPC, OPN, VEC, WAVES, U)                                                \
     Variant{OPN "_" #VEC "_loop_b" #WAVES "_u" #U,                                              \
             mi_norm_variant_info{OPC, DT, VEC, 0, 1, 64, WAVES, U, WAVES, 1, kUnbounded,        \
-                                 VEC > 1 ? 1 : 0},                                              \
+                                 VEC > 1 ? 1 : 0, 1},                                           \
             reinterpret_cast<const void *>(&norm_looped<T, kop(OPC), VEC, WAVES, U, kres(OPC)>)}
+
+// Multi-row variants (norm_multi): two rows per wave group sharing one fetch
+// of the parameters, 4-wave workgroups (8 at 8 waves per row), on the aligned
+// vector path.  Rows of a 16-bit type hold at most four slots: two rows of
+// eight octs plus their parameters do not fit the registers of a 4-wave
+// workgroup without spilling.
+#define MI_MULTI(T, DT, OPC, OPN, VEC, WPR, Q, WAVES)                                           \
+    Variant{OPN "_" #VEC "_r2_w" #WPR "_q" #Q "_b" #WAVES,                                      \
+            mi_norm_variant_info{OPC, DT, VEC, 0, 0, 64, WPR, Q, WAVES, (WAVES / WPR) * 2,      \
+                                 (int64_t)VEC * 64 * WPR * Q, 1, 2},                            \
+            reinterpret_cast<const void *>(&norm_multi<T, kop(OPC), VEC, WPR, Q, 2, WAVES, kres(OPC)>)}
+#define MI_MULTI_Q16(T, DT, OPC, OPN, VEC, WPR, WAVES)                                          \
+    MI_MULTI(T, DT, OPC, OPN, VEC, WPR, 1, WAVES), MI_MULTI(T, DT, OPC, OPN, VEC, WPR, 2, WAVES), \
+    MI_MULTI(T, DT, OPC, OPN, VEC, WPR, 3, WAVES), MI_MULTI(T, DT, OPC, OPN, VEC, WPR, 4, WAVES)
+#define MI_MULTI_Q_4(T, DT, OPC, OPN, WPR, WAVES)                                                \
+    MI_MULTI_Q16(T, DT, OPC, OPN, 4, WPR, WAVES), MI_MULTI(T, DT, OPC, OPN, 4, WPR, 6, WAVES),   \
+    MI_MULTI(T, DT, OPC, OPN, 4, WPR, 8, WAVES)
+#define MI_MULTI_Q_8(T, DT, OPC, OPN, WPR, WAVES) MI_MULTI_Q16(T, DT, OPC, OPN, 8, WPR, WAVES)
+#define MI_MULTI_ALL(T, DT, VW, OPC, OPN)                                                          \
+    MI_MULTI_Q_##VW(T, DT, OPC, OPN, 1, 4), MI_MULTI_Q_##VW(T, DT, OPC, OPN, 2, 4),                   \
+    MI_MULTI_Q_##VW(T, DT, OPC, OPN, 4, 4), MI_MULTI_Q_##VW(T, DT, OPC, OPN, 8, 8)
 
 // every (waves per row, slots) pair of a vector path (VW elements per access:
 // 4 for float32, 8 for the 16-bit types, 16 bytes either way): slots 1, 2,
@@ -103,7 +124,9 @@ constexpr bool kres(int op) { return op >= 2; }
     MI_HELD2(T, DT, OPC, OPN, 1, 0, 64, 8, 8, 8),                                               \
     MI_HELD(T, DT, OPC, OPN, 1, 0, 64, 16, 8, 16), MI_HELD(T, DT, OPC, OPN, 1, 0, 64, 16, 16, 16), \
     /* streamed rows, any width */                                                             \
-    MI_LOOP(T, DT, OPC, OPN, VW, 4, 4), MI_LOOP(T, DT, OPC, OPN, 1, 4, 8)
+    MI_LOOP(T, DT, OPC, OPN, VW, 4, 4), MI_LOOP(T, DT, OPC, OPN, 1, 4, 8),                      \
+    /* two rows per wave group, one fetch of the parameters for both */                       \
+    MI_MULTI_ALL(T, DT, VW, OPC, OPN)
 
 // the four operations of one storage type; VW its vector width in
 // elements, SFX its name suffix

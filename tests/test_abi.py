@@ -206,7 +206,7 @@ def test_variant_table_is_consistent(L):
     assert max(i for i, _, _ in infos) < min(i for i, _, _ in bwd)
     for i, n, v in bwd:
         assert n.startswith(BWD_PREFIX[v["op"]] + DTSFX[v["dtype"]]), n
-        assert v["lanes_per_row"] == 64 and not v["peel"]
+        assert v["lanes_per_row"] == 64 and not v["peel"] and v["rows_per_lane"] == 1
         if v["looped"]:
             assert v["max_d"] == 2**63 - 1 and v["vec"] == 1 and v["needs_aligned"] == 0
             continue
@@ -226,7 +226,13 @@ def test_variant_table_is_consistent(L):
             assert v["max_d"] == 2**63 - 1 and v["rows_per_block"] == 1
             continue
         assert v["max_d"] == v["vec"] * v["lanes_per_row"] * v["waves_per_row"] * v["slots"]
-        if v["waves_per_row"] == 1:
+        assert v["rows_per_lane"] in (1, 2), n
+        if v["rows_per_lane"] == 2:
+            # multi-row: aligned vector path, full-wave rows, two rows per wave group
+            assert "_r2_" in n and v["vec"] > 1 and not v["peel"] and v["lanes_per_row"] == 64, n
+            assert v["rows_per_block"] == 2 * v["waves_per_block"] // v["waves_per_row"], n
+            assert v["waves_per_row"] <= 8 and v["slots"] <= (8 if v["vec"] == 4 else 4), n
+        elif v["waves_per_row"] == 1:
             assert v["rows_per_block"] == v["waves_per_block"] * 64 // v["lanes_per_row"]
         else:
             assert v["lanes_per_row"] == 64
@@ -299,13 +305,23 @@ def test_dispatch_examples(L):
     assert sel(0, 768) == "ln_4_p0_l64_w1_q3_b16"            # 256 workgroups of 16 rows
     assert sel(0, 768, rows=1000) == "ln_4_p0_l64_w2_q2_b4"  # few rows: two waves per row
     assert sel(0, 2048, rows=1024) == "ln_4_p0_l64_w4_q2_b4"
-    assert sel(0, 4096, rows=4096) == "ln_4_p0_l64_w4_q4_b16"
-    assert sel(0, 8192, rows=32768) == "ln_4_p0_l64_w8_q4_b16"
+    assert sel(0, 2048, rows=4096) == "ln_4_p0_l64_w2_q4_b16"  # 32 MiB: one row per wave
+    # from 8192 rows or 64 MiB of rows, two rows per wave group
+    assert sel(0, 4096, rows=4096) == "ln_4_r2_w4_q4_b4"
+    assert sel(0, 8192, rows=32768) == "ln_4_r2_w8_q4_b8"
+    assert sel(0, 768, rows=8192) == "ln_4_r2_w1_q3_b4"
+    assert sel(0, 768, rows=8191) == "ln_4_p0_l64_w1_q3_b16"
+    assert sel(0, 8192, rows=32768, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_r2_w4_q4_b4"
+    assert sel(0, 8192, rows=4096, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_r2_w4_q4_b4"   # 64 MiB
+    assert sel(0, 8192, rows=4095, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w4_q4_b16"
+    # no multi-row variant for 16 waves per row, or for more than 4 slots of 16-bit rows
+    assert sel(0, 16384, rows=8192) == "ln_4_p0_l64_w16_q4_b16"
+    assert sel(0, 6144 * 8, rows=8192, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w16_q6_b16"
     assert sel(0, 128, rows=512) == "ln_4_p0_l32_w1_q1_b4"
     assert sel(1, 8193, rows=256) == "rms_4_p1_l64_w16_q3_b16"
     assert sel(0, 1, rows=64) == "ln_1_p0_l16_w1_q1_b4"
     assert sel(2, 768) == "addln_4_p0_l64_w1_q3_b16"
-    assert sel(3, 8192, rows=32768) == "addrms_4_p0_l64_w8_q4_b16"
+    assert sel(3, 8192, rows=32768) == "addrms_4_r2_w8_q4_b8"
     assert "_loop_" in sel(0, 2**20)
     # gamma misaligned only: no 128-bit parameter reads, so not the aligned path
     assert mn.mi_norm_variant_get_info(mn.mi_norm_select(_prob(0, 4096, 768, g=G + 4)))["needs_aligned"] == 0
@@ -315,6 +331,11 @@ def test_workgroup_size_follows_row_count(L):
     for d in (768, 2048, 4096, 8192, 16384):
         for rows in (1, 100, 1000, 5000, 100000):
             v = mn.mi_norm_variant_get_info(mn.mi_norm_select(_prob(0, rows, d)))
+            if v["rows_per_lane"] == 2:
+                # multi-row variants have a fixed workgroup: 4 waves, 8 at 8 waves per row
+                assert rows >= 8192 or rows * d * 4 >= 64 << 20, (d, rows)
+                assert v["waves_per_block"] == max(4, v["waves_per_row"]), (d, rows)
+                continue
             need = 512 if v["waves_per_row"] > 1 else 256
             per16 = 16 // v["waves_per_row"]
             if v["waves_per_block"] < 16:
