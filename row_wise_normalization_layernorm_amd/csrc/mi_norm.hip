@@ -97,13 +97,17 @@ int find(int op, int dtype, int64_t rows, int vec, int peel, int looped, int lpr
     return pick >= 0 ? base + pick : -1;
 }
 
-// The multi-row variant of an aligned vector shape, or -1.  It pays once a
-// launch has many rows: on MI355X, from 8192 rows or 64 MiB of input rows it
-// measured 3-17% faster than the one-row variant of the same shape (most for
-// 16-bit rows, whose parameter fetches are four times their own bytes), while
-// at 1024 rows it was up to 17% slower and at 4096 rows of 16 to 32 MiB it
-// went either way.
-bool multi_pays(int64_t rows, int64_t d, int64_t es) {
+// Whether the multi-row variant of an aligned vector shape should run.  It
+// pays once a launch has many rows: on MI355X, from 8192 rows or 64 MiB of
+// input rows it measured 3-17% faster than the one-row variant of the same
+// shape (most for 16-bit rows, whose parameter fetches are four times their
+// own bytes), while at 1024 rows it was up to 17% slower and at 4096 rows of
+// 16 to 32 MiB it went either way.  The fused float32 operations move four
+// row streams per parameter fetch, so sharing the fetch saves little there:
+// within 2% either way up to 4 waves per row, and 3-5% slower at 8 waves per
+// row ([32768,8192]), where the one-row variant stays.
+bool multi_pays(int op, int64_t rows, int64_t d, int64_t es, int wpr) {
+    if (kres(op) && es == 4 && wpr >= 8) return false;
     return rows >= 8192 || rows * d * es >= (int64_t(64) << 20);
 }
 
@@ -216,7 +220,7 @@ int select_variant(const mi_norm_problem &P) {
         if (nvec <= 16) return find(op, dt, rows, W, 0, 0, 16, 1, 1);
         if (nvec <= 32) return find(op, dt, rows, W, 0, 0, 32, 1, 1);
         shape_vectors(nvec, rows, wpr, q);
-        if (wpr && multi_pays(rows, d, esize(dt))) {
+        if (wpr && multi_pays(op, rows, d, esize(dt), wpr)) {
             const int m = find_multi(op, dt, W, wpr, q);
             if (m >= 0) return m;
         }
