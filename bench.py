@@ -69,6 +69,7 @@ BENCH_WORKLOADS = {
     "rms_512x128": W("rmsnorm", "f32", 512, 128),
     "rms_4096x768": W("rmsnorm", "f32", 4096, 768),
     "rms_2048x4096": W("rmsnorm", "f32", 2048, 4096),
+    "rms_8192x8192": W("rmsnorm", "f32", 8192, 8192),
     "rms_256x8193": W("rmsnorm", "f32", 256, 8193),
     "addln_4096x768": W("add_layernorm", "f32", 4096, 768, "normal", True),
     "addln_32768x8192": W("add_layernorm", "f32", 32768, 8192),
