@@ -125,6 +125,11 @@ void norm_bwd_held(BwdParams p)
         accb[q] = DT(0.0);
     }
     const bool want_pg = p.part != nullptr;
+    // a lane keeps its columns for every row it visits, so gamma (or w) is
+    // fetched once and held, not once per row
+    VT gam[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) gam[q] = ldp<VEC>(p.p0 + VEC * kc[q]);
 
     const int64_t ngroups = (p.rows + RPB - 1) / RPB;
     int par = 0;
@@ -153,7 +158,7 @@ void norm_bwd_held(BwdParams p)
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             const VT xh = (xv[q] - mu) * rs;
-            const VT g = dv[q] * ldp<VEC>(p.p0 + VEC * kc[q]);
+            const VT g = dv[q] * gam[q];
             s1 += okc[q] ? hsum(g) : 0.f;
             s2 += okc[q] ? hsum(g * xh) : 0.f;
         }
@@ -177,7 +182,7 @@ void norm_bwd_held(BwdParams p)
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             const VT xh = (xv[q] - mu) * rs;
-            const VT g = dv[q] * ldp<VEC>(p.p0 + VEC * kc[q]);
+            const VT g = dv[q] * gam[q];
             VT o;
             if constexpr (OP == OP_LN) o = rs * (g - m1 - xh * m2);
             else o = rs * (g - xh * m2);
