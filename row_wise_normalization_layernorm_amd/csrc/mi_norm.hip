@@ -105,11 +105,18 @@ int find(int op, int dtype, int64_t rows, int vec, int peel, int looped, int lpr
 // 16 to 32 MiB it went either way.  The fused float32 operations move four
 // row streams per parameter fetch, so sharing the fetch saves little there:
 // within 2% either way up to 4 waves per row, and 3-5% slower at 8 waves per
-// row ([32768,8192]), where the one-row variant stays.
-bool multi_pays(int op, int64_t rows, int64_t d, int64_t es, int wpr) {
+// row ([32768,8192]), where the one-row variant stays.  With one wave per
+// row, rows of 3.5 KiB or more apart (the widest row tensor stride, in bytes)
+// also take it: there the one-row variant's 16-wave workgroups ran 5-39%
+// slower than two rows per wave group ([4096,1024]: 7.8 against 6.5 us; the
+// [4096,768] rows at stride 1024: 6.5 against 5.5 us), while 3 KiB rows
+// ([4096,768] contiguous) are 2-3% faster with the one-row variant.
+bool multi_pays(int op, int64_t rows, int64_t d, int64_t es, int wpr, int64_t pitch) {
     if (kres(op) && es == 4 && wpr >= 8) return false;
-    return rows >= 8192 || rows * d * es >= (int64_t(64) << 20);
+    if (rows >= 8192 || rows * d * es >= (int64_t(64) << 20)) return true;
+    return wpr == 1 && pitch >= 3584;
 }
+
 
 int find_multi(int op, int dtype, int vec, int wpr, int q) {
     const VariantTable &T = table(dtype);
@@ -208,6 +215,15 @@ bool shape_ok(const mi_norm_problem &P) {
     return true;
 }
 
+// the widest row stride of the problem's row tensors, in bytes
+int64_t row_pitch(const mi_norm_problem &P) {
+    const Rows R = rows_of(P);
+    int64_t m = 0;
+    for (int i = 0; i < 4; ++i)
+        if (R.p[i] && R.ld[i] > m) m = R.ld[i];
+    return m * esize(P.dtype);
+}
+
 int select_variant(const mi_norm_problem &P) {
     if (!shape_ok(P)) return -1;
     const Layout L = layout_of(P);
@@ -220,7 +236,7 @@ int select_variant(const mi_norm_problem &P) {
         if (nvec <= 16) return find(op, dt, rows, W, 0, 0, 16, 1, 1);
         if (nvec <= 32) return find(op, dt, rows, W, 0, 0, 32, 1, 1);
         shape_vectors(nvec, rows, wpr, q);
-        if (wpr && multi_pays(op, rows, d, esize(dt), wpr)) {
+        if (wpr && multi_pays(op, rows, d, esize(dt), wpr, row_pitch(P))) {
             const int m = find_multi(op, dt, W, wpr, q);
             if (m >= 0) return m;
         }

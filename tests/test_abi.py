@@ -311,6 +311,12 @@ def test_dispatch_examples(L):
     assert sel(0, 8192, rows=32768) == "ln_4_r2_w8_q4_b8"
     assert sel(0, 768, rows=8192) == "ln_4_r2_w1_q3_b4"
     assert sel(0, 768, rows=8191) == "ln_4_p0_l64_w1_q3_b16"
+    # one wave per row on rows 3.5 KiB or more apart: two rows per wave group
+    assert sel(0, 1024, rows=4096) == "ln_4_r2_w1_q4_b4"
+    assert sel(0, 896, rows=4096) == "ln_4_r2_w1_q4_b4"
+    assert sel(0, 768, rows=4096, ldx=1024, ldy=1024) == "ln_4_r2_w1_q3_b4"
+    assert sel(0, 768, rows=4096, ldx=880) == "ln_4_p0_l64_w1_q3_b16"
+    assert sel(0, 2048, rows=4096, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_r2_w1_q4_b4"
     assert sel(0, 8192, rows=32768, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_r2_w4_q4_b4"
     assert sel(0, 8192, rows=4096, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_r2_w4_q4_b4"   # 64 MiB
     assert sel(0, 8192, rows=4095, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w4_q4_b16"
@@ -336,7 +342,8 @@ def test_workgroup_size_follows_row_count(L):
             v = mn.mi_norm_variant_get_info(mn.mi_norm_select(_prob(0, rows, d)))
             if v["rows_per_lane"] == 2:
                 # multi-row variants have a fixed workgroup: 4 waves, 8 at 8 waves per row
-                assert rows >= 8192 or rows * d * 4 >= 64 << 20, (d, rows)
+                assert rows >= 8192 or rows * d * 4 >= 64 << 20 or (v["waves_per_row"] == 1 and 4 * d >= 3584), \
+                    (d, rows)
                 assert v["waves_per_block"] == max(4, v["waves_per_row"]), (d, rows)
                 continue
             need = 512 if v["waves_per_row"] > 1 else 256
