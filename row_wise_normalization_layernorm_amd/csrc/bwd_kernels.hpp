@@ -238,15 +238,15 @@ void norm_bwd_held(BwdParams p)
 // ---------------------------------------------------------------------------
 // Sum of the partial rows: out_g[j] = sum_b part[b][g][j] in float64, in a
 // fixed order.  A workgroup covers 16 columns: 4 column quads by 64 slices of
-// the partial rows (slice s takes rows s, s + 64, ...; with at most 512
-// partial rows a lane issues at most 8 loads, all before any add), then the
+// the partial rows (slice s takes rows s, s + 64, ...; with at most 256
+// partial rows a lane issues at most 4 loads, all before any add), then the
 // slices meet in a fixed binary tree in LDS.  Memory-latency bound: many
 // small workgroups.
 template <int NG>
 __global__ __launch_bounds__(256)
 void norm_bwd_reduce(const float *part, int64_t nblk, int32_t d, int32_t dpad, float *out0, float *out1)
 {
-    constexpr int SL = 64, CQ = 4, U = 8;
+    constexpr int SL = 64, CQ = 4, U = 4;
     const int cq = threadIdx.x % CQ;
     const int sl = threadIdx.x / CQ;
     const int g = blockIdx.y;

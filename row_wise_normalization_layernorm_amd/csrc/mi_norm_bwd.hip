@@ -21,7 +21,11 @@ using namespace minorm::host;
 
 namespace {
 
-constexpr int64_t kMaxPartials = 512;  // partial rows: workgroups of the row kernel, row blocks
+// partial rows: workgroups of the row kernel (one per CU), row blocks of the
+// streamed path.  Measured on MI355X: 512 took LayerNorm backward [4096,768]
+// 15.4 us (13.5 with 256), BF16 15.5 (11.6); 128 left half the CUs idle
+// ([32768,8192] 729 us against 560).
+constexpr int64_t kMaxPartials = 256;
 constexpr int64_t kAlign = 256;        // workspace alignment and section alignment
 constexpr int64_t kMaxGrid = 1 << 20;  // grid cap of the statistics kernel's row loop
 constexpr int kStreamThreads = 256;    // norm_bwd_chunks<..., 4, 8>: 4 waves,

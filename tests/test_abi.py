@@ -483,10 +483,10 @@ def _bprob(op=mn.OP_LAYERNORM, rows=64, d=768, ws=WS, ws_bytes=None, **kw):
 def test_bwd_workspace_size(L):
     p = _bprob(rows=4096, d=768)
     n = mn.mi_norm_bwd_workspace_size(p)
-    # 512 partial rows of (dgamma, dbeta), then the per-row statistics; 256-byte sections
-    assert n == 512 * 2 * 768 * 4 + 4096 * 8
-    assert mn.mi_norm_bwd_workspace_size(_bprob(op=mn.OP_RMSNORM, rows=4096, d=768)) == 512 * 768 * 4 + 4096 * 8
-    assert mn.mi_norm_bwd_workspace_size(_bprob(rows=3, d=5)) == 512 * 2 * 8 * 4 + 256
+    # 256 partial rows of (dgamma, dbeta), then the per-row statistics; 256-byte sections
+    assert n == 256 * 2 * 768 * 4 + 4096 * 8
+    assert mn.mi_norm_bwd_workspace_size(_bprob(op=mn.OP_RMSNORM, rows=4096, d=768)) == 256 * 768 * 4 + 4096 * 8
+    assert mn.mi_norm_bwd_workspace_size(_bprob(rows=3, d=5)) == 256 * 2 * 8 * 4 + 256
     # no parameter gradients: only the statistics section
     assert mn.mi_norm_bwd_workspace_size(_bprob(rows=100, d=64, dparams0=None, dparams1=None)) == 1024
     assert mn.mi_norm_bwd_workspace_size(_bprob(d=0)) == -1
