@@ -132,25 +132,45 @@ void norm_bwd_held(BwdParams p)
     for (int q = 0; q < Q; ++q) gam[q] = ldp<VEC>(p.p0 + VEC * kc[q]);
 
     const int64_t ngroups = (p.rows + RPB - 1) / RPB;
+    // a row slot past the end (last step only) re-reads the last row and
+    // stores nothing; loads stay unconditional at clamped addresses
+    auto row_of = [&](int64_t rg) -> int64_t {
+        const int64_t r = rg * RPB + rib;
+        return r < p.rows ? r : p.rows - 1;
+    };
+    // x and dy of the step's row.  With one wave per row and at most 16
+    // values per lane (PF), also the next step's: its loads are in flight
+    // while this row is reduced and written (4% on [4096,768]; wider rows
+    // gained nothing and would spill with the second copy).
+    constexpr bool PF = WPR == 1 && VEC * Q <= 16;
+    VT xv[Q], dv[Q];
+    auto load_row = [&](int64_t row, VT (&xa)[Q], VT (&da)[Q]) {
+        const T *xr = static_cast<const T *>(p.x) + row * p.ldx;
+        const T *dyr = static_cast<const T *>(p.dy) + row * p.lddy;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            xa[q] = ldv<T, VEC, true>(xr + VEC * kc[q]);
+            da[q] = ldv<T, VEC, true>(dyr + VEC * kc[q]);
+        }
+    };
+    if constexpr (PF) {
+        if ((int64_t)blockIdx.x < ngroups) load_row(row_of(blockIdx.x), xv, dv);
+    }
     int par = 0;
     for (int64_t rg = blockIdx.x; rg < ngroups; rg += gridDim.x) {
-        // a row slot past the end (last step only) re-reads the last row and
-        // stores nothing; loads stay unconditional at clamped addresses
         const int64_t row_raw = rg * RPB + rib;
         const bool rv = row_raw < p.rows;
         const int64_t row = rv ? row_raw : p.rows - 1;
-        const T *xr = static_cast<const T *>(p.x) + row * p.ldx;
-        const T *dyr = static_cast<const T *>(p.dy) + row * p.lddy;
         T *dxr = static_cast<T *>(p.dx) + row * p.lddx;
-
-        VT xv[Q], dv[Q];
-#pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            xv[q] = ldv<T, VEC, true>(xr + VEC * kc[q]);
-            dv[q] = ldv<T, VEC, true>(dyr + VEC * kc[q]);
-        }
         const float mu = (OP == OP_LN) ? p.mean[row] : 0.f;
         const float rs = p.rstd[row];
+        VT xn[PF ? Q : 1], dn[PF ? Q : 1];
+        if constexpr (PF) {
+            const int64_t nrg = rg + gridDim.x;
+            if (nrg < ngroups) load_row(row_of(nrg), xn, dn);
+        } else {
+            load_row(row, xv, dv);
+        }
 
         // xhat and g are formed twice (here for the sums, below for the
         // outputs) rather than held: only x and dy stay in registers
@@ -190,6 +210,13 @@ void norm_bwd_held(BwdParams p)
             if (want_pg && rv && okc[q]) {
                 accg[q] += widen64<VEC>(dv[q] * xh);
                 if constexpr (OP == OP_LN) accb[q] += widen64<VEC>(dv[q]);
+            }
+        }
+        if constexpr (PF) {
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                xv[q] = xn[q];
+                dv[q] = dn[q];
             }
         }
     }
