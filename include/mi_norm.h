@@ -310,8 +310,9 @@ mi_norm_status mi_norm_variant_get_info(int id, mi_norm_variant_info *out);
 
 /* The variant the dispatcher would choose for problem *p (host logic only,
  * no device access; eps, mean and rstd are not consulted): the storage type,
- * row width, alignment and strides pick the shape, the row count picks the
- * waves per row and the workgroup size.  Returns -1 when the problem's shape
+ * row width, alignment and strides pick the shape; the row count picks the
+ * waves per row and the workgroup size; many rows (or rows far apart) pick a
+ * multi-row variant (rows_per_lane 2).  Returns -1 when the problem's shape
  * or pointers are invalid. */
 int mi_norm_select(const mi_norm_problem *p);
 
