@@ -391,7 +391,7 @@ def measure_and_print(args, torch, stream, run_native, run_python, rotated, nset
         copy = {"us": round(copy_us, 3), "bytes": 8 * max(4, (bytes_step // 8) // 4 * 4),
                 "buffer_sets": copy_sets,
                 "pct_of_copy": round(100 * copy_us / (ms_per_step * 1e3), 2),
-                "what": "copy_f4 moving the step's bytes (half read, half written), timed the same way"}
+                "what": "copy_cover moving the step's bytes (half read, half written), timed the same way"}
 
     cpu = None
     if cpu_fn is not None:
@@ -688,7 +688,7 @@ def main(argv=None) -> int:
         sel = vid if vid >= 0 else mn.mi_norm_select(probs[0])
         variant_name = mn.mi_norm_variant_name(sel)
     else:
-        variant_name = "copy_f4"
+        variant_name = "copy_cover"
 
     stream = torch.cuda.Stream(device=dev)
     sh = stream.cuda_stream

@@ -28,8 +28,29 @@ using namespace minorm::host;
 namespace minorm {
 
 // ---------------------------------------------------------------------------
-// Streaming copy (calibration): U 128-bit accesses per lane per step, with
-// the same non-temporal hints as the normalization kernels.
+// Streaming copy (calibration): every lane moves Q 128-bit words, all loads
+// before any store, the grid covering the array once, with the same
+// non-temporal hints as the normalization kernels.  The shape is picked by
+// size in mi_copy_f32.
+template <int BLOCK, int Q>
+__global__ __launch_bounds__(BLOCK)
+void copy_cover(const float *src, float *dst, int64_t n4)
+{
+    const int64_t base = (int64_t)blockIdx.x * BLOCK * Q + threadIdx.x;
+    f4 v[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int64_t i = base + (int64_t)BLOCK * q;
+        v[q] = i < n4 ? ld4<true>(src + 4 * i) : f4(0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int64_t i = base + (int64_t)BLOCK * q;
+        if (i < n4) st4<true>(dst + 4 * i, v[q]);
+    }
+}
+
+// the grid-stride form, for arrays too long for one covering grid
 template <int U>
 __global__ __launch_bounds__(256)
 void copy_f4(const float *src, float *dst, int64_t n4)
@@ -111,9 +132,15 @@ int find(int op, int dtype, int64_t rows, int vec, int peel, int looped, int lpr
 // slower than two rows per wave group ([4096,1024]: 7.8 against 6.5 us; the
 // [4096,768] rows at stride 1024: 6.5 against 5.5 us), while 3 KiB rows
 // ([4096,768] contiguous) are 2-3% faster with the one-row variant.
+//
+// The fused operations take it from 4096 rows: their one-row 16-wave
+// workgroups hold four row streams each, and two rows per wave group with
+// 4-wave workgroups measured 2-16% faster there (add + LayerNorm [4096,768]
+// float32: 8.9 against 10.6 us; [8192,768]: 18.2 against 19.4 us).
 bool multi_pays(int op, int64_t rows, int64_t d, int64_t es, int wpr, int64_t pitch) {
     if (kres(op) && es == 4 && wpr >= 8) return false;
     if (rows >= 8192 || rows * d * es >= (int64_t(64) << 20)) return true;
+    if (kres(op) && rows >= 4096) return true;
     return wpr == 1 && pitch >= 3584;
 }
 
@@ -513,20 +540,34 @@ mi_norm_status mi_copy_f32(const float *src, float *dst, int64_t n, hipStream_t 
     if (meet(vec_ext(src, n, 4), vec_ext(dst, n, 4))) return MI_NORM_ERR_INVALID;
     hipError_t e;
     if (n % 4 == 0 && al16(src) && al16(dst)) {
-        // one 128-bit access per lane for large copies, two below 256 MiB
-        // (the faster shapes on gfx950 at 2 GiB and at 24 MiB)
-        const int64_t n4 = n / 4;
-        const bool big = n4 >= (int64_t(1) << 24);
-        const int U = big ? 1 : 2;
-        int64_t blocks = (n4 + 256 * U - 1) / (256 * U);
-        if (blocks > kMaxGrid) blocks = kMaxGrid;
+        // the fastest covering shape measured on MI355X for the bytes moved
+        // (read + written), rotating buffers past the caches: 12.6 MB 512x3
+        // (3.40 us), 25 MB 256x4 (5.25), 50 and 100 MB 256x8 (8.65, 17.0),
+        // 200 MB 1024x1 (32.6), 1 and 2 GB 256x1 (164, 329)
+        const int64_t n4 = n / 4, bytes = 8 * n;
+        int block = 256, q = 1;
+        const void *fn = reinterpret_cast<const void *>(&copy_cover<256, 1>);
+        if (bytes <= (int64_t(16) << 20)) {
+            block = 512, q = 3, fn = reinterpret_cast<const void *>(&copy_cover<512, 3>);
+        } else if (bytes <= (int64_t(48) << 20)) {
+            q = 4, fn = reinterpret_cast<const void *>(&copy_cover<256, 4>);
+        } else if (bytes <= (int64_t(160) << 20)) {
+            q = 8, fn = reinterpret_cast<const void *>(&copy_cover<256, 8>);
+        } else if (bytes <= (int64_t(768) << 20)) {
+            block = 1024, fn = reinterpret_cast<const void *>(&copy_cover<1024, 1>);
+        }
+        int64_t blocks = (n4 + (int64_t)block * q - 1) / ((int64_t)block * q);
         int64_t n4a = n4;
         const float *s = src;
         float *dd = dst;
         void *args[] = {&s, &dd, &n4a};
-        const void *fn = big ? reinterpret_cast<const void *>(&copy_f4<1>)
-                             : reinterpret_cast<const void *>(&copy_f4<2>);
-        e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, stream);
+        if (blocks <= INT32_MAX) {
+            e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(block), args, 0, stream);
+        } else {
+            blocks = kMaxGrid;
+            e = hipLaunchKernel(reinterpret_cast<const void *>(&copy_f4<1>), dim3((unsigned)blocks), dim3(256),
+                                args, 0, stream);
+        }
     } else {
         int64_t blocks = (n + 255) / 256;
         if (blocks > kMaxGrid) blocks = kMaxGrid;

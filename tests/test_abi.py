@@ -326,7 +326,8 @@ def test_dispatch_examples(L):
     assert sel(0, 128, rows=512) == "ln_4_p0_l32_w1_q1_b4"
     assert sel(1, 8193, rows=256) == "rms_4_p1_l64_w16_q3_b16"
     assert sel(0, 1, rows=64) == "ln_1_p0_l16_w1_q1_b4"
-    assert sel(2, 768) == "addln_4_p0_l64_w1_q3_b16"
+    assert sel(2, 768) == "addln_4_r2_w1_q3_b4"             # fused: two rows per wave group
+    assert sel(2, 768, rows=4095) == "addln_4_p0_l64_w2_q2_b16"
     # fused float32 rows at 8 waves per row keep one row per wave; 16-bit ones do not
     assert sel(3, 8192, rows=32768) == "addrms_4_p0_l64_w8_q4_b16"
     assert sel(2, 4096, rows=16384) == "addln_4_r2_w4_q4_b4"
@@ -456,7 +457,7 @@ def test_strides_and_types_decide_the_layout(L):
 
 def test_named_calls_equal_the_general_call(L):
     p = _prob(mn.OP_ADD_RMSNORM, 4096, 768, dtype=mn.MI_NORM_F32)
-    assert mn.mi_norm_variant_name(mn.mi_norm_select(p)) == "addrms_4_p0_l64_w1_q3_b16"
+    assert mn.mi_norm_variant_name(mn.mi_norm_select(p)) == "addrms_4_r2_w1_q3_b4"
     assert L.mi_add_rmsnorm_fwd(X, R_, G, Y, Y, 4, 8, 1e-5, None, None) == mn.MI_NORM_ERR_INVALID
     assert mn.mi_norm_check(_prob(mn.OP_ADD_RMSNORM, 4, 8, h=Y)) == mn.MI_NORM_ERR_INVALID
 

@@ -300,11 +300,18 @@ def test_rows_zero_and_errors_on_device(torch_dev):
 
 
 def test_copy_calibration_kernel(torch_dev):
+    """Every size band of the copy's shape table (the bytes moved: up to 16,
+    48, 160 and 768 MiB, and beyond), a ragged last workgroup, a length not
+    a multiple of four and a misaligned start; nothing past the end written."""
     torch, dev = torch_dev
-    say("copy kernel")
-    for n, off in ((1 << 20, 0), (1000003, 0), (4096, 1)):
-        src = torch.randn(n + 4, device=dev)[off:off + n]
-        dst = torch.zeros(n + 4, device=dev)[off:off + n]
+    for n, off in ((1 << 20, 0), (1000003, 0), (4096, 1), ((4 << 20) + 36, 0), ((12 << 20) + 4, 0),
+                   ((48 << 20) + 1028, 0), ((128 << 20) + 8, 0)):
+        say(f"copy kernel n={n} off={off}")
+        src = torch.randn(n + 64, device=dev)[off:off + n]
+        dbuf = torch.full((n + 64,), -7.0, device=dev)
+        dst = dbuf[off:off + n]
         mn.mi_copy_f32(src, dst, n)
         torch.cuda.synchronize()
         assert torch.equal(src, dst)
+        assert bool((dbuf[off + n:] == -7.0).all()) and bool((dbuf[:off] == -7.0).all())
+        del src, dbuf, dst
