@@ -60,3 +60,11 @@ from ._binding import (  # noqa: F401
     problem,
     rmsnorm,
 )
+
+
+def __getattr__(name):
+    # the autograd layer imports torch; load it on first use only
+    if name in ("layer_norm", "rms_norm", "LayerNorm", "RMSNorm"):
+        from . import autograd
+        return getattr(autograd, name)
+    raise AttributeError(name)

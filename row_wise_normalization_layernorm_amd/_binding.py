@@ -419,6 +419,21 @@ def _params(t, name: str, d: int):
     return t
 
 
+def _on_stream(stream, device):
+    """(context, handle): inside the context, torch allocations belong to the
+    stream the kernels will run on, so the caching allocator does not hand
+    them to other streams' work before those kernels finish; handle is that
+    stream's hipStream_t.  ``stream`` is None (torch's current stream), a
+    torch stream, or a raw handle."""
+    import contextlib
+    import torch
+    if stream is None:
+        return contextlib.nullcontext(), torch.cuda.current_stream(device).cuda_stream
+    if hasattr(stream, "cuda_stream"):
+        return torch.cuda.stream(stream), stream.cuda_stream
+    return torch.cuda.stream(torch.cuda.ExternalStream(stream, device=device)), stream
+
+
 def _norm(op, x, r, p0, p1, eps, stats, out, write_sum, stream):
     import torch
     dt = _dtype_code(x)
@@ -429,17 +444,19 @@ def _norm(op, x, r, p0, p1, eps, stats, out, write_sum, stream):
         if r.dtype != x.dtype or r.shape != x.shape:
             raise ValueError("r must have x's shape and dtype")
         ldr = _rows_of(r, "r")[1]
-    y = torch.empty(x.shape, device=x.device, dtype=x.dtype) if out is None else out
-    if y.dtype != x.dtype or y.shape != x.shape:
-        raise ValueError("out must have x's shape and dtype")
-    ldy = _rows_of(y, "out")[1]
-    h = torch.empty(x.shape, device=x.device, dtype=x.dtype) if (r is not None and write_sum) else None
-    ln = op in (OP_LAYERNORM, OP_ADD_LAYERNORM)
-    mean = torch.empty(x.shape[:-1], device=x.device, dtype=torch.float32) if (stats and ln) else None
-    rstd = torch.empty(x.shape[:-1], device=x.device, dtype=torch.float32) if stats else None
-    p = problem(op, rows, d, x, y, _params(p0, "gamma" if ln else "w", d), _params(p1, "beta", d), r, h,
-                dtype=dt, ldx=ldx, ldr=ldr, ldy=ldy, ldh=0, eps=eps, mean=mean, rstd=rstd)
-    mi_norm_fwd(p, stream if stream is not None else torch.cuda.current_stream(x.device).cuda_stream)
+    ctx, handle = _on_stream(stream, x.device)
+    with ctx:
+        y = torch.empty(x.shape, device=x.device, dtype=x.dtype) if out is None else out
+        if y.dtype != x.dtype or y.shape != x.shape:
+            raise ValueError("out must have x's shape and dtype")
+        ldy = _rows_of(y, "out")[1]
+        h = torch.empty(x.shape, device=x.device, dtype=x.dtype) if (r is not None and write_sum) else None
+        ln = op in (OP_LAYERNORM, OP_ADD_LAYERNORM)
+        mean = torch.empty(x.shape[:-1], device=x.device, dtype=torch.float32) if (stats and ln) else None
+        rstd = torch.empty(x.shape[:-1], device=x.device, dtype=torch.float32) if stats else None
+        p = problem(op, rows, d, x, y, _params(p0, "gamma" if ln else "w", d), _params(p1, "beta", d), r, h,
+                    dtype=dt, ldx=ldx, ldr=ldr, ldy=ldy, ldh=0, eps=eps, mean=mean, rstd=rstd)
+        mi_norm_fwd(p, handle)
     return y, h, mean, rstd
 
 
@@ -475,24 +492,26 @@ def _norm_bwd(op, dy, x, p0, mean, rstd, param_grads, out, stream):
     d = x.shape[-1]
     rows, ldx = _rows_of(x, "x")
     lddy = _rows_of(dy, "dy")[1]
-    dx = torch.empty(x.shape, device=x.device, dtype=x.dtype) if out is None else out
-    if dx.dtype != x.dtype or dx.shape != x.shape:
-        raise ValueError("out must have x's shape and dtype")
-    lddx = _rows_of(dx, "out")[1]
-    ln = op == OP_LAYERNORM
-    for t, name in ((mean, "mean"), (rstd, "rstd")):
-        if t is None:
-            continue
-        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != rows:
-            raise ValueError(f"{name} must be a contiguous float32 tensor of one value per row")
-    dp0 = torch.empty(d, device=x.device, dtype=torch.float32) if param_grads else None
-    dp1 = torch.empty(d, device=x.device, dtype=torch.float32) if (param_grads and ln) else None
-    p = bwd_problem(op, rows, d, dy, x, dx, _params(p0, "gamma" if ln else "w", d), mean, rstd, dp0, dp1,
-                    dtype=dt, lddy=lddy, ldx=ldx, lddx=lddx)
-    nbytes = mi_norm_bwd_workspace_size(p)
-    ws = torch.empty(max(nbytes, 1), device=x.device, dtype=torch.uint8) if nbytes > 0 else None
-    p.workspace, p.workspace_bytes = (ws.data_ptr() if ws is not None else None), max(nbytes, 0)
-    mi_norm_bwd(p, stream if stream is not None else torch.cuda.current_stream(x.device).cuda_stream)
+    ctx, handle = _on_stream(stream, x.device)
+    with ctx:
+        dx = torch.empty(x.shape, device=x.device, dtype=x.dtype) if out is None else out
+        if dx.dtype != x.dtype or dx.shape != x.shape:
+            raise ValueError("out must have x's shape and dtype")
+        lddx = _rows_of(dx, "out")[1]
+        ln = op == OP_LAYERNORM
+        for t, name in ((mean, "mean"), (rstd, "rstd")):
+            if t is None:
+                continue
+            if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != rows:
+                raise ValueError(f"{name} must be a contiguous float32 tensor of one value per row")
+        dp0 = torch.empty(d, device=x.device, dtype=torch.float32) if param_grads else None
+        dp1 = torch.empty(d, device=x.device, dtype=torch.float32) if (param_grads and ln) else None
+        p = bwd_problem(op, rows, d, dy, x, dx, _params(p0, "gamma" if ln else "w", d), mean, rstd, dp0, dp1,
+                        dtype=dt, lddy=lddy, ldx=ldx, lddx=lddx)
+        nbytes = mi_norm_bwd_workspace_size(p)
+        ws = torch.empty(max(nbytes, 1), device=x.device, dtype=torch.uint8) if nbytes > 0 else None
+        p.workspace, p.workspace_bytes = (ws.data_ptr() if ws is not None else None), max(nbytes, 0)
+        mi_norm_bwd(p, handle)
     return dx, dp0, dp1
 
 
