@@ -308,6 +308,8 @@ def copy_reference(torch, BL, stream, bytes_step: int, steps: int, warmup: int, 
         raise RuntimeError("copy loop failed")
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(200000)  # the same gate as the timed steps
     e0.record(stream)
     if BL.mi_bench_copy_loop(sa, da, nsets, n, steps, sh) != 0:
         raise RuntimeError("copy loop failed")
@@ -348,6 +350,12 @@ def measure_and_print(args, torch, stream, run_native, run_python, rotated, nset
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
+    # A short spin kernel ahead of the start event holds the stream while the
+    # host enqueues the first launches, so the span between the events holds
+    # GPU time only: without it the idle GPU records the start event at once
+    # and then waits for the host's first launch (2-4% of 100 steps at 25 MB).
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(200000)
     t_start.record(stream)
     with torch.cuda.stream(stream):
         runner_t()
