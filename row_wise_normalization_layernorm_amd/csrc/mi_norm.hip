@@ -118,25 +118,23 @@ int find(int op, int dtype, int64_t rows, int vec, int peel, int looped, int lpr
     return pick >= 0 ? base + pick : -1;
 }
 
-// Whether the multi-row variant of an aligned vector shape should run.  It
-// pays once a launch has many rows: on MI355X, from 8192 rows or 64 MiB of
-// input rows it measured 3-17% faster than the one-row variant of the same
-// shape (most for 16-bit rows, whose parameter fetches are four times their
-// own bytes), while at 1024 rows it was up to 17% slower and at 4096 rows of
-// 16 to 32 MiB it went either way.  The fused float32 operations move four
-// row streams per parameter fetch, so sharing the fetch saves little there:
-// within 2% either way up to 4 waves per row, and 3-5% slower at 8 waves per
-// row ([32768,8192]), where the one-row variant stays.  With one wave per
-// row, rows of 3.5 KiB or more apart (the widest row tensor stride, in bytes)
-// also take it: there the one-row variant's 16-wave workgroups ran 5-39%
-// slower than two rows per wave group ([4096,1024]: 7.8 against 6.5 us; the
-// [4096,768] rows at stride 1024: 6.5 against 5.5 us), while 3 KiB rows
-// ([4096,768] contiguous) are 2-3% faster with the one-row variant.
-//
-// The fused operations take it from 4096 rows: their one-row 16-wave
-// workgroups hold four row streams each, and two rows per wave group with
-// 4-wave workgroups measured 2-16% faster there (add + LayerNorm [4096,768]
-// float32: 8.9 against 10.6 us; [8192,768]: 18.2 against 19.4 us).
+// Whether the multi-row variant of an aligned vector shape should run
+// (measured on MI355X against the one-row variant of the same shape):
+// - from 8192 rows or 64 MiB of input rows: 3-17% faster (most for 16-bit
+//   rows, whose parameter fetches are four times their own bytes); at 1024
+//   rows it was up to 17% slower, and at 4096 rows of 16-32 MiB it went
+//   either way;
+// - the fused operations from 4096 rows: their one-row 16-wave workgroups
+//   carry four row streams each, and two rows per wave group with 4-wave
+//   workgroups ran 2-16% faster (add + LayerNorm [4096,768] float32: 8.9
+//   against 10.6 us);
+// - one wave per row on rows 3.5 KiB or more apart (the widest row stride,
+//   in bytes): the one-row 16-wave workgroups ran 5-39% slower ([4096,1024]:
+//   7.8 against 6.5 us; [4096,768] at stride 1024: 6.5 against 5.5 us),
+//   while contiguous 3 KiB rows are 2-3% faster with the one-row variant;
+// - never for fused float32 rows at 8 waves per row: 3-5% slower
+//   ([32768,8192]), since four row streams share each parameter fetch and
+//   the shared fetch saves little.
 bool multi_pays(int op, int64_t rows, int64_t d, int64_t es, int wpr, int64_t pitch) {
     if (kres(op) && es == 4 && wpr >= 8) return false;
     if (rows >= 8192 || rows * d * es >= (int64_t(64) << 20)) return true;
