@@ -292,6 +292,12 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def gate_cycles(steps: int) -> int:
+    """Spin-kernel length (shader clock cycles at 2.4 GHz) that holds a stream
+    for about 5 us per step to be queued behind it, 80 us to 2 ms."""
+    return int(2400 * min(2000.0, max(80.0, 5.0 * steps)))
+
+
 def copy_reference(torch, BL, stream, bytes_step: int, steps: int, warmup: int, mode: str,
                    footprint_gib: float):
     """The calibration copy moving a step's bytes (half read, half written),
@@ -309,7 +315,7 @@ def copy_reference(torch, BL, stream, bytes_step: int, steps: int, warmup: int, 
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
-        torch.cuda._sleep(200000)  # the same gate as the timed steps
+        torch.cuda._sleep(gate_cycles(steps))  # the same gate as the timed steps
     e0.record(stream)
     if BL.mi_bench_copy_loop(sa, da, nsets, n, steps, sh) != 0:
         raise RuntimeError("copy loop failed")
@@ -350,12 +356,15 @@ def measure_and_print(args, torch, stream, run_native, run_python, rotated, nset
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    # A short spin kernel ahead of the start event holds the stream while the
-    # host enqueues the first launches, so the span between the events holds
-    # GPU time only: without it the idle GPU records the start event at once
-    # and then waits for the host's first launch (2-4% of 100 steps at 25 MB).
+    # A spin kernel ahead of the start event holds the stream while the host
+    # enqueues the launches, so the span between the events holds GPU time
+    # only.  Without it the idle GPU records the start event at once and
+    # then waits for the host's first launch; and a host call costs 3-4 us,
+    # close to a small kernel's time, so a host stall could leave the GPU
+    # idle inside the span.  The spin lasts about 5 us per timed step (0.08
+    # to 2 ms) so that every launch is queued before the start event.
     with torch.cuda.stream(stream):
-        torch.cuda._sleep(200000)
+        torch.cuda._sleep(gate_cycles(args.steps))
     t_start.record(stream)
     with torch.cuda.stream(stream):
         runner_t()
