@@ -298,6 +298,39 @@ def gate_cycles(steps: int) -> int:
     return int(2400 * min(2000.0, max(80.0, 5.0 * steps)))
 
 
+def gated_span(torch, stream, steps: int, enqueue, tries: int = 4):
+    """Time ``enqueue()``, which queues ``steps`` launches on ``stream``,
+    between two stream events behind a spin kernel.
+
+    A spin kernel ahead of the start event holds the stream while the host
+    enqueues the launches, so the span between the events holds GPU time
+    only.  Without it the idle GPU records the start event at once and then
+    waits for the host's first launch; and a host call costs 3-4 us, close
+    to a small kernel's time, so a host stall could leave the GPU idle
+    inside the span.  The gate worked if the start event was still pending
+    once the last launch was queued; if it had already completed, the run
+    is repeated behind a spin twice as long (at most ``tries`` runs).
+    Returns (ms of the span, wall ms of the last run, gate us, covered)."""
+    cycles = gate_cycles(steps)
+    for _ in range(tries):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(cycles)
+        t0.record(stream)
+        enqueue()
+        covered = not t0.query()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - w0) * 1e3
+        if covered:
+            break
+        cycles *= 2
+    return t0.elapsed_time(t1), wall_ms, cycles / 2400, covered
+
+
 def copy_reference(torch, BL, stream, bytes_step: int, steps: int, warmup: int, mode: str,
                    footprint_gib: float):
     """The calibration copy moving a step's bytes (half read, half written),
@@ -313,15 +346,13 @@ def copy_reference(torch, BL, stream, bytes_step: int, steps: int, warmup: int, 
     if BL.mi_bench_copy_loop(sa, da, nsets, n, warmup, sh) != 0:
         raise RuntimeError("copy loop failed")
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        torch.cuda._sleep(gate_cycles(steps))  # the same gate as the timed steps
-    e0.record(stream)
-    if BL.mi_bench_copy_loop(sa, da, nsets, n, steps, sh) != 0:
-        raise RuntimeError("copy loop failed")
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / steps
+
+    def enqueue():
+        if BL.mi_bench_copy_loop(sa, da, nsets, n, steps, sh) != 0:
+            raise RuntimeError("copy loop failed")
+
+    ms, _, _, _ = gated_span(torch, stream, steps, enqueue)   # the same gate as the timed steps
+    us = ms * 1e3 / steps
     del srcs, dsts
     return us, nsets
 
@@ -352,26 +383,12 @@ def measure_and_print(args, torch, stream, run_native, run_python, rotated, nset
     with torch.cuda.stream(stream):
         runner_w()
     torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    # A spin kernel ahead of the start event holds the stream while the host
-    # enqueues the launches, so the span between the events holds GPU time
-    # only.  Without it the idle GPU records the start event at once and
-    # then waits for the host's first launch; and a host call costs 3-4 us,
-    # close to a small kernel's time, so a host stall could leave the GPU
-    # idle inside the span.  The spin lasts about 5 us per timed step (0.08
-    # to 2 ms) so that every launch is queued before the start event.
-    with torch.cuda.stream(stream):
-        torch.cuda._sleep(gate_cycles(args.steps))
-    t_start.record(stream)
-    with torch.cuda.stream(stream):
-        runner_t()
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    w1 = time.perf_counter()
-    ms = t_start.elapsed_time(t_end)
+
+    def enqueue():
+        with torch.cuda.stream(stream):
+            runner_t()
+
+    ms, wall_ms, gate_us, covered = gated_span(torch, stream, args.steps, enqueue)
     ms_per_step = ms / args.steps
 
     # single launches on an idle GPU, each between two events: the duration a
@@ -443,7 +460,8 @@ def measure_and_print(args, torch, stream, run_native, run_python, rotated, nset
         "isolated_launch_us": iso_us,
         "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
         "rows_per_s": round(rows / (ms_per_step * 1e-3), 1),
-        "wall_ms_per_step": round((w1 - w0) * 1e3 / args.steps, 6),
+        "wall_ms_per_step": round(wall_ms / args.steps, 6),
+        "gate": {"us": round(gate_us, 1), "covered": covered},
         "parity": parity,
         "roofline": roofline,
         "copy_reference": copy,

@@ -119,7 +119,8 @@ int find(int op, int dtype, int64_t rows, int vec, int peel, int looped, int lpr
 }
 
 // Whether the multi-row variant of an aligned vector shape should run
-// (measured on MI355X against the one-row variant of the same shape):
+// (measured on MI355X against the one-row variant of the same shape; 16-bit
+// rows of one or two waves are settled before this test):
 // - from 8192 rows or 64 MiB of input rows: 3-17% faster (most for 16-bit
 //   rows, whose parameter fetches are four times their own bytes); at 1024
 //   rows it was up to 17% slower, and at 4096 rows of 16-32 MiB it went
@@ -142,6 +143,19 @@ bool multi_pays(int op, int64_t rows, int64_t d, int64_t es, int wpr, int64_t pi
     return wpr == 1 && pitch >= 3584;
 }
 
+
+// the one-row vector variant of (wpr, q) with `waves` waves per workgroup, or -1
+int find_waves(int op, int dtype, int vec, int wpr, int q, int waves) {
+    const VariantTable &T = table(dtype);
+    const int base = table_base(dtype);
+    for (int i = 0; i < T.n; ++i) {
+        const mi_norm_variant_info &v = T.v[i].info;
+        if (v.op == op && v.rows_per_lane == 1 && v.vec == vec && !v.peel && !v.looped && v.lanes_per_row == 64 &&
+            v.waves_per_row == wpr && v.slots == q && v.waves_per_block == waves)
+            return base + i;
+    }
+    return -1;
+}
 
 int find_multi(int op, int dtype, int vec, int wpr, int q) {
     const VariantTable &T = table(dtype);
@@ -261,6 +275,15 @@ int select_variant(const mi_norm_problem &P) {
         if (nvec <= 16) return find(op, dt, rows, W, 0, 0, 16, 1, 1);
         if (nvec <= 32) return find(op, dt, rows, W, 0, 0, 32, 1, 1);
         shape_vectors(nvec, rows, wpr, q);
+        if (wpr && wpr <= 2 && esize(dt) == 2) {
+            // 16-bit rows of one or two waves: the one-row variants, which
+            // stage their parameters in LDS, beat the multi-row ones in 12
+            // of 15 measured shapes (up to 10%: LayerNorm bfloat16
+            // [16384,768] 10.6 against 11.9 us); at one wave per row 4-wave
+            // workgroups were the faster in 6 of 8 shapes.
+            const int s = wpr == 1 ? find_waves(op, dt, W, wpr, q, 4) : -1;
+            return s >= 0 ? s : find(op, dt, rows, W, 0, 0, 64, wpr, q);
+        }
         if (wpr && multi_pays(op, rows, d, esize(dt), wpr, row_pitch(P))) {
             const int m = find_multi(op, dt, W, wpr, q);
             if (m >= 0) return m;

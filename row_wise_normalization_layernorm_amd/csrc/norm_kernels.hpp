@@ -306,8 +306,10 @@ __device__ __forceinline__ float rsq(float v) { return __builtin_amdgcn_rsqf(v);
 //          -1: 1 for 16 waves per row, else 0
 //   PRE    where the output pass gets gamma/beta (or w): 0: global loads in
 //          the output pass; 1: global loads issued while x is in flight;
-//          2: staged once per workgroup in LDS at kernel start (128-bit
-//          aligned path only); -1: 1 or 0 by the register budget
+//          2: staged once per workgroup in LDS at kernel start (aligned
+//          16-byte path only), so each parameter crosses the CU's vector
+//          memory path once per workgroup rather than once per row;
+//          -1: 1 or 0 by the register budget
 //
 // Lane li of wave rank wr holds access k = li + LPR * (wr + WPR * q),
 // q = 0..Q-1: consecutive lanes touch consecutive vectors (or elements), so
@@ -335,9 +337,10 @@ void norm_held(NormParams p)
     constexpr bool PRELOAD = PRE >= 0 ? PRE == 1 : VEC * Q * (1 + kParams) <= kBudget / 4;
     constexpr bool PLDS = PRE == 2;
     constexpr bool MPAR = MRG >= 0 ? MRG == 1 : WPR >= 16;
-    static_assert(!PLDS || (VEC == 4 && !PEEL), "LDS parameters need the aligned 128-bit path");
+    static_assert(!PLDS || (VEC >= 4 && !PEEL), "LDS parameters need the aligned 16-byte path");
     constexpr int kCapV = LPR * WPR * Q;  // 16-byte accesses per row the variant covers
-    static_assert(!PLDS || kCapV * kParams * 16 <= 64 * 1024, "LDS parameter stage too large");
+    constexpr int kF4 = VEC >= 4 ? VEC / 4 : 1;  // float4 parameter words per access
+    static_assert(!PLDS || kCapV * kF4 * kParams * 16 <= 64 * 1024, "LDS parameter stage too large");
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -348,7 +351,7 @@ void norm_held(NormParams p)
 
     // (wave mean or sum of squares, wave M2) per row and wave: the one exchange
     __shared__ float2 xch[RPB][WPR];
-    __shared__ f4 lds_par[PLDS ? kParams : 1][PLDS ? kCapV : 1];
+    __shared__ f4 lds_par[PLDS ? kParams : 1][PLDS ? kCapV * kF4 : 1];
 
     const int d = p.d;
     const float eps = p.eps;
@@ -358,7 +361,7 @@ void norm_held(NormParams p)
         // every lane of the workgroup copies part of gamma/beta into LDS; the
         // barrier before the output pass publishes it
         const int nv = d >> 2;
-        for (int i = tid; i < nv && i < kCapV; i += WAVES * 64) {
+        for (int i = tid; i < nv && i < kCapV * kF4; i += WAVES * 64) {
             lds_par[0][i] = ld4<false>(p.p0 + 4 * i);
             if constexpr (OP == OP_LN) lds_par[kParams - 1][i] = ld4<false>(p.p1 + 4 * i);
         }
@@ -449,9 +452,15 @@ void norm_held(NormParams p)
         // parameters for the output pass: fetched while x is in flight when
         // the register budget allows, else slot by slot in the output pass
         auto load_params = [&](int q, VT &gq, VT &bq) {
-            if constexpr (PLDS) {
+            if constexpr (PLDS && VEC == 4) {
                 gq = lds_par[0][kc[q]];
                 if constexpr (OP == OP_LN) bq = lds_par[kParams - 1][kc[q]];
+            } else if constexpr (PLDS) {
+                // an oct's eight parameters are two consecutive float4 words
+                gq = __builtin_shufflevector(lds_par[0][2 * kc[q]], lds_par[0][2 * kc[q] + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+                if constexpr (OP == OP_LN)
+                    bq = __builtin_shufflevector(lds_par[kParams - 1][2 * kc[q]], lds_par[kParams - 1][2 * kc[q] + 1],
+                                                 0, 1, 2, 3, 4, 5, 6, 7);
             } else if constexpr (!PEEL) {
                 gq = ldp<VEC>(p.p0 + VEC * kc[q]);
                 if constexpr (OP == OP_LN) bq = ldp<VEC>(p.p1 + VEC * kc[q]);

@@ -34,17 +34,29 @@ constexpr bool kres(int op) { return op >= 2; }
 
 }  // namespace minorm
 
+// Where a held variant's output pass gets its parameters (norm_held's PRE).
+// Rows of a 16-bit type on the aligned vector path stage them in LDS once
+// per workgroup when the workgroup holds at least two rows and the stage
+// fits 64 KiB: per row, an oct's parameters are four times its own bytes,
+// and fetching them per row cost 2-9% against staging them (MI355X;
+// float32 rows, at twice their bytes, gained nothing).  Everything else
+// reads them in the output pass.
+constexpr int held_pre(int es, int vec, int peel, int lpr, int wpr, int q, int waves) {
+    return (es == 2 && vec == 8 && !peel && lpr == 64 && waves / wpr >= 2 && wpr * q <= 16) ? 2 : 0;
+}
+
 // Every held variant streams x (and r) in and y (and h) out with
-// non-temporal hints and reads gamma/beta in the output pass (norm_held's
-// NTL/NTS/PRE); the cross-wave merge follows norm_held's default.
-// T is the storage type, DT its mi_norm_dtype, OPN the name prefix.
+// non-temporal hints (norm_held's NTL/NTS); the cross-wave merge follows
+// norm_held's default.  T is the storage type, DT its mi_norm_dtype, OPN
+// the name prefix.
 #define MI_HELD(T, DT, OPC, OPN, VEC, PEEL, LPR, WPR, Q, WAVES)                                \
     Variant{OPN "_" #VEC "_p" #PEEL "_l" #LPR "_w" #WPR "_q" #Q "_b" #WAVES,                  \
             mi_norm_variant_info{OPC, DT, VEC, PEEL, 0, LPR, WPR, Q, WAVES,                     \
                                  (WPR == 1) ? WAVES * (64 / LPR) : WAVES / WPR,                 \
                                  (int64_t)VEC * LPR * WPR * Q, (VEC > 1 && !PEEL) ? 1 : 0, 1},  \
-            reinterpret_cast<const void *>(&norm_held<T, kop(OPC), VEC, (PEEL != 0), LPR, WPR,  \
-                                                      Q, WAVES, true, true, 0, -1, kres(OPC)>)}
+            reinterpret_cast<const void *>(                                                     \
+                &norm_held<T, kop(OPC), VEC, (PEEL != 0), LPR, WPR, Q, WAVES, true, true,       \
+                           held_pre((int)sizeof(T), VEC, PEEL, LPR, WPR, Q, WAVES), -1, kres(OPC)>)}
 
 // the same shape with 4 (or 8) and with 16 waves per workgroup
 #define MI_HELD2(T, DT, OPC, OPN, VEC, PEEL, LPR, WPR, Q, WSMALL)                              \

@@ -316,7 +316,13 @@ def test_dispatch_examples(L):
     assert sel(0, 896, rows=4096) == "ln_4_r2_w1_q4_b4"
     assert sel(0, 768, rows=4096, ldx=1024, ldy=1024) == "ln_4_r2_w1_q3_b4"
     assert sel(0, 768, rows=4096, ldx=880) == "ln_4_p0_l64_w1_q3_b16"
-    assert sel(0, 2048, rows=4096, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_r2_w1_q4_b4"
+    # 16-bit rows of one or two waves: one row per wave group, parameters in LDS
+    assert sel(0, 2048, rows=4096, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w1_q4_b4"
+    assert sel(0, 2048, rows=32768, dtype=mn.MI_NORM_F16) == "ln_f16_8_p0_l64_w1_q4_b4"
+    assert sel(2, 768, rows=8192, dtype=mn.MI_NORM_BF16) == "addln_bf16_8_p0_l64_w1_q2_b4"
+    assert sel(1, 4096, rows=8192, dtype=mn.MI_NORM_BF16) == "rms_bf16_8_p0_l64_w2_q4_b16"
+    assert sel(1, 4096, rows=2048, dtype=mn.MI_NORM_BF16) == "rms_bf16_8_p0_l64_w2_q4_b4"
+    # from four waves per row, the 16-bit rows follow the float32 rules
     assert sel(0, 8192, rows=32768, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_r2_w4_q4_b4"
     assert sel(0, 8192, rows=4096, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_r2_w4_q4_b4"   # 64 MiB
     assert sel(0, 8192, rows=4095, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w4_q4_b16"
@@ -437,8 +443,8 @@ def test_strides_and_types_decide_the_layout(L):
     info = lambda **kw: mn.mi_norm_variant_get_info(mn.mi_norm_select(_prob(0, 4096, 768, **kw)))
     name = lambda **kw: mn.mi_norm_variant_name(mn.mi_norm_select(_prob(0, 4096, 768, **kw)))
     # 16-byte accesses: eight 16-bit elements, 96 of them per row of 768
-    assert name(dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w1_q2_b16"
-    assert name(dtype=mn.MI_NORM_F16) == "ln_f16_8_p0_l64_w1_q2_b16"
+    assert name(dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w1_q2_b4"
+    assert name(dtype=mn.MI_NORM_F16) == "ln_f16_8_p0_l64_w1_q2_b4"
     assert info(dtype=mn.MI_NORM_BF16, x=X + 8, y=Y + 8)["peel"] == 1
     assert info(dtype=mn.MI_NORM_F32, x=X + 8, y=Y + 8)["peel"] == 1
     # a 16-bit row width that is a multiple of 4 but not of 8 is peeled

@@ -90,3 +90,57 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+class _FakeTorch:
+    """Just enough of torch.cuda for gated_span: the start event reads as
+    already completed (the gate ran out) for the first ``late`` runs."""
+
+    def __init__(self, late):
+        self.late, self.sleeps, self.records = late, [], 0
+        fake = self
+
+        class Event:
+            def __init__(self, enable_timing=False):
+                self.n = None
+
+            def record(self, stream):
+                fake.records += 1
+                self.n = fake.records
+
+            def query(self):
+                return len(fake.sleeps) <= fake.late
+
+            def elapsed_time(self, other):
+                return float(other.n - self.n)
+
+        class _Ctx:
+            def __enter__(self):
+                return self
+
+            def __exit__(self, *a):
+                return False
+
+        class cuda:
+            pass
+
+        cuda.Event = Event
+        cuda.synchronize = staticmethod(lambda: None)
+        cuda.stream = staticmethod(lambda s: _Ctx())
+        cuda._sleep = staticmethod(lambda c: fake.sleeps.append(c))
+        self.cuda = cuda
+
+
+def test_gate_repeats_the_span_until_it_covers_the_launches():
+    queued = []
+    t = _FakeTorch(late=2)
+    ms, wall, gate_us, covered = bench.gated_span(t, None, 100, lambda: queued.append(1))
+    g = bench.gate_cycles(100)
+    assert t.sleeps == [g, 2 * g, 4 * g] and len(queued) == 3 and covered
+    assert gate_us == 4 * g / 2400 and ms == 1.0
+    t = _FakeTorch(late=9)
+    _, _, gate_us, covered = bench.gated_span(t, None, 100, lambda: None, tries=4)
+    assert len(t.sleeps) == 4 and not covered
+    t = _FakeTorch(late=0)
+    bench.gated_span(t, None, 100, lambda: None)
+    assert t.sleeps == [g]
