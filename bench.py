@@ -312,7 +312,7 @@ def gated_span(torch, stream, steps: int, enqueue, tries: int = 4):
     is repeated behind a spin twice as long (at most ``tries`` runs).
     Returns (ms of the span, wall ms of the last run, gate us, covered)."""
     cycles = gate_cycles(steps)
-    for _ in range(tries):
+    for attempt in range(tries):
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -325,7 +325,7 @@ def gated_span(torch, stream, steps: int, enqueue, tries: int = 4):
         t1.record(stream)
         torch.cuda.synchronize()
         wall_ms = (time.perf_counter() - w0) * 1e3
-        if covered:
+        if covered or attempt == tries - 1:
             break
         cycles *= 2
     return t0.elapsed_time(t1), wall_ms, cycles / 2400, covered

@@ -140,7 +140,7 @@ def test_gate_repeats_the_span_until_it_covers_the_launches():
     assert gate_us == 4 * g / 2400 and ms == 1.0
     t = _FakeTorch(late=9)
     _, _, gate_us, covered = bench.gated_span(t, None, 100, lambda: None, tries=4)
-    assert len(t.sleeps) == 4 and not covered
+    assert len(t.sleeps) == 4 and not covered and gate_us == 8 * g / 2400
     t = _FakeTorch(late=0)
     bench.gated_span(t, None, 100, lambda: None)
     assert t.sleeps == [g]
