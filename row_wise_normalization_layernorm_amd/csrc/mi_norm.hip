@@ -284,6 +284,18 @@ int select_variant(const mi_norm_problem &P) {
             const int s = wpr == 1 ? find_waves(op, dt, W, wpr, q, 4) : -1;
             return s >= 0 ? s : find(op, dt, rows, W, 0, 0, 64, wpr, q);
         }
+        if (op == MI_NORM_OP_LAYERNORM && esize(dt) == 4 && nvec > 768 && nvec <= 1024 && rows >= 3072 &&
+            rows <= 4096) {
+            // float32 LayerNorm rows of 3-4 K elements, 3072-4096 of them:
+            // one wave per row with sixteen slots and the parameters in LDS
+            // runs 3 waves per SIMD, so one round of resident workgroups
+            // holds 3072 rows in 4-wave workgroups or 2048 in 8-wave ones;
+            // where that fills whole rounds it beat every other shape by
+            // 4-7% ([4096,4096] 23.7 against 24.9 us; [3072,4096] 18.0
+            // against 18.9; [4096,3584] 21.5 against 22.7)
+            const int s = find_waves(op, dt, W, 1, 16, rows <= 3072 ? 4 : 8);
+            if (s >= 0) return s;
+        }
         if (wpr && multi_pays(op, rows, d, esize(dt), wpr, row_pitch(P))) {
             const int m = find_multi(op, dt, W, wpr, q);
             if (m >= 0) return m;

@@ -39,10 +39,14 @@ constexpr bool kres(int op) { return op >= 2; }
 // per workgroup when the workgroup holds at least two rows and the stage
 // fits 64 KiB: per row, an oct's parameters are four times its own bytes,
 // and fetching them per row cost 2-9% against staging them (MI355X;
-// float32 rows, at twice their bytes, gained nothing).  Everything else
-// reads them in the output pass.
+// float32 rows at up to eight slots, at twice their bytes, gained nothing).
+// The float32 one-wave rows of sixteen slots stage them too: there the
+// output pass's parameter fetch was the last global round trip of a wave
+// that holds a 16 KiB row.  Everything else reads them in the output pass.
 constexpr int held_pre(int es, int vec, int peel, int lpr, int wpr, int q, int waves) {
-    return (es == 2 && vec == 8 && !peel && lpr == 64 && waves / wpr >= 2 && wpr * q <= 16) ? 2 : 0;
+    if (es == 2 && vec == 8 && !peel && lpr == 64 && waves / wpr >= 2 && wpr * q <= 16) return 2;
+    if (es == 4 && vec == 4 && !peel && lpr == 64 && wpr == 1 && q == 16 && waves >= 2) return 2;
+    return 0;
 }
 
 // Every held variant streams x (and r) in and y (and h) out with
@@ -122,10 +126,26 @@ constexpr int held_pre(int es, int vec, int peel, int lpr, int wpr, int q, int w
     MI_SLOTS(T, DT, VW, OPC, OPN, PEEL, 4, 4), MI_SLOTS(T, DT, VW, OPC, OPN, PEEL, 8, 8),               \
     MI_SLOTS16(T, DT, VW, OPC, OPN, PEEL)
 
+// One wave per float32 LayerNorm row of up to 4096 elements holding sixteen
+// 16-byte slots (3 waves per SIMD), in 4- and 8-wave workgroups: the
+// dispatcher's choice for rows of 3-4 K elements where its grid fills whole
+// rounds of resident workgroups.  Other operations and storage types have
+// none (16-bit octs would need twice the registers).
+#define MI_WIDE16_4_MI_NORM_OP_LAYERNORM(T, DT, OPC, OPN)                                          \
+    MI_HELD(T, DT, OPC, OPN, 4, 0, 64, 1, 16, 4), MI_HELD(T, DT, OPC, OPN, 4, 0, 64, 1, 16, 8),
+#define MI_WIDE16_4_MI_NORM_OP_RMSNORM(T, DT, OPC, OPN)
+#define MI_WIDE16_4_MI_NORM_OP_ADD_LAYERNORM(T, DT, OPC, OPN)
+#define MI_WIDE16_4_MI_NORM_OP_ADD_RMSNORM(T, DT, OPC, OPN)
+#define MI_WIDE16_8_MI_NORM_OP_LAYERNORM(T, DT, OPC, OPN)
+#define MI_WIDE16_8_MI_NORM_OP_RMSNORM(T, DT, OPC, OPN)
+#define MI_WIDE16_8_MI_NORM_OP_ADD_LAYERNORM(T, DT, OPC, OPN)
+#define MI_WIDE16_8_MI_NORM_OP_ADD_RMSNORM(T, DT, OPC, OPN)
+
 #define MI_OP_TABLE(T, DT, VW, OPC, OPN)                                                           \
     /* vectors, aligned, d % VW == 0; 16 or 32 lanes per row for narrow rows */                 \
     MI_HELD2(T, DT, OPC, OPN, VW, 0, 16, 1, 1, 4), MI_HELD2(T, DT, OPC, OPN, VW, 0, 32, 1, 1, 4), \
     MI_PATHV(T, DT, VW, OPC, OPN, 0),                                                               \
+    MI_WIDE16_##VW##_##OPC(T, DT, OPC, OPN)                                                         \
     /* vector body with a per-row scalar head and tail: any d, rows in one phase */            \
     MI_PATHV(T, DT, VW, OPC, OPN, 1),                                                               \
     /* single-element accesses: any d, any element alignment */                                \

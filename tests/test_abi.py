@@ -244,9 +244,13 @@ def test_variant_table_is_consistent(L):
     assert {v["op"] for _, _, v in infos} == set(OPS)
     assert {v["dtype"] for _, _, v in infos} == set(DTYPES)
     # within a storage type every operation has the same family of shapes,
-    # and the two 16-bit types have the same family
+    # and the two 16-bit types have the same family; float32 LayerNorm alone
+    # adds one wave per row with sixteen slots (4- and 8-wave workgroups)
     shapes = {(op, dt): sorted(n[len(PREFIX[op] + DTSFX[dt]):] for _, n, v in infos
                                if v["op"] == op and v["dtype"] == dt) for op in OPS for dt in DTYPES}
+    wide16 = ["4_p0_l64_w1_q16_b4", "4_p0_l64_w1_q16_b8"]
+    assert all(w in shapes[(0, mn.MI_NORM_F32)] for w in wide16)
+    shapes[(0, mn.MI_NORM_F32)] = [n for n in shapes[(0, mn.MI_NORM_F32)] if n not in wide16]
     for dt in DTYPES:
         assert shapes[(0, dt)] and all(shapes[(op, dt)] == shapes[(0, dt)] for op in OPS)
     assert shapes[(0, mn.MI_NORM_F16)] == shapes[(0, mn.MI_NORM_BF16)]
@@ -306,8 +310,16 @@ def test_dispatch_examples(L):
     assert sel(0, 768, rows=1000) == "ln_4_p0_l64_w2_q2_b4"  # few rows: two waves per row
     assert sel(0, 2048, rows=1024) == "ln_4_p0_l64_w4_q2_b4"
     assert sel(0, 2048, rows=4096) == "ln_4_p0_l64_w2_q4_b16"  # 32 MiB: one row per wave
+    # float32 LayerNorm rows of 3-4 K elements, 3072-4096 rows: one wave per
+    # row with sixteen slots, in workgroups that fill whole rounds
+    assert sel(0, 4096, rows=4096) == "ln_4_p0_l64_w1_q16_b8"
+    assert sel(0, 3584, rows=3500) == "ln_4_p0_l64_w1_q16_b8"
+    assert sel(0, 4096, rows=3072) == "ln_4_p0_l64_w1_q16_b4"
+    assert sel(0, 4096, rows=3071) == "ln_4_p0_l64_w4_q4_b16"
+    assert sel(0, 3072, rows=4096) == "ln_4_p0_l64_w4_q3_b16"
+    assert sel(1, 4096, rows=4096) == "rms_4_r2_w4_q4_b4"
     # from 8192 rows or 64 MiB of rows, two rows per wave group
-    assert sel(0, 4096, rows=4096) == "ln_4_r2_w4_q4_b4"
+    assert sel(0, 4096, rows=4097) == "ln_4_r2_w4_q4_b4"
     assert sel(0, 8192, rows=32768) == "ln_4_r2_w8_q4_b8"
     assert sel(0, 768, rows=8192) == "ln_4_r2_w1_q3_b4"
     assert sel(0, 768, rows=8191) == "ln_4_p0_l64_w1_q3_b16"
@@ -365,7 +377,7 @@ def test_workgroup_size_follows_row_count(L):
 def test_rows_spread_over_more_waves_when_few(L):
     # about four accesses per lane with many rows; more waves per row with few
     for d, rows, wpr, q in ((768, 4096, 1, 3), (2048, 4096, 2, 4), (2048, 1024, 4, 2),
-                            (4096, 4096, 4, 4), (8192, 32768, 8, 4), (16384, 8192, 16, 4),
+                            (4096, 8192, 4, 4), (4096, 2048, 4, 4), (8192, 32768, 8, 4), (16384, 8192, 16, 4),
                             (768, 100, 2, 2), (32768, 64, 16, 8)):
         v = mn.mi_norm_variant_get_info(mn.mi_norm_select(_prob(0, rows, d)))
         assert (v["waves_per_row"], v["slots"]) == (wpr, q), (d, rows, v)
