@@ -99,6 +99,7 @@ BENCH_WORKLOADS = {
     "copy_32768x8192": W("copy", "f32", 32768, 8192),
     "copy_4096x384": W("copy", "f32", 4096, 384),      # the bytes of a 16-bit [4096,768]
     "copy_16384x8192": W("copy", "f32", 16384, 8192),  # the bytes of a 16-bit [32768,8192]
+    "copy_4096x4096": W("copy", "f32", 4096, 4096),
 }
 
 ESIZE = {"f32": 4, "f16": 2, "bf16": 2}
