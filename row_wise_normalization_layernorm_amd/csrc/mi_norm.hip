@@ -87,13 +87,20 @@ constexpr int64_t kMaxGrid = 1 << 20;
 // row groups per launch of a held-row kernel
 constexpr int64_t kMaxRowGroups = int64_t(1) << 30;
 
-// Fewest workgroups that still cover every CU: of the variants with this
-// shape, the one with the most waves per workgroup whose grid has at least
-// min_blocks(wpr) workgroups; failing that, the one with the most
-// workgroups.  Rows of one wave need one workgroup per CU (256); rows of
-// several waves share one barrier per workgroup, and 16-wave workgroups only
-// paid off with two of them per CU (512).
+// Fewest workgroups that still cover every CU evenly: of the variants with
+// this shape, the one with the most waves per workgroup whose grid has at
+// least min_blocks(wpr) workgroups and spreads evenly over the 256 CUs;
+// failing that, the one with the most workgroups.  Rows of one wave need one
+// workgroup per CU (256); rows of several waves share one barrier per
+// workgroup, and 16-wave workgroups only paid off with two of them per CU
+// (512).  A grid whose busiest CU would hold more than 15% over the average
+// is uneven: 384 16-wave workgroups (LayerNorm and RMSNorm [6144,768] float32,
+// 1.5 per CU) ran 8.2 us against 7.1-7.3 us for 1536 4-wave ones.
 int64_t min_blocks(int wpr) { return wpr > 1 ? 512 : 256; }
+bool even_spread(int64_t blocks) {
+    const int64_t per = (blocks + 255) / 256;      // workgroups on the busiest CU
+    return per * 256 * 100 <= blocks * 115;
+}
 
 int find(int op, int dtype, int64_t rows, int vec, int peel, int looped, int lpr, int wpr, int q) {
     const VariantTable &T = table(dtype);
@@ -107,7 +114,8 @@ int find(int op, int dtype, int64_t rows, int vec, int peel, int looped, int lpr
         if (looped) return base + i;
         if (v.lanes_per_row != lpr || v.waves_per_row != wpr || v.slots != q) continue;
         const int64_t blocks = (rows + v.rows_per_block - 1) / v.rows_per_block;
-        if (blocks >= min_blocks(wpr) && (best < 0 || v.waves_per_block > T.v[best].info.waves_per_block))
+        if (blocks >= min_blocks(wpr) && even_spread(blocks) &&
+            (best < 0 || v.waves_per_block > T.v[best].info.waves_per_block))
             best = i;
         if (blocks > fallback_blocks) {
             fallback = i;
@@ -299,6 +307,15 @@ int select_variant(const mi_norm_problem &P) {
         if (wpr && multi_pays(op, rows, d, esize(dt), wpr, row_pitch(P))) {
             const int m = find_multi(op, dt, W, wpr, q);
             if (m >= 0) return m;
+        }
+        if (esize(dt) == 4 && !kres(op) && (wpr == 2 || wpr == 4) && q <= 4 && rows * (wpr / 2) > 4096) {
+            // float32 rows of 2-4 K elements on the one-row path with more
+            // than 4096 waves at half the waves per row: half the waves, twice
+            // the slots, one fewer cross-wave exchange ([2560,4096] 14.6
+            // against 16.2 us; [4096,3072] 17.1 against 19.5; [6144,2048]
+            // 17.3 against 19.5; at [2048,4096] four waves stay 2% ahead)
+            wpr /= 2;
+            q *= 2;
         }
         if (wpr) return find(op, dt, rows, W, 0, 0, 64, wpr, q);
         return find(op, dt, rows, W, 0, 1, 0, 0, 0);

@@ -315,9 +315,20 @@ def test_dispatch_examples(L):
     assert sel(0, 4096, rows=4096) == "ln_4_p0_l64_w1_q16_b8"
     assert sel(0, 3584, rows=3500) == "ln_4_p0_l64_w1_q16_b8"
     assert sel(0, 4096, rows=3072) == "ln_4_p0_l64_w1_q16_b4"
-    assert sel(0, 4096, rows=3071) == "ln_4_p0_l64_w4_q4_b16"
-    assert sel(0, 3072, rows=4096) == "ln_4_p0_l64_w4_q3_b16"
+    assert sel(0, 4096, rows=3071) == "ln_4_p0_l64_w2_q8_b4"
+    assert sel(0, 3072, rows=4096) == "ln_4_p0_l64_w2_q6_b16"
     assert sel(1, 4096, rows=4096) == "rms_4_r2_w4_q4_b4"
+    # float32 one-row path with more than 4096 waves at half the waves per
+    # row: half the waves, twice the slots
+    assert sel(1, 4096, rows=3072) == "rms_4_p0_l64_w2_q8_b4"
+    assert sel(0, 2048, rows=6144) == "ln_4_p0_l64_w1_q8_b4"     # 16-wave grid uneven: 4 waves
+    assert sel(0, 4096, rows=2048) == "ln_4_p0_l64_w4_q4_b16"    # 4096 waves: no change
+    assert sel(2, 4096, rows=3000) == "addln_4_p0_l64_w4_q4_b16"  # fused rows keep theirs
+    # workgroups spread evenly over the CUs: 384 16-wave workgroups would load
+    # half the CUs twice, so 4-wave ones
+    assert sel(0, 768, rows=6144) == "ln_4_p0_l64_w1_q3_b4"
+    assert sel(1, 768, rows=5000) == "rms_4_p0_l64_w1_q3_b4"
+    assert sel(0, 768, rows=4096) == "ln_4_p0_l64_w1_q3_b16"
     # from 8192 rows or 64 MiB of rows, two rows per wave group
     assert sel(0, 4096, rows=4097) == "ln_4_r2_w4_q4_b4"
     assert sel(0, 8192, rows=32768) == "ln_4_r2_w8_q4_b8"
@@ -367,15 +378,20 @@ def test_workgroup_size_follows_row_count(L):
                 continue
             need = 512 if v["waves_per_row"] > 1 else 256
             per16 = 16 // v["waves_per_row"]
+            even = lambda blocks: -(-blocks // 256) * 256 * 100 <= blocks * 115
             if v["waves_per_block"] < 16:
-                # a 16-wave workgroup would have left too few workgroups
-                assert -(-rows // per16) < need, (d, rows)
+                # a 16-wave workgroup would have left too few workgroups, or
+                # spread them unevenly over the 256 CUs
+                b16 = -(-rows // per16)
+                assert b16 < need or not even(b16), (d, rows)
             else:
-                assert -(-rows // v["rows_per_block"]) >= need or v["waves_per_row"] == 16, (d, rows)
+                blocks = -(-rows // v["rows_per_block"])
+                assert (blocks >= need and even(blocks)) or v["waves_per_row"] == 16, (d, rows)
 
 
 def test_rows_spread_over_more_waves_when_few(L):
-    # about four accesses per lane with many rows; more waves per row with few
+    # about four accesses per lane with many rows (float32 one-row rows of
+    # 2-4 K elements: up to eight); more waves per row with few
     for d, rows, wpr, q in ((768, 4096, 1, 3), (2048, 4096, 2, 4), (2048, 1024, 4, 2),
                             (4096, 8192, 4, 4), (4096, 2048, 4, 4), (8192, 32768, 8, 4), (16384, 8192, 16, 4),
                             (768, 100, 2, 2), (32768, 64, 16, 8)):
