@@ -487,7 +487,7 @@ const char *mi_norm_status_string(mi_norm_status s) {
     return "MI_NORM_UNKNOWN_STATUS";
 }
 
-const char *mi_norm_version(void) { return "mi_norm 0.4.0 gfx950"; }
+const char *mi_norm_version(void) { return "mi_norm 0.5.0 gfx950"; }
 
 mi_norm_status mi_layernorm_fwd(const float *x, const float *gamma, const float *beta, float *y,
                                 int64_t rows, int64_t d, float eps, float *mean, float *rstd,
