@@ -287,8 +287,16 @@ int select_variant(const mi_norm_problem &P) {
             // 16-bit rows of one or two waves: the one-row variants, which
             // stage their parameters in LDS, beat the multi-row ones in 12
             // of 15 measured shapes (up to 10%: LayerNorm bfloat16
-            // [16384,768] 10.6 against 11.9 us); at one wave per row 4-wave
-            // workgroups were the faster in 6 of 8 shapes.
+            // [16384,768] 10.6 against 11.9 us).  With 2560-8192 rows, rows
+            // of two waves run as one wave with twice the slots in 16-wave
+            // workgroups: 4-27% faster in eight shapes (RMSNorm [4096,4096]
+            // 11.5 against 13.7 us; LayerNorm [2560,4096] 8.7 against 11.0),
+            // equal in one; at 12288 rows it lost 4%.  One wave of up to four
+            // slots takes 4-wave workgroups (the faster in 6 of 8 shapes).
+            if (wpr == 2 && q <= 4 && rows >= 2560 && rows <= 8192) {
+                const int s = find_waves(op, dt, W, 1, 2 * q, 16);
+                if (s >= 0) return s;
+            }
             const int s = wpr == 1 ? find_waves(op, dt, W, wpr, q, 4) : -1;
             return s >= 0 ? s : find(op, dt, rows, W, 0, 0, 64, wpr, q);
         }
