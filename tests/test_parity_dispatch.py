@@ -1,0 +1,59 @@
+"""GPU parity at shapes where each of the dispatcher's row-count rules fires.
+
+The variants themselves are covered one by one elsewhere; these cases run
+the library's own choice (mi_norm_fwd, no forced variant) at the geometry
+that makes each rule pick it, with ragged last workgroups, and check the
+outputs against the float64 oracle with the bounds of test_parity_storage.
+The expected variant names pin the host rules: a change in what the
+dispatcher picks shows here before any timing does.
+"""
+from __future__ import annotations
+
+import pytest
+
+import row_wise_normalization_layernorm_amd as mn
+from test_parity_storage import inputs, run_case, say, torch_dev  # noqa: F401  (fixture)
+
+pytestmark = pytest.mark.gpu
+
+F32, F16, BF16 = mn.MI_NORM_F32, mn.MI_NORM_F16, mn.MI_NORM_BF16
+OPS = {"layernorm": mn.OP_LAYERNORM, "rmsnorm": mn.OP_RMSNORM,
+       "add_layernorm": mn.OP_ADD_LAYERNORM, "add_rmsnorm": mn.OP_ADD_RMSNORM}
+
+CASES = [
+    # workgroups spread evenly over the CUs: 4-wave workgroups where 16-wave
+    # ones would load half the CUs twice
+    ("layernorm", F32, 6144, 768, "ln_4_p0_l64_w1_q3_b4"),
+    ("rmsnorm", F32, 5001, 768, "rms_4_p0_l64_w1_q3_b4"),
+    # float32 LayerNorm rows of 3-4 K elements, 3072-4096 rows: sixteen slots
+    ("layernorm", F32, 3072, 4096, "ln_4_p0_l64_w1_q16_b4"),
+    ("layernorm", F32, 3501, 3584, "ln_4_p0_l64_w1_q16_b8"),
+    # float32 one-row rows of 2-4 K elements with many rows: half the waves
+    ("rmsnorm", F32, 2561, 4096, "rms_4_p0_l64_w2_q8_b4"),
+    ("layernorm", F32, 4097, 3072, "ln_4_p0_l64_w2_q6_b4"),
+    ("layernorm", F32, 6145, 2048, "ln_4_p0_l64_w1_q8_b4"),
+    # 16-bit rows of two waves with 2560-8192 rows: one wave, twice the slots
+    ("layernorm", BF16, 2561, 4096, "ln_bf16_8_p0_l64_w1_q8_b16"),
+    ("add_layernorm", F16, 4097, 3072, "addln_f16_8_p0_l64_w1_q6_b16"),
+    ("rmsnorm", BF16, 3584, 3584, "rms_bf16_8_p0_l64_w1_q8_b16"),
+    # 16-bit rows of one wave: 4-wave workgroups
+    ("add_rmsnorm", BF16, 6145, 2048, "addrms_bf16_8_p0_l64_w1_q4_b4"),
+]
+
+
+def _chosen(op, dt, rows, d):
+    base = 1 << 40
+    ln, add = op.endswith("layernorm"), op.startswith("add_")
+    p = mn.problem(OPS[op], rows, d, base, base + (1 << 36), base + (2 << 36),
+                   base + (2 << 36) + (1 << 20) if ln else None,
+                   r=base + (3 << 36) if add else None, h=base + (4 << 36) if add else None, dtype=dt)
+    return mn.mi_norm_variant_name(mn.mi_norm_select(p))
+
+
+@pytest.mark.parametrize("op,dt,rows,d,name", CASES, ids=[f"{c[0]}-{c[1]}-{c[2]}x{c[3]}" for c in CASES])
+def test_dispatch_rule_shapes(torch_dev, op, dt, rows, d, name):
+    torch, dev = torch_dev
+    assert _chosen(op, dt, rows, d) == name
+    say(f"dispatch rule {op} dt={dt} [{rows}x{d}] -> {name}")
+    x, r, params = inputs(op, dt, rows, d, "offset", [31, rows, d])
+    run_case(torch, dev, op, dt, x, r, params)
