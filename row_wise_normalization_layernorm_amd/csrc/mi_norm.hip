@@ -304,11 +304,10 @@ int select_variant(const mi_norm_problem &P) {
             rows <= 4096) {
             // float32 LayerNorm rows of 3-4 K elements, 3072-4096 of them:
             // one wave per row with sixteen slots and the parameters in LDS
-            // runs 3 waves per SIMD, so one round of resident workgroups
-            // holds 3072 rows in 4-wave workgroups or 2048 in 8-wave ones;
-            // where that fills whole rounds it beat every other shape by
-            // 4-7% ([4096,4096] 23.7 against 24.9 us; [3072,4096] 18.0
-            // against 18.9; [4096,3584] 21.5 against 22.7)
+            // (5 waves per SIMD), measured on MI355X as the fastest shape or
+            // within 2.5% of it ([4096,4096] 22.4 us; [3072,4096] 17.7 against
+            // 17.4 for 16-wave workgroups; [4096,3200] 18.1), and up to 7%
+            // ahead of the one-row shapes outside it
             const int s = find_waves(op, dt, W, 1, 16, rows <= 3072 ? 4 : 8);
             if (s >= 0) return s;
         }

@@ -609,6 +609,240 @@ void norm_held(NormParams p)
 }
 
 // ---------------------------------------------------------------------------
+// Aligned held rows with buffer loads: the 16-byte vector path of norm_held
+// (LPR = 64, no peel) with x (and r) and, unless staged in LDS, the
+// parameters read through raw buffer instructions.  The row's resource
+// spans exactly its d elements (none for a row past the end), and gfx950
+// range-checks the whole offset (VGPR, SGPR and immediate): an access past
+// the row reads zero.  So a lane keeps one VGPR offset, each slot's offset
+// is a scalar, and the clamped addresses and zeroing selects of norm_held go
+// away; one wave holding a 16 KiB float32 row drops from 147 to 99 VGPRs,
+// which lets 16 such waves share a CU.  Stores are norm_held's predicated
+// global stores.  Sums, merge and output expression are norm_held's, so for
+// equal (WPR, Q) the outputs carry the same bits.
+
+// a raw buffer over `bytes` bytes from `base` (stride 0; the fourth word is
+// the 32-bit data format gfx950 expects of untyped buffer accesses)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_buffer(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// VEC elements of T (16 bytes) at byte offset voff + soff, widened to float32
+template <typename T, int VEC, bool NT>
+__device__ __forceinline__ vf<VEC> bldv(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u4 raw = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, NT ? 2 : 0));
+    if constexpr (std::is_same_v<T, float>) {
+        static_assert(VEC == 4, "four float32 per access");
+        return __builtin_bit_cast(f4, raw);
+    } else {
+        static_assert(VEC == 8 && sizeof(T) == 2, "eight 16-bit elements per access");
+        typedef T t8 __attribute__((ext_vector_type(8)));
+        return __builtin_convertvector(__builtin_bit_cast(t8, raw), f8);
+    }
+}
+
+// VEC float32 parameters at byte offset voff + soff
+template <int VEC>
+__device__ __forceinline__ vf<VEC> bldp(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const f4 a = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+    if constexpr (VEC == 4) {
+        return a;
+    } else {
+        const f4 b = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff + 16, 0));
+        return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+}
+
+template <typename T, int OP, int VEC, int WPR, int Q, int WAVES, bool PLDS, bool RES>
+__global__ __launch_bounds__(WAVES * 64)
+void norm_aligned(NormParams p)
+{
+    static_assert(VEC == 4 || (VEC == 8 && sizeof(T) == 2), "16-byte accesses");
+    static_assert(WAVES % WPR == 0 && WPR <= 16, "whole rows per workgroup");
+    using VT = vf<VEC>;
+    constexpr int RPB = WAVES / WPR;
+    constexpr int kParams = (OP == OP_LN) ? 2 : 1;
+    constexpr int kCapV = 64 * WPR * Q;
+    constexpr int kF4 = VEC / 4;
+    static_assert(!PLDS || kCapV * kF4 * kParams * 16 <= 64 * 1024, "LDS parameter stage too large");
+    constexpr uint32_t kAcc = 16;           // bytes of one row access
+    constexpr uint32_t kPar = VEC * 4;      // bytes of its parameters
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int wr = (WPR == 1) ? 0 : wave % WPR;
+    const int rib = (WPR == 1) ? wave : wave / WPR;
+    __shared__ float2 xch[RPB][WPR];
+    __shared__ f4 lds_par[PLDS ? kParams : 1][PLDS ? kCapV * kF4 : 1];
+
+    const int d = p.d;
+    const float eps = p.eps;
+    const float inv_d = p.inv_d;
+    const int nvec = (int)((unsigned)d / VEC);  // >= 1: d % VEC == 0, d >= VEC
+    const uint32_t rbytes = (uint32_t)d * (uint32_t)sizeof(T);
+
+    if constexpr (PLDS) {
+        // every lane of the workgroup copies part of gamma/beta into LDS; a
+        // barrier before the output pass publishes it
+        const int nv = d >> 2;
+        for (int i = tid; i < nv && i < kCapV * kF4; i += WAVES * 64) {
+            lds_par[0][i] = ld4<false>(p.p0 + 4 * i);
+            if constexpr (OP == OP_LN) lds_par[kParams - 1][i] = ld4<false>(p.p1 + 4 * i);
+        }
+    }
+
+    const int64_t row_raw = (int64_t)blockIdx.x * RPB + rib;
+    const bool rv = row_raw < p.rows;
+    const int64_t row = rv ? row_raw : 0;
+    const uint32_t nb = rv ? rbytes : 0u;   // a row past the end reads zeros
+    const uint32_t voff = (uint32_t)lane * kAcc;
+    auto soff = [&](int q) -> uint32_t { return (uint32_t)(64 * (wr + WPR * q)) * kAcc; };
+    int kc[Q];        // access index, clamped into the row for LDS and stores
+    bool ok[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int k = lane + 64 * (wr + WPR * q);
+        ok[q] = rv && k < nvec;
+        kc[q] = k < nvec ? k : nvec - 1;
+    }
+
+    // 1. every load of the row before any use
+    VT v[Q];
+    {
+        const auto rx = row_buffer(static_cast<const T *>(p.x) + row * p.ldx, nb);
+#pragma unroll
+        for (int q = 0; q < Q; ++q) v[q] = bldv<T, VEC, true>(rx, voff, soff(q));
+    }
+    if constexpr (RES) {
+        const auto rr = row_buffer(static_cast<const T *>(p.r) + row * p.ldr, nb);
+        VT w[Q];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) w[q] = bldv<T, VEC, true>(rr, voff, soff(q));
+#pragma unroll
+        for (int q = 0; q < Q; ++q) v[q] = as_stored<T>(v[q] + w[q]);
+        // the sums leave as soon as they exist; every element is owned by one
+        // lane, so h may alias x or r
+        if (p.h) {
+            T *hr = static_cast<T *>(p.h) + row * p.ldh;
+#pragma unroll
+            for (int q = 0; q < Q; ++q)
+                if (ok[q]) stv<T, VEC, true>(hr + VEC * kc[q], v[q]);
+        }
+    }
+
+    // elements held by wave rank w of the row (all lanes agree)
+    auto wave_count = [&](int w) -> int {
+        int n = 0;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int c = nvec - 64 * (w + WPR * q);
+            n += c <= 0 ? 0 : (c >= 64 ? 64 : c);
+        }
+        return n * VEC;
+    };
+
+    float mu, rs;
+    if constexpr (OP == OP_LN) {
+        float s = 0.f;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) s += hsum(v[q]);
+        const float S = group_sum<64>(s);
+        float mu_w;
+        if constexpr (WPR == 1) {
+            mu_w = S * inv_d;
+        } else {
+            const int n_w = wave_count(wr);
+            mu_w = n_w > 0 ? S / (float)n_w : 0.f;
+        }
+        float m = 0.f;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) m += ok[q] ? csq(v[q], mu_w) : 0.f;
+        const float M2_w = group_sum<64>(m);
+        float M2;
+        if constexpr (WPR == 1) {
+            mu = mu_w;
+            M2 = M2_w;
+        } else {
+            if (lane == 0) xch[rib][wr] = make_float2(mu_w, M2_w);
+            __syncthreads();
+            if constexpr (WPR >= 16) {
+                const bool own = lane < WPR;
+                const float2 e = xch[rib][own ? lane : 0];
+                const float n_e = own ? (float)wave_count(lane) : 0.f;
+                mu = readlane(group_sum<16>(own ? n_e * e.x : 0.f), 0) * inv_d;
+                const float dm = e.x - mu;
+                M2 = readlane(group_sum<16>(own ? e.y + n_e * dm * dm : 0.f), 0);
+            } else {
+                float tot = 0.f;
+#pragma unroll
+                for (int w = 0; w < WPR; ++w) tot += (float)wave_count(w) * xch[rib][w].x;
+                mu = tot * inv_d;
+                M2 = 0.f;
+#pragma unroll
+                for (int w = 0; w < WPR; ++w) {
+                    const float2 e = xch[rib][w];
+                    const float dm = e.x - mu;
+                    M2 += e.y + (float)wave_count(w) * dm * dm;
+                }
+            }
+        }
+        rs = rsq(M2 * inv_d + eps);
+    } else {
+        float s2 = 0.f;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) s2 += sq(v[q]);
+        float S2 = group_sum<64>(s2);
+        if constexpr (WPR > 1) {
+            if (lane == 0) xch[rib][wr] = make_float2(S2, 0.f);
+            __syncthreads();
+            if constexpr (WPR >= 16) {
+                const bool own = lane < WPR;
+                const float e = xch[rib][own ? lane : 0].x;
+                S2 = readlane(group_sum<16>(own ? e : 0.f), 0);
+            } else {
+                S2 = 0.f;
+#pragma unroll
+                for (int w = 0; w < WPR; ++w) S2 += xch[rib][w].x;
+            }
+        }
+        mu = 0.f;
+        rs = rsq(S2 * inv_d + eps);
+    }
+
+    // 4. normalize, scale, shift; store from the same registers
+    if constexpr (PLDS && WPR == 1) __syncthreads();  // the LDS parameters are complete
+    const auto rp0 = row_buffer(p.p0, (uint32_t)d * 4u);
+    const auto rp1 = row_buffer(OP == OP_LN ? p.p1 : p.p0, (uint32_t)d * 4u);
+    T *yr = static_cast<T *>(p.y) + row * p.ldy;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        VT gq, bq = VT(0.f);
+        if constexpr (PLDS && VEC == 4) {
+            gq = lds_par[0][kc[q]];
+            if constexpr (OP == OP_LN) bq = lds_par[kParams - 1][kc[q]];
+        } else if constexpr (PLDS) {
+            // an oct's eight parameters are two consecutive float4 words
+            gq = __builtin_shufflevector(lds_par[0][2 * kc[q]], lds_par[0][2 * kc[q] + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+            if constexpr (OP == OP_LN)
+                bq = __builtin_shufflevector(lds_par[kParams - 1][2 * kc[q]], lds_par[kParams - 1][2 * kc[q] + 1],
+                                             0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+            const uint32_t ps = (uint32_t)(64 * (wr + WPR * q)) * kPar;
+            gq = bldp<VEC>(rp0, (uint32_t)lane * kPar, ps);
+            if constexpr (OP == OP_LN) bq = bldp<VEC>(rp1, (uint32_t)lane * kPar, ps);
+        }
+        VT o;
+        if constexpr (OP == OP_LN) o = (v[q] - mu) * rs * gq + bq;
+        else o = v[q] * gq * rs;
+        if (ok[q]) stv<T, VEC, true>(yr + VEC * kc[q], o);
+    }
+    if (rv && wr == 0 && lane == 0) {
+        if (OP == OP_LN && p.mean) p.mean[row] = mu;
+        if (p.rstd) p.rstd[row] = rs;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Multi-row held kernel: the 16-byte vector path of norm_held (LPR = 64, no
 // peel) with RV rows held at once by every group of WPR waves.  A lane holds
 // the same Q accesses, hence the same columns, of each of its RV rows, so one

@@ -49,18 +49,28 @@ constexpr int held_pre(int es, int vec, int peel, int lpr, int wpr, int q, int w
     return 0;
 }
 
-// Every held variant streams x (and r) in and y (and h) out with
-// non-temporal hints (norm_held's NTL/NTS); the cross-wave merge follows
-// norm_held's default.  T is the storage type, DT its mi_norm_dtype, OPN
-// the name prefix.
+// The kernel of a held variant.  Aligned vector rows of full waves run
+// norm_aligned (buffer loads, same bits as norm_held); peeled, scalar and
+// narrow rows run norm_held.  Every held variant streams x (and r) in and y
+// (and h) out with non-temporal hints; the cross-wave merge follows
+// norm_held's default.
+template <typename T, int OP, int VEC, int PEEL, int LPR, int WPR, int Q, int WAVES, bool RES>
+inline const void *held_kernel() {
+    constexpr int PRE = held_pre((int)sizeof(T), VEC, PEEL, LPR, WPR, Q, WAVES);
+    if constexpr (VEC > 1 && !PEEL && LPR == 64)
+        return reinterpret_cast<const void *>(&minorm::norm_aligned<T, OP, VEC, WPR, Q, WAVES, PRE == 2, RES>);
+    else
+        return reinterpret_cast<const void *>(
+            &minorm::norm_held<T, OP, VEC, (PEEL != 0), LPR, WPR, Q, WAVES, true, true, PRE, -1, RES>);
+}
+
+// T is the storage type, DT its mi_norm_dtype, OPN the name prefix.
 #define MI_HELD(T, DT, OPC, OPN, VEC, PEEL, LPR, WPR, Q, WAVES)                                \
     Variant{OPN "_" #VEC "_p" #PEEL "_l" #LPR "_w" #WPR "_q" #Q "_b" #WAVES,                  \
             mi_norm_variant_info{OPC, DT, VEC, PEEL, 0, LPR, WPR, Q, WAVES,                     \
                                  (WPR == 1) ? WAVES * (64 / LPR) : WAVES / WPR,                 \
                                  (int64_t)VEC * LPR * WPR * Q, (VEC > 1 && !PEEL) ? 1 : 0, 1},  \
-            reinterpret_cast<const void *>(                                                     \
-                &norm_held<T, kop(OPC), VEC, (PEEL != 0), LPR, WPR, Q, WAVES, true, true,       \
-                           held_pre((int)sizeof(T), VEC, PEEL, LPR, WPR, Q, WAVES), -1, kres(OPC)>)}
+            held_kernel<T, kop(OPC), VEC, PEEL, LPR, WPR, Q, WAVES, kres(OPC)>()}
 
 // the same shape with 4 (or 8) and with 16 waves per workgroup
 #define MI_HELD2(T, DT, OPC, OPN, VEC, PEEL, LPR, WPR, Q, WSMALL)                              \
@@ -127,12 +137,13 @@ constexpr int held_pre(int es, int vec, int peel, int lpr, int wpr, int q, int w
     MI_SLOTS16(T, DT, VW, OPC, OPN, PEEL)
 
 // One wave per float32 LayerNorm row of up to 4096 elements holding sixteen
-// 16-byte slots (3 waves per SIMD), in 4- and 8-wave workgroups: the
-// dispatcher's choice for rows of 3-4 K elements where its grid fills whole
-// rounds of resident workgroups.  Other operations and storage types have
-// none (16-bit octs would need twice the registers).
+// 16-byte slots (norm_aligned: 99 VGPRs, 5 waves per SIMD), in 4-, 8- and
+// 16-wave workgroups: the dispatcher's choice for rows of 3-4 K elements
+// with 3072-4096 rows.  Other operations and storage types have none
+// (16-bit octs would need twice the registers).
 #define MI_WIDE16_4_MI_NORM_OP_LAYERNORM(T, DT, OPC, OPN)                                          \
-    MI_HELD(T, DT, OPC, OPN, 4, 0, 64, 1, 16, 4), MI_HELD(T, DT, OPC, OPN, 4, 0, 64, 1, 16, 8),
+    MI_HELD(T, DT, OPC, OPN, 4, 0, 64, 1, 16, 4), MI_HELD(T, DT, OPC, OPN, 4, 0, 64, 1, 16, 8),      \
+    MI_HELD(T, DT, OPC, OPN, 4, 0, 64, 1, 16, 16),
 #define MI_WIDE16_4_MI_NORM_OP_RMSNORM(T, DT, OPC, OPN)
 #define MI_WIDE16_4_MI_NORM_OP_ADD_LAYERNORM(T, DT, OPC, OPN)
 #define MI_WIDE16_4_MI_NORM_OP_ADD_RMSNORM(T, DT, OPC, OPN)

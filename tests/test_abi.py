@@ -248,7 +248,7 @@ def test_variant_table_is_consistent(L):
     # adds one wave per row with sixteen slots (4- and 8-wave workgroups)
     shapes = {(op, dt): sorted(n[len(PREFIX[op] + DTSFX[dt]):] for _, n, v in infos
                                if v["op"] == op and v["dtype"] == dt) for op in OPS for dt in DTYPES}
-    wide16 = ["4_p0_l64_w1_q16_b4", "4_p0_l64_w1_q16_b8"]
+    wide16 = ["4_p0_l64_w1_q16_b4", "4_p0_l64_w1_q16_b8", "4_p0_l64_w1_q16_b16"]
     assert all(w in shapes[(0, mn.MI_NORM_F32)] for w in wide16)
     shapes[(0, mn.MI_NORM_F32)] = [n for n in shapes[(0, mn.MI_NORM_F32)] if n not in wide16]
     for dt in DTYPES:
