@@ -144,6 +144,8 @@ int find(int op, int dtype, int64_t rows, int vec, int peel, int looped, int lpr
 // - never for fused float32 rows at 8 waves per row: 3-5% slower
 //   ([32768,8192]), since four row streams share each parameter fetch and
 //   the shared fetch saves little.
+// Fused rows of four or eight waves from 8192 rows are settled before this
+// test (the one-row kernel with twice the waves).
 bool multi_pays(int op, int64_t rows, int64_t d, int64_t es, int wpr, int64_t pitch) {
     if (kres(op) && es == 4 && wpr >= 8) return false;
     if (rows >= 8192 || rows * d * es >= (int64_t(64) << 20)) return true;
@@ -309,6 +311,16 @@ int select_variant(const mi_norm_problem &P) {
             // 17.4 for 16-wave workgroups; [4096,3200] 18.1), and up to 7%
             // ahead of the one-row shapes outside it
             const int s = find_waves(op, dt, W, 1, 16, rows <= 3072 ? 4 : 8);
+            if (s >= 0) return s;
+        }
+        if (kres(op) && (wpr == 4 || wpr == 8) && rows >= 8192) {
+            // fused rows of four or eight waves with many rows: the one-row
+            // kernel with twice the waves per row and half the slots.  On
+            // MI355X, add + LayerNorm [32768,8192] float32 716 against 731 us,
+            // bfloat16 342 against 365 (the multi-row kernel); on seven
+            // further shapes faster in six by 1.7-12% ([16384,8192] 349
+            // against 395 us), 1% slower at [8192,4096]
+            const int s = find(op, dt, rows, W, 0, 0, 64, 2 * wpr, (q + 1) / 2);
             if (s >= 0) return s;
         }
         if (wpr && multi_pays(op, rows, d, esize(dt), wpr, row_pitch(P))) {

@@ -362,10 +362,13 @@ def test_dispatch_examples(L):
     assert sel(0, 1, rows=64) == "ln_1_p0_l16_w1_q1_b4"
     assert sel(2, 768) == "addln_4_r2_w1_q3_b4"             # fused: two rows per wave group
     assert sel(2, 768, rows=4095) == "addln_4_p0_l64_w2_q2_b16"
-    # fused float32 rows at 8 waves per row keep one row per wave; 16-bit ones do not
-    assert sel(3, 8192, rows=32768) == "addrms_4_p0_l64_w8_q4_b16"
-    assert sel(2, 4096, rows=16384) == "addln_4_r2_w4_q4_b4"
-    assert sel(2, 8192, rows=32768, dtype=mn.MI_NORM_BF16) == "addln_bf16_8_r2_w4_q4_b4"
+    # fused rows of four or eight waves with many rows: one row per wave group,
+    # twice the waves and half the slots
+    assert sel(3, 8192, rows=32768) == "addrms_4_p0_l64_w16_q2_b16"
+    assert sel(2, 4096, rows=16384) == "addln_4_p0_l64_w8_q2_b16"
+    assert sel(2, 8192, rows=32768, dtype=mn.MI_NORM_BF16) == "addln_bf16_8_p0_l64_w8_q2_b16"
+    assert sel(2, 6144, rows=16384) == "addln_4_p0_l64_w16_q2_b16"
+    assert sel(2, 4096, rows=8191) == "addln_4_r2_w4_q4_b4"      # fewer rows: two rows per wave group
     assert "_loop_" in sel(0, 2**20)
     # gamma misaligned only: no 128-bit parameter reads, so not the aligned path
     assert mn.mi_norm_variant_get_info(mn.mi_norm_select(_prob(0, 4096, 768, g=G + 4)))["needs_aligned"] == 0
