@@ -324,6 +324,18 @@ int select_variant(const mi_norm_problem &P) {
             if (s >= 0) return s;
         }
         if (wpr && multi_pays(op, rows, d, esize(dt), wpr, row_pitch(P))) {
+            if (op == MI_NORM_OP_LAYERNORM && esize(dt) == 4 && (wpr == 2 || wpr == 4) && rows >= 8192 &&
+                (q * wpr) % 8 == 0) {
+                // float32 LayerNorm rows of two or four waves from 8192 rows,
+                // whose slots split evenly over eight waves: eight waves per
+                // row with as many fewer slots ([16384,4096] 88.8 against
+                // 91.1 us, [32768,2048] 86.0 against 88.9 or more, [65536,2048]
+                // 171 against 186; ties at [8192,2048]).  Splits that leave
+                // slots idle ([16384,2560]: three slots of four waves) lost
+                // 3-4%.
+                const int m = find_multi(op, dt, W, 8, q * wpr / 8);
+                if (m >= 0) return m;
+            }
             const int m = find_multi(op, dt, W, wpr, q);
             if (m >= 0) return m;
         }

@@ -399,9 +399,10 @@ def test_workgroup_size_follows_row_count(L):
 
 def test_rows_spread_over_more_waves_when_few(L):
     # about four accesses per lane with many rows (float32 one-row rows of
-    # 2-4 K elements: up to eight); more waves per row with few
+    # 2-4 K elements: up to eight; float32 LayerNorm multi-row rows from 8192
+    # rows: eight waves when the slots split evenly); more waves per row with few
     for d, rows, wpr, q in ((768, 4096, 1, 3), (2048, 4096, 2, 4), (2048, 1024, 4, 2),
-                            (4096, 8192, 4, 4), (4096, 2048, 4, 4), (8192, 32768, 8, 4), (16384, 8192, 16, 4),
+                            (4096, 8192, 8, 2), (4096, 2048, 4, 4), (8192, 32768, 8, 4), (16384, 8192, 16, 4),
                             (768, 100, 2, 2), (32768, 64, 16, 8)):
         v = mn.mi_norm_variant_get_info(mn.mi_norm_select(_prob(0, rows, d)))
         assert (v["waves_per_row"], v["slots"]) == (wpr, q), (d, rows, v)
