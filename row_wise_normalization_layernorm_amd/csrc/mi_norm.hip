@@ -299,7 +299,14 @@ int select_variant(const mi_norm_problem &P) {
                 const int s = find_waves(op, dt, W, 1, 2 * q, 16);
                 if (s >= 0) return s;
             }
-            const int s = wpr == 1 ? find_waves(op, dt, W, wpr, q, 4) : -1;
+            // With the buffer-load kernel, plain (not fused) rows of one or
+            // two slots up to 8192 rows run faster in the workgroup rule's
+            // 16-wave workgroups (LayerNorm bfloat16 [4096,768] 4.03 against
+            // 4.22 us, [8192,768] 5.92 against 6.46; RMSNorm [4096,768] a
+            // tie); from 16384 rows, for fused rows and for four slots the
+            // 4-wave ones kept a 2-13% lead.
+            const bool small = wpr == 1 && q <= 2 && !kres(op) && rows <= 8192;
+            const int s = (wpr == 1 && !small) ? find_waves(op, dt, W, wpr, q, 4) : -1;
             return s >= 0 ? s : find(op, dt, rows, W, 0, 0, 64, wpr, q);
         }
         if (op == MI_NORM_OP_LAYERNORM && esize(dt) == 4 && nvec > 768 && nvec <= 1024 && rows >= 3072 &&

@@ -343,6 +343,10 @@ def test_dispatch_examples(L):
     assert sel(0, 2048, rows=4096, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w1_q4_b4"
     assert sel(0, 2048, rows=32768, dtype=mn.MI_NORM_F16) == "ln_f16_8_p0_l64_w1_q4_b4"
     assert sel(2, 768, rows=8192, dtype=mn.MI_NORM_BF16) == "addln_bf16_8_p0_l64_w1_q2_b4"
+    # plain 16-bit rows of one or two slots up to 8192 rows: the workgroup rule
+    assert sel(0, 768, rows=8192, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w1_q2_b16"
+    assert sel(0, 768, rows=16384, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w1_q2_b4"
+    assert sel(0, 768, rows=2048, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w1_q2_b4"
     # with 2560-8192 rows, rows of two waves run as one wave with twice the
     # slots in 16-wave workgroups
     assert sel(1, 4096, rows=8192, dtype=mn.MI_NORM_BF16) == "rms_bf16_8_p0_l64_w1_q8_b16"
@@ -480,8 +484,8 @@ def test_strides_and_types_decide_the_layout(L):
     info = lambda **kw: mn.mi_norm_variant_get_info(mn.mi_norm_select(_prob(0, 4096, 768, **kw)))
     name = lambda **kw: mn.mi_norm_variant_name(mn.mi_norm_select(_prob(0, 4096, 768, **kw)))
     # 16-byte accesses: eight 16-bit elements, 96 of them per row of 768
-    assert name(dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w1_q2_b4"
-    assert name(dtype=mn.MI_NORM_F16) == "ln_f16_8_p0_l64_w1_q2_b4"
+    assert name(dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w1_q2_b16"
+    assert name(dtype=mn.MI_NORM_F16) == "ln_f16_8_p0_l64_w1_q2_b16"
     assert info(dtype=mn.MI_NORM_BF16, x=X + 8, y=Y + 8)["peel"] == 1
     assert info(dtype=mn.MI_NORM_F32, x=X + 8, y=Y + 8)["peel"] == 1
     # a 16-bit row width that is a multiple of 4 but not of 8 is peeled
