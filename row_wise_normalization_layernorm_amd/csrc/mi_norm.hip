@@ -330,6 +330,16 @@ int select_variant(const mi_norm_problem &P) {
             const int s = find(op, dt, rows, W, 0, 0, 64, 2 * wpr, (q + 1) / 2);
             if (s >= 0) return s;
         }
+        if (op == MI_NORM_OP_RMSNORM && esize(dt) == 4 && wpr == 4 && rows >= 8192) {
+            // float32 RMSNorm rows of four waves from 8192 rows: the one-row
+            // kernel with eight waves per row and half the slots, in 8-wave
+            // workgroups ([32768,4096] 168.0 against 176.8 us for the
+            // multi-row kernel, [16384,4096] 85.4 against 88.6, [8192,3584]
+            // 39.4 against 39.8, [12288,3072] 49.8 against 50.1; 16-wave
+            // workgroups lost 2-5%)
+            const int s = find_waves(op, dt, W, 8, (q + 1) / 2, 8);
+            if (s >= 0) return s;
+        }
         if (wpr && multi_pays(op, rows, d, esize(dt), wpr, row_pitch(P))) {
             if (op == MI_NORM_OP_LAYERNORM && esize(dt) == 4 && (wpr == 2 || wpr == 4) && rows >= 8192 &&
                 (q * wpr) % 8 == 0) {

@@ -318,6 +318,7 @@ def test_dispatch_examples(L):
     assert sel(0, 4096, rows=3071) == "ln_4_p0_l64_w2_q8_b4"
     assert sel(0, 3072, rows=4096) == "ln_4_p0_l64_w2_q6_b16"
     assert sel(1, 4096, rows=4096) == "rms_4_r2_w4_q4_b4"
+    assert sel(1, 4096, rows=8192) == "rms_4_p0_l64_w8_q2_b8"     # RMSNorm rows of four waves, many rows
     # float32 one-row path with more than 4096 waves at half the waves per
     # row: half the waves, twice the slots
     assert sel(1, 4096, rows=3072) == "rms_4_p0_l64_w2_q8_b4"

@@ -40,6 +40,8 @@ CASES = [
     ("add_rmsnorm", BF16, 6145, 2048, "addrms_bf16_8_p0_l64_w1_q4_b4"),
     # float32 LayerNorm multi-row rows from 8192 rows: eight waves per row
     ("layernorm", F32, 8193, 4096, "ln_4_r2_w8_q2_b8"),
+    # float32 RMSNorm rows of four waves from 8192 rows: one row, eight waves
+    ("rmsnorm", F32, 8193, 3072, "rms_4_p0_l64_w8_q2_b8"),
     # fused rows of four or eight waves with many rows: twice the waves
     ("add_layernorm", F32, 8193, 4096, "addln_4_p0_l64_w8_q2_b16"),
     ("add_rmsnorm", BF16, 8193, 8192, "addrms_bf16_8_p0_l64_w8_q2_b16"),

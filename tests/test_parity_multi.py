@@ -100,9 +100,10 @@ def test_multi_row_in_place_and_aliased(torch_dev, dt, op):
     input: y over x, and for the fused operations h over x or over r;
     strided rows with gaps."""
     torch, dev = torch_dev
-    add = op.startswith("add_")
-    # fused float32 rows of four waves from 8192 rows run one row per wave group
-    shapes = ((8193, 768), (4097 if add else 8193, 4096)) if dt == mn.MI_NORM_F32 else ((4097, 8192),)
+    one_row = op.startswith("add_") or op == "rmsnorm"
+    # float32 fused and RMSNorm rows of four waves from 8192 rows run one row
+    # per wave group; 4097 rows of 4096 (64 MiB) are multi-row
+    shapes = ((8193, 768), (4097 if one_row else 8193, 4096)) if dt == mn.MI_NORM_F32 else ((4097, 8192),)
     for rows, d in shapes:
         x, r, params = inputs(op, dt, rows, d, "offset", [22, d])
         ld = {k: d + 16 for k in "xryh"}
