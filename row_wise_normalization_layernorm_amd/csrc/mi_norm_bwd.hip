@@ -92,12 +92,13 @@ bool vec_layout(const mi_norm_bwd_problem &P) {
     return true;
 }
 
-int find_bwd(int op, int dt, int vec, int looped, int wpr, int q) {
+int find_bwd(int op, int dt, int vec, int looped, int wpr, int q, int waves = 8) {
     const VariantTable &T = bwd_table(dt);
     for (int i = 0; i < T.n; ++i) {
         const mi_norm_variant_info &v = T.v[i].info;
         if (v.op != bwd_opcode(op) || v.vec != vec || v.looped != looped) continue;
-        if (looped || (v.waves_per_row == wpr && v.slots == q)) return bwd_table_base(dt) + i;
+        if (looped || (v.waves_per_row == wpr && v.slots == q && v.waves_per_block == waves))
+            return bwd_table_base(dt) + i;
     }
     return -1;
 }
@@ -131,6 +132,18 @@ int select_bwd(const mi_norm_bwd_problem &P) {
         } else {
             wpr = nvec <= 128 * q4 ? 2 : (nvec <= 256 * q4 ? 4 : 8);
             q = pick_q(nvec, 64 * wpr, qs + 1, (wpr == 8 ? nq : (q4 == 3 ? 3 : 4)) - 1);
+        }
+        // float32 rows of two or four waves: 16-wave workgroups, twice the
+        // rows in flight per CU (one step of 16 / wpr rows where 8 waves
+        // take two); four slots move to twice the waves at two.  Measured
+        // from 1024 to 65536 rows: LN [4096,1536] 20.6 against 22.2 us,
+        // [4096,2048] 25.6 against 26.5, [65536,2048] 263 against 269,
+        // [8192,4096] 74.6 against 76.2; RMSNorm [4096,1536] 19.3 against
+        // 20.7, [8192,2048] 39.9 against 40.7.  One-wave rows (from 4096
+        // rows) and eight-wave rows of four slots ran slower so.
+        if (q && dt == MI_NORM_F32 && (wpr == 2 || wpr == 4)) {
+            const int id = q == 4 ? find_bwd(op, dt, W, 0, 2 * wpr, 2, 16) : find_bwd(op, dt, W, 0, wpr, q, 16);
+            if (id >= 0) return id;
         }
         if (q) return find_bwd(op, dt, W, 0, wpr, q);
         return find_bwd(op, dt, 1, 1, 0, 0);

@@ -68,10 +68,11 @@ def bwd_ref(op: str, dt: int, dy, x, p0, mean, rstd) -> dict:
 
 
 def run_bwd_case(torch, dev, op: str, dt: int, dy, x, p0, mean, rstd, *, ld=None, off=None, po: int = 0,
-                 dx_mode=None, param_grads=True, variant=None, ref=None) -> None:
+                 dx_mode=None, param_grads=True, variant=None, ref=None, expect=None) -> None:
     """One mi_norm_bwd (or forced variant) call on guarded buffers, checked
     against the oracle.  ld / off: per-tensor stride / element offset dicts
-    over 'dy', 'x', 'dx'; dx_mode 'dy' or 'x' writes dx over that input."""
+    over 'dy', 'x', 'dx'; dx_mode 'dy' or 'x' writes dx over that input;
+    expect: the name the dispatcher must choose for this problem."""
     rows, d = x.shape
     ln = op == "layernorm"
     ld = {k: d for k in ("dy", "x", "dx")} | (ld or {})
@@ -93,6 +94,8 @@ def run_bwd_case(torch, dev, op: str, dt: int, dy, x, p0, mean, rstd, *, ld=None
     WSB = GuardedVec(torch, dev, max(1, (nbytes + 3) // 4), 0, np.full(max(1, (nbytes + 3) // 4), np.nan, np.float32))
     prob.workspace, prob.workspace_bytes = WSB.ptr, nbytes
     stream = torch.cuda.current_stream().cuda_stream
+    if expect is not None:
+        assert mn.mi_norm_variant_name(mn.mi_norm_bwd_select(prob)) == expect
     if variant is None:
         mn.mi_norm_bwd(prob, stream)
     else:
@@ -146,6 +149,23 @@ def test_bwd_wide_and_streamed(torch_dev, op, dt):
         say(f"bwd wide {op} dt={dt} [{rows}x{d}]")
         dy, x, p0, mean, rstd = bwd_inputs(op, dt, rows, d, "offset", [33, rows, d])
         run_bwd_case(torch, dev, op, dt, dy, x, p0, mean, rstd, ld={"dy": d + 8, "x": d + 16, "dx": d + 24})
+
+
+# --- the dispatcher's 16-wave workgroups (float32 rows of two or four waves) ---
+
+SIXTEEN = [("layernorm", 4099, 1536, "lnbwd_4_w2_q3_b16"), ("layernorm", 2051, 2048, "lnbwd_4_w4_q2_b16"),
+           ("layernorm", 1027, 3072, "lnbwd_4_w4_q3_b16"), ("layernorm", 515, 4096, "lnbwd_4_w8_q2_b16"),
+           ("rmsnorm", 4099, 1536, "rmsbwd_4_w2_q3_b16"), ("rmsnorm", 2051, 2048, "rmsbwd_4_w4_q2_b16"),
+           ("rmsnorm", 1027, 3072, "rmsbwd_4_w4_q3_b16"), ("rmsnorm", 515, 4096, "rmsbwd_4_w8_q2_b16")]
+
+
+@pytest.mark.parametrize("op,rows,d,name", SIXTEEN)
+def test_bwd_sixteen_wave_dispatch(torch_dev, op, rows, d, name):
+    """Row counts that leave the last step's row slots partly empty."""
+    torch, dev = torch_dev
+    say(f"bwd 16-wave {op} [{rows}x{d}] {name}")
+    dy, x, p0, mean, rstd = bwd_inputs(op, mn.MI_NORM_F32, rows, d, "offset", [36, rows, d])
+    run_bwd_case(torch, dev, op, mn.MI_NORM_F32, dy, x, p0, mean, rstd, expect=name)
 
 
 # --- every compiled backward variant, forced ----------------------------------
