@@ -295,6 +295,16 @@ int select_variant(const mi_norm_problem &P) {
             // 11.5 against 13.7 us; LayerNorm [2560,4096] 8.7 against 11.0),
             // equal in one; at 12288 rows it lost 4%.  One wave of up to four
             // slots takes 4-wave workgroups (the faster in 6 of 8 shapes).
+            // Under 2560 rows, rows of two waves and three or four slots
+            // take the multi-row kernel of the same shape: bfloat16
+            // RMSNorm [2048,4096] 6.43 against 6.84 us, LayerNorm 7.26
+            // against 7.58, add + RMSNorm 11.8 against 13.1, RMSNorm
+            // [2048,3072] 5.33 against more than 5.44 (two slots: LayerNorm
+            // [2048,2048] lost).
+            if (wpr == 2 && q >= 3 && rows < 2560) {
+                const int m = find_multi(op, dt, W, 2, q);
+                if (m >= 0) return m;
+            }
             if (wpr == 2 && q <= 4 && rows >= 2560 && rows <= 8192) {
                 const int s = find_waves(op, dt, W, 1, 2 * q, 16);
                 if (s >= 0) return s;

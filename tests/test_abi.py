@@ -359,7 +359,12 @@ def test_dispatch_examples(L):
     assert sel(1, 4096, rows=8192, dtype=mn.MI_NORM_BF16) == "rms_bf16_8_p0_l64_w1_q8_b16"
     assert sel(0, 4096, rows=2560, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w1_q8_b16"
     assert sel(2, 3072, rows=4096, dtype=mn.MI_NORM_F16) == "addln_f16_8_p0_l64_w1_q6_b16"
-    assert sel(1, 4096, rows=2048, dtype=mn.MI_NORM_BF16) == "rms_bf16_8_p0_l64_w2_q4_b4"
+    # under 2560 rows, rows of two waves and three or four slots: multi-row
+    assert sel(1, 4096, rows=2048, dtype=mn.MI_NORM_BF16) == "rms_bf16_8_r2_w2_q4_b4"
+    assert sel(3, 4096, rows=2559, dtype=mn.MI_NORM_BF16) == "addrms_bf16_8_r2_w2_q4_b4"
+    assert sel(0, 3072, rows=2048, dtype=mn.MI_NORM_F16) == "ln_f16_8_r2_w2_q3_b4"
+    assert sel(0, 2048, rows=2048, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w2_q2_b4"   # two slots
+    assert sel(0, 4096, rows=1024, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w4_q2_b4"   # four waves
     assert sel(0, 4096, rows=8193, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w2_q4_b4"
     # from four waves per row, the 16-bit rows follow the float32 rules
     assert sel(0, 8192, rows=32768, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_r2_w4_q4_b4"
