@@ -375,6 +375,17 @@ int select_variant(const mi_norm_problem &P) {
             wpr /= 2;
             q *= 2;
         }
+        if (esize(dt) == 2 && wpr == 4 && q <= 4 && rows >= 2048) {
+            // 16-bit rows of four waves on the one-row path from 2048 rows:
+            // two waves with twice the slots in 16-wave workgroups (bfloat16
+            // LayerNorm [2048,4608] 8.18 against 9.07 us, [4096,6144] 19.5
+            // against 21.4, [2048,8192] 12.9 against 13.6; RMSNorm
+            // [2048,8192] 12.1 against 13.5, [4096,6144] 17.8 against more
+            // than 19.5; add + RMSNorm [2048,8192] 23.3 against 24.5); at
+            // 1024 rows it lost
+            const int s = find_waves(op, dt, W, 2, 2 * q, 16);
+            if (s >= 0) return s;
+        }
         if (wpr) return find(op, dt, rows, W, 0, 0, 64, wpr, q);
         return find(op, dt, rows, W, 0, 1, 0, 0, 0);
     }

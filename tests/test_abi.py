@@ -369,7 +369,12 @@ def test_dispatch_examples(L):
     # from four waves per row, the 16-bit rows follow the float32 rules
     assert sel(0, 8192, rows=32768, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_r2_w4_q4_b4"
     assert sel(0, 8192, rows=4096, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_r2_w4_q4_b4"   # 64 MiB
-    assert sel(0, 8192, rows=4095, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w4_q4_b16"
+    # 16-bit rows of four waves on the one-row path from 2048 rows: two waves,
+    # twice the slots, 16-wave workgroups
+    assert sel(0, 8192, rows=4095, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w2_q8_b16"
+    assert sel(1, 6144, rows=4096, dtype=mn.MI_NORM_F16) == "rms_f16_8_p0_l64_w2_q6_b16"
+    assert sel(3, 8192, rows=2048, dtype=mn.MI_NORM_BF16) == "addrms_bf16_8_p0_l64_w2_q8_b16"
+    assert sel(0, 8192, rows=2047, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w4_q4_b16"
     # no multi-row variant for 16 waves per row, or for more than 4 slots of 16-bit rows
     assert sel(0, 16384, rows=8192) == "ln_4_p0_l64_w16_q4_b16"
     assert sel(0, 6144 * 8, rows=8192, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w16_q6_b16"

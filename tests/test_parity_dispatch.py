@@ -39,6 +39,9 @@ CASES = [
     # 16-bit rows of two waves and three or four slots under 2560 rows: multi-row
     ("rmsnorm", BF16, 2049, 4096, "rms_bf16_8_r2_w2_q4_b4"),
     ("add_layernorm", F16, 2049, 3072, "addln_f16_8_r2_w2_q3_b4"),
+    # 16-bit rows of four waves from 2048 rows, one-row path: two waves, twice the slots
+    ("layernorm", BF16, 2049, 4608, "ln_bf16_8_p0_l64_w2_q6_b16"),
+    ("add_rmsnorm", F16, 2051, 8192, "addrms_f16_8_p0_l64_w2_q8_b16"),
     # 16-bit rows of one wave: 4-wave workgroups
     ("add_rmsnorm", BF16, 6145, 2048, "addrms_bf16_8_p0_l64_w1_q4_b4"),
     # float32 LayerNorm multi-row rows from 8192 rows: eight waves per row
