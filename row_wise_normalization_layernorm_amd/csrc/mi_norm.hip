@@ -350,6 +350,18 @@ int select_variant(const mi_norm_problem &P) {
             const int s = find_waves(op, dt, W, 8, (q + 1) / 2, 8);
             if (s >= 0) return s;
         }
+        if (kres(op) && esize(dt) == 4 && wpr == 2 && nvec > 256 && rows <= 4096) {
+            // fused float32 rows of two waves by width (more than 256
+            // quads, not doubled for few rows), up to 4096 rows: one wave of
+            // eight slots in 4-wave workgroups (add + LayerNorm [2048,1536]
+            // 8.82 against 10.2 us, [4096,2048] 23.0 against 24.7 for the
+            // multi-row kernel, [2048,2048] 11.6 against 12.3; add + RMSNorm
+            // [3072,2048] 16.9 against 18.2, [4096,1536] 16.8 against 17.5);
+            // eight slots beat six for rows of six ([2048,1536] 8.82 against
+            // 9.31); at 6144 rows the multi-row kernel tied
+            const int s = find_waves(op, dt, W, 1, 8, 4);
+            if (s >= 0) return s;
+        }
         if (wpr && multi_pays(op, rows, d, esize(dt), wpr, row_pitch(P))) {
             if (op == MI_NORM_OP_LAYERNORM && esize(dt) == 4 && (wpr == 2 || wpr == 4) && rows >= 8192 &&
                 (q * wpr) % 8 == 0) {
