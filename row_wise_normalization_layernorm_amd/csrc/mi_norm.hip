@@ -362,6 +362,16 @@ int select_variant(const mi_norm_problem &P) {
             const int s = find_waves(op, dt, W, 1, 8, 4);
             if (s >= 0) return s;
         }
+        if (op == MI_NORM_OP_RMSNORM && esize(dt) == 4 && wpr == 2 && nvec > 256 && rows >= 2048 &&
+            rows <= 4096) {
+            // float32 RMSNorm rows of two waves by width, 2048-4096 rows:
+            // the multi-row kernel of the same shape ([2560,2048] 7.55
+            // against 7.94 us, [2048,2048] 6.41 against 6.70, [4096,1536]
+            // 8.63 against 8.96, [4096,2048] 11.79 against 11.88); LayerNorm
+            // tied or lost there ([4096,2048] 13.2 against 11.5)
+            const int m = find_multi(op, dt, W, 2, q);
+            if (m >= 0) return m;
+        }
         if (wpr && multi_pays(op, rows, d, esize(dt), wpr, row_pitch(P))) {
             if (op == MI_NORM_OP_LAYERNORM && esize(dt) == 4 && (wpr == 2 || wpr == 4) && rows >= 8192 &&
                 (q * wpr) % 8 == 0) {

@@ -359,6 +359,10 @@ def test_dispatch_examples(L):
     assert sel(1, 4096, rows=8192, dtype=mn.MI_NORM_BF16) == "rms_bf16_8_p0_l64_w1_q8_b16"
     assert sel(0, 4096, rows=2560, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w1_q8_b16"
     assert sel(2, 3072, rows=4096, dtype=mn.MI_NORM_F16) == "addln_f16_8_p0_l64_w1_q6_b16"
+    # float32 RMSNorm rows of two waves, 2048-4096 rows: multi-row
+    assert sel(1, 2048, rows=2560) == "rms_4_r2_w2_q4_b4"
+    assert sel(1, 1536, rows=4096) == "rms_4_r2_w2_q3_b4"
+    assert sel(0, 2048, rows=4096) == "ln_4_p0_l64_w2_q4_b16"
     # fused float32 rows of two waves up to 4096 rows: one wave of eight slots
     assert sel(2, 1536, rows=2048) == "addln_4_p0_l64_w1_q8_b4"
     assert sel(3, 2048, rows=4096) == "addrms_4_p0_l64_w1_q8_b4"
