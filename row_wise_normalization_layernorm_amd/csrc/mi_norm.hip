@@ -362,6 +362,14 @@ int select_variant(const mi_norm_problem &P) {
             const int s = find_waves(op, dt, W, 1, 8, 4);
             if (s >= 0) return s;
         }
+        if (kres(op) && esize(dt) == 4 && wpr == 4 && nvec > 512 && q <= 4 && rows >= 2048 && rows < 4096) {
+            // fused float32 rows of four waves by width, 2048-4095 rows: the
+            // multi-row kernel with two waves per row and twice the slots
+            // (add + LayerNorm [3000,3000] 26.8 against 29.3 us, add +
+            // RMSNorm [2048,3072] 16.9 against 18.2)
+            const int m = find_multi(op, dt, W, 2, 2 * q);
+            if (m >= 0) return m;
+        }
         if (op == MI_NORM_OP_RMSNORM && esize(dt) == 4 && wpr == 2 && nvec > 256 && rows >= 2048 &&
             rows <= 4096) {
             // float32 RMSNorm rows of two waves by width, 2048-4096 rows:
@@ -397,14 +405,15 @@ int select_variant(const mi_norm_problem &P) {
             wpr /= 2;
             q *= 2;
         }
-        if (esize(dt) == 2 && wpr == 4 && q <= 4 && rows >= 2048) {
+        if (esize(dt) == 2 && wpr == 4 && q <= 4 && rows >= 2048 && (!kres(op) || rows < 2560)) {
             // 16-bit rows of four waves on the one-row path from 2048 rows:
             // two waves with twice the slots in 16-wave workgroups (bfloat16
             // LayerNorm [2048,4608] 8.18 against 9.07 us, [4096,6144] 19.5
             // against 21.4, [2048,8192] 12.9 against 13.6; RMSNorm
             // [2048,8192] 12.1 against 13.5, [4096,6144] 17.8 against more
             // than 19.5; add + RMSNorm [2048,8192] 23.3 against 24.5); at
-            // 1024 rows it lost
+            // 1024 rows it lost, and fused rows from 2560 rows lost 5-15%
+            // (add + RMSNorm [3000,6000] 31.6 against 27.5 us)
             const int s = find_waves(op, dt, W, 2, 2 * q, 16);
             if (s >= 0) return s;
         }

@@ -330,7 +330,7 @@ def test_dispatch_examples(L):
     assert sel(1, 4096, rows=3072) == "rms_4_p0_l64_w2_q8_b4"
     assert sel(0, 2048, rows=6144) == "ln_4_p0_l64_w1_q8_b4"     # 16-wave grid uneven: 4 waves
     assert sel(0, 4096, rows=2048) == "ln_4_p0_l64_w4_q4_b16"    # 4096 waves: no change
-    assert sel(2, 4096, rows=3000) == "addln_4_p0_l64_w4_q4_b16"  # fused rows keep theirs
+    assert sel(2, 4096, rows=3000) == "addln_4_r2_w2_q8_b4"       # fused rows: their own rule
     # workgroups spread evenly over the CUs: 384 16-wave workgroups would load
     # half the CUs twice, so 4-wave ones
     assert sel(0, 768, rows=6144) == "ln_4_p0_l64_w1_q3_b4"
@@ -359,6 +359,14 @@ def test_dispatch_examples(L):
     assert sel(1, 4096, rows=8192, dtype=mn.MI_NORM_BF16) == "rms_bf16_8_p0_l64_w1_q8_b16"
     assert sel(0, 4096, rows=2560, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w1_q8_b16"
     assert sel(2, 3072, rows=4096, dtype=mn.MI_NORM_F16) == "addln_f16_8_p0_l64_w1_q6_b16"
+    # fused float32 rows of four waves, 2048-4095 rows: multi-row, two waves,
+    # twice the slots
+    assert sel(2, 3000, rows=3000) == "addln_4_r2_w2_q6_b4"
+    assert sel(3, 4096, rows=2048) == "addrms_4_r2_w2_q8_b4"
+    assert sel(2, 3072, rows=4096) == "addln_4_r2_w4_q3_b4"
+    # fused 16-bit rows of four waves keep four waves from 2560 rows
+    assert sel(3, 6000, rows=3000, dtype=mn.MI_NORM_BF16) == "addrms_bf16_8_p0_l64_w4_q3_b16"
+    assert sel(2, 6144, rows=2048, dtype=mn.MI_NORM_BF16) == "addln_bf16_8_p0_l64_w2_q6_b16"
     # float32 RMSNorm rows of two waves, 2048-4096 rows: multi-row
     assert sel(1, 2048, rows=2560) == "rms_4_r2_w2_q4_b4"
     assert sel(1, 1536, rows=4096) == "rms_4_r2_w2_q3_b4"

@@ -44,6 +44,8 @@ CASES = [
     ("add_rmsnorm", F16, 2051, 8192, "addrms_f16_8_p0_l64_w2_q8_b16"),
     # 16-bit rows of one wave: 4-wave workgroups
     ("add_rmsnorm", BF16, 6145, 2048, "addrms_bf16_8_p0_l64_w1_q4_b4"),
+    # fused float32 rows of four waves, 2048-4095 rows: multi-row, two waves, twice the slots
+    ("add_layernorm", F32, 3001, 3000, "addln_4_r2_w2_q6_b4"),
     # float32 RMSNorm rows of two waves, 2048-4096 rows: multi-row
     ("rmsnorm", F32, 3001, 1800, "rms_4_r2_w2_q4_b4"),
     # fused float32 rows of two waves up to 4096 rows: one wave of eight slots
