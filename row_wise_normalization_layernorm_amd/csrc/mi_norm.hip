@@ -306,8 +306,16 @@ int select_variant(const mi_norm_problem &P) {
                 if (m >= 0) return m;
             }
             if (wpr == 2 && q <= 4 && rows >= 2560 && rows <= 8192) {
-                const int s = find_waves(op, dt, W, 1, 2 * q, 16);
+                // 4-wave workgroups where more than 256 16-wave ones would
+                // spread unevenly over the CUs: bfloat16 LayerNorm
+                // [5000,3000] (313 workgroups) 13.7 against 15.8 us,
+                // [4500,4096] 16.0 against 17.8, RMSNorm [6144,3072] 14.4
+                // against 15.7, add + LayerNorm [6144,4096] 37.1 against 40.1
+                const int64_t b16 = (rows + 15) / 16;
+                const int s = (b16 > 256 && !even_spread(b16)) ? find_waves(op, dt, W, 1, 2 * q, 4) : -1;
                 if (s >= 0) return s;
+                const int t = find_waves(op, dt, W, 1, 2 * q, 16);
+                if (t >= 0) return t;
             }
             // With the buffer-load kernel, plain (not fused) rows of one or
             // two slots up to 8192 rows run faster in the workgroup rule's

@@ -34,8 +34,9 @@ CASES = [
     ("layernorm", F32, 6145, 2048, "ln_4_p0_l64_w1_q8_b4"),
     # 16-bit rows of two waves with 2560-8192 rows: one wave, twice the slots
     ("layernorm", BF16, 2561, 4096, "ln_bf16_8_p0_l64_w1_q8_b16"),
-    ("add_layernorm", F16, 4097, 3072, "addln_f16_8_p0_l64_w1_q6_b16"),
+    ("add_layernorm", F16, 4095, 3072, "addln_f16_8_p0_l64_w1_q6_b16"),
     ("rmsnorm", BF16, 3584, 3584, "rms_bf16_8_p0_l64_w1_q8_b16"),
+    ("layernorm", BF16, 5001, 3000, "ln_bf16_8_p0_l64_w1_q6_b4"),      # 16-wave grid uneven
     # 16-bit rows of two waves and three or four slots under 2560 rows: multi-row
     ("rmsnorm", BF16, 2049, 4096, "rms_bf16_8_r2_w2_q4_b4"),
     ("add_layernorm", F16, 2049, 3072, "addln_f16_8_r2_w2_q3_b4"),
