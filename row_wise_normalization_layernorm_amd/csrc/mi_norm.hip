@@ -305,6 +305,16 @@ int select_variant(const mi_norm_problem &P) {
                 const int m = find_multi(op, dt, W, 2, q);
                 if (m >= 0) return m;
             }
+            if (kres(op) && wpr == 2 && q == 4 && rows > 4096 && rows <= 8192) {
+                // fused rows of two waves and four slots, 4097-8192 rows:
+                // four waves of two slots in 16-wave workgroups (add +
+                // LayerNorm bfloat16 [8000,4096] 44.3 against 48.8 us,
+                // [6144,4096] 34.8 against 37.1; add + RMSNorm [5000,4096]
+                // 28.3 against 29.2); at 4096 rows (24.4 against 23.1) and
+                // for rows of three slots it lost
+                const int s = find_waves(op, dt, W, 4, 2, 16);
+                if (s >= 0) return s;
+            }
             if (wpr == 2 && q <= 4 && rows >= 2560 && rows <= 8192) {
                 // 4-wave workgroups where more than 256 16-wave ones would
                 // spread unevenly over the CUs: bfloat16 LayerNorm

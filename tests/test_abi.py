@@ -367,6 +367,9 @@ def test_dispatch_examples(L):
     # ... in 4-wave workgroups where more than 256 16-wave ones spread unevenly
     assert sel(0, 3000, rows=5000, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w1_q6_b4"
     assert sel(0, 3072, rows=8000, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w1_q6_b16"   # 500: even
+    # fused 16-bit rows of two waves and four slots, 4097-8192 rows: four waves
+    assert sel(2, 4096, rows=8000, dtype=mn.MI_NORM_BF16) == "addln_bf16_8_p0_l64_w4_q2_b16"
+    assert sel(3, 4096, rows=4096, dtype=mn.MI_NORM_BF16) == "addrms_bf16_8_p0_l64_w1_q8_b16"
     # fused 16-bit rows of four waves keep four waves from 2560 rows
     assert sel(3, 6000, rows=3000, dtype=mn.MI_NORM_BF16) == "addrms_bf16_8_p0_l64_w4_q3_b16"
     assert sel(2, 6144, rows=2048, dtype=mn.MI_NORM_BF16) == "addln_bf16_8_p0_l64_w2_q6_b16"

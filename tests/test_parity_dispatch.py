@@ -37,6 +37,7 @@ CASES = [
     ("add_layernorm", F16, 4095, 3072, "addln_f16_8_p0_l64_w1_q6_b16"),
     ("rmsnorm", BF16, 3584, 3584, "rms_bf16_8_p0_l64_w1_q8_b16"),
     ("layernorm", BF16, 5001, 3000, "ln_bf16_8_p0_l64_w1_q6_b4"),      # 16-wave grid uneven
+    ("add_rmsnorm", F16, 5003, 4096, "addrms_f16_8_p0_l64_w4_q2_b16"),  # fused, four slots: four waves
     # 16-bit rows of two waves and three or four slots under 2560 rows: multi-row
     ("rmsnorm", BF16, 2049, 4096, "rms_bf16_8_r2_w2_q4_b4"),
     ("add_layernorm", F16, 2049, 3072, "addln_f16_8_r2_w2_q3_b4"),
