@@ -100,6 +100,11 @@ BENCH_WORKLOADS = {
     "copy_4096x384": W("copy", "f32", 4096, 384),      # the bytes of a 16-bit [4096,768]
     "copy_16384x8192": W("copy", "f32", 16384, 8192),  # the bytes of a 16-bit [32768,8192]
     "copy_4096x4096": W("copy", "f32", 4096, 4096),
+    # the parts of a launch: an empty kernel, and passes that only read or
+    # only write the bytes of x (or y) of [4096,768]
+    "empty": W("empty", "f32", 0, 0),
+    "read_4096x768": W("read", "f32", 4096, 768),
+    "write_4096x768": W("write", "f32", 4096, 768),
 }
 
 ESIZE = {"f32": 4, "f16": 2, "bf16": 2}
@@ -159,6 +164,10 @@ def algorithmic_bytes(op: str, rows: int, d: int, stats: bool, storage: str = "f
     if op.endswith("_bwd"):
         ln = op.startswith("layernorm")
         return 3 * e * rows * d + (12 if ln else 8) * d + (8 if ln else 4) * rows
+    if op in ("read", "write"):
+        return 4 * rows * d
+    if op == "empty":
+        return 0
     per_elem = (4 if op.startswith("add_") else 2) * e
     if op.endswith("layernorm"):
         return per_elem * rows * d + 8 * d + (8 * rows if stats else 0)
@@ -170,6 +179,10 @@ def algorithmic_bytes(op: str, rows: int, d: int, stats: bool, storage: str = "f
 def describe(op: str, rows: int, d: int, stats: bool, storage: str = "f32", pad: int = 0) -> str:
     if op == "copy":
         return f"streaming copy FP32 {rows*d} elements (calibration, bytes of [{rows},{d}])"
+    if op == "empty":
+        return "empty kernel, 256 workgroups of 1024 threads (calibration)"
+    if op in ("read", "write"):
+        return f"{op}-only pass over {rows*d} FP32 elements (calibration, the bytes of x of [{rows},{d}])"
     kind = {"f32": "FP32", "f16": "FP16 storage, FP32 statistics",
             "bf16": "BF16 storage, FP32 statistics"}[storage]
     if op.endswith("_bwd"):
@@ -203,6 +216,28 @@ def pmc_traffic(workload: str, variant: str):
     return float(t.group(1)), path
 
 
+def trace_stats(workload: str, variant: str):
+    """Per-dispatch kernel durations (µs: median, min, max, mean over the
+    timed steps) from the committed rocprofv3 kernel-trace summary, or None
+    when there is none, the kernels changed since it was taken, or the run
+    uses another variant than the one traced."""
+    path = os.path.join(ROOT, "profiles", f"trace_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    field = lambda k: (re.search(rf"^{k}:\s*(\S+)", text, re.M) or [None, None])[1]
+    if field("kernel_source_sha256") != kernel_source_hash(direction_of(workload)) or field("kernel_variant") != variant:
+        return None
+    try:
+        out = {k: float(field(f"dispatch_us_{k}")) for k in ("median", "min", "max", "mean")}
+        out["dispatches"] = int(field("dispatches"))
+    except (TypeError, ValueError):
+        return None
+    out["source"] = os.path.relpath(path, ROOT)
+    out["what"] = "rocprofv3 --kernel-trace, per-dispatch durations of the timed steps (back to back)"
+    return out
+
+
 def load_bench_lib():
     import row_wise_normalization_layernorm_amd as mn
     mn.lib()
@@ -218,6 +253,7 @@ def load_bench_lib():
     L.mi_bench_copy_loop.argtypes = [P, P, I, I64, I, P]
     L.mi_bench_norm_loop.argtypes = [P, P, P, P, P, P, P, I, I, I, P]
     L.mi_bench_bwd_loop.argtypes = [P, P, P, P, P, P, P, P, I, I, I, P]
+    L.mi_bench_calib_loop.argtypes = [I, P, P, I, I64, I, P]
     return L
 
 
@@ -389,7 +425,8 @@ def measure_and_print(args, torch, stream, run_native, run_python, rotated, nset
         with torch.cuda.stream(stream):
             runner_t()
 
-    ms, wall_ms, gate_us, covered = gated_span(torch, stream, args.steps, enqueue)
+    ms, wall_ms, gate_us, covered = gated_span(torch, stream, args.steps, enqueue,
+                                               tries=1 if args.profile else 4)
     ms_per_step = ms / args.steps
 
     # single launches on an idle GPU, each between two events: the duration a
@@ -397,7 +434,7 @@ def measure_and_print(args, torch, stream, run_native, run_python, rotated, nset
     # A short spin kernel holds the stream while the host enqueues the first
     # event and the launch, so the span holds no host time.
     iso = []
-    if args.launch == "native":
+    if args.launch == "native" and not args.profile:
         for i in range(20):
             arrays = rotated((args.steps + i) % nsets)   # a set last touched about n_sets steps ago
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -413,6 +450,7 @@ def measure_and_print(args, torch, stream, run_native, run_python, rotated, nset
     gbps = bytes_step / (ms_per_step * 1e-3) / 1e9
 
     traffic, _ = pmc_traffic(args.workload, variant_name)
+    dispatch = trace_stats(args.workload, variant_name)
     roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(gbps / PEAK_HBM_GBPS, 4),
                 "traffic": traffic, "kernel": variant_name,
@@ -420,7 +458,8 @@ def measure_and_print(args, torch, stream, run_native, run_python, rotated, nset
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-scaled)"}
 
     copy = None
-    if not args.no_copy and args.launch == "native" and not args.workload.startswith("copy_"):
+    calib = BENCH_WORKLOADS[args.workload].op in ("copy", "empty", "read", "write")
+    if not args.no_copy and not args.profile and args.launch == "native" and not calib:
         copy_us, copy_sets = copy_reference(torch, load_bench_lib(), stream, bytes_step, args.steps,
                                             args.warmup, args.mode, args.footprint_gib)
         copy = {"us": round(copy_us, 3), "bytes": 8 * max(4, (bytes_step // 8) // 4 * 4),
@@ -429,7 +468,7 @@ def measure_and_print(args, torch, stream, run_native, run_python, rotated, nset
                 "what": "copy_cover moving the step's bytes (half read, half written), timed the same way"}
 
     cpu = None
-    if cpu_fn is not None:
+    if cpu_fn is not None and not args.profile:
         reps, el, threads = cpu_fn(args.cpu_seconds, None)
         reps1, el1, _ = cpu_fn(args.cpu_seconds / 2, 1)
         cpu = {"value": round(bytes_step * reps / el / 1e9, 3), "unit": "GB/s", "cores": threads,
@@ -452,12 +491,14 @@ def measure_and_print(args, torch, stream, run_native, run_python, rotated, nset
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": config.get("storage", "f32"),
         "data": "synthetic",
         "config": {"workload": workload, **config, "mode": args.mode, "buffer_sets": nsets,
                    "footprint_bytes": nsets * per_set, "launch": args.launch, "variant": variant_name,
+                   "arithmetic": "f32", "hip_force_dev_kernarg": os.environ.get("HIP_FORCE_DEV_KERNARG"),
                    "parallelism": "single GPU"},
-        "kernel_us": round(ms_per_step * 1e3, 3),
+        "span_us_per_step": round(ms_per_step * 1e3, 3),
+        "kernel_dispatch_us": dispatch,
         "isolated_launch_us": iso_us,
         "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
         "rows_per_s": round(rows / (ms_per_step * 1e-3), 1),
@@ -468,6 +509,7 @@ def measure_and_print(args, torch, stream, run_native, run_python, rotated, nset
         "copy_reference": copy,
         "cpu_baseline": cpu,
         "kernel_source_sha256": kernel_source_hash(direction_of(args.workload)),
+        "profile_run": bool(args.profile),
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -609,6 +651,49 @@ def bench_bwd(args, torch, np, mn, wl, dev, wk) -> int:
                               "pattern": pattern, "seed": seed, "workspace_bytes": nbytes}, rows)
 
 
+def bench_calib(args, torch, np, mn, dev, wk) -> int:
+    """The parts of a launch (mi_calib_launch): an empty kernel, a read-only
+    and a write-only pass over rotated buffers, timed like a step."""
+    op, _, rows, d, _, _, _ = wk
+    kind = {"empty": 0, "read": 1, "write": 2}[op]
+    BL = load_bench_lib()
+    n = rows * d
+    per_set = 4 * n
+    nsets = 1 if (args.mode == "warm" or kind == 0) else max(1, math.ceil(args.footprint_gib * 2**30 / per_set))
+    bufs = [torch.zeros(n, device=dev) for _ in range(nsets)] if kind else []
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream(device=dev)
+    sh = stream.cuda_stream
+
+    def rotated(first: int):
+        return (ptr_array(bufs[first:] + bufs[:first]),) if kind else (None,)
+
+    base = rotated(0)
+
+    def run_native(k: int, arrays=None):
+        a = (arrays or base)[0]
+        st = BL.mi_bench_calib_loop(kind, a if kind == 1 else None, a if kind == 2 else None, nsets, n, k, sh)
+        if st != 0:
+            raise RuntimeError(f"calibration loop failed: {mn.mi_norm_status_string(st)}")
+
+    def run_python(k: int, start: int = 0):
+        for s_ in range(start, start + k):
+            b = bufs[s_ % nsets] if kind else None
+            mn.mi_calib_launch(kind, b if kind == 1 else None, b if kind == 2 else None, n, stream=sh)
+
+    with torch.cuda.stream(stream):
+        run_python(1)
+    torch.cuda.synchronize()
+    if kind == 2 and not bool((bufs[0] == 1.0).all()):
+        print("PARITY FAILURE: the write-only pass left other values", file=sys.stderr)
+        return 3
+    name = {0: "calib_empty", 1: "read_cover", 2: "write_cover"}[kind]
+    return measure_and_print(args, torch, stream, run_native, run_python, rotated, nsets, per_set, name,
+                             algorithmic_bytes(op, rows, d, False), {"exact": True}, None,
+                             describe(op, rows, d, False), {"rows": rows, "d": d, "storage": "f32"},
+                             max(rows, 1))
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -624,7 +709,15 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy", action="store_true",
                     help="skip the calibration copy of the step's bytes")
+    ap.add_argument("--profile", action="store_true",
+                    help="the run a kernel tracer or counter pass wraps: the parity call, W warm-up "
+                         "steps and one span of K steps, nothing else (no copy, no single launches, "
+                         "no CPU baseline)")
+    ap.add_argument("--kernarg", default="device", choices=["device", "host"],
+                    help="where HIP places kernel arguments (HIP_FORCE_DEV_KERNARG=1 or 0, set before "
+                         "the HIP runtime starts)")
     args = ap.parse_args(argv)
+    os.environ["HIP_FORCE_DEV_KERNARG"] = "1" if args.kernarg == "device" else "0"
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -646,6 +739,8 @@ def main(argv=None) -> int:
     wk = BENCH_WORKLOADS[args.workload]
     if wk.op.endswith("_bwd"):
         return bench_bwd(args, torch, np, mn, wl, dev, wk)
+    if wk.op in ("empty", "read", "write"):
+        return bench_calib(args, torch, np, mn, dev, wk)
     op, storage, rows, d, pattern, stats, pad = wk
     eps = wl.EPS
     add = op.startswith("add_")

@@ -43,6 +43,7 @@ from ._binding import (  # noqa: F401
     mi_add_rmsnorm_fwd,
     mi_add_rmsnorm_fwd_variant,
     mi_copy_f32,
+    mi_calib_launch,
     mi_layernorm_fwd,
     mi_layernorm_fwd_variant,
     mi_norm_check,

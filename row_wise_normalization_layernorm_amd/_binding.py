@@ -1,4 +1,5 @@
-"""ctypes binding of libmi_norm.so (include/mi_norm.h).
+"""ctypes binding of libmi_norm.so (include/mi_norm.h, and the tuning and
+calibration calls of include/mi_norm_tuning.h).
 
 Argument marshalling only: every arithmetic step runs in the library's HIP
 kernels.  Functions accept torch CUDA tensors (their device pointer is taken)
@@ -21,6 +22,7 @@ import re
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmi_norm.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "mi_norm.h")
+TUNING_HEADER = os.path.join(os.path.dirname(PKG), "include", "mi_norm_tuning.h")
 
 MI_NORM_OK = 0
 MI_NORM_ERR_INVALID = 1
@@ -107,6 +109,7 @@ _SIGNATURES = {
     "mi_layernorm_fwd_variant": (_I, [_I, _VP, _VP, _VP, _VP, _I64, _I64, _F, _VP, _VP, _VP]),
     "mi_rmsnorm_fwd_variant": (_I, [_I, _VP, _VP, _VP, _I64, _I64, _F, _VP, _VP]),
     "mi_copy_f32": (_I, [_VP, _VP, _I64, _VP]),
+    "mi_calib_launch": (_I, [_I, _VP, _VP, _I64, _VP]),
     "mi_norm_bwd_workspace_size": (_I64, [ctypes.POINTER(BwdProblem)]),
     "mi_norm_bwd": (_I, [ctypes.POINTER(BwdProblem), _VP]),
     "mi_norm_bwd_check": (_I, [ctypes.POINTER(BwdProblem)]),
@@ -118,11 +121,14 @@ _SIGNATURES = {
 }
 
 
-def header_functions() -> list[str]:
-    """Names of the functions include/mi_norm.h declares."""
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mi_\w+)\s*\(", text)))
+def header_functions(path: str | None = None) -> list[str]:
+    """Names of the functions a header declares: include/mi_norm.h and
+    include/mi_norm_tuning.h together by default."""
+    names = set()
+    for p in ([path] if path else [HEADER, TUNING_HEADER]):
+        text = re.sub(r"/\*.*?\*/", "", open(p).read(), flags=re.S)
+        names |= set(re.findall(r"\b(mi_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def lib() -> ctypes.CDLL:
@@ -265,6 +271,14 @@ def mi_copy_f32(src, dst, n: int, stream=None) -> None:
     _check(st, "mi_copy_f32")
 
 
+def mi_calib_launch(kind: int, src, dst, n: int, stream=None) -> None:
+    """A calibration launch (mi_norm_tuning.h): kind 0 empty, 1 read n float32
+    from src, 2 write n float32 to dst."""
+    st = lib().mi_calib_launch(kind, _ptr(src, "src", n if kind == 1 else None),
+                               _ptr(dst, "dst", n if kind == 2 else None), n, _stream(stream, src, dst))
+    _check(st, "mi_calib_launch")
+
+
 def mi_norm_status_string(status: int) -> str:
     return lib().mi_norm_status_string(status).decode()
 
@@ -385,29 +399,48 @@ def _dtype_code(t) -> int:
     return codes[t.dtype]
 
 
-def _rows_of(t, name: str) -> tuple[int, int]:
-    """(rows, row stride in elements) of a device tensor [..., d] whose last
-    dimension is contiguous and whose leading dimensions form one strided row
-    index; no copy is made."""
-    if not _is_tensor(t) or t.device.type != "cuda":
-        raise ValueError(f"{name} must be a device tensor")
-    if t.dim() == 0:
+def _row_geometry(shape, strides, name: str) -> tuple[int, int]:
+    """(rows, row stride in elements) of a tensor of ``shape``/``strides``
+    [..., d] whose last dimension is contiguous and whose leading dimensions
+    form one strided row index.  Rows that repeat one another (a leading
+    dimension expanded with stride 0) are refused: the C ABI reads a row
+    stride of 0 as d, so such rows would be addressed past the tensor's
+    storage."""
+    if len(shape) == 0:
         raise ValueError(f"{name} must have a last dimension")
-    d = t.shape[-1]
-    if d > 1 and t.stride(-1) != 1:
+    d = shape[-1]
+    if d > 1 and strides[-1] != 1:
         raise ValueError(f"{name}: the last dimension must be contiguous")
-    if t.dim() == 1:
+    if len(shape) == 1:
         return 1, d
-    lead = [(s, st) for s, st in zip(t.shape[:-1], t.stride()[:-1]) if s != 1]
+    lead = [(s, st) for s, st in zip(shape[:-1], strides[:-1]) if s != 1]
     rows = 1
     for s, _ in lead:
         rows *= s
     if not lead:
         return rows, d
+    if any(st == 0 for _, st in lead):
+        raise ValueError(f"{name}: rows repeat one another (a leading dimension has stride 0)")
     for (s0, st0), (s1, st1) in zip(lead, lead[1:]):
         if st0 != st1 * s1:
             raise ValueError(f"{name}: leading dimensions do not form one row stride")
     return rows, lead[-1][1]
+
+
+def _rows_of(t, name: str) -> tuple[int, int]:
+    """(rows, row stride in elements) of a device row tensor; no copy is made."""
+    if not _is_tensor(t) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    return _row_geometry(tuple(t.shape), tuple(t.stride()), name)
+
+
+def _input_rows(t):
+    """An input row tensor as the kernels can read it: one whose rows repeat
+    one another (stride 0, e.g. the upstream gradient of a sum over rows)
+    is made contiguous; anything else is passed as it is."""
+    if _is_tensor(t) and t.dim() > 1 and any(s != 1 and st == 0 for s, st in zip(t.shape[:-1], t.stride()[:-1])):
+        return t.contiguous()
+    return t
 
 
 def _params(t, name: str, d: int):
@@ -438,6 +471,9 @@ def _norm(op, x, r, p0, p1, eps, stats, out, write_sum, stream):
     import torch
     dt = _dtype_code(x)
     d = x.shape[-1]
+    if out is not None:
+        _rows_of(out, "out")   # an output is never copied: refuse repeating rows before any copy
+    x, r = _input_rows(x), _input_rows(r)
     rows, ldx = _rows_of(x, "x")
     ldr = 0
     if r is not None:
@@ -490,6 +526,9 @@ def _norm_bwd(op, dy, x, p0, mean, rstd, param_grads, out, stream):
     if dy.dtype != x.dtype or dy.shape != x.shape:
         raise ValueError("dy must have x's shape and dtype")
     d = x.shape[-1]
+    if out is not None:
+        _rows_of(out, "out")
+    dy, x = _input_rows(dy), _input_rows(x)
     rows, ldx = _rows_of(x, "x")
     lddy = _rows_of(dy, "dy")[1]
     ctx, handle = _on_stream(stream, x.device)

@@ -61,7 +61,7 @@ def torch_lib_dir() -> str:
 
 
 def source_paths() -> list[str]:
-    return [os.path.join(CSRC, s) for s in SOURCES + HEADERS] + [os.path.join(INCLUDE, "mi_norm.h")]
+    return [os.path.join(CSRC, s) for s in SOURCES + HEADERS] + [os.path.join(INCLUDE, h) for h in ("mi_norm.h", "mi_norm_tuning.h")]
 
 
 def _run(cmd: list[str], verbose: bool, stderr_to: str | None = None) -> None:

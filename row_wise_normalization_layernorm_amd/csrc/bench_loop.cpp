@@ -7,7 +7,7 @@
 // costs more than a kernel of a few microseconds.
 #include <cstdint>
 
-#include "mi_norm.h"
+#include "mi_norm_tuning.h"
 
 extern "C" {
 
@@ -130,6 +130,19 @@ int mi_bench_copy_loop(const float *const *srcs, float *const *dsts, int nsets, 
     for (int s = 0; s < steps; ++s) {
         const int k = s % nsets;
         const mi_norm_status st = mi_copy_f32(srcs[k], dsts[k], n, stream);
+        if (st != MI_NORM_OK) return st;
+    }
+    return MI_NORM_OK;
+}
+
+// The calibration launches of mi_calib_launch: kind 0 empty, 1 read srcs[k],
+// 2 write dsts[k] (n float32 each).
+int mi_bench_calib_loop(int kind, const float *const *srcs, float *const *dsts, int nsets, int64_t n,
+                        int steps, hipStream_t stream) {
+    for (int s = 0; s < steps; ++s) {
+        const int k = s % nsets;
+        const mi_norm_status st =
+            mi_calib_launch(kind, srcs ? srcs[k] : nullptr, dsts ? dsts[k] : nullptr, n, stream);
         if (st != MI_NORM_OK) return st;
     }
     return MI_NORM_OK;

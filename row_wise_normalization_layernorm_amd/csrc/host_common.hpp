@@ -5,7 +5,7 @@
 
 #include <cstdint>
 
-#include "mi_norm.h"
+#include "mi_norm_tuning.h"
 #include "variant_table.hpp"
 
 namespace minorm {

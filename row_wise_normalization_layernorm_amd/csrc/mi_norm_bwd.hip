@@ -14,7 +14,7 @@
 
 #include "bwd_kernels.hpp"
 #include "host_common.hpp"
-#include "mi_norm.h"
+#include "mi_norm_tuning.h"
 
 using namespace minorm;
 using namespace minorm::host;

@@ -743,9 +743,11 @@ void norm_aligned(NormParams p)
 
     float mu, rs;
     if constexpr (OP == OP_LN) {
+        // slots past the row read zero through the range check; masking
+        // them anyway keeps the sums independent of that behaviour
         float s = 0.f;
 #pragma unroll
-        for (int q = 0; q < Q; ++q) s += hsum(v[q]);
+        for (int q = 0; q < Q; ++q) s += ok[q] ? hsum(v[q]) : 0.f;
         const float S = group_sum<64>(s);
         float mu_w;
         if constexpr (WPR == 1) {
@@ -790,7 +792,7 @@ void norm_aligned(NormParams p)
     } else {
         float s2 = 0.f;
 #pragma unroll
-        for (int q = 0; q < Q; ++q) s2 += sq(v[q]);
+        for (int q = 0; q < Q; ++q) s2 += ok[q] ? sq(v[q]) : 0.f;
         float S2 = group_sum<64>(s2);
         if constexpr (WPR > 1) {
             if (lane == 0) xch[rib][wr] = make_float2(S2, 0.f);

@@ -8,7 +8,7 @@
 #include <climits>
 #include <cstdint>
 
-#include "mi_norm.h"
+#include "mi_norm_tuning.h"
 #include "norm_kernels.hpp"
 
 namespace minorm {

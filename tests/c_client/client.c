@@ -1,4 +1,5 @@
-/* A C99 caller of libmi_norm.so through include/mi_norm.h alone.
+/* A C99 caller of libmi_norm.so through its headers alone: the operations of
+ * include/mi_norm.h, and the variant queries of include/mi_norm_tuning.h.
  *
  *   client layout            struct sizes and member offsets, one per line
  *   client host              results of the host-only calls (no device use)
@@ -19,6 +20,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include "mi_norm.h"
+#include "mi_norm_tuning.h"
 
 #define FIELD(T, m) printf("%s.%s %zu\n", #T, #m, offsetof(T, m))
 

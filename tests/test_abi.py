@@ -34,16 +34,33 @@ def test_exports_every_declared_symbol(L):
     declared = B.header_functions()
     assert {"mi_layernorm_fwd", "mi_rmsnorm_fwd", "mi_norm_status_string"} <= set(declared)
     for name in declared:
-        assert hasattr(L, name), f"{name} declared in mi_norm.h but not exported"
+        assert hasattr(L, name), f"{name} declared in mi_norm.h or mi_norm_tuning.h but not exported"
     nm = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True,
                         check=True).stdout
     exported = {l.split()[-1] for l in nm.splitlines() if " T " in l and l.split()[-1].startswith("mi_")}
     assert exported == set(declared), exported ^ set(declared)
 
 
-def test_header_compiles_as_plain_c():
+def test_public_header_holds_the_interface_only():
+    """mi_norm.h declares the operations and their checks; the variant table,
+    forced variants and calibration kernels live in mi_norm_tuning.h."""
+    public = set(B.header_functions(B.HEADER))
+    tuning = set(B.header_functions(B.TUNING_HEADER))
+    assert public == {
+        "mi_norm_status_string", "mi_norm_version", "mi_layernorm_fwd", "mi_rmsnorm_fwd",
+        "mi_add_layernorm_fwd", "mi_add_rmsnorm_fwd", "mi_norm_fwd", "mi_norm_check",
+        "mi_norm_bwd_workspace_size", "mi_norm_bwd", "mi_norm_bwd_check", "mi_layernorm_bwd",
+        "mi_rmsnorm_bwd"}, public
+    assert not public & tuning
+    assert {"mi_norm_select", "mi_norm_fwd_variant", "mi_norm_bwd_variant", "mi_copy_f32",
+            "mi_calib_launch"} <= tuning
+
+
+@pytest.mark.parametrize("header", ["mi_norm.h", "mi_norm_tuning.h"])
+def test_header_compiles_as_plain_c(header):
     r = subprocess.run(["gcc", "-std=c99", "-fsyntax-only", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
-                        "-I/opt/rocm/include", "-x", "c", os.path.join(ROOT, "include", "mi_norm.h")],
+                        "-I/opt/rocm/include", "-I", os.path.join(ROOT, "include"), "-x", "c",
+                        os.path.join(ROOT, "include", header)],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
 
@@ -116,6 +133,34 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(4, 8)
     with pytest.raises(ValueError):
         mn.mi_layernorm_fwd(x, torch.ones(8), torch.zeros(8), x, 4, 8)
+
+
+def test_row_geometry_of_torch_layouts():
+    """The row count and stride the torch conveniences hand the C ABI, from a
+    tensor's shape and strides; rows that repeat one another (stride 0, as
+    in the upstream gradient of a sum over rows) are refused rather than
+    passed as a stride of 0, which the ABI reads as d, and the binding
+    copies such an input before it reaches the ABI."""
+    import torch
+    assert B._row_geometry((4096, 768), (768, 1), "x") == (4096, 768)
+    assert B._row_geometry((64, 768), (1024, 1), "x") == (64, 1024)       # column slice
+    assert B._row_geometry((3, 97, 768), (97 * 1024, 1024, 1), "x") == (291, 1024)
+    assert B._row_geometry((1, 5, 768), (0, 768, 1), "x") == (5, 768)      # size-1 dims carry no stride
+    assert B._row_geometry((768,), (1,), "x") == (1, 768)
+    for shape, strides in (((64, 768), (0, 1)), ((2, 3, 768), (0, 0, 1)), ((2, 3, 768), (768, 0, 1))):
+        with pytest.raises(ValueError, match="repeat"):
+            B._row_geometry(shape, strides, "dy")
+    with pytest.raises(ValueError):
+        B._row_geometry((64, 768), (768, 2), "x")                          # last dimension strided
+    with pytest.raises(ValueError):
+        B._row_geometry((2, 3, 768), (4 * 768, 768 + 1, 1), "x")           # no single row stride
+    # the loss sum(0)-then-square hands backward a dy of strides (0, 1)
+    dy = torch.ones(768).expand(64, 768)
+    assert dy.stride() == (0, 1)
+    fixed = B._input_rows(dy)
+    assert fixed.is_contiguous() and torch.equal(fixed, dy)
+    plain = torch.zeros(64, 1024)[:, :768]
+    assert B._input_rows(plain) is plain and B._input_rows(None) is None
 
 
 def test_binding_raises_status(L):

@@ -123,3 +123,33 @@ def test_side_streams_give_the_default_streams_results(torch_dev):
         side.synchronize()
         for a, c in zip((y0, m0, r0) + tuple(b0), (y1, m1, r1) + tuple(b1)):
             assert torch.equal(a, c)
+
+
+def test_expanded_upstream_gradient_and_inputs(torch_dev):
+    """A loss that sums over rows hands the backward an upstream gradient
+    whose rows repeat (stride 0); the binding copies such an input rather
+    than pass a row stride the kernels would read as d.  An expanded x in
+    the forward is copied the same way, and an expanded output is refused."""
+    torch, dev = torch_dev
+    print("autograd expanded dy [256x768]", flush=True)
+    x = (torch.randn(256, 768, device=dev) * 3 + 0.5).requires_grad_(True)
+    g = (torch.randn(768, device=dev) * 0.1 + 1).requires_grad_(True)
+    b = (torch.randn(768, device=dev) * 0.1).requires_grad_(True)
+    y = mn.layer_norm(x, g, b)
+    y.sum(0).pow(2).sum().backward()
+    torch.cuda.synchronize()
+    # the same loss through torch's own float64 layer norm on the CPU
+    xd = x.detach().cpu().double().requires_grad_(True)
+    gd = g.detach().cpu().double().requires_grad_(True)
+    bd = b.detach().cpu().double().requires_grad_(True)
+    torch.nn.functional.layer_norm(xd, (768,), gd, bd, 1e-5).sum(0).pow(2).sum().backward()
+    for got, want in ((x.grad, xd.grad), (g.grad, gd.grad), (b.grad, bd.grad)):
+        err = (got.cpu().double() - want).abs()
+        assert bool((err <= 1e-4 + 1e-3 * want.abs()).all()), float(err.max())
+
+    row = torch.randn(1, 768, device=dev)
+    xe = row.expand(64, 768)
+    ye = mn.layernorm(xe, g.detach(), b.detach())
+    assert torch.equal(ye, mn.layernorm(xe.contiguous(), g.detach(), b.detach()))
+    with pytest.raises(ValueError):
+        mn.layernorm(torch.randn(64, 768, device=dev), g.detach(), b.detach(), out=torch.empty(1, 768, device=dev).expand(64, 768))

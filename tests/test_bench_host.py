@@ -33,12 +33,38 @@ def test_algorithmic_bytes():
 
 def test_every_workload_is_described_and_sized():
     for name, wk in bench.BENCH_WORKLOADS.items():
+        if wk.op == "empty":
+            assert bench.algorithmic_bytes(wk.op, wk.rows, wk.d, wk.stats) == 0
+            assert "empty kernel" in bench.describe(wk.op, wk.rows, wk.d, wk.stats)
+            continue
         assert bench.algorithmic_bytes(wk.op, wk.rows, wk.d, wk.stats, wk.storage) > 0, name
         desc = bench.describe(wk.op, wk.rows, wk.d, wk.stats, wk.storage, wk.pad)
         assert f"[{wk.rows},{wk.d}]" in desc or "bytes of" in desc, (name, desc)
         assert bench.direction_of(name) == ("bwd" if wk.op.endswith("_bwd") else "fwd")
     # the default workload is the headline: LayerNorm FP32 [4096,768] with mean/rstd
     assert bench.BENCH_WORKLOADS["ln_4096x768"] == bench.W("layernorm", "f32", 4096, 768, "normal", True)
+
+
+def test_trace_pairing(tmp_path, monkeypatch):
+    """Per-dispatch kernel times count only for the kernel sources and the
+    variant the trace was taken with, as the counters do."""
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    for rel in set(bench.KERNEL_SOURCES["fwd"] + bench.KERNEL_SOURCES["bwd"]):
+        dst = tmp_path / rel
+        dst.parent.mkdir(parents=True, exist_ok=True)
+        dst.write_bytes(open(os.path.join(ROOT, rel), "rb").read())
+    h = bench.kernel_source_hash("fwd")
+    f = tmp_path / "profiles" / "trace_ln_4096x768.txt"
+    body = ("dispatch_us_median: 5.3\ndispatch_us_min: 4.9\ndispatch_us_max: 6.7\n"
+            "dispatch_us_mean: 5.6\ndispatches: 100\n")
+    f.write_text(f"kernel_variant: ln_4_p0_l64_w1_q3_b16\nkernel_source_sha256: {h}\n" + body)
+    got = bench.trace_stats("ln_4096x768", "ln_4_p0_l64_w1_q3_b16")
+    assert got["median"] == 5.3 and got["min"] == 4.9 and got["max"] == 6.7 and got["dispatches"] == 100
+    assert bench.trace_stats("ln_4096x768", "ln_4_p0_l64_w1_q3_b4") is None        # another variant
+    f.write_text("kernel_variant: ln_4_p0_l64_w1_q3_b16\nkernel_source_sha256: 0000000000000000\n" + body)
+    assert bench.trace_stats("ln_4096x768", "ln_4_p0_l64_w1_q3_b16") is None       # kernels changed
+    assert bench.trace_stats("rms_4096x768", "x") is None                           # no trace
 
 
 def test_profile_pairing(tmp_path, monkeypatch):

@@ -1,5 +1,5 @@
 """The C ABI from plain C: tests/c_client/client.c includes only
-include/mi_norm.h (and HIP's C runtime header), links libmi_norm.so, and is
+include/mi_norm.h, include/mi_norm_tuning.h (and HIP's C runtime header), links libmi_norm.so, and is
 compiled here with gcc -std=c99 -Werror.  On the CPU its struct layouts and
 the host-only calls must agree with the Python binding; on the GPU it runs
 LayerNorm (named call) and bfloat16 fused add + RMSNorm (general call) and
