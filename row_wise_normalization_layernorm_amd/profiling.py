@@ -1,7 +1,20 @@
-"""Summarize rocprofv3 output (kernel trace + stats, or counter collection).
+"""Collect and summarize rocprofv3 profiles of bench.py workloads.
 
+    python -m row_wise_normalization_layernorm_amd.profiling collect OUT WORKLOAD [WORKLOAD ...]
     python -m row_wise_normalization_layernorm_amd.profiling trace DIR PREFIX [--skip S] [--last N]
     python -m row_wise_normalization_layernorm_amd.profiling pmc DIR PREFIX COUNTER
+
+``collect`` runs, for each workload, three rocprofv3 passes over
+``bench.py --profile`` (the parity call, W warm-up steps and one span of K
+timed steps, nothing else): a kernel trace with statistics, then the
+FETCH_SIZE and WRITE_SIZE counters each in a run of its own; plus the same
+counter passes over the calibration copy copy_4096x4096 (64 MiB read, 64 MiB
+written), whose known bytes scale the counters to bytes.  It writes
+OUT/<workload>.txt: the commands, the per-dispatch durations of the timed
+steps per kernel, the counter means of the main kernel, HBM bytes per
+launch, and machine-readable lines that bench.py pairs with a run (kernel
+variant and kernel-source hash).  It must run where a GPU is visible; it
+touches the GPU only through the child processes it starts.
 
 ``trace`` reads ``PREFIX_kernel_stats.csv`` and ``PREFIX_kernel_trace.csv``
 (``rocprofv3 --kernel-trace --stats --output-format csv``) and prints, per
@@ -56,9 +69,155 @@ def pmc_means(directory: str, prefix: str, counter: str) -> dict:
     return {k: (statistics.mean(v), len(v)) for k, v in per.items()}
 
 
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+_SKIP = ("spin_kernel", "__amd_rocclr", "elementwise", "fill", "copy_", "reduce_kernel")
+
+
+def _run(cmd: list[str], log: str, timeout: int = 300) -> str:
+    """Run a rocprofv3 pass (the program right after --, no re-exec), return stdout."""
+    import subprocess
+    print("+ " + " ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=timeout, cwd="/tmp",
+                       env={**os.environ, "TMPDIR": "/tmp"})
+    with open(log, "a") as f:
+        f.write("$ " + " ".join(cmd) + "\n" + r.stdout + r.stderr + "\n")
+    if r.returncode != 0:
+        raise RuntimeError(f"rocprofv3 pass failed ({r.returncode}); see {log}")
+    return r.stdout
+
+
+def _bench_line(stdout: str) -> dict:
+    import json
+    for line in reversed(stdout.splitlines()):
+        if line.startswith("{"):
+            return json.loads(line)
+    raise RuntimeError("bench.py printed no JSON line")
+
+
+def _kernel_durations(directory: str, prefix: str) -> dict:
+    rows = list(csv.DictReader(open(os.path.join(directory, f"{prefix}_kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    per = defaultdict(list)
+    for r in rows:
+        per[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return per
+
+
+def _find_csv(base: str, suffix: str) -> tuple[str, str]:
+    """(directory, prefix) of the rocprofv3 csv under base ending in suffix."""
+    for d, _, files in os.walk(base):
+        for f in files:
+            if f.endswith(suffix):
+                return d, f[: -len(suffix)]
+    raise RuntimeError(f"no *{suffix} under {base}")
+
+
+def collect(out: str, workloads: list[str], steps: int = 100, warmup: int = 20, pmc_steps: int = 20,
+            pmc_warmup: int = 5) -> None:
+    os.makedirs(out, exist_ok=True)
+    raw = os.path.join(out, "raw")
+    os.makedirs(raw, exist_ok=True)
+    log = os.path.join(out, "collect.log")
+    py = sys.executable
+    bench = os.path.join(ROOT, "bench.py")
+
+    def pmc_pass(w: str, counter: str) -> tuple[dict, str]:
+        d = os.path.join(raw, f"pmc_{w}_{counter}")
+        cmd = ["rocprofv3", "--pmc", counter, "--output-format", "csv", "-d", d, "-o", "p", "--", py, "-u",
+               bench, "--profile", "--workload", w, "--steps", str(pmc_steps), "--warmup", str(pmc_warmup),
+               "--no-cpu-baseline"]
+        _run(cmd, log)
+        dd, pre = _find_csv(d, "_counter_collection.csv")
+        return pmc_means(dd, pre, counter), " ".join(cmd)
+
+    # the calibration: counter KiB per dispatch against the copy's known bytes
+    cal = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        means, _ = pmc_pass("copy_4096x4096", counter)
+        kib = max(means.values(), key=lambda t: t[1])[0]
+        cal[counter] = (4096 * 4096 * 4 / 1024) / kib   # true KiB / counter KiB
+    print(f"calibration: fetch x{cal['FETCH_SIZE']:.4f}, write x{cal['WRITE_SIZE']:.4f}", flush=True)
+
+    for w in workloads:
+        d = os.path.join(raw, f"trace_{w}")
+        tcmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", d, "-o", "t", "--", py,
+                "-u", bench, "--profile", "--workload", w, "--steps", str(steps), "--warmup", str(warmup),
+                "--no-cpu-baseline"]
+        line = _bench_line(_run(tcmd, log))
+        dd, pre = _find_csv(d, "_kernel_trace.csv")
+        per = _kernel_durations(dd, pre)
+        ours = {k: v for k, v in per.items() if not any(s_ in k for s_ in _SKIP) or "minorm" in k or "norm" in k}
+        total = 1 + warmup + steps
+        table = ["kernel | dispatches | window | mean us | median us | min us | max us"]
+        main_k, main_win = None, None
+        for name, ds in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            win = ds[-steps:] if len(ds) == total else ds
+            table.append(f"{_short(name)} | {len(ds)} | {len(win)} | {statistics.mean(win):.3f} | "
+                         f"{statistics.median(win):.3f} | {min(win):.3f} | {max(win):.3f}")
+            if name in ours and len(ds) == total and (main_k is None or sum(win) > sum(main_win)):
+                main_k, main_win = name, win
+        step_kernels = [n for n, ds in ours.items() if len(ds) == total]
+        step_win = [sum(per[n][-steps + i] for n in step_kernels) for i in range(steps)] if step_kernels else []
+        counters = {}
+        cmds = [" ".join(tcmd)]
+        if main_k is not None:
+            for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+                means, c = pmc_pass(w, counter)
+                cmds.append(c)
+                counters[counter] = means.get(main_k, (float("nan"), 0))
+        alg = line["roofline"]["algorithmic_bytes_per_launch"]
+        traffic = None
+        if counters and all(n for _, n in counters.values()):
+            traffic = int(round(sum(counters[c][0] * 1024 * cal[c] for c in counters)))
+        text = [f"# rocprofv3 profile — {line['config']['workload']}", "",
+                f"Workload: bench.py --workload {w} --profile (rotate mode, {line['config']['buffer_sets']} "
+                f"buffer set(s)); kernel arguments in device memory (HIP_FORCE_DEV_KERNARG="
+                f"{line['config'].get('hip_force_dev_kernarg')}).",
+                f"Each pass: 1 parity-gate call, {warmup} warm-up steps, then one span of {steps} timed steps "
+                f"(counter passes: {pmc_warmup} and {pmc_steps}).  The window is the last {steps} dispatches "
+                "of each kernel a step launches.", "",
+                "Commands (run from /tmp with TMPDIR=/tmp; R = repository root):"]
+        text += ["    " + c.replace(ROOT, "R").replace(py, "python3") for c in cmds]
+        text += ["", "Per-dispatch durations (kernel trace):"] + ["  " + t for t in table]
+        if step_win:
+            text += ["", f"Per step, the sum of the step's kernels ({len(step_kernels)}): median "
+                         f"{statistics.median(step_win):.3f} us, mean {statistics.mean(step_win):.3f} us"]
+        text += ["", f"bench.py line of the traced run: span {line['span_us_per_step']} us per step "
+                     "(stream events; tracer gaps between dispatches included)."]
+        if counters:
+            text += ["", f"Counters of {_short(main_k)} (KiB per dispatch, mean over the dispatches):"]
+            for c in counters:
+                text.append(f"  {c} {counters[c][0]:.1f} over {counters[c][1]} dispatches (x{cal[c]:.4f} "
+                            "from the calibration copy copy_4096x4096)")
+            if traffic:
+                text.append(f"HBM bytes per launch {traffic}; algorithmic bytes {alg} (ratio {traffic / alg:.4f})"
+                            if alg else f"HBM bytes per launch {traffic}")
+        med = statistics.median(main_win) if main_win else None
+        text += ["", f"kernel_variant: {line['config']['variant']}",
+                 f"kernel_source_sha256: {line['kernel_source_sha256']}"]
+        if main_win:
+            text += [f"kernel: {_short(main_k)}",
+                     f"dispatch_us_median: {med:.3f}", f"dispatch_us_min: {min(main_win):.3f}",
+                     f"dispatch_us_max: {max(main_win):.3f}", f"dispatch_us_mean: {statistics.mean(main_win):.3f}",
+                     f"dispatches: {len(main_win)}"]
+            if step_win and len(step_kernels) > 1:
+                text.append(f"step_us_median: {statistics.median(step_win):.3f}")
+        if traffic:
+            text.append(f"traffic_bytes_per_launch: {traffic}")
+        text.append(f"algorithmic_bytes_per_launch: {alg}")
+        with open(os.path.join(out, f"{w}.txt"), "w") as f:
+            f.write("\n".join(text) + "\n")
+        print(f"{w}: median {med} us, traffic {traffic}", flush=True)
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
+    c = sub.add_parser("collect")
+    c.add_argument("out")
+    c.add_argument("workloads", nargs="+")
+    c.add_argument("--steps", type=int, default=100)
+    c.add_argument("--warmup", type=int, default=20)
     t = sub.add_parser("trace")
     t.add_argument("dir")
     t.add_argument("prefix")
@@ -69,6 +228,9 @@ def main(argv=None) -> int:
     p.add_argument("prefix")
     p.add_argument("counter")
     a = ap.parse_args(argv)
+    if a.cmd == "collect":
+        collect(a.out, a.workloads, a.steps, a.warmup)
+        return 0
     if a.cmd == "trace":
         print(trace_summary(a.dir, a.prefix, a.last, a.skip))
     else:

@@ -283,6 +283,42 @@ def test_bwd_deterministic(torch_dev):
             assert torch.equal(a, b)
 
 
+def test_bwd_workspace_reused_across_shapes(torch_dev):
+    """One workspace serves calls of several shapes in turn, each matching
+    the oracle: nothing a call leaves in the workspace leaks into the next
+    one's results (the last call repeats the first shape with new inputs)."""
+    torch, dev = torch_dev
+    say("bwd one workspace, several shapes")
+    cases = [("layernorm", 4096, 768), ("rmsnorm", 3000, 2048), ("layernorm", 2048, 4096),
+             ("layernorm", 300, 1024), ("rmsnorm", 4096, 768), ("layernorm", 4096, 768)]
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    most = 0
+    for op, rows, d in cases:
+        # the size depends on the op, shape and which gradients are wanted
+        # (non-null), not on the addresses
+        p = mn.bwd_problem(OPS[op], rows, d, 0, 0, 0, 0, 0, 0, 256, 256 if op == "layernorm" else None)
+        most = max(most, mn.mi_norm_bwd_workspace_size(p))
+    WS = torch.full((most,), 0x7F, dtype=torch.uint8, device=dev)   # contents on entry do not matter
+    for k, (op, rows, d) in enumerate(cases):
+        say(f"  {op} [{rows},{d}]")
+        dy, x, p0, mean, rstd = bwd_inputs(op, mn.MI_NORM_F32, rows, d, "offset", [44, k])
+        ln = op == "layernorm"
+        DY, X, P0, S = t(dy), t(x), t(p0), t(rstd)
+        M = t(mean) if ln else None
+        DX, DG = torch.empty_like(X), torch.empty(d, device=dev)
+        DB = torch.empty(d, device=dev) if ln else None
+        p = mn.bwd_problem(OPS[op], rows, d, DY, X, DX, P0, M, S, DG, DB)
+        p.workspace, p.workspace_bytes = WS.data_ptr(), most
+        mn.mi_norm_bwd(p)
+        torch.cuda.synchronize()
+        ref = bwd_ref(op, mn.MI_NORM_F32, dy, x, p0, mean, rstd)
+        assert oracle.dx_tolerance_ok(DX.cpu().numpy(), ref["dx64"], ref["dx_scale"])[0]
+        key = "dgamma" if ln else "dw"
+        assert oracle.colsum_tolerance_ok(DG.cpu().numpy(), ref[key + "64"], ref["abs_" + key])[0]
+        if ln:
+            assert oracle.colsum_tolerance_ok(DB.cpu().numpy(), ref["dbeta64"], ref["abs_dbeta"])[0]
+
+
 @pytest.mark.parametrize("dt", DTS)
 def test_bwd_full_size(torch_dev, dt):
     """[32768, 8192] through the dispatcher: dx on sampled rows and every
