@@ -262,6 +262,26 @@ mi_norm_status mi_norm_bwd(const mi_norm_bwd_problem *p, hipStream_t stream);
 /* The argument checks of mi_norm_bwd alone (nothing launched). */
 mi_norm_status mi_norm_bwd_check(const mi_norm_bwd_problem *p);
 
+/* mi_norm_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and results, with the workspace taken from a scratch array
+ * the library holds on each GPU (32 MiB, held from the library's first use
+ * on that GPU until the process ends) instead of the caller's.
+ * p->workspace must be NULL and p->workspace_bytes 0.  Returns
+ * MI_NORM_ERR_INVALID, launching nothing, when the problem needs more
+ * workspace than the array holds (mi_norm_bwd_workspace_size(p) >
+ * mi_norm_bwd_noalloc_limit(): LayerNorm with d up to 8192 fits for up to
+ * 2 million rows) and MI_NORM_ERR_HIP when the array's address cannot be
+ * had.  The stream must belong to the current device.  The call allocates
+ * and frees nothing.  Every call on one GPU shares that GPU's array, whose
+ * contents on entry do not matter: calls that overlap in time on one GPU
+ * (different streams, or host threads) race on it and must be serialized by
+ * the caller. */
+mi_norm_status mi_norm_bwd_noalloc(const mi_norm_bwd_problem *p, hipStream_t stream);
+
+/* Bytes of the scratch array mi_norm_bwd_noalloc uses (33554432). */
+int64_t mi_norm_bwd_noalloc_limit(void);
+
 /* The float32 contiguous forms (row stride d). */
 mi_norm_status mi_layernorm_bwd(const float *dy, const float *x, const float *gamma,
                                 const float *mean, const float *rstd, float *dx,

@@ -27,6 +27,8 @@ from ._binding import (  # noqa: F401
     mi_norm_bwd,
     mi_norm_bwd_check,
     mi_norm_bwd_eligible,
+    mi_norm_bwd_noalloc,
+    mi_norm_bwd_noalloc_limit,
     mi_norm_bwd_select,
     mi_norm_bwd_variant,
     mi_norm_bwd_workspace_size,

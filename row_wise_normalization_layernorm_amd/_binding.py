@@ -112,6 +112,8 @@ _SIGNATURES = {
     "mi_calib_launch": (_I, [_I, _VP, _VP, _I64, _VP]),
     "mi_norm_bwd_workspace_size": (_I64, [ctypes.POINTER(BwdProblem)]),
     "mi_norm_bwd": (_I, [ctypes.POINTER(BwdProblem), _VP]),
+    "mi_norm_bwd_noalloc": (_I, [ctypes.POINTER(BwdProblem), _VP]),
+    "mi_norm_bwd_noalloc_limit": (_I64, []),
     "mi_norm_bwd_check": (_I, [ctypes.POINTER(BwdProblem)]),
     "mi_norm_bwd_select": (_I, [ctypes.POINTER(BwdProblem)]),
     "mi_norm_bwd_eligible": (_I, [_I, ctypes.POINTER(BwdProblem)]),
@@ -352,6 +354,16 @@ def mi_norm_bwd_workspace_size(p: BwdProblem) -> int:
 
 def mi_norm_bwd(p: BwdProblem, stream=None) -> None:
     _check(lib().mi_norm_bwd(ctypes.byref(p), _stream(stream)), "mi_norm_bwd")
+
+
+def mi_norm_bwd_noalloc(p: BwdProblem, stream=None) -> None:
+    """mi_norm_bwd with the library's own scratch array as the workspace
+    (p.workspace None, p.workspace_bytes 0); allocates nothing."""
+    _check(lib().mi_norm_bwd_noalloc(ctypes.byref(p), _stream(stream)), "mi_norm_bwd_noalloc")
+
+
+def mi_norm_bwd_noalloc_limit() -> int:
+    return int(lib().mi_norm_bwd_noalloc_limit())
 
 
 def mi_norm_bwd_check(p: BwdProblem) -> int:

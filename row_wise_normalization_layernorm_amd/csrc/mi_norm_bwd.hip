@@ -8,9 +8,11 @@
 // and a column-chunk kernel in place of the row kernel.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "bwd_kernels.hpp"
 #include "host_common.hpp"
@@ -18,6 +20,13 @@
 
 using namespace minorm;
 using namespace minorm::host;
+
+// The workspace of mi_norm_bwd_noalloc: one array per GPU, held from the
+// moment the library's code is loaded on that GPU until the process ends.
+// Host code never uses this name as an address: each device's address comes
+// from hipGetSymbolAddress (scratch_ptr below).
+constexpr int64_t kScratchBytes = int64_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -80,6 +89,14 @@ bool bshape_ok(const mi_norm_bwd_problem &P) {
 }
 
 int64_t workspace_needed(const mi_norm_bwd_problem &P) { return part_bytes(P) + stats_bytes(P); }
+
+// the workspace bytes of *p, or -1 when its op, type or shape is invalid
+int64_t workspace_needed_checked(const mi_norm_bwd_problem &P) {
+    if ((P.op != MI_NORM_OP_LAYERNORM && P.op != MI_NORM_OP_RMSNORM) || P.dtype < 0 || P.dtype >= kDtypes ||
+        P.d < 1 || P.d > INT32_MAX || P.rows < 0 || P.rows > INT64_MAX / 64)
+        return -1;
+    return workspace_needed(P);
+}
 
 // every row tensor 16-byte aligned, strides and d multiples of the vector
 // width, gamma (w) 16-byte aligned: the vector path
@@ -334,15 +351,45 @@ mi_norm_bwd_problem make_bwd(int op, const float *dy, const float *x, const floa
     return P;
 }
 
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The address of the scratch array on the current device, looked up once
+// per device with that device current; nullptr when it cannot be had.
+void *scratch_ptr() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
 
+mi_norm_status mi_norm_bwd_noalloc(const mi_norm_bwd_problem *p, hipStream_t stream) {
+    if (!p || p->workspace || p->workspace_bytes) return MI_NORM_ERR_INVALID;
+    const int64_t need = workspace_needed_checked(*p);
+    if (need < 0 || need > kScratchBytes) return MI_NORM_ERR_INVALID;
+    mi_norm_bwd_problem q = *p;
+    q.workspace = scratch_ptr();
+    if (!q.workspace) return MI_NORM_ERR_HIP;
+    q.workspace_bytes = kScratchBytes;
+    return run_bwd(-1, q, stream);
+}
+
+int64_t mi_norm_bwd_noalloc_limit(void) { return kScratchBytes; }
+
 int64_t mi_norm_bwd_workspace_size(const mi_norm_bwd_problem *p) {
-    if (!p || (p->op != MI_NORM_OP_LAYERNORM && p->op != MI_NORM_OP_RMSNORM) || p->dtype < 0 ||
-        p->dtype >= kDtypes || p->d < 1 || p->d > INT32_MAX || p->rows < 0 || p->rows > INT64_MAX / 64)
-        return -1;
-    return workspace_needed(*p);
+    return p ? workspace_needed_checked(*p) : -1;
 }
 
 mi_norm_status mi_norm_bwd(const mi_norm_bwd_problem *p, hipStream_t stream) {

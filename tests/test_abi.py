@@ -50,7 +50,7 @@ def test_public_header_holds_the_interface_only():
         "mi_norm_status_string", "mi_norm_version", "mi_layernorm_fwd", "mi_rmsnorm_fwd",
         "mi_add_layernorm_fwd", "mi_add_rmsnorm_fwd", "mi_norm_fwd", "mi_norm_check",
         "mi_norm_bwd_workspace_size", "mi_norm_bwd", "mi_norm_bwd_check", "mi_layernorm_bwd",
-        "mi_rmsnorm_bwd"}, public
+        "mi_rmsnorm_bwd", "mi_norm_bwd_noalloc", "mi_norm_bwd_noalloc_limit"}, public
     assert not public & tuning
     assert {"mi_norm_select", "mi_norm_fwd_variant", "mi_norm_bwd_variant", "mi_copy_f32",
             "mi_calib_launch"} <= tuning
