@@ -67,6 +67,9 @@ struct NormParams {
     int32_t d;
     float eps;
     float inv_d;       // 1/d rounded to float32
+    int32_t peel_align;  // peeled rows: the body starts on a multiple of this
+                         // many elements (16 bytes', or 128 bytes' when every
+                         // row tensor shares its phase within a cache line)
 };
 
 // ---------------------------------------------------------------------------
@@ -280,6 +283,12 @@ __device__ __forceinline__ float sq(f8 v) { return sq(v.lo) + sq(v.hi); }
 
 __device__ __forceinline__ float rsq(float v) { return __builtin_amdgcn_rsqf(v); }
 
+// an empty asm that takes v: the value must exist here (its load has
+// returned), and nothing computed from it moves above this point
+template <typename V>
+__device__ __forceinline__ void keep(V &v) { asm volatile("" : "+v"(v)); }
+
+
 // ---------------------------------------------------------------------------
 // Held-row kernel.
 //
@@ -290,9 +299,11 @@ __device__ __forceinline__ float rsq(float v) { return __builtin_amdgcn_rsqf(v);
 //          d % VEC == 0 and rows aligned to an access - or 1 (any d, any
 //          element alignment)
 //   PEEL   VEC > 1 only: per row, scalar head elements up to the row's first
-//          access boundary, a vector body, and a scalar tail; needs every
-//          row tensor in the same phase modulo an access, any d; gamma/beta
-//          are then read as scalars since their phase follows the row's
+//          p.peel_align boundary (16 bytes, or a 128-byte cache line), a
+//          vector body, and a scalar tail; needs every row tensor in the
+//          same phase modulo that boundary and d >= 128 (the body is never
+//          empty); gamma/beta are read unaligned since their phase follows
+//          the row's
 //   LPR    lanes of one wave sharing a row (16, 32, 64); 64 / LPR rows per wave
 //   WPR    waves sharing a row (LPR == 64 when WPR > 1)
 //   Q      accesses held per lane; capacity = VEC * LPR * WPR * Q elements
@@ -381,19 +392,21 @@ void norm_held(NormParams p)
         const T *rr = RES ? static_cast<const T *>(p.r) + row * p.ldr : nullptr;
         T *hr = (RES && p.h) ? static_cast<T *>(p.h) + row * p.ldh : nullptr;
 
-        // row geometry: h head scalars, nvec body accesses, t tail scalars
+        // row geometry: h head scalars, nvec body accesses, t tail scalars.
+        // A peeled row's body starts on a multiple of A elements (a 16-byte
+        // access, or a 128-byte cache line, so that each wave-wide access
+        // covers whole lines); h < A <= 64 head elements go to the lanes of
+        // wave 0, and the body holds at most d / VEC accesses.
         int h = 0, t = 0, nvec;
         if constexpr (PEEL) {
-            const int mis = (int)((reinterpret_cast<uintptr_t>(xr) / sizeof(T)) & (VEC - 1));
-            h = (VEC - mis) & (VEC - 1);
-            if (h > d) h = d;
-            nvec = (int)((unsigned)(d - h) / VEC);
+            const int A = p.peel_align;
+            const int mis = (int)((reinterpret_cast<uintptr_t>(xr) / sizeof(T)) & (A - 1));
+            h = (A - mis) & (A - 1);
+            nvec = (int)((unsigned)(d - h) / VEC);   // >= 1: d >= 128 > h + VEC
             t = d - h - VEC * nvec;
         } else {
             nvec = (int)((unsigned)d / VEC);  // >= 1 for these paths
         }
-        // only a peeled row narrower than 8 elements can have no body
-        const bool body = PEEL ? nvec > 0 : true;
 
         // 1. issue every load of the row before using any.  Lane li of wave
         // rank wr holds access k = li + LPR*(wr + WPR*q) of the body; an
@@ -409,18 +422,14 @@ void norm_held(NormParams p)
         VT v[Q];
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
-            VT raw = VT(0.f);
-            if (body) raw = ldv<T, VEC, NTL>(xr + h + VEC * kc[q]);
-            if constexpr (RES) {
-                VT rres = VT(0.f);
-                if (body) rres = ldv<T, VEC, NTL>(rr + h + VEC * kc[q]);
-                raw = as_stored<T>(raw + rres);
-            }
+            VT raw = ldv<T, VEC, NTL>(xr + h + VEC * kc[q]);
+            if constexpr (RES) raw = as_stored<T>(raw + ldv<T, VEC, NTL>(rr + h + VEC * kc[q]));
             v[q] = ok[q] ? raw : VT(0.f);
         }
         float hx = 0.f, tx = 0.f;
         bool hok = false, tok = false;
         int hi = 0, ti = 0;
+        float gh = 0.f, gt = 0.f, bh = 0.f, bt = 0.f;   // head/tail parameters
         if constexpr (PEEL) {
             hok = rv && wr == 0 && li < h;
             tok = rv && wr == 0 && li < t;
@@ -434,6 +443,14 @@ void norm_held(NormParams p)
             }
             hx = hok ? rh : 0.f;
             tx = tok ? rt : 0.f;
+            // fetched with the row: a load in the output pass would wait on
+            // the stores issued before it (vmcnt counts both)
+            gh = p.p0[hi];
+            gt = p.p0[ti];
+            if constexpr (OP == OP_LN) {
+                bh = p.p1[hi];
+                bt = p.p1[ti];
+            }
         }
         if constexpr (RES) {
             // the sums leave as soon as they exist, overlapping the reductions;
@@ -474,9 +491,8 @@ void norm_held(NormParams p)
         if constexpr (PRELOAD) {
 #pragma unroll
             for (int q = 0; q < Q; ++q) {
-                g[q] = VT(1.f);
                 b[q] = VT(0.f);
-                if (body) load_params(q, g[q], b[q]);
+                load_params(q, g[q], b[q]);
             }
         }
 
@@ -576,6 +592,22 @@ void norm_held(NormParams p)
         }
 
         if constexpr (PLDS && WPR == 1) __syncthreads();  // the LDS parameters are complete
+        if constexpr (PEEL && PRELOAD) {
+            // every load has returned before the first store, so the output
+            // pass holds no wait on a store still in flight: 7-9% on peeled
+            // rows ([256,8193])
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                keep(g[q]);
+                if constexpr (OP == OP_LN) keep(b[q]);
+            }
+            keep(gh);
+            keep(gt);
+            if constexpr (OP == OP_LN) {
+                keep(bh);
+                keep(bt);
+            }
+        }
         // 4. normalize, scale, shift; store from the same registers
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
@@ -584,8 +616,7 @@ void norm_held(NormParams p)
                 gq = g[q];
                 bq = b[q];
             } else {
-                gq = VT(1.f);
-                if (body) load_params(q, gq, bq);
+                load_params(q, gq, bq);
             }
             VT o;
             if constexpr (OP == OP_LN) o = (v[q] - mu) * rs * gq + bq;
@@ -593,9 +624,6 @@ void norm_held(NormParams p)
             if (ok[q]) stv<T, VEC, NTS>(yr + h + VEC * kc[q], o);
         }
         if constexpr (PEEL) {
-            const float gh = p.p0[hi], gt = p.p0[ti];
-            const float bh = (OP == OP_LN) ? p.p1[hi] : 0.f;
-            const float bt = (OP == OP_LN) ? p.p1[ti] : 0.f;
             const float oh = (OP == OP_LN) ? (hx - mu) * rs * gh + bh : hx * gh * rs;
             const float ot = (OP == OP_LN) ? (tx - mu) * rs * gt + bt : tx * gt * rs;
             if (hok) ste<T, false>(yr + hi, oh);
@@ -864,8 +892,6 @@ void norm_aligned(NormParams p)
 // within the workgroup's RPB rows; a row past the end re-reads the last row
 // and stores nothing.
 
-template <typename V>
-__device__ __forceinline__ void keep(V &v) { asm volatile("" : "+v"(v)); }
 
 template <typename T, int OP, int VEC, int WPR, int Q, int RV, int WAVES, bool RES>
 __global__ __launch_bounds__(WAVES * 64)

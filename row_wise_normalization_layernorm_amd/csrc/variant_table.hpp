@@ -69,7 +69,8 @@ inline const void *held_kernel() {
     Variant{OPN "_" #VEC "_p" #PEEL "_l" #LPR "_w" #WPR "_q" #Q "_b" #WAVES,                  \
             mi_norm_variant_info{OPC, DT, VEC, PEEL, 0, LPR, WPR, Q, WAVES,                     \
                                  (WPR == 1) ? WAVES * (64 / LPR) : WAVES / WPR,                 \
-                                 (int64_t)VEC * LPR * WPR * Q, (VEC > 1 && !PEEL) ? 1 : 0, 1},  \
+                                 (int64_t)VEC * LPR * WPR * Q + (PEEL ? VEC - 1 : 0),           \
+                                 (VEC > 1 && !PEEL) ? 1 : 0, 1},                                \
             held_kernel<T, kop(OPC), VEC, PEEL, LPR, WPR, Q, WAVES, kres(OPC)>()}
 
 // the same shape with 4 (or 8) and with 16 waves per workgroup

@@ -276,7 +276,9 @@ def test_variant_table_is_consistent(L):
         if v["looped"]:
             assert v["max_d"] == 2**63 - 1 and v["rows_per_block"] == 1
             continue
-        assert v["max_d"] == v["vec"] * v["lanes_per_row"] * v["waves_per_row"] * v["slots"]
+        # a peeled row holds its head and tail apart from the body
+        assert v["max_d"] == v["vec"] * v["lanes_per_row"] * v["waves_per_row"] * v["slots"] + (
+            v["vec"] - 1 if v["peel"] else 0)
         assert v["rows_per_lane"] in (1, 2), n
         if v["rows_per_lane"] == 2:
             # multi-row: aligned vector path, full-wave rows, two rows per wave group
@@ -448,7 +450,8 @@ def test_dispatch_examples(L):
     assert sel(0, 16384, rows=8192) == "ln_4_p0_l64_w16_q4_b16"
     assert sel(0, 6144 * 8, rows=8192, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p0_l64_w16_q6_b16"
     assert sel(0, 128, rows=512) == "ln_4_p0_l32_w1_q1_b4"
-    assert sel(1, 8193, rows=256) == "rms_4_p1_l64_w16_q3_b16"
+    # a peeled row's body holds at most d / 4 accesses: 8193 fits 16 waves of two
+    assert sel(1, 8193, rows=256) == "rms_4_p1_l64_w16_q2_b16"
     assert sel(0, 1, rows=64) == "ln_1_p0_l16_w1_q1_b4"
     assert sel(2, 768) == "addln_4_r2_w1_q3_b4"             # fused: two rows per wave group
     assert sel(2, 768, rows=4095) == "addln_4_p0_l64_w2_q2_b16"
@@ -577,8 +580,12 @@ def test_strides_and_types_decide_the_layout(L):
     # a 16-bit row width that is a multiple of 4 but not of 8 is peeled
     v = mn.mi_norm_variant_get_info(mn.mi_norm_select(_prob(0, 4096, 772, dtype=mn.MI_NORM_BF16)))
     assert v["peel"] == 1 and v["vec"] == 8
-    # peeled 16-bit rows stop at six slots (49152 elements), then stream
-    v = mn.mi_norm_variant_get_info(mn.mi_norm_select(_prob(2, 64, 49153, x=X + 2, y=Y + 2, r=R_ + 2,
+    # peeled 16-bit rows stop at six slots (a body of 49152 elements, and a
+    # head and tail of up to seven), then stream
+    v = mn.mi_norm_variant_get_info(mn.mi_norm_select(_prob(2, 64, 49159, x=X + 2, y=Y + 2, r=R_ + 2,
+                                                            h=H_ + 2, dtype=mn.MI_NORM_BF16)))
+    assert v["peel"] == 1 and v["slots"] == 6
+    v = mn.mi_norm_variant_get_info(mn.mi_norm_select(_prob(2, 64, 49160, x=X + 2, y=Y + 2, r=R_ + 2,
                                                             h=H_ + 2, dtype=mn.MI_NORM_BF16)))
     assert v["looped"] == 1 and v["vec"] == 1
     # strides that keep every row on a quad boundary keep the quad path

@@ -179,7 +179,9 @@ def _variant_widths(v):
         return [4 * 1237, 40000] if v["vec"] == 4 else [4947, 40001]
     cap = v["max_d"]
     if v["peel"]:
-        return sorted(w for w in {cap - 3, cap - 1 - 4 * 64, max(3, cap // 3 - 1), 5} if w >= 1)
+        # a body that fills the variant with the widest tail, a ragged one,
+        # and the narrowest row a peeled variant takes (128)
+        return sorted(w for w in {cap, cap - 4, cap - 1 - 4 * 64, max(128, cap // 3 - 1), 128} if w >= 128)
     step = 4 if v["vec"] == 4 else 1
     widths = {cap, cap - step * max(1, cap // (7 * step)), step}
     return sorted(w for w in widths if w >= 1)
@@ -189,7 +191,7 @@ def _variant_layout(v):
     if v["needs_aligned"]:
         return dict(xo=0, yo=0, po=0)
     if v["peel"]:
-        return dict(xo=1, yo=1, po=2)   # x and y share their 16-byte phase
+        return dict(xo=1, yo=1, po=2)   # x and y share their phase (within a cache line: a head of 31)
     return dict(xo=1, yo=2, po=3)       # nothing aligned
 
 

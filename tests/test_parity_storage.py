@@ -267,19 +267,23 @@ def _variant_widths(v):
         return [v["vec"] * 1237, 40000] if v["vec"] > 1 else [4947, 40001]
     cap = v["max_d"]
     if v["peel"]:
-        return sorted(w for w in {cap - 3, cap - 1 - 4 * 64, max(3, cap // 3 - 1), 5} if w >= 1)
+        return sorted(w for w in {cap, cap - 1 - 4 * 64, max(128, cap // 3 - 1), 128} if w >= 128)
     step = v["vec"]
     return sorted(w for w in {cap, cap - step * max(1, cap // (7 * step)), step} if w >= 1)
 
 
-def _variant_layout(v, d):
+def _variant_layouts(v, d):
     """Row strides and offsets that the variant accepts, with gaps between rows."""
     if v["needs_aligned"]:
-        return dict(ld={k: d + 8 for k in "xryh"}, off={k: 0 for k in "xryh"}, po=0)
+        return [dict(ld={k: d + 8 for k in "xryh"}, off={k: 0 for k in "xryh"}, po=0)]
     if v["peel"]:
-        # one phase within a vector on every row: equal offsets, strides equal mod 8
-        return dict(ld={"x": d + 5, "r": d + 13, "y": d + 21, "h": d + 5}, off={k: 1 for k in "xryh"}, po=2)
-    return dict(ld={"x": d + 3, "r": d + 2, "y": d + 1, "h": d + 7}, off={"x": 1, "r": 2, "y": 3, "h": 0}, po=3)
+        # one phase within 16 bytes on every row (equal offsets, strides equal
+        # mod 8 elements: the body starts on a 16-byte boundary), and one phase
+        # within a cache line (strides equal mod 64 elements: the body starts
+        # on a line, after a head of up to 31 or 63 elements)
+        return [dict(ld={"x": d + 5, "r": d + 13, "y": d + 21, "h": d + 5}, off={k: 1 for k in "xryh"}, po=2),
+                dict(ld={"x": d + 5, "r": d + 69, "y": d + 133, "h": d + 5}, off={k: 3 for k in "xryh"}, po=1)]
+    return [dict(ld={"x": d + 3, "r": d + 2, "y": d + 1, "h": d + 7}, off={"x": 1, "r": 2, "y": 3, "h": 0}, po=3)]
 
 
 OPNAME = {v: k for k, v in OPS.items()}
@@ -297,11 +301,11 @@ def test_every_variant_strided(torch_dev, dt):
         op = OPNAME[v["op"]]
         for d in _variant_widths(v):
             rows = min(3 * v["rows_per_block"] + 1, max(2, 300000 // d))
-            lay = _variant_layout(v, d)
-            say(f"variant {vid} {name} rows={rows} d={d} {lay}")
-            x, r, params = inputs(op, dt, rows, d, "offset", [13, vid, d])
-            run_case(torch, dev, op, dt, x, r, params, variant=vid, **lay)
-            n += 1
+            for lay in _variant_layouts(v, d):
+                say(f"variant {vid} {name} rows={rows} d={d} {lay}")
+                x, r, params = inputs(op, dt, rows, d, "offset", [13, vid, d])
+                run_case(torch, dev, op, dt, x, r, params, variant=vid, **lay)
+                n += 1
     assert n > 0
 
 
