@@ -87,12 +87,17 @@ def _wait(job) -> None:
         raise subprocess.CalledProcessError(rc, cmd)
 
 
-def build(verbose: bool = False, resource_report: bool = True) -> str:
+def build(verbose: bool = False, resource_report: bool = True, full_table: bool | None = None) -> str:
     """Compile and link libmi_norm.so; returns its path.
 
     With ``resource_report`` the compiler's per-kernel resource remarks
     (VGPRs, SGPRs, LDS, occupancy) are written to _build/resource_usage.txt.
+    ``full_table`` (default: the environment variable MI_NORM_FULL_TABLE set
+    to 1) compiles every (waves per row, slots, workgroup) variant instead of
+    the ones the dispatcher can choose, for sweeps that force variants.
     """
+    if full_table is None:
+        full_table = os.environ.get("MI_NORM_FULL_TABLE") == "1"
     hipcc = os.path.join(rocm_path(), "bin", "hipcc")
     if not os.path.exists(hipcc):
         hipcc = shutil.which("hipcc") or hipcc
@@ -101,7 +106,8 @@ def build(verbose: bool = False, resource_report: bool = True) -> str:
     for src in SOURCES:
         stem = os.path.splitext(src)[0]
         obj = os.path.join(BUILD_DIR, stem + ".o")
-        cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *HIPCC_FLAGS, *(["-DMI_NORM_FULL_TABLE"] if full_table else []), "-I", INCLUDE, "-I", CSRC,
+               "-c", os.path.join(CSRC, src), "-o", obj]
         report = os.path.join(BUILD_DIR, f"remarks_{stem}.txt")
         if resource_report:
             cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")

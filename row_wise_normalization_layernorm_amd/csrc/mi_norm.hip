@@ -321,181 +321,76 @@ int64_t row_pitch(const mi_norm_problem &P) {
     return m * esize(P.dtype);
 }
 
+// The aligned vector path.  A base shape, then at most one adjustment; each
+// adjustment was measured on MI355X against the base (rotated buffers,
+// medians of five) and kept when it won by more than the ~7% by which one
+// shape varies from box to box, or when a benchmark workload takes it.
+int select_vector(const mi_norm_problem &P) {
+    const int op = P.op, dt = P.dtype, W = (int)vwidth(dt);
+    const int64_t rows = P.rows, nvec = P.d / W;
+    const bool f32 = esize(dt) == 4, res = kres(op);
+    if (nvec <= 16) return find(op, dt, rows, W, 0, 0, 16, 1, 1);
+    if (nvec <= 32) return find(op, dt, rows, W, 0, 0, 32, 1, 1);
+    int wpr, q;
+    shape_vectors(nvec, rows, wpr, q);
+    if (!wpr) return find(op, dt, rows, W, 0, 1, 0, 0, 0);   // wider than any held row: streamed
+    // a one-row variant of (w, s): with `waves` waves per workgroup, or by the row count
+    auto one = [&](int w, int s, int waves = 0) {
+        return waves ? find_waves(op, dt, W, w, s, waves) : find(op, dt, rows, W, 0, 0, 64, w, s);
+    };
+    auto multi = [&](int w, int s) { return find_multi(op, dt, W, w, s); };
+    int v = -1;
+    if (op == MI_NORM_OP_LAYERNORM && f32 && nvec > 768 && nvec <= 1024 && rows >= 3072 && rows <= 4096) {
+        // float32 LayerNorm rows of 3-4 K elements: one wave of sixteen slots,
+        // parameters in LDS (LayerNorm [4096,4096] 22.2 against 24.0 us)
+        v = one(1, 16, rows <= 3072 ? 4 : 8);
+    } else if (!f32 && wpr <= 2) {
+        // 16-bit rows of one or two waves: the one-row kernel, whose
+        // parameters sit in LDS (it beat the multi-row one in 12 of 15 shapes)
+        if (wpr == 2 && q >= 3 && rows < 2560) {
+            v = multi(2, q);   // RMSNorm BF16 [2048,4096] 6.43 against 6.84 us; add + RMSNorm 11.8 against 13.1
+        } else if (res && wpr == 2 && q == 4 && rows > 4096 && rows <= 8192) {
+            v = one(4, 2, 16); // fused: four waves of two slots (add + RMSNorm BF16 [8192,4096] 44.5 against 49.5 us)
+        } else if (wpr == 2 && q <= 4 && rows >= 2560 && rows <= 8192) {
+            // one wave with twice the slots: 4-27% ([4096,4096] RMSNorm 11.5 against
+            // 13.7 us), in 4-wave workgroups where 16-wave ones spread unevenly
+            const int64_t b16 = (rows + 15) / 16;
+            v = one(1, 2 * q, (b16 > 256 && !even_spread(b16)) ? 4 : 16);
+        } else if (wpr == 1 && !(q <= 2 && !res && rows <= 8192)) {
+            v = one(1, q, 4);  // one-wave rows: 4-wave workgroups won in 6 of 8 shapes
+        }
+    } else if (res && (wpr == 4 || wpr == 8) && rows >= 8192) {
+        // fused rows of four or eight waves, many rows: twice the waves, half the
+        // slots (add + LayerNorm [16384,8192] 349 against 395 us; BF16 [32768,8192] 342 against 365)
+        v = one(2 * wpr, (q + 1) / 2);
+    } else if (res && f32 && wpr == 2 && nvec > 256 && rows <= 4096) {
+        v = one(1, 8, 4);      // fused float32 rows of two waves: one wave of eight slots (add + LN [2048,1536] 8.89 against 9.90 us)
+    } else if (res && f32 && wpr == 4 && nvec > 512 && q <= 4 && rows >= 2048 && rows < 4096) {
+        v = multi(2, 2 * q);   // fused float32 rows of four waves: add + RMSNorm [2048,3072] 16.9 against 18.2 us
+    } else if (multi_pays(op, rows, P.d, esize(dt), wpr, row_pitch(P))) {
+        v = multi(wpr, q);     // many rows: two rows per wave group, one parameter fetch for both
+    } else if (f32 && !res && (wpr == 2 || wpr == 4) && q <= 4 && rows * wpr > 8192) {
+        v = one(wpr / 2, 2 * q);   // more than 4096 waves even at half the waves: 10-12%
+    } else if (!f32 && wpr == 4 && q <= 4 && rows >= 2048 && (!res || rows < 2560)) {
+        v = one(2, 2 * q, 16);     // 16-bit rows of four waves: 5-11%
+    }
+    return v >= 0 ? v : one(wpr, q);
+}
+
 int select_variant(const mi_norm_problem &P) {
     if (!shape_ok(P)) return -1;
     const Layout L = layout_of(P);
+    const int op = P.op, dt = P.dtype, W = (int)vwidth(dt);
     const int64_t d = P.d, rows = P.rows;
-    const int op = P.op, dt = P.dtype;
-    const int W = (int)vwidth(dt);
     int lpr, wpr, q;
-    if (L.aq) {
-        const int64_t nvec = d / W;
-        if (nvec <= 16) return find(op, dt, rows, W, 0, 0, 16, 1, 1);
-        if (nvec <= 32) return find(op, dt, rows, W, 0, 0, 32, 1, 1);
-        shape_vectors(nvec, rows, wpr, q);
-        if (wpr && wpr <= 2 && esize(dt) == 2) {
-            // 16-bit rows of one or two waves: the one-row variants, which
-            // stage their parameters in LDS, beat the multi-row ones in 12
-            // of 15 measured shapes (up to 10%: LayerNorm bfloat16
-            // [16384,768] 10.6 against 11.9 us).  With 2560-8192 rows, rows
-            // of two waves run as one wave with twice the slots in 16-wave
-            // workgroups: 4-27% faster in eight shapes (RMSNorm [4096,4096]
-            // 11.5 against 13.7 us; LayerNorm [2560,4096] 8.7 against 11.0),
-            // equal in one; at 12288 rows it lost 4%.  One wave of up to four
-            // slots takes 4-wave workgroups (the faster in 6 of 8 shapes).
-            // Under 2560 rows, rows of two waves and three or four slots
-            // take the multi-row kernel of the same shape: bfloat16
-            // RMSNorm [2048,4096] 6.43 against 6.84 us, LayerNorm 7.26
-            // against 7.58, add + RMSNorm 11.8 against 13.1, RMSNorm
-            // [2048,3072] 5.33 against more than 5.44 (two slots: LayerNorm
-            // [2048,2048] lost).
-            if (wpr == 2 && q >= 3 && rows < 2560) {
-                const int m = find_multi(op, dt, W, 2, q);
-                if (m >= 0) return m;
-            }
-            if (kres(op) && wpr == 2 && q == 4 && rows > 4096 && rows <= 8192) {
-                // fused rows of two waves and four slots, 4097-8192 rows:
-                // four waves of two slots in 16-wave workgroups (add +
-                // LayerNorm bfloat16 [8000,4096] 44.3 against 48.8 us,
-                // [6144,4096] 34.8 against 37.1; add + RMSNorm [5000,4096]
-                // 28.3 against 29.2); at 4096 rows (24.4 against 23.1) and
-                // for rows of three slots it lost
-                const int s = find_waves(op, dt, W, 4, 2, 16);
-                if (s >= 0) return s;
-            }
-            if (wpr == 2 && q <= 4 && rows >= 2560 && rows <= 8192) {
-                // 4-wave workgroups where more than 256 16-wave ones would
-                // spread unevenly over the CUs: bfloat16 LayerNorm
-                // [5000,3000] (313 workgroups) 13.7 against 15.8 us,
-                // [4500,4096] 16.0 against 17.8, RMSNorm [6144,3072] 14.4
-                // against 15.7, add + LayerNorm [6144,4096] 37.1 against 40.1
-                const int64_t b16 = (rows + 15) / 16;
-                const int s = (b16 > 256 && !even_spread(b16)) ? find_waves(op, dt, W, 1, 2 * q, 4) : -1;
-                if (s >= 0) return s;
-                const int t = find_waves(op, dt, W, 1, 2 * q, 16);
-                if (t >= 0) return t;
-            }
-            // With the buffer-load kernel, plain (not fused) rows of one or
-            // two slots up to 8192 rows run faster in the workgroup rule's
-            // 16-wave workgroups (LayerNorm bfloat16 [4096,768] 4.03 against
-            // 4.22 us, [8192,768] 5.92 against 6.46; RMSNorm [4096,768] a
-            // tie); from 16384 rows, for fused rows and for four slots the
-            // 4-wave ones kept a 2-13% lead.
-            const bool small = wpr == 1 && q <= 2 && !kres(op) && rows <= 8192;
-            const int s = (wpr == 1 && !small) ? find_waves(op, dt, W, wpr, q, 4) : -1;
-            return s >= 0 ? s : find(op, dt, rows, W, 0, 0, 64, wpr, q);
-        }
-        if (op == MI_NORM_OP_LAYERNORM && esize(dt) == 4 && nvec > 768 && nvec <= 1024 && rows >= 3072 &&
-            rows <= 4096) {
-            // float32 LayerNorm rows of 3-4 K elements, 3072-4096 of them:
-            // one wave per row with sixteen slots and the parameters in LDS
-            // (5 waves per SIMD), measured on MI355X as the fastest shape or
-            // within 2.5% of it ([4096,4096] 22.4 us; [3072,4096] 17.7 against
-            // 17.4 for 16-wave workgroups; [4096,3200] 18.1), and up to 7%
-            // ahead of the one-row shapes outside it
-            const int s = find_waves(op, dt, W, 1, 16, rows <= 3072 ? 4 : 8);
-            if (s >= 0) return s;
-        }
-        if (kres(op) && (wpr == 4 || wpr == 8) && rows >= 8192) {
-            // fused rows of four or eight waves with many rows: the one-row
-            // kernel with twice the waves per row and half the slots.  On
-            // MI355X, add + LayerNorm [32768,8192] float32 716 against 731 us,
-            // bfloat16 342 against 365 (the multi-row kernel); on seven
-            // further shapes faster in six by 1.7-12% ([16384,8192] 349
-            // against 395 us), 1% slower at [8192,4096]
-            const int s = find(op, dt, rows, W, 0, 0, 64, 2 * wpr, (q + 1) / 2);
-            if (s >= 0) return s;
-        }
-        if (op == MI_NORM_OP_RMSNORM && esize(dt) == 4 && wpr == 4 && rows >= 8192) {
-            // float32 RMSNorm rows of four waves from 8192 rows: the one-row
-            // kernel with eight waves per row and half the slots, in 8-wave
-            // workgroups ([32768,4096] 168.0 against 176.8 us for the
-            // multi-row kernel, [16384,4096] 85.4 against 88.6, [8192,3584]
-            // 39.4 against 39.8, [12288,3072] 49.8 against 50.1; 16-wave
-            // workgroups lost 2-5%)
-            const int s = find_waves(op, dt, W, 8, (q + 1) / 2, 8);
-            if (s >= 0) return s;
-        }
-        if (kres(op) && esize(dt) == 4 && wpr == 2 && nvec > 256 && rows <= 4096) {
-            // fused float32 rows of two waves by width (more than 256
-            // quads, not doubled for few rows), up to 4096 rows: one wave of
-            // eight slots in 4-wave workgroups (add + LayerNorm [2048,1536]
-            // 8.82 against 10.2 us, [4096,2048] 23.0 against 24.7 for the
-            // multi-row kernel, [2048,2048] 11.6 against 12.3; add + RMSNorm
-            // [3072,2048] 16.9 against 18.2, [4096,1536] 16.8 against 17.5);
-            // eight slots beat six for rows of six ([2048,1536] 8.82 against
-            // 9.31); at 6144 rows the multi-row kernel tied
-            const int s = find_waves(op, dt, W, 1, 8, 4);
-            if (s >= 0) return s;
-        }
-        if (kres(op) && esize(dt) == 4 && wpr == 4 && nvec > 512 && q <= 4 && rows >= 2048 && rows < 4096) {
-            // fused float32 rows of four waves by width, 2048-4095 rows: the
-            // multi-row kernel with two waves per row and twice the slots
-            // (add + LayerNorm [3000,3000] 26.8 against 29.3 us, add +
-            // RMSNorm [2048,3072] 16.9 against 18.2)
-            const int m = find_multi(op, dt, W, 2, 2 * q);
-            if (m >= 0) return m;
-        }
-        if (op == MI_NORM_OP_RMSNORM && esize(dt) == 4 && wpr == 2 && nvec > 256 && rows >= 2048 &&
-            rows <= 4096) {
-            // float32 RMSNorm rows of two waves by width, 2048-4096 rows:
-            // the multi-row kernel of the same shape ([2560,2048] 7.55
-            // against 7.94 us, [2048,2048] 6.41 against 6.70, [4096,1536]
-            // 8.63 against 8.96, [4096,2048] 11.79 against 11.88); LayerNorm
-            // tied or lost there ([4096,2048] 13.2 against 11.5)
-            const int m = find_multi(op, dt, W, 2, q);
-            if (m >= 0) return m;
-        }
-        if (wpr && multi_pays(op, rows, d, esize(dt), wpr, row_pitch(P))) {
-            if (op == MI_NORM_OP_LAYERNORM && esize(dt) == 4 && (wpr == 2 || wpr == 4) && rows >= 8192 &&
-                (q * wpr) % 8 == 0) {
-                // float32 LayerNorm rows of two or four waves from 8192 rows,
-                // whose slots split evenly over eight waves: eight waves per
-                // row with as many fewer slots ([16384,4096] 88.8 against
-                // 91.1 us, [32768,2048] 86.0 against 88.9 or more, [65536,2048]
-                // 171 against 186; ties at [8192,2048]).  Splits that leave
-                // slots idle ([16384,2560]: three slots of four waves) lost
-                // 3-4%.
-                const int m = find_multi(op, dt, W, 8, q * wpr / 8);
-                if (m >= 0) return m;
-            }
-            const int m = find_multi(op, dt, W, wpr, q);
-            if (m >= 0) return m;
-        }
-        if (esize(dt) == 4 && !kres(op) && (wpr == 2 || wpr == 4) && q <= 4 && rows * (wpr / 2) > 4096) {
-            // float32 rows of 2-4 K elements on the one-row path with more
-            // than 4096 waves at half the waves per row: half the waves, twice
-            // the slots, one fewer cross-wave exchange ([2560,4096] 14.6
-            // against 16.2 us; [4096,3072] 17.1 against 19.5; [6144,2048]
-            // 17.3 against 19.5; at [2048,4096] four waves stay 2% ahead)
-            wpr /= 2;
-            q *= 2;
-        }
-        if (esize(dt) == 2 && wpr == 4 && q <= 4 && rows >= 2048 && (!kres(op) || rows < 2560)) {
-            // 16-bit rows of four waves on the one-row path from 2048 rows:
-            // two waves with twice the slots in 16-wave workgroups (bfloat16
-            // LayerNorm [2048,4608] 8.18 against 9.07 us, [4096,6144] 19.5
-            // against 21.4, [2048,8192] 12.9 against 13.6; RMSNorm
-            // [2048,8192] 12.1 against 13.5, [4096,6144] 17.8 against more
-            // than 19.5; add + RMSNorm [2048,8192] 23.3 against 24.5); at
-            // 1024 rows it lost, and fused rows from 2560 rows lost 5-15%
-            // (add + RMSNorm [3000,6000] 31.6 against 27.5 us)
-            const int s = find_waves(op, dt, W, 2, 2 * q, 16);
-            if (s >= 0) return s;
-        }
-        if (wpr) return find(op, dt, rows, W, 0, 0, 64, wpr, q);
-        return find(op, dt, rows, W, 0, 1, 0, 0, 0);
-    }
+    if (L.aq) return select_vector(P);
     if (L.peel_ok && d >= 256) {
-        // the head and tail are held apart from the body, which holds at
-        // most d / W accesses
+        // the head and tail are held apart from the body, which holds at most d / W accesses
         shape_vectors(d / W, rows, wpr, q, W == 8 ? 6 : 8);
-        if (wpr) return find(op, dt, rows, W, 1, 0, 64, wpr, q);
-        return find(op, dt, rows, 1, 0, 1, 0, 0, 0);
+        return wpr ? find(op, dt, rows, W, 1, 0, 64, wpr, q) : find(op, dt, rows, 1, 0, 1, 0, 0, 0);
     }
     ladder1(d, lpr, wpr, q);
-    if (wpr) return find(op, dt, rows, 1, 0, 0, lpr, wpr, q);
-    return find(op, dt, rows, 1, 0, 1, 0, 0, 0);
+    return wpr ? find(op, dt, rows, 1, 0, 0, lpr, wpr, q) : find(op, dt, rows, 1, 0, 1, 0, 0, 0);
 }
 
 bool eligible(int id, const mi_norm_problem &P) {

@@ -172,10 +172,67 @@ inline const void *held_kernel() {
     /* two rows per wave group, one fetch of the parameters for both */                       \
     MI_MULTI_ALL(T, DT, VW, OPC, OPN)
 
+// ---------------------------------------------------------------------------
+// The default table: the shapes the dispatcher can choose for some problem
+// (checked over a dense grid of operations, storage types, layouts, widths
+// and row counts), kept whole per (waves per row, slots) where the
+// workgroup-size rule reaches one size of a pair for only some of them.
+// Builds with MI_NORM_FULL_TABLE defined compile MI_OP_TABLE above instead,
+// every (waves per row, slots, workgroup) pair, for sweeps that force
+// variants the dispatcher does not choose.
+//   vectors, aligned: one wave 1-4, 6, 8 slots; two waves 1-4, 6, 8; four and
+//     eight waves 1-4 (one slot in the smaller workgroup only); 16 waves 1-8
+//   peeled: one wave 1-4; two, four, eight waves as the aligned path; 16 waves
+//   two rows per wave group: float32 one wave 1-4, two waves 3, 4, 6, 8;
+//     four and eight waves 3, 4 (16-bit: two, four, eight waves 3, 4)
+#define MI_D_H4(T, DT, OPC, OPN, VW, PEEL, WPR, WS)                                                 \
+    MI_HELD(T, DT, OPC, OPN, VW, PEEL, 64, WPR, 1, WS), MI_HELD2(T, DT, OPC, OPN, VW, PEEL, 64, WPR, 2, WS), \
+    MI_HELD2(T, DT, OPC, OPN, VW, PEEL, 64, WPR, 3, WS), MI_HELD2(T, DT, OPC, OPN, VW, PEEL, 64, WPR, 4, WS)
+#define MI_D_W1(T, DT, OPC, OPN, VW, PEEL)                                                          \
+    MI_HELD2(T, DT, OPC, OPN, VW, PEEL, 64, 1, 1, 4), MI_HELD2(T, DT, OPC, OPN, VW, PEEL, 64, 1, 2, 4), \
+    MI_HELD2(T, DT, OPC, OPN, VW, PEEL, 64, 1, 3, 4), MI_HELD2(T, DT, OPC, OPN, VW, PEEL, 64, 1, 4, 4)
+#define MI_D_Q68(T, DT, OPC, OPN, VW, WPR)                                                          \
+    MI_HELD2(T, DT, OPC, OPN, VW, 0, 64, WPR, 6, 4), MI_HELD2(T, DT, OPC, OPN, VW, 0, 64, WPR, 8, 4)
+#define MI_D_MULTI_4(T, DT, OPC, OPN)                                                               \
+    MI_MULTI_Q16(T, DT, OPC, OPN, 4, 1, 4),                                                          \
+    MI_MULTI(T, DT, OPC, OPN, 4, 2, 3, 4), MI_MULTI(T, DT, OPC, OPN, 4, 2, 4, 4),                   \
+    MI_MULTI(T, DT, OPC, OPN, 4, 2, 6, 4), MI_MULTI(T, DT, OPC, OPN, 4, 2, 8, 4),                   \
+    MI_MULTI(T, DT, OPC, OPN, 4, 4, 3, 4), MI_MULTI(T, DT, OPC, OPN, 4, 4, 4, 4),                   \
+    MI_MULTI(T, DT, OPC, OPN, 4, 8, 3, 8), MI_MULTI(T, DT, OPC, OPN, 4, 8, 4, 8)
+#define MI_D_MULTI_8(T, DT, OPC, OPN)                                                               \
+    MI_MULTI(T, DT, OPC, OPN, 8, 2, 3, 4), MI_MULTI(T, DT, OPC, OPN, 8, 2, 4, 4),                   \
+    MI_MULTI(T, DT, OPC, OPN, 8, 4, 3, 4), MI_MULTI(T, DT, OPC, OPN, 8, 4, 4, 4),                   \
+    MI_MULTI(T, DT, OPC, OPN, 8, 8, 3, 8), MI_MULTI(T, DT, OPC, OPN, 8, 8, 4, 8)
+
+#define MI_D_OP_TABLE(T, DT, VW, OPC, OPN)                                                         \
+    MI_HELD2(T, DT, OPC, OPN, VW, 0, 16, 1, 1, 4), MI_HELD2(T, DT, OPC, OPN, VW, 0, 32, 1, 1, 4), \
+    MI_D_W1(T, DT, OPC, OPN, VW, 0), MI_D_Q68(T, DT, OPC, OPN, VW, 1),                              \
+    MI_D_H4(T, DT, OPC, OPN, VW, 0, 2, 4), MI_D_Q68(T, DT, OPC, OPN, VW, 2),                        \
+    MI_D_H4(T, DT, OPC, OPN, VW, 0, 4, 4), MI_D_H4(T, DT, OPC, OPN, VW, 0, 8, 8),                   \
+    MI_SLOTS16(T, DT, VW, OPC, OPN, 0),                                                             \
+    MI_WIDE16_##VW##_##OPC(T, DT, OPC, OPN)                                                         \
+    MI_D_W1(T, DT, OPC, OPN, VW, 1),                                                                \
+    MI_D_H4(T, DT, OPC, OPN, VW, 1, 2, 4), MI_D_H4(T, DT, OPC, OPN, VW, 1, 4, 4),                   \
+    MI_D_H4(T, DT, OPC, OPN, VW, 1, 8, 8), MI_SLOTS16(T, DT, VW, OPC, OPN, 1),                      \
+    MI_HELD2(T, DT, OPC, OPN, 1, 0, 16, 1, 1, 4), MI_HELD2(T, DT, OPC, OPN, 1, 0, 32, 1, 1, 4), \
+    MI_HELD2(T, DT, OPC, OPN, 1, 0, 64, 1, 1, 4), MI_HELD2(T, DT, OPC, OPN, 1, 0, 64, 1, 2, 4), \
+    MI_HELD2(T, DT, OPC, OPN, 1, 0, 64, 1, 4, 4), MI_HELD2(T, DT, OPC, OPN, 1, 0, 64, 1, 8, 4), \
+    MI_HELD2(T, DT, OPC, OPN, 1, 0, 64, 4, 4, 4), MI_HELD2(T, DT, OPC, OPN, 1, 0, 64, 4, 8, 4), \
+    MI_HELD2(T, DT, OPC, OPN, 1, 0, 64, 8, 8, 8),                                               \
+    MI_HELD(T, DT, OPC, OPN, 1, 0, 64, 16, 8, 16), MI_HELD(T, DT, OPC, OPN, 1, 0, 64, 16, 16, 16), \
+    MI_LOOP(T, DT, OPC, OPN, VW, 4, 4), MI_LOOP(T, DT, OPC, OPN, 1, 4, 8),                      \
+    MI_D_MULTI_##VW(T, DT, OPC, OPN)
+
+#ifdef MI_NORM_FULL_TABLE
+#define MI_TABLE_OF MI_OP_TABLE
+#else
+#define MI_TABLE_OF MI_D_OP_TABLE
+#endif
+
 // the four operations of one storage type; VW its vector width in
 // elements, SFX its name suffix
 #define MI_DTYPE_TABLE(T, DT, VW, SFX)                                                             \
-    MI_OP_TABLE(T, DT, VW, MI_NORM_OP_LAYERNORM, "ln" SFX),                                         \
-    MI_OP_TABLE(T, DT, VW, MI_NORM_OP_RMSNORM, "rms" SFX),                                          \
-    MI_OP_TABLE(T, DT, VW, MI_NORM_OP_ADD_LAYERNORM, "addln" SFX),                                  \
-    MI_OP_TABLE(T, DT, VW, MI_NORM_OP_ADD_RMSNORM, "addrms" SFX)
+    MI_TABLE_OF(T, DT, VW, MI_NORM_OP_LAYERNORM, "ln" SFX),                                         \
+    MI_TABLE_OF(T, DT, VW, MI_NORM_OP_RMSNORM, "rms" SFX),                                          \
+    MI_TABLE_OF(T, DT, VW, MI_NORM_OP_ADD_LAYERNORM, "addln" SFX),                                  \
+    MI_TABLE_OF(T, DT, VW, MI_NORM_OP_ADD_RMSNORM, "addrms" SFX)

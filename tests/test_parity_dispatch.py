@@ -48,15 +48,14 @@ CASES = [
     ("add_rmsnorm", BF16, 6145, 2048, "addrms_bf16_8_p0_l64_w1_q4_b4"),
     # fused float32 rows of four waves, 2048-4095 rows: multi-row, two waves, twice the slots
     ("add_layernorm", F32, 3001, 3000, "addln_4_r2_w2_q6_b4"),
-    # float32 RMSNorm rows of two waves, 2048-4096 rows: multi-row
-    ("rmsnorm", F32, 3001, 1800, "rms_4_r2_w2_q4_b4"),
+    # float32 RMSNorm rows of two waves, 2048-4096 rows: the base shape
+    ("rmsnorm", F32, 3001, 1800, "rms_4_p0_l64_w2_q4_b4"),
     # fused float32 rows of two waves up to 4096 rows: one wave of eight slots
     ("add_layernorm", F32, 2049, 1536, "addln_4_p0_l64_w1_q8_b4"),
     ("add_rmsnorm", F32, 4095, 2048, "addrms_4_p0_l64_w1_q8_b4"),
-    # float32 LayerNorm multi-row rows from 8192 rows: eight waves per row
-    ("layernorm", F32, 8193, 4096, "ln_4_r2_w8_q2_b8"),
-    # float32 RMSNorm rows of four waves from 8192 rows: one row, eight waves
-    ("rmsnorm", F32, 8193, 3072, "rms_4_p0_l64_w8_q2_b8"),
+    # many rows: two rows per wave group, the base shape's waves and slots
+    ("layernorm", F32, 8193, 4096, "ln_4_r2_w4_q4_b4"),
+    ("rmsnorm", F32, 8193, 3072, "rms_4_r2_w4_q3_b4"),
     # fused rows of four or eight waves with many rows: twice the waves
     ("add_layernorm", F32, 8193, 4096, "addln_4_p0_l64_w8_q2_b16"),
     ("add_rmsnorm", BF16, 8193, 8192, "addrms_bf16_8_p0_l64_w8_q2_b16"),

@@ -53,7 +53,9 @@ def test_multi_row_matches_one_row_bit_for_bit(torch_dev):
     torch, dev = torch_dev
     infos = _infos()
     multi = [(i, n, v) for i, n, v in infos if v["rows_per_lane"] == 2]
-    assert len(multi) == 4 * (24 + 2 * 16)
+    # per operation: float32 one wave 1-4 slots, two waves 3, 4, 6, 8, four and
+    # eight waves 3, 4 (12); each 16-bit type two, four, eight waves 3, 4 (6)
+    assert len(multi) == 4 * (12 + 2 * 6)
     tdt = {mn.MI_NORM_F32: torch.float32, mn.MI_NORM_F16: torch.float16, mn.MI_NORM_BF16: torch.bfloat16}
     stream = torch.cuda.current_stream().cuda_stream
     for vid, name, v in multi:
