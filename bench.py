@@ -204,7 +204,7 @@ def pmc_traffic(workload: str, variant: str):
     """HBM bytes per launch from the committed counter summary, or None when
     there is none, the kernels changed since it was taken, or the run uses
     another variant than the one profiled."""
-    path = os.path.join(ROOT, "profiles", f"pmc_{workload}.txt")
+    path = os.path.join(ROOT, "profiles", f"{workload}.txt")
     if not os.path.exists(path):
         return None, None
     text = open(path).read()
@@ -221,7 +221,7 @@ def trace_stats(workload: str, variant: str):
     timed steps) from the committed rocprofv3 kernel-trace summary, or None
     when there is none, the kernels changed since it was taken, or the run
     uses another variant than the one traced."""
-    path = os.path.join(ROOT, "profiles", f"trace_{workload}.txt")
+    path = os.path.join(ROOT, "profiles", f"{workload}.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -234,7 +234,10 @@ def trace_stats(workload: str, variant: str):
     except (TypeError, ValueError):
         return None
     out["source"] = os.path.relpath(path, ROOT)
-    out["what"] = "rocprofv3 --kernel-trace, per-dispatch durations of the timed steps (back to back)"
+    out["what"] = ("rocprofv3 --kernel-trace, per-dispatch durations of the timed steps; the tracer runs "
+                   "each dispatch longer than an untraced back-to-back one (the summary gives both)")
+    u = field("untraced_span_us_per_step")
+    out["untraced_span_us_of_that_run"] = float(u) if u else None
     return out
 
 

@@ -139,6 +139,15 @@ def collect(out: str, workloads: list[str], steps: int = 100, warmup: int = 20, 
     print(f"calibration: fetch x{cal['FETCH_SIZE']:.4f}, write x{cal['WRITE_SIZE']:.4f}", flush=True)
 
     for w in workloads:
+        # the same command without a tracer: the span per step it measures
+        ucmd = [py, "-u", bench, "--profile", "--workload", w, "--steps", str(steps), "--warmup", str(warmup),
+                "--no-cpu-baseline"]
+        print("+ " + " ".join(ucmd), flush=True)
+        import subprocess
+        ur = subprocess.run(ucmd, capture_output=True, text=True, timeout=300, cwd="/tmp", env={**os.environ, "TMPDIR": "/tmp"})
+        if ur.returncode != 0:
+            raise RuntimeError(f"untraced run failed ({ur.returncode}): {ur.stderr[-2000:]}")
+        uline = _bench_line(ur.stdout)
         d = os.path.join(raw, f"trace_{w}")
         tcmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", d, "-o", "t", "--", py,
                 "-u", bench, "--profile", "--workload", w, "--steps", str(steps), "--warmup", str(warmup),
@@ -176,14 +185,24 @@ def collect(out: str, workloads: list[str], steps: int = 100, warmup: int = 20, 
                 f"Each pass: 1 parity-gate call, {warmup} warm-up steps, then one span of {steps} timed steps "
                 f"(counter passes: {pmc_warmup} and {pmc_steps}).  The window is the last {steps} dispatches "
                 "of each kernel a step launches.", "",
-                "Commands (run from /tmp with TMPDIR=/tmp; R = repository root):"]
+                "Made by (from the repository root R, on a GPU host): python3 -m "
+                f"row_wise_normalization_layernorm_amd.profiling collect R/gpurun_out/prof {w}",
+                "which runs (from /tmp with TMPDIR=/tmp): the same bench.py command untraced, then"]
         text += ["    " + c.replace(ROOT, "R").replace(py, "python3") for c in cmds]
         text += ["", "Per-dispatch durations (kernel trace):"] + ["  " + t for t in table]
         if step_win:
             text += ["", f"Per step, the sum of the step's kernels ({len(step_kernels)}): median "
                          f"{statistics.median(step_win):.3f} us, mean {statistics.mean(step_win):.3f} us"]
-        text += ["", f"bench.py line of the traced run: span {line['span_us_per_step']} us per step "
-                     "(stream events; tracer gaps between dispatches included)."]
+        text += ["", f"bench.py lines of the same command: traced, span {line['span_us_per_step']} us per step "
+                     "(stream events; tracer gaps between dispatches included); untraced, span "
+                     f"{uline['span_us_per_step']} us per step = "
+                     f"{uline['roofline']['achieved']} GB/s = {100 * uline['roofline']['frac']:.1f}% of 8 TB/s.",
+                 (f"Traced median per dispatch over the untraced span per step: "
+                  f"{statistics.median(main_win) / uline['span_us_per_step']:.3f}.  From about 25 MB per launch "
+                  "down, the tracer's handling of each dispatch lengthens it (with kernel arguments in device "
+                  "memory it also leaves gaps between dispatches); from 50 MB up the two agree within 2%.  The "
+                  "untraced span is the throughput figure, the traced durations the per-dispatch spread."
+                  if main_win else "")]
         if counters:
             text += ["", f"Counters of {_short(main_k)} (KiB per dispatch, mean over the dispatches):"]
             for c in counters:
@@ -205,6 +224,7 @@ def collect(out: str, workloads: list[str], steps: int = 100, warmup: int = 20, 
         if traffic:
             text.append(f"traffic_bytes_per_launch: {traffic}")
         text.append(f"algorithmic_bytes_per_launch: {alg}")
+        text.append(f"untraced_span_us_per_step: {uline['span_us_per_step']}")
         with open(os.path.join(out, f"{w}.txt"), "w") as f:
             f.write("\n".join(text) + "\n")
         print(f"{w}: median {med} us, traffic {traffic}", flush=True)

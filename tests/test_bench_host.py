@@ -55,7 +55,7 @@ def test_trace_pairing(tmp_path, monkeypatch):
         dst.parent.mkdir(parents=True, exist_ok=True)
         dst.write_bytes(open(os.path.join(ROOT, rel), "rb").read())
     h = bench.kernel_source_hash("fwd")
-    f = tmp_path / "profiles" / "trace_ln_4096x768.txt"
+    f = tmp_path / "profiles" / "ln_4096x768.txt"
     body = ("dispatch_us_median: 5.3\ndispatch_us_min: 4.9\ndispatch_us_max: 6.7\n"
             "dispatch_us_mean: 5.6\ndispatches: 100\n")
     f.write_text(f"kernel_variant: ln_4_p0_l64_w1_q3_b16\nkernel_source_sha256: {h}\n" + body)
@@ -77,7 +77,7 @@ def test_profile_pairing(tmp_path, monkeypatch):
         dst.parent.mkdir(parents=True, exist_ok=True)
         dst.write_bytes(open(os.path.join(ROOT, rel), "rb").read())
     h = bench.kernel_source_hash("fwd")
-    f = tmp_path / "profiles" / "pmc_ln_4096x768.txt"
+    f = tmp_path / "profiles" / "ln_4096x768.txt"
     f.write_text(f"kernel_variant: ln_4_p0_l64_w1_q3_b16\nkernel_source_sha256: {h}\n"
                  "traffic_bytes_per_launch: 25264977\n")
     assert bench.pmc_traffic("ln_4096x768", "ln_4_p0_l64_w1_q3_b16")[0] == 25264977
