@@ -210,14 +210,19 @@ mi_norm_status mi_norm_check(const mi_norm_problem *p);
  *
  * dy, x and dx share a storage type (float32, binary16, bfloat16; each with
  * its own row stride); gamma/w, mean, rstd, dgamma/dw and dbeta are float32.
- * dx is within 1e-5 + 1e-4 |ref| + 64 u rstd_i (|g_ij| + mean_k |g_ik| +
- * |xhat_ij| mean_k |g_ik xhat_ik|) of the float64 derivative (plus half a
- * 16-bit ulp for 16-bit dx): the subtraction of the row means amplifies
- * float32 rounding by rstd, which is large for rows of near-zero variance.  The parameter gradients are sums over rows: the
- * terms are formed in float32 and summed in float64 registers, partial sums
- * of each workgroup are stored as float32 and added in float64 in a fixed
- * order, so results are deterministic and within 1e-5 + 1e-4 |ref| +
- * 12 u sum_i |term_i| (u = 2^-24).
+ * Arithmetic: every term (g, g xhat, dy xhat, dy) is formed in float32 from
+ * the float32 inputs.  A row's two sums add at most eight consecutive terms
+ * in float32 and carry the rest in float64; each mean is rounded once to
+ * float32.  A column sum is carried in float64, rounded to float32 at most
+ * twice on the way (once for a subset of a workgroup's rows, once for the
+ * workgroup's), the workgroups' partial rows added in float64 in a fixed
+ * order and rounded once (deterministic results).  Hence, with u = 2^-24
+ * and whatever the launch shape, dx is within 1e-5 + 1e-4 |ref| +
+ * 16 u rstd_i (|g_ij| + mean_k |g_ik| + |xhat_ij| mean_k |g_ik xhat_ik|) of
+ * the float64 derivative (plus half a 16-bit ulp for 16-bit dx; the
+ * subtraction of the row means amplifies float32 rounding by rstd, which is
+ * large for rows of near-zero variance), and the parameter gradients within
+ * 1e-5 + 1e-4 |ref| + 6 u sum_i |term_i|.
  *
  * The parameter gradients need device scratch memory that the caller owns:
  * mi_norm_bwd_workspace_size says how many bytes (it depends on the shape

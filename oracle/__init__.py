@@ -392,16 +392,20 @@ def rmsnorm_bwd16(dy, x, fmt: int, w, rstd, lib: ctypes.CDLL | None = None) -> d
 U32 = 2.0 ** -24  # unit roundoff of float32
 
 
-def colsum_tolerance_ok(got, ref64, abs_sum, atol: float = 1e-5, rtol: float = 1e-4, k: float = 12.0):
+def colsum_tolerance_ok(got, ref64, abs_sum, atol: float = 1e-5, rtol: float = 1e-4, k: float = 6.0):
     """Acceptance for a float32 sum over rows (the parameter gradients).
 
-    The float32 bound of the forward outputs plus k * u * sum|terms|, from
-    the arithmetic the kernels use: each term dy * xhat carries three float32
-    roundings (x - mean, times rstd, times dy: relative error <= ~3u); a lane
-    adds its terms in float64 and rounds the sum once to float32 (<= u); the
-    row slots of a workgroup meet in a float32 tree of at most three levels
-    (<= 3u); the partial rows are added in float64 and rounded once, which
-    rtol covers.  That is <= 7u * sum|terms|; k = 12 leaves margin.
+    The float32 bound of the forward outputs plus k * u * sum|terms|, for any
+    evaluation that forms each term in float32 from the float32 inputs,
+    carries every sum in float64, and rounds to float32 only partial sums
+    over subsets of the rows, at most two nested levels of them (each
+    partial once), and the final sum: each term dy * xhat carries at most
+    three float32 roundings (x - mean, times rstd, times dy: <= 3u of
+    |term|); each level of partial sums adds <= u * sum|terms| whatever the
+    partition; a float64 sum of n terms in any order errs by
+    <= n 2^-53 sum|terms|, which is <= u * sum|terms| for up to 2^29 rows;
+    the final rounding is inside rtol.  That is k = 6, whatever the order of
+    the additions or the split of the rows into partial sums.
     Returns ``(ok, max_abs_err, max_ratio)``."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref64, np.float64)
@@ -418,18 +422,24 @@ def colsum_tolerance_ok(got, ref64, abs_sum, atol: float = 1e-5, rtol: float = 1
 
 
 def dx_tolerance_ok(got, ref64, scale64, fmt: int | None = None, atol: float = 1e-5, rtol: float = 1e-4,
-                    k: float = 64.0, lib: ctypes.CDLL | None = None):
+                    k: float = 16.0, lib: ctypes.CDLL | None = None):
     """Acceptance for dx: the float32 bound plus k * u * scale (and, for a
     16-bit dx given as patterns with ``fmt``, half a 16-bit ulp).
 
     dx = rstd * (g - mean(g) - xhat * mean(g xhat)) subtracts quantities of
     the size of |g|, mean|g| and |xhat| mean|g xhat| (``dx_scale`` holds
-    rstd times their sum): a float32 evaluation errs by a few u of each local
-    term and by the summation depth times u of each mean.  The kernels' row
-    sums have depth <= 48 (at most 32 values per lane, six cross-lane steps,
-    up to eight waves, the division); the local terms add a few roundings;
-    k = 64 covers both.  When rstd is large (a row of near-zero variance
-    gives ~1/sqrt(eps)), these errors are far above the float32 bound of the
+    rstd times their sum).  Consider any evaluation that forms g, xhat and
+    g xhat in float32 from the float32 inputs, adds a row's terms in float32
+    only within groups of at most eight (a pairwise sum: three roundings),
+    carries the rest of the row sum in float64 in any order and rounds each
+    mean once to float32.  Its errors, in units of u and to first order:
+    g 1, xhat 2; mean(g) 5 of mean|g| (its terms' rounding, the group's
+    three, its own); mean(g xhat) 8 of mean|g xhat| (four for the terms,
+    three, one); xhat * mean(g xhat) 11 of |xhat| mean|g xhat|; then the two
+    subtractions and the product with rstd, one each of the whole scale.  The
+    sum is <= 14 u * scale (the float64 sums add d 2^-53, nothing at these
+    widths); k = 16.  When rstd is large (a row of near-zero variance gives
+    ~1/sqrt(eps)), these errors are far above the float32 bound of the
     forward outputs while the exact dx may be ~0, which is why the bound
     scales with rstd.  Returns ``(ok, max_abs_err, max_ratio)``."""
     ref = np.asarray(ref64, np.float64)

@@ -15,6 +15,16 @@
 // registers; at the end the row slots of the workgroup meet in an LDS tree
 // and the workgroup writes one float32 partial row; a second kernel sums the
 // partial rows in float64 in a fixed order (deterministic results).
+//
+// Accumulation contract: every term (g, g xhat, dy xhat, dy) is formed in
+// float32 from the float32 inputs.  A row's two sums add the terms in
+// groups of at most eight, pairwise, in float32 and carry everything from
+// there in float64 (lanes, waves); each mean is rounded once to float32.  A column sum is carried in float64 per lane, rounded once to
+// float32 per row slot, the slots of a workgroup added in float64 and
+// rounded once to the workgroup's partial row, and the partial rows added in
+// float64 and rounded once.  The error of the results is then bounded by a
+// few float32 roundings of each term, however the rows and columns are split
+// among lanes, waves and workgroups.
 // Rows wider than the held variants take a streamed path: per-row sums first
 // (one workgroup per row), then a two-dimensional grid of column chunks by
 // row blocks that computes dx and the partial sums.
@@ -43,6 +53,69 @@ __device__ __forceinline__ vf<VEC> narrow32(vd<VEC> v) {
     else return __builtin_convertvector(v, vf<VEC>);
 }
 
+// float64 cross-lane moves: the two 32-bit halves move separately.  With
+// every row and bank enabled the destination's old value is not used; a
+// partial row mask keeps zero in the rows not written.
+typedef int i2 __attribute__((ext_vector_type(2)));
+template <int CTRL>
+__device__ __forceinline__ double dpp64(double v) {
+    const i2 b = __builtin_bit_cast(i2, v);
+    i2 r;
+    r.x = __builtin_amdgcn_mov_dpp(b.x, CTRL, 0xF, 0xF, false);
+    r.y = __builtin_amdgcn_mov_dpp(b.y, CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, r);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp64_rows(double v) {
+    const i2 b = __builtin_bit_cast(i2, v);
+    i2 r;
+    r.x = __builtin_amdgcn_update_dpp(0, b.x, CTRL, ROWS, 0xF, false);
+    r.y = __builtin_amdgcn_update_dpp(0, b.y, CTRL, ROWS, 0xF, false);
+    return __builtin_bit_cast(double, r);
+}
+__device__ __forceinline__ double readlane64(double v, int lane) {
+    const i2 b = __builtin_bit_cast(i2, v);
+    i2 r;
+    r.x = __builtin_amdgcn_readlane(b.x, lane);
+    r.y = __builtin_amdgcn_readlane(b.y, lane);
+    return __builtin_bit_cast(double, r);
+}
+
+// Sum over the 64 lanes of a wave in float64, in a fixed order: butterflies
+// within each 16-lane row, then row_bcast:15 adds row 0's sum into row 1 and
+// row 2's into row 3, row_bcast:31 adds rows 0-1 into rows 2-3; lane 63 ends
+// with the total, read into scalars (a wave-uniform result).
+__device__ __forceinline__ double wave_sum64(double v) {
+    v += dpp64<0xB1>(v);            // lane ^ 1
+    v += dpp64<0x4E>(v);            // lane ^ 2
+    v += dpp64<0x141>(v);           // the other quad of each 8 lanes
+    v += dpp64<0x140>(v);           // the other half of each 16-lane row
+    v += dpp64_rows<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp64_rows<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return readlane64(v, 63);
+}
+
+// Pairwise float32 sum of N values (N <= 8: at most three roundings per value)
+template <int N>
+__device__ __forceinline__ float pair_sum(const float *a) {
+    if constexpr (N == 1) return a[0];
+    else return pair_sum<N / 2>(a) + pair_sum<N - N / 2>(a + N / 2);
+}
+
+// Sum over a workgroup's WAVES waves in float64: wave sums, one LDS exchange
+// (double-buffered by slot, so one barrier per call), waves added in order.
+template <int WAVES>
+__device__ __forceinline__ double block_sum64(double v, double (*red)[WAVES], int &slot, int wave, int lane) {
+    v = wave_sum64(v);
+    if (lane == 0) red[slot][wave] = v;
+    __syncthreads();
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) t += red[slot][w];
+    slot ^= 1;
+    return t;
+}
+
 // VEC float32 values stored to consecutive addresses (partial rows)
 template <int VEC>
 __device__ __forceinline__ void stp(float *p, vf<VEC> v) {
@@ -69,7 +142,7 @@ struct BwdParams {
     int64_t lddy, ldx, lddx;
     int32_t d;
     int32_t dpad;         // partial row pitch: d rounded up to a multiple of 4
-    float inv_d;
+    double inv_d;         // 1 / d
 };
 
 // ---------------------------------------------------------------------------
@@ -90,7 +163,6 @@ void norm_bwd_held(BwdParams p)
     constexpr int RPB = WAVES / WPR;
     static_assert(RPB == 1 || RPB == 2 || RPB == 4 || RPB == 8 || RPB == 16, "row slots meet in a binary tree");
     constexpr int NG = (OP == OP_LN) ? 2 : 1;
-    constexpr int CAP = 64 * WPR * Q;  // accesses per row
     using VT = vf<VEC>;
     using DT = vd<VEC>;
 
@@ -101,13 +173,15 @@ void norm_bwd_held(BwdParams p)
     const int rib = wave / WPR;
     const int d = p.d;
     const int nvec = (int)((unsigned)d / VEC);
-    const float inv_d = p.inv_d;
+    const double inv_d = p.inv_d;
 
     // (sum g, sum g xhat) of each wave, double-buffered across steps so one
     // barrier per step suffices
-    __shared__ float2 xch[2][RPB][WPR];
-    // row slots' partial sums meeting pairwise
-    __shared__ VT tree[RPB > 1 ? RPB / 2 : 1][RPB > 1 ? NG * CAP : 1];
+    __shared__ double xch[2][RPB][WPR][2];
+    // the row slots' partial column sums (float32), for the workgroup's sum
+    constexpr int TW = 64 * WPR;   // lanes per row slot
+    constexpr int NV = TW * Q;     // accesses per partial row
+    __shared__ VT stage[RPB > 1 ? RPB : 1][RPB > 1 ? NG : 1][RPB > 1 ? NV : 1];
 
     int kc[Q];
     bool okc[Q];
@@ -173,31 +247,62 @@ void norm_bwd_held(BwdParams p)
         }
 
         // xhat and g are formed twice (here for the sums, below for the
-        // outputs) rather than held: only x and dy stay in registers
-        float s1 = 0.f, s2 = 0.f;
+        // outputs) rather than held: only x and dy stay in registers.  The
+        // terms of a group of eight (one 16-bit access, two float32 ones,
+        // eight single elements) are added pairwise in float32, the groups in
+        // float64.
+        double s1 = 0.0, s2 = 0.0;
+        if constexpr (VEC == 8 || Q == 1) {
 #pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const VT xh = (xv[q] - mu) * rs;
-            const VT g = dv[q] * gam[q];
-            s1 += okc[q] ? hsum(g) : 0.f;
-            s2 += okc[q] ? hsum(g * xh) : 0.f;
+            for (int q = 0; q < Q; ++q) {
+                const VT xh = (xv[q] - mu) * rs;
+                const VT g = dv[q] * gam[q];
+                if (okc[q]) {
+                    if (OP == OP_LN) s1 += (double)hsum(g);
+                    s2 += (double)hsum(g * xh);
+                }
+            }
+        } else {
+            // access q0 + j of a group lies past the row's end when q0 does
+            constexpr int GA = 8 / VEC;  // accesses per group
+#pragma unroll
+            for (int q0 = 0; q0 < Q; q0 += GA) {
+                if (!okc[q0]) continue;
+                float t1[GA], t2[GA];
+#pragma unroll
+                for (int j = 0; j < GA; ++j) {
+                    const int q = q0 + j;
+                    t1[j] = 0.f;
+                    t2[j] = 0.f;
+                    if (q < Q) {
+                        const VT xh = (xv[q] - mu) * rs;
+                        const VT g = dv[q] * gam[q];
+                        t1[j] = okc[q] ? hsum(g) : 0.f;
+                        t2[j] = okc[q] ? hsum(g * xh) : 0.f;
+                    }
+                }
+                if (OP == OP_LN) s1 += (double)pair_sum<GA>(t1);
+                s2 += (double)pair_sum<GA>(t2);
+            }
         }
-        float S1 = (OP == OP_LN) ? group_sum<64>(s1) : 0.f;
-        float S2 = group_sum<64>(s2);
+        double S1 = (OP == OP_LN) ? wave_sum64(s1) : 0.0;
+        double S2 = wave_sum64(s2);
         if constexpr (WPR > 1) {
-            if (lane == 0) xch[par][rib][wr] = make_float2(S1, S2);
+            if (lane == 0) {
+                xch[par][rib][wr][0] = S1;
+                xch[par][rib][wr][1] = S2;
+            }
             __syncthreads();
-            S1 = 0.f;
-            S2 = 0.f;
+            S1 = 0.0;
+            S2 = 0.0;
 #pragma unroll
             for (int w = 0; w < WPR; ++w) {
-                const float2 e = xch[par][rib][w];
-                S1 += e.x;
-                S2 += e.y;
+                S1 += xch[par][rib][w][0];
+                S2 += xch[par][rib][w][1];
             }
             par ^= 1;
         }
-        const float m1 = S1 * inv_d, m2 = S2 * inv_d;
+        const float m1 = (float)(S1 * inv_d), m2 = (float)(S2 * inv_d);
 
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
@@ -222,42 +327,32 @@ void norm_bwd_held(BwdParams p)
     }
     if (!want_pg) return;
 
-    // the workgroup's row slots meet pairwise (float32), slot 0 writes
-    VT pg[Q], pb[Q];
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        pg[q] = narrow32<VEC>(accg[q]);
-        pb[q] = narrow32<VEC>(accb[q]);
-    }
-    if constexpr (RPB > 1) {
-        const int slot = wr * 64 + lane;
-#pragma unroll
-        for (int half = RPB / 2; half >= 1; half /= 2) {
-            if (rib >= half && rib < 2 * half) {
-#pragma unroll
-                for (int q = 0; q < Q; ++q) {
-                    tree[rib - half][slot + 64 * WPR * q] = pg[q];
-                    if constexpr (NG == 2) tree[rib - half][CAP + slot + 64 * WPR * q] = pb[q];
-                }
-            }
-            __syncthreads();
-            if (rib < half) {
-#pragma unroll
-                for (int q = 0; q < Q; ++q) {
-                    pg[q] += tree[rib][slot + 64 * WPR * q];
-                    if constexpr (NG == 2) pb[q] += tree[rib][CAP + slot + 64 * WPR * q];
-                }
-            }
-            __syncthreads();
-        }
-    }
-    if (rib == 0) {
-        float *pr = p.part + (int64_t)blockIdx.x * NG * p.dpad;
+    float *pr = p.part + (int64_t)blockIdx.x * NG * p.dpad;
+    if constexpr (RPB == 1) {
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             if (!okc[q]) continue;
-            stp<VEC>(pr + VEC * kc[q], pg[q]);
-            if constexpr (NG == 2) stp<VEC>(pr + p.dpad + VEC * kc[q], pb[q]);
+            stp<VEC>(pr + VEC * kc[q], narrow32<VEC>(accg[q]));
+            if constexpr (NG == 2) stp<VEC>(pr + p.dpad + VEC * kc[q], narrow32<VEC>(accb[q]));
+        }
+    } else {
+        // each row slot rounds its sums once and stages them; then every
+        // thread takes some accesses of the partial row and adds the slots'
+        // values in float64, in slot order, rounding once
+        const int sl = wr * 64 + lane;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            stage[rib][0][sl + TW * q] = narrow32<VEC>(accg[q]);
+            if constexpr (NG == 2) stage[rib][1][sl + TW * q] = narrow32<VEC>(accb[q]);
+        }
+        __syncthreads();
+        for (int i = tid; i < NG * NV; i += WAVES * 64) {
+            const int gi = i / NV, k = i - gi * NV;
+            if (k >= nvec) continue;
+            DT t = DT(0.0);
+#pragma unroll
+            for (int r = 0; r < RPB; ++r) t += widen64<VEC>(stage[r][gi][k]);
+            stp<VEC>(pr + gi * p.dpad + VEC * k, narrow32<VEC>(t));
         }
     }
 }
@@ -314,13 +409,13 @@ void norm_bwd_reduce(const float *part, int64_t nblk, int32_t d, int32_t dpad, f
 // ---------------------------------------------------------------------------
 // Streamed rows, step 1: per row, stats = (mean_j g, mean_j g xhat); one
 // workgroup of WAVES waves per row (grid-stride), single-element accesses.
-// A lane adds its d / (64 WAVES) terms in float64 so that the rounding of
-// the means stays that of a short sum however wide the row.
+// The sums are carried in float64 (lanes, waves, the workgroup) and each
+// mean is rounded once.
 template <typename T, int OP, int WAVES>
 __global__ __launch_bounds__(WAVES * 64)
 void norm_bwd_rowstats(BwdParams p)
 {
-    __shared__ float red[2][WAVES];
+    __shared__ double red[2][WAVES];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
@@ -337,9 +432,9 @@ void norm_bwd_rowstats(BwdParams p)
             s1 += (double)g;
             s2 += (double)(g * xh);
         }
-        const float S1 = (OP == OP_LN) ? block_sum<WAVES>((float)s1, red, slot, wave, lane) : 0.f;
-        const float S2 = block_sum<WAVES>((float)s2, red, slot, wave, lane);
-        if (tid == 0) p.stats[row] = make_float2(S1 * p.inv_d, S2 * p.inv_d);
+        const double S1 = (OP == OP_LN) ? block_sum64<WAVES>(s1, red, slot, wave, lane) : 0.0;
+        const double S2 = block_sum64<WAVES>(s2, red, slot, wave, lane);
+        if (tid == 0) p.stats[row] = make_float2((float)(S1 * p.inv_d), (float)(S2 * p.inv_d));
     }
 }
 

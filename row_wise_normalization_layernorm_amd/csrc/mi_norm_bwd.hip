@@ -294,7 +294,7 @@ mi_norm_status run_bwd(int forced, const mi_norm_bwd_problem &P, hipStream_t str
     K.rows = P.rows;
     K.d = (int32_t)P.d;
     K.dpad = (int32_t)dpad_of(P.d);
-    K.inv_d = (float)(1.0 / (double)P.d);
+    K.inv_d = 1.0 / (double)P.d;
     int64_t nblk;
     if (!V.info.looped) {
         const int64_t rpb = V.info.rows_per_block;

@@ -688,6 +688,22 @@ def check_bwd16(lib):
     terms32 = (dy * xh32).astype(np.float32)
     got = terms32.astype(np.float64).sum(axis=0).astype(np.float32)
     assert oracle.colsum_tolerance_ok(got, o["dgamma64"], o["abs_dgamma"])[0]
+    # any split of the rows into partial sums and each of those again,
+    # every partial rounded once to float32, and any order of the float64
+    # additions
+    rng = np.random.default_rng(79)
+
+    def split_sum(idx, levels):
+        if levels == 0 or len(idx) < 2:
+            return terms32[idx].astype(np.float64).sum(axis=0).astype(np.float32)
+        parts = int(rng.integers(2, min(len(idx), 64) + 1))
+        cut = np.sort(rng.choice(np.arange(1, len(idx)), parts - 1, replace=False))
+        partial = [split_sum(idx[i:j], levels - 1) for i, j in zip(np.r_[0, cut], np.r_[cut, len(idx)])]
+        return np.sum(np.asarray(partial, np.float64)[rng.permutation(parts)], axis=0).astype(np.float32)
+
+    for levels in (1, 2, 3):
+        split = split_sum(rng.permutation(rows), levels)
+        assert oracle.colsum_tolerance_ok(split, o["dgamma64"], o["abs_dgamma"])[0], levels
     missing = terms32[1:].astype(np.float64).sum(axis=0).astype(np.float32)
     assert not oracle.colsum_tolerance_ok(missing, o["dgamma64"], o["abs_dgamma"])[0]
 
@@ -697,25 +713,40 @@ ALL_CHECKS = ALL_CHECKS + BWD_CHECKS
 
 
 def check_dx_tolerance(lib):
-    """The dx acceptance bound passes a float32 evaluation of the same formula
-    (including rows of zero variance, where rstd ~ 1/sqrt(eps) amplifies its
-    rounding), and refuses dx without the mean of g or with a flipped
-    projection term."""
+    """The dx acceptance bound passes an evaluation of the same formula with
+    every term and product in float32, a row's terms added in float32 in
+    groups of eight consecutive ones and in float64 from there, in either
+    order, each mean rounded once (including rows of zero variance, where
+    rstd ~ 1/sqrt(eps) amplifies the rounding), and refuses dx without the
+    mean of g or with a flipped projection term."""
     for rows, d, pat in ((64, 1, "normal"), (32, 256, "normal"), (16, 8, "zero"), (16, 77, "offset")):
         x = wl.make_x(rows, d, pat, [80, d])
         dy = wl.make_x(rows, d, "normal", [81, d])
         g, _ = wl.make_affine(d, [80, d])
         _, mean, rstd, _, _ = oracle.layernorm(x, g, np.zeros(d, np.float32), float(EPS32), lib=lib)
         ref = oracle.layernorm_bwd(dy, x, g, mean, rstd, lib=lib)
-        # a float32 evaluation: every operation rounded to float32
+        # every term and product rounded to float32; a row's terms summed
+        # pairwise in float32 in groups of eight, the group sums in float64
+        # (forwards, then backwards); each mean rounded once
         f = np.float32
         xh = ((x - mean[:, None]).astype(f) * rstd[:, None]).astype(f)
         gg = (dy * g).astype(f)
-        m1 = (gg.sum(axis=1, dtype=f) * f(1.0 / d)).astype(f)
-        m2 = ((gg * xh).astype(f).sum(axis=1, dtype=f) * f(1.0 / d)).astype(f)
-        dx32 = (rstd[:, None] * ((gg - m1[:, None]).astype(f) - (xh * m2[:, None]).astype(f)).astype(f)).astype(f)
-        ok, _, ratio = oracle.dx_tolerance_ok(dx32, ref["dx64"], ref["dx_scale"])
-        assert ok, f"float32 evaluation refused ({rows}x{d} {pat}, ratio {ratio:.2f})"
+        gx = (gg * xh).astype(f)
+
+        def groups8(t):
+            pad = np.zeros((rows, -(-d // 8) * 8), f)
+            pad[:, :d] = t
+            v = pad.reshape(rows, -1, 8)
+            while v.shape[2] > 1:
+                v = (v[:, :, 0::2] + v[:, :, 1::2]).astype(f)
+            return v[:, :, 0].astype(np.float64)
+
+        for order in (slice(None), slice(None, None, -1)):
+            m1 = (np.cumsum(groups8(gg)[:, order], axis=1)[:, -1] / d).astype(f)
+            m2 = (np.cumsum(groups8(gx)[:, order], axis=1)[:, -1] / d).astype(f)
+            dx32 = (rstd[:, None] * ((gg - m1[:, None]).astype(f) - (xh * m2[:, None]).astype(f)).astype(f)).astype(f)
+            ok, _, ratio = oracle.dx_tolerance_ok(dx32, ref["dx64"], ref["dx_scale"])
+            assert ok, f"float32 evaluation refused ({rows}x{d} {pat}, ratio {ratio:.2f})"
         if d > 1 and pat != "zero":
             bad = ref["dx64"] + rstd[:, None].astype(np.float64) * (gg.astype(np.float64).mean(axis=1))[:, None]
             assert not oracle.dx_tolerance_ok(bad, ref["dx64"], ref["dx_scale"])[0], "mean of g dropped"
