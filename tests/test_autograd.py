@@ -132,20 +132,29 @@ def test_expanded_upstream_gradient_and_inputs(torch_dev):
     the forward is copied the same way, and an expanded output is refused."""
     torch, dev = torch_dev
     print("autograd expanded dy [256x768]", flush=True)
-    x = (torch.randn(256, 768, device=dev) * 3 + 0.5).requires_grad_(True)
-    g = (torch.randn(768, device=dev) * 0.1 + 1).requires_grad_(True)
-    b = (torch.randn(768, device=dev) * 0.1).requires_grad_(True)
+    gen = torch.Generator(device="cpu").manual_seed(31)
+    x = (torch.randn(256, 768, generator=gen) * 3 + 0.5).to(dev).requires_grad_(True)
+    g = (torch.randn(768, generator=gen) * 0.1 + 1).to(dev).requires_grad_(True)
+    b = (torch.randn(768, generator=gen) * 0.1).to(dev).requires_grad_(True)
     y = mn.layer_norm(x, g, b)
     y.sum(0).pow(2).sum().backward()
     torch.cuda.synchronize()
-    # the same loss through torch's own float64 layer norm on the CPU
-    xd = x.detach().cpu().double().requires_grad_(True)
-    gd = g.detach().cpu().double().requires_grad_(True)
-    bd = b.detach().cpu().double().requires_grad_(True)
-    torch.nn.functional.layer_norm(xd, (768,), gd, bd, 1e-5).sum(0).pow(2).sum().backward()
-    for got, want in ((x.grad, xd.grad), (g.grad, gd.grad), (b.grad, bd.grad)):
-        err = (got.cpu().double() - want).abs()
-        assert bool((err <= 1e-4 + 1e-3 * want.abs()).all()), float(err.max())
+    # the upstream gradient autograd handed the backward: 2 * y.sum(0) for
+    # every row (stride 0), from the same forward kernel's y
+    y2, mean, rstd = mn.layernorm(x.detach(), g.detach(), b.detach(), stats=True)
+    assert torch.equal(y2, y.detach())
+    dy = (2 * y2.sum(0)).expand_as(y2)
+    assert dy.stride(0) == 0
+    ref = oracle.layernorm_bwd(dy.contiguous().cpu().numpy(), x.detach().cpu().numpy(), g.detach().cpu().numpy(),
+                               mean.cpu().numpy(), rstd.cpu().numpy())
+    ok, err, ratio = oracle.dx_tolerance_ok(x.grad.cpu().numpy(), ref["dx64"], ref["dx_scale"])
+    assert ok, (err, ratio)
+    for got, key in ((g.grad, "dgamma"), (b.grad, "dbeta")):
+        ok, err, ratio = oracle.colsum_tolerance_ok(got.cpu().numpy(), ref[key + "64"], ref["abs_" + key])
+        assert ok, (key, err, ratio)
+    # the direct call with the expanded gradient gives autograd's bits
+    dx, dg, db = mn.layernorm_bwd(dy, x.detach(), g.detach(), mean, rstd)
+    assert torch.equal(dx, x.grad) and torch.equal(dg, g.grad) and torch.equal(db, b.grad)
 
     row = torch.randn(1, 768, device=dev)
     xe = row.expand(64, 768)

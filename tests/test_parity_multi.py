@@ -93,6 +93,66 @@ def test_multi_row_matches_one_row_bit_for_bit(torch_dev):
                 assert np.array_equal(a, b), name
 
 
+def test_workgroup_twins_match_bit_for_bit(torch_dev):
+    """Variants that differ only in their workgroup's size (how many rows a
+    workgroup holds) sum, merge and normalize each row in the same order, so
+    their outputs agree in every bit.  Among them are the 16-bit rows whose
+    larger workgroups stage the parameters in LDS while the one-row
+    workgroups fetch them in the output pass: the comparison is the
+    regression check on that staging (a 16-byte store followed by an LDS read
+    that reuses its data registers)."""
+    torch, dev = torch_dev
+    infos = _infos()
+    groups = {}
+    for i, n, v in infos:
+        if v["looped"] or v["rows_per_lane"] != 1 or v["op"] not in OPNAME:
+            continue                     # backward variants: test_parity_bwd.py
+        key = (v["op"], v["dtype"], v["vec"], v["peel"], v["lanes_per_row"], v["waves_per_row"], v["slots"])
+        groups.setdefault(key, []).append((i, n, v))
+    twins = [g for g in groups.values() if len(g) > 1]
+    assert len(twins) > 100
+    tdt = {mn.MI_NORM_F32: torch.float32, mn.MI_NORM_F16: torch.float16, mn.MI_NORM_BF16: torch.bfloat16}
+    stream = torch.cuda.current_stream().cuda_stream
+    checked = 0
+    for g in twins:
+        _, name0, v = g[0]
+        op, dt = OPNAME[v["op"]], v["dtype"]
+        ln, add = op.endswith("layernorm"), op.startswith("add_")
+        cap, step = min(u["max_d"] for _, _, u in g), v["vec"]
+        d = max(step, cap - step * max(1, cap // (7 * step)))
+        rows = 2 * max(u["rows_per_block"] for _, _, u in g) + 1
+        x, r, params = inputs(op, dt, rows, d, "offset", [23, v["op"], dt, d])
+
+        def dev_rows(a):
+            if a is None:
+                return None
+            if dt == mn.MI_NORM_F32:
+                return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(tdt[dt])
+
+        X, R = dev_rows(x), dev_rows(r)
+        P = [torch.from_numpy(p).to(dev) for p in params]
+        outs = []
+        for k, name, _ in g:
+            Y = torch.empty(rows, d, dtype=tdt[dt], device=dev)
+            H = torch.empty(rows, d, dtype=tdt[dt], device=dev) if add else None
+            M = torch.empty(rows, device=dev) if ln else None
+            S = torch.empty(rows, device=dev)
+            prob = mn.problem(v["op"], rows, d, X, Y, P[0], P[1] if ln else None, r=R, h=H, dtype=dt,
+                              eps=wl.EPS, mean=M, rstd=S)
+            if not mn.mi_norm_eligible(k, prob):
+                continue
+            say(f"workgroup twins {name} rows={rows} d={d}")
+            mn.mi_norm_fwd_variant(k, prob, stream)
+            torch.cuda.synchronize()
+            outs.append((name, [_bits(t) for t in (Y, H, M, S) if t is not None]))
+        for name, o in outs[1:]:
+            for a, b in zip(outs[0][1], o):
+                assert np.array_equal(a, b), f"{name} differs from {outs[0][0]}"
+            checked += 1
+    assert checked > 100
+
+
 @pytest.mark.parametrize("dt", [pytest.param(mn.MI_NORM_F32, id="f32")] + DT16)
 @pytest.mark.parametrize("op", list(OPNAME.values()))
 def test_multi_row_in_place_and_aliased(torch_dev, dt, op):
