@@ -63,7 +63,7 @@
  *   layout a scalar path with the same results.
  * - Errors: MI_NORM_ERR_INVALID is returned before any launch for a NULL
  *   required pointer, a misaligned pointer, an unknown op or dtype, rows < 0,
- *   d < 1, d > 2^31 - 1, a row stride below d, a size overflow, eps NaN or
+ *   d < 1, d > 2^31 - 2^16, a row stride below d, a size overflow, eps NaN or
  *   negative, or an aliasing pattern the rule above excludes.  rows == 0
  *   returns MI_NORM_OK and launches nothing.
  *   MI_NORM_ERR_HIP reports a failed launch (the HIP error is not kept;
@@ -240,7 +240,7 @@ typedef struct mi_norm_bwd_problem {
     int op;                 /* MI_NORM_OP_LAYERNORM or MI_NORM_OP_RMSNORM */
     int dtype;              /* mi_norm_dtype of dy, x and dx */
     int64_t rows;           /* >= 0 */
-    int64_t d;              /* >= 1 */
+    int64_t d;              /* >= 1 and <= 2^31 - 2^16, as for the forward */
     const void *dy;         /* upstream gradient rows                         (required) */
     int64_t lddy;
     const void *x;          /* the forward's input rows                       (required) */

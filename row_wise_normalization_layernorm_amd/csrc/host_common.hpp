@@ -22,6 +22,12 @@ namespace host {
 constexpr int kDtypes = 3;
 constexpr int kTables = 2 * kDtypes;
 
+// The widest row a problem may have (2^31 - 2^16 elements).  The kernels
+// that stream a row walk it with an int32 element index stepped by at most
+// a few thousand past its last value; this margin below 2^31 keeps every
+// index and step of it representable.
+constexpr int64_t kMaxD = INT32_MAX - 65535;
+
 inline const VariantTable &table_at(int t) {
     switch (t) {
     case 0: return kTableF32;

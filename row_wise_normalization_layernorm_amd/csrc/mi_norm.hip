@@ -296,7 +296,7 @@ bool shape_ok(const mi_norm_problem &P) {
     if (P.op < 0 || P.op >= kOps || P.dtype < 0 || P.dtype >= kDtypes) return false;
     if (!P.x || !P.y || !P.params0 || (kop(P.op) == OP_LN && !P.params1) || (kres(P.op) && !P.r))
         return false;
-    if (P.d < 1 || P.d > INT32_MAX || P.rows < 0) return false;
+    if (P.d < 1 || P.d > kMaxD || P.rows < 0) return false;
     if (!al4(P.params0) || (kop(P.op) == OP_LN && !al4(P.params1))) return false;
     const int64_t es = esize(P.dtype);
     const int64_t raw[4] = {P.ldx, P.ldr, P.ldy, P.ldh};

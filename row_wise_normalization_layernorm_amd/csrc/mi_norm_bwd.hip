@@ -72,7 +72,7 @@ bool bshape_ok(const mi_norm_bwd_problem &P) {
     if ((P.op != MI_NORM_OP_LAYERNORM && P.op != MI_NORM_OP_RMSNORM) || P.dtype < 0 || P.dtype >= kDtypes)
         return false;
     if (!P.dy || !P.x || !P.dx || !P.params0 || !P.rstd || (is_ln(P) && !P.mean)) return false;
-    if (P.d < 1 || P.d > INT32_MAX || P.rows < 0) return false;
+    if (P.d < 1 || P.d > kMaxD || P.rows < 0) return false;
     for (const void *q : {(const void *)P.params0, (const void *)P.rstd, (const void *)(is_ln(P) ? P.mean : nullptr),
                           (const void *)P.dparams0, (const void *)(is_ln(P) ? P.dparams1 : nullptr)})
         if (q && !al4(q)) return false;
@@ -93,7 +93,7 @@ int64_t workspace_needed(const mi_norm_bwd_problem &P) { return part_bytes(P) + 
 // the workspace bytes of *p, or -1 when its op, type or shape is invalid
 int64_t workspace_needed_checked(const mi_norm_bwd_problem &P) {
     if ((P.op != MI_NORM_OP_LAYERNORM && P.op != MI_NORM_OP_RMSNORM) || P.dtype < 0 || P.dtype >= kDtypes ||
-        P.d < 1 || P.d > INT32_MAX || P.rows < 0 || P.rows > INT64_MAX / 64)
+        P.d < 1 || P.d > kMaxD || P.rows < 0 || P.rows > INT64_MAX / 64)
         return -1;
     return workspace_needed(P);
 }

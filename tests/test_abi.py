@@ -635,6 +635,25 @@ def test_bwd_workspace_size(L):
     assert L.mi_norm_bwd_workspace_size(None) == -1
 
 
+def test_widest_row(L):
+    """The widest row accepted is 2^31 - 2^16 elements: the streamed-row
+    kernels step an int32 element index by up to a few thousand past the
+    row's end, which must stay representable.  Far-apart fake pointers keep
+    8 GiB rows from overlapping; nothing is launched."""
+    widest = 2**31 - 2**16
+    x, y, g, b = 1 << 40, 1 << 41, 1 << 42, (1 << 42) + (1 << 36)
+    for op in (mn.OP_LAYERNORM, mn.OP_RMSNORM, mn.OP_ADD_LAYERNORM):
+        for d, want in ((widest, mn.MI_NORM_OK), (widest + 1, mn.MI_NORM_ERR_INVALID)):
+            p = _prob(op, 1, d, x=x, y=y, g=g, b=b, r=1 << 43, h=None)
+            assert mn.mi_norm_check(p) == want, (op, d)
+    assert L.mi_rmsnorm_fwd(x, g, y, 1, widest + 1, 1e-5, None, None) == mn.MI_NORM_ERR_INVALID
+    bw = dict(dy=1 << 40, x=1 << 41, dx=1 << 42, params0=(1 << 43), mean=(1 << 43) + (1 << 36),
+              rstd=(1 << 43) + (1 << 37), dparams0=None, dparams1=None, ws=1 << 44, ws_bytes=1 << 20)
+    assert mn.mi_norm_bwd_check(_bprob(rows=1, d=widest, **bw)) == mn.MI_NORM_OK
+    assert mn.mi_norm_bwd_check(_bprob(rows=1, d=widest + 1, **bw)) == mn.MI_NORM_ERR_INVALID
+    assert mn.mi_norm_bwd_workspace_size(_bprob(rows=1, d=widest + 1, **bw)) == -1
+
+
 def test_bwd_validation(L):
     OK, BAD = mn.MI_NORM_OK, mn.MI_NORM_ERR_INVALID
     chk = lambda **kw: mn.mi_norm_bwd_check(_bprob(**kw))
