@@ -42,10 +42,14 @@ constexpr bool kres(int op) { return op >= 2; }
 // float32 rows at up to eight slots, at twice their bytes, gained nothing).
 // The float32 one-wave rows of sixteen slots stage them too: there the
 // output pass's parameter fetch was the last global round trip of a wave
-// that holds a 16 KiB row.  Everything else reads them in the output pass.
+// that holds a 16 KiB row.  Peeled rows fetch them with the row's loads
+// where the register budget allows (norm_held's default), so that every
+// load has returned before the first store: 7-9% on [256,8193].  Everything
+// else reads them in the output pass.
 constexpr int held_pre(int es, int vec, int peel, int lpr, int wpr, int q, int waves) {
     if (es == 2 && vec == 8 && !peel && lpr == 64 && waves / wpr >= 2 && wpr * q <= 16) return 2;
     if (es == 4 && vec == 4 && !peel && lpr == 64 && wpr == 1 && q == 16 && waves >= 2) return 2;
+    if (peel) return -1;
     return 0;
 }
 

@@ -453,6 +453,13 @@ def test_dispatch_examples(L):
     assert sel(0, 128, rows=512) == "ln_4_p0_l32_w1_q1_b4"
     # a peeled row's body holds at most d / 4 accesses: 8193 fits 16 waves of two
     assert sel(1, 8193, rows=256) == "rms_4_p1_l64_w16_q2_b16"
+    # peeled rows of fewer than eight waves keep the fewest waves that hold
+    # them in four slots, in the largest workgroups that still give every CU one
+    assert sel(0, 2049, rows=1024) == "ln_4_p1_l64_w2_q4_b4"
+    assert sel(1, 4097, rows=1024) == "rms_4_p1_l64_w4_q4_b16"
+    assert sel(0, 1025, rows=2048) == "ln_4_p1_l64_w1_q4_b4"
+    assert sel(0, 8193, rows=512) == "ln_4_p1_l64_w8_q4_b16"
+    assert sel(0, 4100, rows=1024, dtype=mn.MI_NORM_BF16) == "ln_bf16_8_p1_l64_w2_q4_b4"
     assert sel(0, 1, rows=64) == "ln_1_p0_l16_w1_q1_b4"
     assert sel(2, 768) == "addln_4_r2_w1_q3_b4"             # fused: two rows per wave group
     assert sel(2, 768, rows=4095) == "addln_4_p0_l64_w2_q2_b16"

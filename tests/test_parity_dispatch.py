@@ -53,6 +53,11 @@ CASES = [
     # fused float32 rows of two waves up to 4096 rows: one wave of eight slots
     ("add_layernorm", F32, 2049, 1536, "addln_4_p0_l64_w1_q8_b4"),
     ("add_rmsnorm", F32, 4095, 2048, "addrms_4_p0_l64_w1_q8_b4"),
+    # peeled rows of fewer than eight waves: the fewest waves that hold them in
+    # four slots, the largest workgroups that still give every CU one
+    ("layernorm", F32, 1023, 2049, "ln_4_p1_l64_w2_q4_b4"),
+    ("rmsnorm", F32, 1021, 4097, "rms_4_p1_l64_w4_q4_b16"),
+    ("layernorm", BF16, 1001, 4100, "ln_bf16_8_p1_l64_w2_q4_b4"),
     # many rows: two rows per wave group, the base shape's waves and slots
     ("layernorm", F32, 8193, 4096, "ln_4_r2_w4_q4_b4"),
     ("rmsnorm", F32, 8193, 3072, "rms_4_r2_w4_q3_b4"),
