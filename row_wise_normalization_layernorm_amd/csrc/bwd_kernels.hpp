@@ -12,19 +12,20 @@
 // stored from the same registers.  The column part is a reduction across
 // rows, so a lane keeps the same columns for every row its workgroup visits
 // (a grid-stride loop over row groups) and adds its terms into float64
-// registers; at the end the row slots of the workgroup meet in an LDS tree
-// and the workgroup writes one float32 partial row; a second kernel sums the
-// partial rows in float64 in a fixed order (deterministic results).
+// registers; at the end the row slots of the workgroup stage their sums in
+// LDS and the workgroup writes one float32 partial row; a second kernel sums
+// the partial rows in float64 in a fixed order (deterministic results).
 //
 // Accumulation contract: every term (g, g xhat, dy xhat, dy) is formed in
 // float32 from the float32 inputs.  A row's two sums add the terms in
 // groups of at most eight, pairwise, in float32 and carry everything from
-// there in float64 (lanes, waves); each mean is rounded once to float32.  A column sum is carried in float64 per lane, rounded once to
-// float32 per row slot, the slots of a workgroup added in float64 and
-// rounded once to the workgroup's partial row, and the partial rows added in
-// float64 and rounded once.  The error of the results is then bounded by a
-// few float32 roundings of each term, however the rows and columns are split
-// among lanes, waves and workgroups.
+// there in float64 (lanes, waves); each mean is rounded once to float32.
+// A column sum is carried in float64 per lane, rounded once to float32 per
+// row slot, the slots of a workgroup added in float64 and rounded once to
+// the workgroup's partial row, and the partial rows added in float64 and
+// rounded once.  The error of the results is then bounded by a few float32
+// roundings of each term, however the rows and columns are split among
+// lanes, waves and workgroups.
 // Rows wider than the held variants take a streamed path: per-row sums first
 // (one workgroup per row), then a two-dimensional grid of column chunks by
 // row blocks that computes dx and the partial sums.
