@@ -147,6 +147,33 @@ struct BwdParams {
 };
 
 // ---------------------------------------------------------------------------
+// One row slot's inputs for one step of the pipelined loop below: x and dy as
+// loaded (16-byte accesses, or single elements, not yet widened) and the
+// row's statistics.
+template <typename T, int VEC, int Q>
+struct RowIn {
+    using R = std::conditional_t<VEC == 1, uint32_t, u4>;
+    R x[Q], dy[Q];
+    float mu, rs;
+};
+
+// what one access loaded, widened to float32
+template <typename T, int VEC>
+__device__ __forceinline__ vf<VEC> widen_raw(std::conditional_t<VEC == 1, uint32_t, u4> r) {
+    if constexpr (VEC == 1) {
+        if constexpr (std::is_same_v<T, float>) return __builtin_bit_cast(float, r);
+        else return (float)__builtin_bit_cast(T, (uint16_t)r);
+    } else if constexpr (std::is_same_v<T, float>) {
+        static_assert(VEC == 4, "four float32 per access");
+        return __builtin_bit_cast(f4, r);
+    } else {
+        static_assert(VEC == 8 && sizeof(T) == 2, "eight 16-bit elements per access");
+        typedef T t8 __attribute__((ext_vector_type(8)));
+        return __builtin_convertvector(__builtin_bit_cast(t8, r), f8);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Held rows.
 //   T      storage type of dy, x, dx
 //   OP     OP_LN or OP_RMS
@@ -155,6 +182,17 @@ struct BwdParams {
 //   Q      accesses held per lane; capacity VEC * 64 * WPR * Q elements
 // Lane li of wave rank wr holds access k = li + 64 * (wr + WPR * q) of every
 // row its row slot visits.
+//
+// Rows of several waves with at most 16 values per lane run a pipelined
+// loop: two input sets alternate, and a step's loads (raw buffer loads over
+// the row, so a prefetch past the last row moves no data) are issued before
+// the previous step's sums, which wait only for their own set.  The waves of
+// a row meet at a barrier every step, so without the second set a
+// workgroup's loads and its arithmetic never overlap (BF16 LayerNorm
+// [32768,8192] 320 against 273 us, [8192,3072] 61 against 56).  Rows of one
+// wave have no barrier; they keep the loop that prefetches the next row
+// into a copy (with the alternating sets [4096,768] ran 4% and
+// [65536,768] 6% slower).
 template <typename T, int OP, int VEC, int WPR, int Q, int WAVES>
 __global__ __launch_bounds__(WAVES * 64)
 void norm_bwd_held(BwdParams p)
@@ -166,6 +204,7 @@ void norm_bwd_held(BwdParams p)
     constexpr int NG = (OP == OP_LN) ? 2 : 1;
     using VT = vf<VEC>;
     using DT = vd<VEC>;
+    constexpr bool PIPE = WPR > 1 && VEC * Q <= 16;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -207,45 +246,14 @@ void norm_bwd_held(BwdParams p)
     for (int q = 0; q < Q; ++q) gam[q] = ldp<VEC>(p.p0 + VEC * kc[q]);
 
     const int64_t ngroups = (p.rows + RPB - 1) / RPB;
-    // a row slot past the end (last step only) re-reads the last row and
-    // stores nothing; loads stay unconditional at clamped addresses
-    auto row_of = [&](int64_t rg) -> int64_t {
-        const int64_t r = rg * RPB + rib;
-        return r < p.rows ? r : p.rows - 1;
-    };
-    // x and dy of the step's row.  With one wave per row and at most 16
-    // values per lane (PF), also the next step's: its loads are in flight
-    // while this row is reduced and written (4% on [4096,768]; wider rows
-    // gained nothing and would spill with the second copy).
-    constexpr bool PF = WPR == 1 && VEC * Q <= 16;
-    VT xv[Q], dv[Q];
-    auto load_row = [&](int64_t row, VT (&xa)[Q], VT (&da)[Q]) {
-        const T *xr = static_cast<const T *>(p.x) + row * p.ldx;
-        const T *dyr = static_cast<const T *>(p.dy) + row * p.lddy;
-#pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            xa[q] = ldv<T, VEC, true>(xr + VEC * kc[q]);
-            da[q] = ldv<T, VEC, true>(dyr + VEC * kc[q]);
-        }
-    };
-    if constexpr (PF) {
-        if ((int64_t)blockIdx.x < ngroups) load_row(row_of(blockIdx.x), xv, dv);
-    }
     int par = 0;
-    for (int64_t rg = blockIdx.x; rg < ngroups; rg += gridDim.x) {
+    // One step of row group rg: the row's two sums, dx, and the terms of the
+    // column sums.  A row slot past the end (last step only) stores nothing.
+    auto step = [&](int64_t rg, const VT (&xv)[Q], const VT (&dv)[Q], float mu, float rs) {
         const int64_t row_raw = rg * RPB + rib;
         const bool rv = row_raw < p.rows;
         const int64_t row = rv ? row_raw : p.rows - 1;
         T *dxr = static_cast<T *>(p.dx) + row * p.lddx;
-        const float mu = (OP == OP_LN) ? p.mean[row] : 0.f;
-        const float rs = p.rstd[row];
-        VT xn[PF ? Q : 1], dn[PF ? Q : 1];
-        if constexpr (PF) {
-            const int64_t nrg = rg + gridDim.x;
-            if (nrg < ngroups) load_row(row_of(nrg), xn, dn);
-        } else {
-            load_row(row, xv, dv);
-        }
 
         // xhat and g are formed twice (here for the sums, below for the
         // outputs) rather than held: only x and dy stay in registers.  The
@@ -318,11 +326,114 @@ void norm_bwd_held(BwdParams p)
                 if constexpr (OP == OP_LN) accb[q] += widen64<VEC>(dv[q]);
             }
         }
-        if constexpr (PF) {
+    };
+
+    if constexpr (PIPE) {
+        using In = RowIn<T, VEC, Q>;
+        constexpr uint32_t ES = sizeof(T);
+        const uint32_t row_bytes = (uint32_t)d * ES;
+        uint32_t voff[Q];   // past the row's end the range check reads zero
+#pragma unroll
+        for (int q = 0; q < Q; ++q) voff[q] = (uint32_t)(lane + 64 * (wr + WPR * q)) * (ES * VEC);
+        // x, dy and the statistics of row group rg, each through a raw buffer
+        // over exactly what it reads: empty for a row past the end, whose
+        // loads then read zero and move no data
+        auto load = [&](int64_t rg, In &S) {
+            const int64_t r = rg * RPB + rib;
+            const bool ok = r < p.rows;
+            const int64_t rc = ok ? r : p.rows - 1;
+            const auto bx = row_buffer(static_cast<const T *>(p.x) + rc * p.ldx, ok ? row_bytes : 0u);
+            const auto bdy = row_buffer(static_cast<const T *>(p.dy) + rc * p.lddy, ok ? row_bytes : 0u);
 #pragma unroll
             for (int q = 0; q < Q; ++q) {
-                xv[q] = xn[q];
-                dv[q] = dn[q];
+                if constexpr (VEC > 1) {
+                    S.x[q] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(bx, (int)voff[q], 0, 2));
+                    S.dy[q] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(bdy, (int)voff[q], 0, 2));
+                } else if constexpr (ES == 4) {
+                    S.x[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(bx, (int)voff[q], 0, 2);
+                    S.dy[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(bdy, (int)voff[q], 0, 2);
+                } else {
+                    S.x[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(bx, (int)voff[q], 0, 2);
+                    S.dy[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(bdy, (int)voff[q], 0, 2);
+                }
+            }
+            S.mu = 0.f;
+            if constexpr (OP == OP_LN)
+                S.mu = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(row_buffer(p.mean + rc, ok ? 4u : 0u), 0, 0, 0));
+            S.rs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(row_buffer(p.rstd + rc, ok ? 4u : 0u), 0, 0, 0));
+        };
+        // A set's values are used only after this point, which the loads
+        // issued before it may not pass: they stay in flight during the step.
+        auto run = [&](int64_t rg, In &S) {
+#pragma unroll
+            for (int q = 0; q < Q; ++q) asm volatile("" : "+v"(S.x[q]), "+v"(S.dy[q])::"memory");
+            asm volatile("" : "+v"(S.mu), "+v"(S.rs)::"memory");
+            VT xv[Q], dv[Q];
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                xv[q] = widen_raw<T, VEC>(S.x[q]);
+                dv[q] = widen_raw<T, VEC>(S.dy[q]);
+            }
+            step(rg, xv, dv, S.mu, S.rs);
+        };
+        const int64_t G = gridDim.x;
+        int64_t rg = blockIdx.x;
+        if (rg < ngroups) {
+            In A, B;
+            load(rg, A);
+            for (;;) {
+                load(rg + G, B);
+                run(rg, A);
+                if (rg + G >= ngroups) break;
+                load(rg + 2 * G, A);
+                run(rg + G, B);
+                rg += 2 * G;
+                if (rg >= ngroups) break;
+            }
+        }
+    } else {
+        // a row slot past the end re-reads the last row; loads stay
+        // unconditional at clamped addresses
+        auto row_of = [&](int64_t rg) -> int64_t {
+            const int64_t r = rg * RPB + rib;
+            return r < p.rows ? r : p.rows - 1;
+        };
+        // x and dy of the step's row.  With one wave per row and at most 16
+        // values per lane (PF), also the next step's: its loads are in flight
+        // while this row is reduced and written (4% on [4096,768]; wider rows
+        // gained nothing and would spill with the second copy).
+        constexpr bool PF = WPR == 1 && VEC * Q <= 16;
+        VT xv[Q], dv[Q];
+        auto load_row = [&](int64_t row, VT (&xa)[Q], VT (&da)[Q]) {
+            const T *xr = static_cast<const T *>(p.x) + row * p.ldx;
+            const T *dyr = static_cast<const T *>(p.dy) + row * p.lddy;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                xa[q] = ldv<T, VEC, true>(xr + VEC * kc[q]);
+                da[q] = ldv<T, VEC, true>(dyr + VEC * kc[q]);
+            }
+        };
+        if constexpr (PF) {
+            if ((int64_t)blockIdx.x < ngroups) load_row(row_of(blockIdx.x), xv, dv);
+        }
+        for (int64_t rg = blockIdx.x; rg < ngroups; rg += gridDim.x) {
+            const int64_t row = row_of(rg);
+            const float mu = (OP == OP_LN) ? p.mean[row] : 0.f;
+            const float rs = p.rstd[row];
+            VT xn[PF ? Q : 1], dn[PF ? Q : 1];
+            if constexpr (PF) {
+                const int64_t nrg = rg + gridDim.x;
+                if (nrg < ngroups) load_row(row_of(nrg), xn, dn);
+            } else {
+                load_row(row, xv, dv);
+            }
+            step(rg, xv, dv, mu, rs);
+            if constexpr (PF) {
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    xv[q] = xn[q];
+                    dv[q] = dn[q];
+                }
             }
         }
     }

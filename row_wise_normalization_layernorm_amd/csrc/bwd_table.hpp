@@ -2,7 +2,7 @@
 // table per storage type, instantiated in bwd_variants_{f32,f16,bf16}.hip.
 //
 // Held variants run 8 waves per workgroup: WPR waves per row and 8 / WPR
-// rows per step; a few float32 ones run 16 waves (16 / WPR rows per step).
+// rows per step.
 // Vector variants hold VW elements per access (4 float32, 8 of a 16-bit
 // type), single-element variants 1.  A float32 or a 16-bit lane
 // holds at most 8 or 4 vector accesses of x and dy plus float64 column sums,
@@ -18,23 +18,6 @@
                                  (int64_t)VEC * 64 * WPR * Q, VEC > 1 ? 1 : 0, 1},               \
             reinterpret_cast<const void *>(                                                     \
                 &norm_bwd_held<T, (OPC == MI_NORM_OP_LAYERNORM_BWD ? OP_LN : OP_RMS), VEC, WPR, Q, 8>)}
-
-#define MI_BWD_HELD16(T, DT, OPC, OPN, VEC, WPR, Q)                                             \
-    Variant{OPN "_" #VEC "_w" #WPR "_q" #Q "_b16",                                               \
-            mi_norm_variant_info{OPC, DT, VEC, 0, 0, 64, WPR, Q, 16, 16 / WPR,                   \
-                                 (int64_t)VEC * 64 * WPR * Q, VEC > 1 ? 1 : 0, 1},               \
-            reinterpret_cast<const void *>(                                                     \
-                &norm_bwd_held<T, (OPC == MI_NORM_OP_LAYERNORM_BWD ? OP_LN : OP_RMS), VEC, WPR, Q, 16>)}
-// float32 rows of two to eight waves also in 16-wave workgroups, twice the
-// rows in flight per CU; at most three slots (LayerNorm's four slots spill
-// past the 128 VGPRs a 16-wave workgroup allows)
-#define MI_BWD_B16_OP(T, DT, OPC, OPN)                                                         \
-    , MI_BWD_HELD16(T, DT, OPC, OPN, 4, 2, 3), MI_BWD_HELD16(T, DT, OPC, OPN, 4, 4, 2),          \
-    MI_BWD_HELD16(T, DT, OPC, OPN, 4, 4, 3), MI_BWD_HELD16(T, DT, OPC, OPN, 4, 8, 2)
-#define MI_BWD_B16_4(T, DT, SFX)                                                               \
-    MI_BWD_B16_OP(T, DT, MI_NORM_OP_LAYERNORM_BWD, "lnbwd" SFX)                                 \
-    MI_BWD_B16_OP(T, DT, MI_NORM_OP_RMSNORM_BWD, "rmsbwd" SFX)
-#define MI_BWD_B16_8(T, DT, SFX)
 
 // streamed rows: the column-chunk kernel (4 waves, 8 elements per lane)
 #define MI_BWD_STREAM(T, DT, OPC, OPN)                                                         \
@@ -81,5 +64,4 @@
     MI_BWD_STREAM(T, DT, MI_NORM_OP_LAYERNORM_BWD, "lnbwd" SFX),                               \
     MI_BWD_VEC_RMS_##VW(T, DT, MI_NORM_OP_RMSNORM_BWD, "rmsbwd" SFX),                          \
     MI_BWD_SCALAR(T, DT, MI_NORM_OP_RMSNORM_BWD, "rmsbwd" SFX),                                \
-    MI_BWD_STREAM(T, DT, MI_NORM_OP_RMSNORM_BWD, "rmsbwd" SFX)                                 \
-    MI_BWD_B16_##VW(T, DT, SFX)
+    MI_BWD_STREAM(T, DT, MI_NORM_OP_RMSNORM_BWD, "rmsbwd" SFX)

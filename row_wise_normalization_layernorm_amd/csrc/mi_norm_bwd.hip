@@ -128,10 +128,19 @@ int max_slots(int op, int W) {
     return W == 4 ? 8 : 4;
 }
 
-// One wave per row while up to four (at most max_slots) slots hold it, else
-// the fewest of 2, 4, 8 waves per row that hold it in at most four slots
-// (at 8 waves, up to max_slots); single-element rows likewise with 1-8
-// slots for one wave, 4-16 for more.
+// One wave per row while up to four (at most max_slots) slots hold it.
+// Wider rows take the fewest of 2 and 4 waves whose lanes hold them in at
+// most three float32 slots or two 16-bit ones (12 or 16 values, which the
+// pipelined loop of norm_bwd_held keeps two of), else 8 waves with up to
+// max_slots; single-element rows likewise with 1-8 slots for one wave, 4-16
+// for more.  Measured with the pipelined loop (8-wave workgroups): LayerNorm
+// [4096,2048] 24.0 us at four waves of two slots against 24.1 at two of
+// four, [65536,2048] 263 against 278, [8192,4096] 71.0 against 73.1; RMSNorm
+// [8192,4096] 67.7 against 70.3; BF16 RMSNorm [8192,8192] 70.8 against 77.0,
+// [16384,4096] 69.1 against 75.4, BF16 LayerNorm [4096,6144] 37.1 against
+// 42.1.  16-wave workgroups, which had doubled the rows in flight per CU
+// before the pipelined loop, now ran no faster (LayerNorm [4096,3072] 32.9
+// against 36.6, [8192,4096] 71.0 against 72.5).
 int select_bwd(const mi_norm_bwd_problem &P) {
     if (!bshape_ok(P)) return -1;
     const int op = P.op, dt = P.dtype;
@@ -147,20 +156,9 @@ int select_bwd(const mi_norm_bwd_problem &P) {
             wpr = 1;
             q = pick_q(nvec, 64, qs, q4 == 3 ? 3 : 4);
         } else {
-            wpr = nvec <= 128 * q4 ? 2 : (nvec <= 256 * q4 ? 4 : 8);
-            q = pick_q(nvec, 64 * wpr, qs + 1, (wpr == 8 ? nq : (q4 == 3 ? 3 : 4)) - 1);
-        }
-        // float32 rows of two or four waves: 16-wave workgroups, twice the
-        // rows in flight per CU (one step of 16 / wpr rows where 8 waves
-        // take two); four slots move to twice the waves at two.  Measured
-        // from 1024 to 65536 rows: LN [4096,1536] 20.6 against 22.2 us,
-        // [4096,2048] 25.6 against 26.5, [65536,2048] 263 against 269,
-        // [8192,4096] 74.6 against 76.2; RMSNorm [4096,1536] 19.3 against
-        // 20.7, [8192,2048] 39.9 against 40.7.  One-wave rows (from 4096
-        // rows) and eight-wave rows of four slots ran slower so.
-        if (q && dt == MI_NORM_F32 && (wpr == 2 || wpr == 4)) {
-            const int id = q == 4 ? find_bwd(op, dt, W, 0, 2 * wpr, 2, 16) : find_bwd(op, dt, W, 0, wpr, q, 16);
-            if (id >= 0) return id;
+            const int c = W == 4 ? 3 : 2;   // slots of the pipelined rows of 2 and 4 waves
+            wpr = nvec <= 128 * c ? 2 : (nvec <= 256 * c ? 4 : 8);
+            q = pick_q(nvec, 64 * wpr, qs + 1, (wpr == 8 ? nq : c) - 1);
         }
         if (q) return find_bwd(op, dt, W, 0, wpr, q);
         return find_bwd(op, dt, 1, 1, 0, 0);

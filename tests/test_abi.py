@@ -256,12 +256,7 @@ def test_variant_table_is_consistent(L):
             assert v["max_d"] == 2**63 - 1 and v["vec"] == 1 and v["needs_aligned"] == 0
             continue
         assert v["rows_per_block"] * v["waves_per_row"] == v["waves_per_block"]
-        if v["waves_per_block"] == 16:
-            # float32 rows of two to eight waves, at most three slots
-            assert v["dtype"] == mn.MI_NORM_F32 and v["vec"] == 4, n
-            assert v["waves_per_row"] >= 2 and v["slots"] <= 3 and n.endswith("_b16"), n
-        else:
-            assert v["waves_per_block"] == 8 and n.endswith("_b8"), n
+        assert v["waves_per_block"] == 8 and n.endswith("_b8"), n
         assert v["max_d"] == v["vec"] * 64 * v["waves_per_row"] * v["slots"]
         assert v["needs_aligned"] == (1 if v["vec"] > 1 else 0)
         assert v["vec"] in (1, 16 // ESIZE[v["dtype"]])
@@ -694,15 +689,15 @@ def test_bwd_dispatch(L):
     name = lambda **kw: mn.mi_norm_variant_name(mn.mi_norm_bwd_select(_bprob(**kw)))
     assert name(rows=4096, d=768) == "lnbwd_4_w1_q3_b8"
     assert name(rows=32768, d=8192) == "lnbwd_4_w8_q4_b8"
-    # float32 rows of two or four waves: 16-wave workgroups; four slots
-    # become twice the waves at two
+    # rows of several waves: the fewest of 2 and 4 waves with at most three
+    # float32 slots or two 16-bit ones, else 8 waves
     assert name(rows=4096, d=1024) == "lnbwd_4_w1_q4_b8"
-    assert name(rows=4096, d=1536) == "lnbwd_4_w2_q3_b16"
-    assert name(rows=65536, d=2048) == "lnbwd_4_w4_q2_b16"
-    assert name(rows=4096, d=3072) == "lnbwd_4_w4_q3_b16"
-    assert name(rows=8192, d=4096) == "lnbwd_4_w8_q2_b16"
-    assert name(op=mn.OP_RMSNORM, rows=8192, d=2048) == "rmsbwd_4_w4_q2_b16"
-    assert name(op=mn.OP_RMSNORM, rows=2048, d=4096) == "rmsbwd_4_w8_q2_b16"
+    assert name(rows=4096, d=1536) == "lnbwd_4_w2_q3_b8"
+    assert name(rows=65536, d=2048) == "lnbwd_4_w4_q2_b8"
+    assert name(rows=4096, d=3072) == "lnbwd_4_w4_q3_b8"
+    assert name(rows=8192, d=4096) == "lnbwd_4_w8_q2_b8"
+    assert name(op=mn.OP_RMSNORM, rows=8192, d=2048) == "rmsbwd_4_w4_q2_b8"
+    assert name(op=mn.OP_RMSNORM, rows=2048, d=4096) == "rmsbwd_4_w8_q2_b8"
     assert name(op=mn.OP_RMSNORM, rows=8192, d=8192) == "rmsbwd_4_w8_q4_b8"
     assert name(dtype=mn.MI_NORM_BF16, d=4096) == "lnbwd_bf16_8_w4_q2_b8"
     assert name(op=mn.OP_RMSNORM, d=16384) == "rmsbwd_4_w8_q8_b8"
@@ -712,6 +707,10 @@ def test_bwd_dispatch(L):
     assert name(dtype=mn.MI_NORM_BF16, d=768) == "lnbwd_bf16_8_w1_q2_b8"
     assert name(dtype=mn.MI_NORM_BF16, op=mn.OP_RMSNORM, d=2048) == "rmsbwd_bf16_8_w1_q4_b8"
     assert name(dtype=mn.MI_NORM_BF16, d=2048) == "lnbwd_bf16_8_w2_q2_b8"
+    assert name(dtype=mn.MI_NORM_BF16, d=3072) == "lnbwd_bf16_8_w4_q2_b8"
+    assert name(dtype=mn.MI_NORM_BF16, d=6144) == "lnbwd_bf16_8_w8_q2_b8"
+    assert name(dtype=mn.MI_NORM_BF16, op=mn.OP_RMSNORM, d=4096) == "rmsbwd_bf16_8_w4_q2_b8"
+    assert name(dtype=mn.MI_NORM_BF16, op=mn.OP_RMSNORM, d=8192) == "rmsbwd_bf16_8_w8_q2_b8"
     assert name(d=767) == "lnbwd_1_w2_q8_b8"                  # scalar: 767 elements over 2 waves
     assert name(x=X + 4) == "lnbwd_1_w2_q8_b8"
     assert name(d=9000, x=X + 4) == "lnbwd_1_stream_b4_u8"

@@ -154,21 +154,30 @@ def test_bwd_wide_and_streamed(torch_dev, op, dt):
         run_bwd_case(torch, dev, op, dt, dy, x, p0, mean, rstd, ld={"dy": d + 8, "x": d + 16, "dx": d + 24})
 
 
-# --- the dispatcher's 16-wave workgroups (float32 rows of two or four waves) ---
+# --- the pipelined loop (rows of several waves) --------------------------------
+# Row counts that leave the last step's row slots partly empty, workgroups of
+# one step (the prefetch runs past the last row), and odd and even step counts.
 
-SIXTEEN = [("layernorm", 4099, 1536, "lnbwd_4_w2_q3_b16"), ("layernorm", 2051, 2048, "lnbwd_4_w4_q2_b16"),
-           ("layernorm", 1027, 3072, "lnbwd_4_w4_q3_b16"), ("layernorm", 515, 4096, "lnbwd_4_w8_q2_b16"),
-           ("rmsnorm", 4099, 1536, "rmsbwd_4_w2_q3_b16"), ("rmsnorm", 2051, 2048, "rmsbwd_4_w4_q2_b16"),
-           ("rmsnorm", 1027, 3072, "rmsbwd_4_w4_q3_b16"), ("rmsnorm", 515, 4096, "rmsbwd_4_w8_q2_b16")]
+PIPELINED = [("layernorm", mn.MI_NORM_F32, 4099, 1536, "lnbwd_4_w2_q3_b8"),
+             ("layernorm", mn.MI_NORM_F32, 2051, 2048, "lnbwd_4_w4_q2_b8"),
+             ("layernorm", mn.MI_NORM_F32, 1027, 3072, "lnbwd_4_w4_q3_b8"),
+             ("layernorm", mn.MI_NORM_F32, 515, 4096, "lnbwd_4_w8_q2_b8"),
+             ("layernorm", mn.MI_NORM_F32, 100, 4096, "lnbwd_4_w8_q2_b8"),
+             ("rmsnorm", mn.MI_NORM_F32, 4099, 1536, "rmsbwd_4_w2_q3_b8"),
+             ("rmsnorm", mn.MI_NORM_F32, 2051, 2048, "rmsbwd_4_w4_q2_b8"),
+             ("rmsnorm", mn.MI_NORM_F32, 777, 8192, "rmsbwd_4_w8_q4_b8"),
+             ("layernorm", mn.MI_NORM_BF16, 1029, 6144, "lnbwd_bf16_8_w8_q2_b8"),
+             ("layernorm", mn.MI_NORM_F16, 1023, 3072, "lnbwd_f16_8_w4_q2_b8"),
+             ("rmsnorm", mn.MI_NORM_BF16, 517, 8192, "rmsbwd_bf16_8_w8_q2_b8"),
+             ("rmsnorm", mn.MI_NORM_BF16, 30, 4096, "rmsbwd_bf16_8_w4_q2_b8")]
 
 
-@pytest.mark.parametrize("op,rows,d,name", SIXTEEN)
-def test_bwd_sixteen_wave_dispatch(torch_dev, op, rows, d, name):
-    """Row counts that leave the last step's row slots partly empty."""
+@pytest.mark.parametrize("op,dt,rows,d,name", PIPELINED)
+def test_bwd_pipelined_dispatch(torch_dev, op, dt, rows, d, name):
     torch, dev = torch_dev
-    say(f"bwd 16-wave {op} [{rows}x{d}] {name}")
-    dy, x, p0, mean, rstd = bwd_inputs(op, mn.MI_NORM_F32, rows, d, "offset", [36, rows, d])
-    run_bwd_case(torch, dev, op, mn.MI_NORM_F32, dy, x, p0, mean, rstd, expect=name)
+    say(f"bwd pipelined {op} dt={dt} [{rows}x{d}] {name}")
+    dy, x, p0, mean, rstd = bwd_inputs(op, dt, rows, d, "offset", [36, rows, d])
+    run_bwd_case(torch, dev, op, dt, dy, x, p0, mean, rstd, expect=name)
 
 
 # --- every compiled backward variant, forced ----------------------------------
