@@ -15,6 +15,8 @@
 // registers; at the end the row slots of the workgroup stage their sums in
 // LDS and the workgroup writes one float32 partial row; a second kernel sums
 // the partial rows in float64 in a fixed order (deterministic results).
+// Rows of several waves load each step's inputs while the previous step
+// runs (two input sets; see norm_bwd_held).
 //
 // Accumulation contract: every term (g, g xhat, dy xhat, dy) is formed in
 // float32 from the float32 inputs.  A row's two sums add the terms in
