@@ -223,7 +223,8 @@ def test_bwd_every_variant(torch_dev):
 @pytest.mark.parametrize("dx_mode", ["dy", "x"])
 def test_bwd_in_place(torch_dev, op, dt, dx_mode):
     torch, dev = torch_dev
-    for rows, d in ((300, 768), (33, 2049), (4, 40000)):
+    # one-wave rows, pipelined vector rows, pipelined single-element rows, streamed rows
+    for rows, d in ((300, 768), (515, 3072), (33, 2049), (4, 40000)):
         say(f"bwd in place {op} dt={dt} dx={dx_mode} [{rows}x{d}]")
         dy, x, p0, mean, rstd = bwd_inputs(op, dt, rows, d, "offset", [35, rows, d])
         ld = d + 8
@@ -281,11 +282,12 @@ def test_bwd_stream_ordering_and_repeat(torch_dev):
     assert oracle.colsum_tolerance_ok(dg1.cpu().numpy(), r1["dgamma64"], r1["abs_dgamma"])[0]
 
 
-def test_bwd_deterministic(torch_dev):
-    """The parameter gradients come out bit for bit the same on every call."""
+@pytest.mark.parametrize("rows,d", [(8192, 1024), (4099, 3072)])
+def test_bwd_deterministic(torch_dev, rows, d):
+    """dx and the parameter gradients come out bit for bit the same on every
+    call (one-wave rows, and the pipelined loop of rows of several waves)."""
     torch, dev = torch_dev
-    rows, d = 8192, 1024
-    say("bwd deterministic")
+    say(f"bwd deterministic [{rows}x{d}]")
     dy, x, p0, mean, rstd = bwd_inputs("layernorm", mn.MI_NORM_F32, rows, d, "offset", [39])
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     outs = [mn.layernorm_bwd(t(dy), t(x), t(p0), t(mean), t(rstd)) for _ in range(3)]
