@@ -540,17 +540,22 @@ void norm_bwd_reduce(const float *part, int64_t nblk, int32_t d, int32_t dpad, f
 
 // ---------------------------------------------------------------------------
 // Streamed rows, step 1: per row, stats = (mean_j g, mean_j g xhat); one
-// workgroup of WAVES waves per row (grid-stride), single-element accesses.
-// The sums are carried in float64 (lanes, waves, the workgroup) and each
-// mean is rounded once.
-template <typename T, int OP, int WAVES>
+// workgroup of WAVES waves per row (grid-stride).  VEC elements per access
+// (16-byte accesses on aligned rows, else single elements), U accesses per
+// lane in flight.  The terms of an access are added pairwise in float32 (a
+// group of at most eight), the groups in float64 (lanes, waves, the
+// workgroup), and each mean is rounded once.
+template <typename T, int OP, int VEC, int WAVES, int U>
 __global__ __launch_bounds__(WAVES * 64)
 void norm_bwd_rowstats(BwdParams p)
 {
+    using VT = vf<VEC>;
+    constexpr int NT = WAVES * 64;
     __shared__ double red[2][WAVES];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
+    const int nvec = (int)((unsigned)p.d / VEC);
     int slot = 0;
     for (int64_t row = blockIdx.x; row < p.rows; row += gridDim.x) {
         const T *xr = static_cast<const T *>(p.x) + row * p.ldx;
@@ -558,11 +563,24 @@ void norm_bwd_rowstats(BwdParams p)
         const float mu = (OP == OP_LN) ? p.mean[row] : 0.f;
         const float rs = p.rstd[row];
         double s1 = 0.0, s2 = 0.0;
-        for (int j = tid; j < p.d; j += WAVES * 64) {
-            const float xh = (lde<T, false>(xr + j) - mu) * rs;
-            const float g = lde<T, false>(dyr + j) * p.p0[j];
-            s1 += (double)g;
-            s2 += (double)(g * xh);
+        for (int k0 = tid; k0 < nvec; k0 += NT * U) {
+            VT xv[U], dv[U], gv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k = k0 + NT * u;
+                const int kc = k < nvec ? k : nvec - 1;
+                xv[u] = ldv<T, VEC, true>(xr + VEC * kc);
+                dv[u] = ldv<T, VEC, true>(dyr + VEC * kc);
+                gv[u] = ldp<VEC>(p.p0 + VEC * kc);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (k0 + NT * u >= nvec) continue;
+                const VT xh = (xv[u] - mu) * rs;
+                const VT g = dv[u] * gv[u];
+                if (OP == OP_LN) s1 += (double)hsum(g);
+                s2 += (double)hsum(g * xh);
+            }
         }
         const double S1 = (OP == OP_LN) ? block_sum64<WAVES>(s1, red, slot, wave, lane) : 0.0;
         const double S2 = block_sum64<WAVES>(s2, red, slot, wave, lane);
@@ -571,54 +589,69 @@ void norm_bwd_rowstats(BwdParams p)
 }
 
 // Streamed rows, step 2: workgroup (blockIdx.x, blockIdx.y) covers column
-// chunk x (WAVES * 64 * U elements, single-element accesses) of the rows of
-// row block y; it writes dx there and the block's partial sums of those
-// columns into partial row y.
-template <typename T, int OP, int WAVES, int U>
+// chunk x (WAVES * 64 * U accesses of VEC elements) of the rows of row block
+// y; it writes dx there and the block's partial sums of those columns into
+// partial row y.  The next row's x and dy are loaded while a row is written.
+template <typename T, int OP, int VEC, int WAVES, int U>
 __global__ __launch_bounds__(WAVES * 64)
 void norm_bwd_chunks(BwdParams p, int64_t rows_per_block)
 {
+    using VT = vf<VEC>;
+    using DT = vd<VEC>;
     constexpr int NG = (OP == OP_LN) ? 2 : 1;
     constexpr int NT = WAVES * 64;
     const int tid = threadIdx.x;
-    const int64_t c0 = (int64_t)blockIdx.x * NT * U;
+    const int nvec = (int)((unsigned)p.d / VEC);
+    const int64_t k0 = (int64_t)blockIdx.x * NT * U + tid;
     const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
     const int64_t r1 = r0 + rows_per_block < p.rows ? r0 + rows_per_block : p.rows;
-    double accg[U], accb[U];
-    float gm[U];
+    DT accg[U], accb[U];
+    VT gm[U];
+    int kc[U];
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t j = c0 + tid + NT * u;
-        ok[u] = j < p.d;
-        gm[u] = ok[u] ? p.p0[j] : 0.f;
-        accg[u] = 0.0;
-        accb[u] = 0.0;
+        const int64_t k = k0 + NT * u;
+        ok[u] = k < nvec;
+        kc[u] = ok[u] ? (int)k : nvec - 1;
+        gm[u] = ldp<VEC>(p.p0 + VEC * kc[u]);
+        accg[u] = DT(0.0);
+        accb[u] = DT(0.0);
     }
-    for (int64_t row = r0; row < r1; ++row) {
+    VT xv[U], dv[U];
+    auto load_row = [&](int64_t row, VT (&xa)[U], VT (&da)[U]) {
         const T *xr = static_cast<const T *>(p.x) + row * p.ldx;
         const T *dyr = static_cast<const T *>(p.dy) + row * p.lddy;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            xa[u] = ldv<T, VEC, true>(xr + VEC * kc[u]);
+            da[u] = ldv<T, VEC, true>(dyr + VEC * kc[u]);
+        }
+    };
+    if (r0 < r1) load_row(r0, xv, dv);
+    for (int64_t row = r0; row < r1; ++row) {
         T *dxr = static_cast<T *>(p.dx) + row * p.lddx;
         const float mu = (OP == OP_LN) ? p.mean[row] : 0.f;
         const float rs = p.rstd[row];
         const float2 st = p.stats[row];
-        float xv[U], dv[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t j = c0 + tid + NT * u;
-            xv[u] = ok[u] ? lde<T, false>(xr + j) : 0.f;
-            dv[u] = ok[u] ? lde<T, false>(dyr + j) : 0.f;
-        }
+        VT xn[U], dn[U];
+        if (row + 1 < r1) load_row(row + 1, xn, dn);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (!ok[u]) continue;
-            const int64_t j = c0 + tid + NT * u;
-            const float xh = (xv[u] - mu) * rs;
-            const float g = dv[u] * gm[u];
-            const float o = (OP == OP_LN) ? rs * (g - st.x - xh * st.y) : rs * (g - xh * st.y);
-            ste<T, false>(dxr + j, o);
-            accg[u] += (double)(dv[u] * xh);
-            accb[u] += (double)dv[u];
+            const VT xh = (xv[u] - mu) * rs;
+            const VT g = dv[u] * gm[u];
+            VT o;
+            if constexpr (OP == OP_LN) o = rs * (g - st.x - xh * st.y);
+            else o = rs * (g - xh * st.y);
+            stv<T, VEC, true>(dxr + VEC * kc[u], o);
+            accg[u] += widen64<VEC>(dv[u] * xh);
+            if constexpr (OP == OP_LN) accb[u] += widen64<VEC>(dv[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            xv[u] = xn[u];
+            dv[u] = dn[u];
         }
     }
     if (p.part == nullptr) return;
@@ -626,9 +659,8 @@ void norm_bwd_chunks(BwdParams p, int64_t rows_per_block)
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if (!ok[u]) continue;
-        const int64_t j = c0 + tid + NT * u;
-        pr[j] = (float)accg[u];
-        if constexpr (NG == 2) pr[p.dpad + j] = (float)accb[u];
+        stp<VEC>(pr + VEC * kc[u], narrow32<VEC>(accg[u]));
+        if constexpr (NG == 2) stp<VEC>(pr + p.dpad + VEC * kc[u], narrow32<VEC>(accb[u]));
     }
 }
 

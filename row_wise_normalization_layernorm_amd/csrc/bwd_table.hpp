@@ -19,12 +19,19 @@
             reinterpret_cast<const void *>(                                                     \
                 &norm_bwd_held<T, (OPC == MI_NORM_OP_LAYERNORM_BWD ? OP_LN : OP_RMS), VEC, WPR, Q, 8>)}
 
-// streamed rows: the column-chunk kernel (4 waves, 8 elements per lane)
-#define MI_BWD_STREAM(T, DT, OPC, OPN)                                                         \
-    Variant{OPN "_1_stream_b4_u8",                                                              \
-            mi_norm_variant_info{OPC, DT, 1, 0, 1, 64, 4, 8, 4, 1, kUnbounded, 0, 1},          \
+// streamed rows: the column-chunk kernel, 4 waves; single elements (8 per
+// lane per row) on any layout, 16-byte accesses (two float32 or one 16-bit
+// per lane per row) on aligned rows
+#define MI_BWD_STREAM_V(T, DT, OPC, OPN, VEC, U)                                               \
+    Variant{OPN "_" #VEC "_stream_b4_u" #U,                                                     \
+            mi_norm_variant_info{OPC, DT, VEC, 0, 1, 64, 4, U, 4, 1, kUnbounded, VEC > 1 ? 1 : 0, 1}, \
             reinterpret_cast<const void *>(                                                     \
-                &norm_bwd_chunks<T, (OPC == MI_NORM_OP_LAYERNORM_BWD ? OP_LN : OP_RMS), 4, 8>)}
+                &norm_bwd_chunks<T, (OPC == MI_NORM_OP_LAYERNORM_BWD ? OP_LN : OP_RMS), VEC, 4, U>)}
+#define MI_BWD_STREAM_X(T, DT, OPC, OPN, VW, U) MI_BWD_STREAM_V(T, DT, OPC, OPN, VW, U)
+#define MI_BWD_STREAM(T, DT, OPC, OPN, VW)                                                     \
+    MI_BWD_STREAM_V(T, DT, OPC, OPN, 1, 8), MI_BWD_STREAM_X(T, DT, OPC, OPN, VW, MI_BWD_STREAM_U##VW)
+#define MI_BWD_STREAM_U4 2
+#define MI_BWD_STREAM_U8 1
 
 // vector accesses: one wave per row with 1-4 slots, then 2, 4, 8 waves per
 // row with 2-4 slots (float32 also 6 and 8 at 8 waves per row).  LayerNorm
@@ -61,7 +68,7 @@
 #define MI_BWD_DTYPE_TABLE(T, DT, VW, SFX)                                                     \
     MI_BWD_VEC_LN_##VW(T, DT, MI_NORM_OP_LAYERNORM_BWD, "lnbwd" SFX),                          \
     MI_BWD_SCALAR(T, DT, MI_NORM_OP_LAYERNORM_BWD, "lnbwd" SFX),                               \
-    MI_BWD_STREAM(T, DT, MI_NORM_OP_LAYERNORM_BWD, "lnbwd" SFX),                               \
+    MI_BWD_STREAM(T, DT, MI_NORM_OP_LAYERNORM_BWD, "lnbwd" SFX, VW),                               \
     MI_BWD_VEC_RMS_##VW(T, DT, MI_NORM_OP_RMSNORM_BWD, "rmsbwd" SFX),                          \
     MI_BWD_SCALAR(T, DT, MI_NORM_OP_RMSNORM_BWD, "rmsbwd" SFX),                                \
-    MI_BWD_STREAM(T, DT, MI_NORM_OP_RMSNORM_BWD, "rmsbwd" SFX)
+    MI_BWD_STREAM(T, DT, MI_NORM_OP_RMSNORM_BWD, "rmsbwd" SFX, VW)

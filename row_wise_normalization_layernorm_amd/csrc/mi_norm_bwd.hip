@@ -37,8 +37,7 @@ namespace {
 constexpr int64_t kMaxPartials = 256;
 constexpr int64_t kAlign = 256;        // workspace alignment and section alignment
 constexpr int64_t kMaxGrid = 1 << 20;  // grid cap of the statistics kernel's row loop
-constexpr int kStreamThreads = 256;    // norm_bwd_chunks<..., 4, 8>: 4 waves,
-constexpr int kStreamPerLane = 8;      //   8 elements per lane per row
+constexpr int kRowstatsU = 4;          // norm_bwd_rowstats: accesses per lane in flight
 
 inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 inline int64_t dpad_of(int64_t d) { return (d + 3) & ~int64_t(3); }
@@ -161,7 +160,7 @@ int select_bwd(const mi_norm_bwd_problem &P) {
             q = pick_q(nvec, 64 * wpr, qs + 1, (wpr == 8 ? nq : c) - 1);
         }
         if (q) return find_bwd(op, dt, W, 0, wpr, q);
-        return find_bwd(op, dt, 1, 1, 0, 0);
+        return find_bwd(op, dt, W, 1, 0, 0);
     }
     const int64_t n = P.d;
     static const int s1[] = {1, 2, 4, 8};
@@ -178,7 +177,7 @@ bool eligible_bwd(int id, const mi_norm_bwd_problem &P) {
     if (!V || !bshape_ok(P)) return false;
     const mi_norm_variant_info &v = V->info;
     if (v.op != bwd_opcode(P.op) || v.dtype != P.dtype) return false;
-    if (v.looped) return true;
+    if (v.looped) return v.vec == 1 || vec_layout(P);
     if (v.vec > 1) return vec_layout(P) && P.d <= v.max_d;
     return P.d <= v.max_d;
 }
@@ -233,17 +232,18 @@ mi_norm_status validate_bwd(const mi_norm_bwd_problem &P) {
     return MI_NORM_OK;
 }
 
-const void *rowstats_fn(int dtype, bool ln) {
+// the per-row statistics kernel of the streamed path, with the chunk
+// kernel's access width (vec 1, or 16 bytes)
+template <typename T, int VEC>
+const void *rowstats_of(bool ln) {
+    return ln ? reinterpret_cast<const void *>(&norm_bwd_rowstats<T, OP_LN, VEC, 4, kRowstatsU>)
+              : reinterpret_cast<const void *>(&norm_bwd_rowstats<T, OP_RMS, VEC, 4, kRowstatsU>);
+}
+const void *rowstats_fn(int dtype, bool ln, int vec) {
     switch (dtype) {
-    case MI_NORM_F32:
-        return ln ? reinterpret_cast<const void *>(&norm_bwd_rowstats<float, OP_LN, 4>)
-                  : reinterpret_cast<const void *>(&norm_bwd_rowstats<float, OP_RMS, 4>);
-    case MI_NORM_F16:
-        return ln ? reinterpret_cast<const void *>(&norm_bwd_rowstats<_Float16, OP_LN, 4>)
-                  : reinterpret_cast<const void *>(&norm_bwd_rowstats<_Float16, OP_RMS, 4>);
-    default:
-        return ln ? reinterpret_cast<const void *>(&norm_bwd_rowstats<__bf16, OP_LN, 4>)
-                  : reinterpret_cast<const void *>(&norm_bwd_rowstats<__bf16, OP_RMS, 4>);
+    case MI_NORM_F32: return vec > 1 ? rowstats_of<float, 4>(ln) : rowstats_of<float, 1>(ln);
+    case MI_NORM_F16: return vec > 1 ? rowstats_of<_Float16, 8>(ln) : rowstats_of<_Float16, 1>(ln);
+    default: return vec > 1 ? rowstats_of<__bf16, 8>(ln) : rowstats_of<__bf16, 1>(ln);
     }
 }
 
@@ -306,11 +306,12 @@ mi_norm_status run_bwd(int forced, const mi_norm_bwd_problem &P, hipStream_t str
         {
             const int64_t g = P.rows < kMaxGrid ? P.rows : kMaxGrid;
             void *args[] = {&K};
-            if (hipLaunchKernel(rowstats_fn(P.dtype, is_ln(P)), dim3((unsigned)g), dim3(256), args, 0, stream) !=
-                hipSuccess)
+            if (hipLaunchKernel(rowstats_fn(P.dtype, is_ln(P), V.info.vec), dim3((unsigned)g), dim3(256), args, 0,
+                                stream) != hipSuccess)
                 return MI_NORM_ERR_HIP;
         }
-        const int64_t chunk = (int64_t)kStreamThreads * kStreamPerLane;
+        // columns per workgroup: its lanes' accesses of one row
+        const int64_t chunk = (int64_t)V.info.waves_per_block * 64 * V.info.slots * V.info.vec;
         const int64_t gx = (P.d + chunk - 1) / chunk;
         int64_t nrb = 2048 / gx;
         if (nrb < 1) nrb = 1;
@@ -319,7 +320,8 @@ mi_norm_status run_bwd(int forced, const mi_norm_bwd_problem &P, hipStream_t str
         int64_t rows_per_block = (P.rows + nrb - 1) / nrb;
         nrb = (P.rows + rows_per_block - 1) / rows_per_block;
         void *args[] = {&K, &rows_per_block};
-        if (hipLaunchKernel(V.fn, dim3((unsigned)gx, (unsigned)nrb), dim3(kStreamThreads), args, 0, stream) !=
+        if (hipLaunchKernel(V.fn, dim3((unsigned)gx, (unsigned)nrb), dim3(V.info.waves_per_block * 64), args, 0,
+                            stream) !=
             hipSuccess)
             return MI_NORM_ERR_HIP;
         nblk = nrb;

@@ -253,7 +253,8 @@ def test_variant_table_is_consistent(L):
         assert n.startswith(BWD_PREFIX[v["op"]] + DTSFX[v["dtype"]]), n
         assert v["lanes_per_row"] == 64 and not v["peel"] and v["rows_per_lane"] == 1
         if v["looped"]:
-            assert v["max_d"] == 2**63 - 1 and v["vec"] == 1 and v["needs_aligned"] == 0
+            assert v["max_d"] == 2**63 - 1 and v["vec"] in (1, 16 // ESIZE[v["dtype"]])
+            assert v["needs_aligned"] == (1 if v["vec"] > 1 else 0)
             continue
         assert v["rows_per_block"] * v["waves_per_row"] == v["waves_per_block"]
         assert v["waves_per_block"] == 8 and n.endswith("_b8"), n
@@ -701,7 +702,9 @@ def test_bwd_dispatch(L):
     assert name(op=mn.OP_RMSNORM, rows=8192, d=8192) == "rmsbwd_4_w8_q4_b8"
     assert name(dtype=mn.MI_NORM_BF16, d=4096) == "lnbwd_bf16_8_w4_q2_b8"
     assert name(op=mn.OP_RMSNORM, d=16384) == "rmsbwd_4_w8_q8_b8"
-    assert name(d=16384) == "lnbwd_1_stream_b4_u8"           # past LayerNorm's 24 values per lane
+    assert name(d=16384) == "lnbwd_4_stream_b4_u2"           # past LayerNorm's 24 values per lane
+    assert name(dtype=mn.MI_NORM_BF16, d=16384) == "lnbwd_bf16_8_stream_b4_u1"
+    assert name(op=mn.OP_RMSNORM, d=32768) == "rmsbwd_4_stream_b4_u2"
     assert name(d=12288) == "lnbwd_4_w8_q6_b8"
     assert name(dtype=mn.MI_NORM_BF16, d=8192) == "lnbwd_bf16_8_w8_q2_b8"
     assert name(dtype=mn.MI_NORM_BF16, d=768) == "lnbwd_bf16_8_w1_q2_b8"
