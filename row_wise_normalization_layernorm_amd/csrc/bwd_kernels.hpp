@@ -202,7 +202,7 @@ void norm_bwd_held(BwdParams p)
     static_assert(VEC == 1 || VEC == 4 || (VEC == 8 && sizeof(T) == 2), "VEC");
     static_assert(WAVES % WPR == 0, "whole rows per workgroup");
     constexpr int RPB = WAVES / WPR;
-    static_assert(RPB == 1 || RPB == 2 || RPB == 4 || RPB == 8 || RPB == 16, "row slots meet in a binary tree");
+    static_assert(RPB == 1 || RPB == 2 || RPB == 4 || RPB == 8 || RPB == 16, "1, 2, 4, 8 or 16 row slots");
     constexpr int NG = (OP == OP_LN) ? 2 : 1;
     using VT = vf<VEC>;
     using DT = vd<VEC>;
