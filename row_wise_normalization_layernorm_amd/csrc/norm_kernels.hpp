@@ -1118,8 +1118,8 @@ void norm_multi(NormParams p)
 
 // ---------------------------------------------------------------------------
 // Streamed-row kernel for rows wider than the held variants cover: one
-// workgroup per row, the row read in chunks; LayerNorm reads x three times
-// (sum, centered sum of squares, output), RMSNorm twice.  VEC as above
+// workgroup per row, the row read in chunks, twice: the statistics, then the
+// output.  VEC as above
 // (no peel).  U accesses per lane per chunk are kept in flight.
 
 template <int WAVES>
@@ -1170,14 +1170,19 @@ void norm_looped(NormParams p)
             }
         };
 
-        // pass 1: sum (LayerNorm) or sum of squares (RMSNorm)
-        float s = 0.f;
+        // pass 1: RMSNorm the sum of squares; LayerNorm each lane's count,
+        // mean and centered sum of squares, the chunk in registers centered
+        // on its own mean and merged into the lane's running pair (Chan,
+        // Golub and LeVeque), so x is read once for the statistics
+        float s = 0.f, ln_n = 0.f, ln_m = 0.f;
         for (int k0 = 0; k0 < nvec; k0 += NT * U) {
             VT v[U];
+            bool ok[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int k = k0 + tid + NT * u;
-                v[u] = k < nvec ? value(k, false) : VT(0.f);
+                ok[u] = k < nvec;
+                v[u] = ok[u] ? value(k, false) : VT(0.f);
             }
             if constexpr (RES) {
                 if (hr) {
@@ -1189,30 +1194,39 @@ void norm_looped(NormParams p)
                     }
                 }
             }
-#pragma unroll
-            for (int u = 0; u < U; ++u) s += (OP == OP_LN) ? hsum(v[u]) : sq(v[u]);
-        }
-        const float S = block_sum<WAVES>(s, red, slot, wave, lane);
-
-        if constexpr (OP == OP_LN) {
-            mu = S * p.inv_d;
-            // pass 2: squared deviations around the mean
-            float m = 0.f;
-            for (int k0 = 0; k0 < nvec; k0 += NT * U) {
-                VT v[U];
-                bool ok[U];
+            if constexpr (OP == OP_LN) {
+                float c = 0.f, cs = 0.f;
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const int k = k0 + tid + NT * u;
-                    ok[u] = k < nvec;
-                    v[u] = ok[u] ? value(k, true) : VT(0.f);
+                    c += ok[u] ? (float)VEC : 0.f;
+                    cs += hsum(v[u]);
                 }
+                if (c > 0.f) {
+                    const float cm = cs / c;
+                    float c2 = 0.f;
 #pragma unroll
-                for (int u = 0; u < U; ++u) m += ok[u] ? csq(v[u], mu) : 0.f;
+                    for (int u = 0; u < U; ++u) c2 += ok[u] ? csq(v[u], cm) : 0.f;
+                    const float n1 = ln_n + c;
+                    const float dm = cm - ln_m;
+                    ln_m += dm * (c / n1);
+                    s += c2 + dm * dm * (ln_n * c / n1);
+                    ln_n = n1;
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; ++u) s += sq(v[u]);
             }
-            const float M2 = block_sum<WAVES>(m, red, slot, wave, lane);
+        }
+
+        if constexpr (OP == OP_LN) {
+            // the lanes' pairs merged: mean = sum n_l m_l / d, M2 = sum of
+            // M2_l + n_l (m_l - mean)^2
+            mu = block_sum<WAVES>(ln_n * ln_m, red, slot, wave, lane) * p.inv_d;
+            const float dl = ln_m - mu;
+            const float M2 = block_sum<WAVES>(s + ln_n * dl * dl, red, slot, wave, lane);
             rs = rsq(M2 * p.inv_d + p.eps);
         } else {
+            const float S = block_sum<WAVES>(s, red, slot, wave, lane);
             rs = rsq(S * p.inv_d + p.eps);
         }
 

@@ -220,6 +220,19 @@ def test_every_variant(torch_dev):
             run_case(torch, dev, op, x, params, variant=vid, r=r, **lay)
 
 
+@pytest.mark.parametrize("pattern", ["normal", "alternating", "tiny", "offset"])
+@pytest.mark.parametrize("op", ["layernorm", "add_layernorm"])
+def test_streamed_rows_patterns(torch_dev, op, pattern):
+    """Rows past the held variants (the streamed kernel, whose LayerNorm
+    statistics merge per-chunk centered sums) on the pages' four patterns."""
+    torch, dev = torch_dev
+    for rows, d in ((5, 40000), (3, 65536), (2, 98307)):
+        say(f"streamed {op} [{rows}x{d}] {pattern}")
+        x = wl.make_x(rows, d, pattern, [61, rows, d])
+        r = wl.make_x(rows, d, "normal", [62, rows, d]) if op.startswith("add_") else None
+        run_case(torch, dev, op, x, wl.make_affine(d, [61, d]), r=r, xo=0 if d % 4 == 0 else 1)
+
+
 # --- layouts, aliasing, ordering ---------------------------------------------
 
 @pytest.mark.parametrize("op", ["layernorm", "rmsnorm"])
