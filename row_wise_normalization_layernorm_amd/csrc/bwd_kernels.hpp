@@ -191,10 +191,11 @@ __device__ __forceinline__ vf<VEC> widen_raw(std::conditional_t<VEC == 1, uint32
 // the previous step's sums, which wait only for their own set.  The waves of
 // a row meet at a barrier every step, so without the second set a
 // workgroup's loads and its arithmetic never overlap (BF16 LayerNorm
-// [32768,8192] 320 against 273 us, [8192,3072] 61 against 56).  Rows of one
-// wave have no barrier; they keep the loop that prefetches the next row
-// into a copy (with the alternating sets [4096,768] ran 4% and
-// [65536,768] 6% slower).
+// [32768,8192] 320 against 273 us, [8192,3072] 61 against 56).  16-bit rows
+// of one wave take it too (BF16 LayerNorm [8192,512] 13.1 against 11.3 us,
+// [65536,768] 63.8 against 58.3, [4096,768] 2-3%).  Float32 rows of one
+// wave keep the loop that prefetches the next row into a copy (with the
+// alternating sets [4096,768] ran 4% and [65536,768] 6% slower).
 template <typename T, int OP, int VEC, int WPR, int Q, int WAVES>
 __global__ __launch_bounds__(WAVES * 64)
 void norm_bwd_held(BwdParams p)
@@ -206,7 +207,7 @@ void norm_bwd_held(BwdParams p)
     constexpr int NG = (OP == OP_LN) ? 2 : 1;
     using VT = vf<VEC>;
     using DT = vd<VEC>;
-    constexpr bool PIPE = WPR > 1 && VEC * Q <= 16;
+    constexpr bool PIPE = VEC * Q <= 16 && (WPR > 1 || VEC == 8);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
